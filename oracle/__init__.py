@@ -1,0 +1,197 @@
+"""CPU oracle for C = ReLU(A·B) with fp16 storage (binary64 accumulation).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  It shares no code with the HIP
+library under ``tiled_dense_gemm_05_amd`` and never imports it.
+
+The arithmetic lives in ``gemm_relu_oracle.c`` (plain C, compiled with gcc,
+no BLAS, no SIMD intrinsics, no fast-math); this module only builds it, loads it
+with ctypes and marshals numpy arrays.  What it computes, and the passages it
+follows, are stated at the top of the C file: the matmul_relu tile program in
+section 2 of the "TileLang paper reading" page (hotelren.com) and the serial,
+fp32-or-wider K accumulation in section 3.2 of the "tilelang practitioner's
+notes" page (dpshk.com).
+
+Every fp16 array here is passed as its raw bit patterns (``numpy.uint16``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gemm_relu_oracle.c")
+_LIB = os.path.join(_HERE, "_build", "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into ``oracle/_build/liboracle.so``."""
+    if not force and os.path.exists(_LIB):
+        return _LIB
+    os.makedirs(os.path.dirname(_LIB), exist_ok=True)
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11",
+           "-D_GNU_SOURCE", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm", "-lpthread"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    i64 = ctypes.c_int64
+    vp = ctypes.c_void_p
+    lib.oracle_dec16_array.argtypes = [vp, vp, i64]
+    lib.oracle_dec16_array.restype = None
+    lib.oracle_enc16_array.argtypes = [vp, vp, i64]
+    lib.oracle_enc16_array.restype = None
+    lib.oracle_relu_store_array.argtypes = [vp, vp, i64]
+    lib.oracle_relu_store_array.restype = None
+    lib.oracle_gemm_relu_f16.argtypes = [vp, vp, vp] + [i64] * 10 + [vp, vp, ctypes.c_int]
+    lib.oracle_gemm_relu_f16.restype = ctypes.c_int
+    lib.oracle_gemm_relu_f16_sampled.argtypes = [vp, vp] + [i64] * 5 + [vp, i64, vp, vp, vp,
+                                                                        ctypes.c_int]
+    lib.oracle_gemm_relu_f16_sampled.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def host_threads() -> int:
+    """Threads the oracle uses by default: the CPUs this process may run on."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _u16(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float16:
+        a = a.view(np.uint16)
+    if a.dtype != np.uint16:
+        raise TypeError("fp16 operands are passed as uint16 bit patterns")
+    return a
+
+
+def dec16(bits) -> np.ndarray:
+    """Exact binary16 -> binary64 decode of an array of bit patterns."""
+    b = _u16(bits)
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().oracle_dec16_array(_ptr(b), _ptr(out), b.size)
+    return out
+
+
+def enc16(x) -> np.ndarray:
+    """binary64 -> binary16 bit patterns, round to nearest, ties to even."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().oracle_enc16_array(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def relu_store(x) -> np.ndarray:
+    """ReLU (s if s > 0 else +0) followed by the fp16 store, on binary64 sums."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().oracle_relu_store_array(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def _check_extent(buf: np.ndarray, rows: int, cols: int, ld: int, stride: int, batch: int,
+                  name: str) -> None:
+    if rows == 0 or cols == 0 or batch == 0:
+        return
+    need = (batch - 1) * stride + (rows - 1) * ld + cols
+    if buf.size < need:
+        raise ValueError(f"{name} holds {buf.size} elements, layout needs {need}")
+
+
+def gemm_relu(A, B, M: int, N: int, K: int, lda: int | None = None, ldb: int | None = None,
+              ldc: int | None = None, batch: int = 1, sA: int | None = None,
+              sB: int | None = None, sC: int | None = None, C=None, want_sums: bool = False,
+              threads: int | None = None):
+    """Every output of C = ReLU(A·B), strided-batched.
+
+    A, B: flat uint16 arrays (fp16 bits) in the row-major layouts given by
+    lda / ldb and the batch strides sA / sB (elements).  C, if given, is a flat
+    uint16 array updated in place inside the M×N windows only; otherwise a new
+    one of (batch-1)*sC + (M-1)*ldc + N elements is returned.
+    With ``want_sums`` also returns the binary64 sums s and Σ|A_ik·B_kj|, each
+    shaped (batch, M, N).
+    """
+    lda = K if lda is None else lda
+    ldb = N if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    sA = M * lda if sA is None else sA
+    sB = K * ldb if sB is None else sB
+    sC = M * ldc if sC is None else sC
+    A = _u16(A).reshape(-1)
+    B = _u16(B).reshape(-1)
+    if M > 0 and N > 0:
+        _check_extent(A, M, K, lda, sA, batch, "A")
+        _check_extent(B, K, N, ldb, sB, batch, "B")
+    if C is None:
+        size = 0 if (M == 0 or N == 0 or batch == 0) else (batch - 1) * sC + (M - 1) * ldc + N
+        C = np.zeros(size, dtype=np.uint16)
+    else:
+        if C.dtype != np.uint16 or not C.flags.c_contiguous:
+            raise TypeError("C must be a contiguous uint16 array")
+        C = C.reshape(-1)
+    _check_extent(C, M, N, ldc, sC, batch, "C")
+    S = Sa = None
+    if want_sums:
+        S = np.zeros((batch, M, N), dtype=np.float64)
+        Sa = np.zeros((batch, M, N), dtype=np.float64)
+    rc = _load().oracle_gemm_relu_f16(
+        _ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc, sA, sB, sC, batch,
+        _ptr(S) if S is not None else None, _ptr(Sa) if Sa is not None else None,
+        host_threads() if threads is None else threads)
+    if rc != 0:
+        raise MemoryError("oracle ran out of memory")
+    if want_sums:
+        return C, S, Sa
+    return C
+
+
+def gemm_relu_sampled(A, B, K: int, lda: int, ldb: int, idx, sA: int = 0, sB: int = 0,
+                      threads: int | None = None):
+    """Outputs at chosen positions: idx is an (n, 3) int array of (b, i, j).
+
+    Returns (c_bits uint16[n], s float64[n], abs_sum float64[n]).  The caller
+    guarantees the positions lie inside the operands' layouts.
+    """
+    A = _u16(A).reshape(-1)
+    B = _u16(B).reshape(-1)
+    idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int64).reshape(-1, 3))
+    n = idx.shape[0]
+    if n:
+        bmax, imax, jmax = idx.max(axis=0)
+        if idx.min() < 0:
+            raise ValueError("negative index")
+        if K > 0:
+            if bmax * sA + imax * lda + K > A.size:
+                raise ValueError("sample outside A")
+            if bmax * sB + (K - 1) * ldb + jmax >= B.size:
+                raise ValueError("sample outside B")
+    out = np.zeros(n, dtype=np.uint16)
+    s = np.zeros(n, dtype=np.float64)
+    sa = np.zeros(n, dtype=np.float64)
+    _load().oracle_gemm_relu_f16_sampled(
+        _ptr(A), _ptr(B), K, lda, ldb, sA, sB, _ptr(idx), n, _ptr(out), _ptr(s), _ptr(sa),
+        host_threads() if threads is None else threads)
+    return out, s, sa

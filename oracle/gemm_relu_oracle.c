@@ -1,0 +1,308 @@
+/*
+ * CPU oracle for the fused GEMM + ReLU with fp16 storage.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may include, link or
+ * call this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header or table with the HIP
+ * library.
+ *
+ * What it computes (the definition, written out; no blocking or reordering):
+ *
+ *   for every batch b, row i < M, column j < N:
+ *     s  = sum_{k=0}^{K-1} dec(A[b][i*lda + k]) * dec(B[b][k*ldb + j])
+ *          accumulated in IEEE binary64, k ascending
+ *     r  = s if s > 0 else +0.0                                    (ReLU)
+ *     C[b][i*ldc + j] = enc(r)          binary64 -> binary16, round to nearest,
+ *                                       ties to even; |r| >= 65520 -> inf
+ *
+ * Sources on the pages:
+ *  - "TileLang paper reading" (hotelren.com page), section 2: the matmul_relu
+ *    tile program: A is a (M,K) fp16 tensor, B a (K,N) fp16 tensor, the block
+ *    accumulator is an fp32 fragment cleared to zero, K is walked tile by tile
+ *    and added into it, the accumulator is clamped at zero with a max against
+ *    0, then copied out to the fp16 C.  On a CPU the tile grid is only a pair
+ *    of outer loops, so tiling does not change the value computed.
+ *  - "tilelang practitioner's notes" (dpshk.com page), section 3.2: the K loop
+ *    is a serial accumulation into one accumulator, and the accumulator is kept
+ *    in a wider type than fp16 because fp16 accumulation is too inexact.
+ * The oracle accumulates in binary64 (wider than the kernel's fp32), so it is
+ * the exact sum up to binary64 rounding; the kernel is expected to agree within
+ * fp32 summation error plus one fp16 rounding.
+ *
+ * Readings where the pages are silent:
+ *  - ReLU maps s <= 0 (and NaN) to +0.0, the behaviour of max(x, 0) taken as
+ *    "x if x > 0 else 0".
+ *  - The fp16 store rounds to nearest even (the IEEE default conversion).
+ *  - Subnormal fp16 inputs and outputs are exact (no flushing).
+ *
+ * Also exported: dec/enc on arrays (for the pins in the tests), a sampled
+ * variant that computes chosen (b, i, j) outputs one by one, and the optional
+ * per-element s and sum_k |A_ik * B_kj| used by the fp32 error-bound gate.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* binary16 bit pattern -> exact binary64 value. */
+static double dec16(uint16_t h)
+{
+    int sign = h >> 15;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);                 /* subnormal: m * 2^-24 */
+    else if (e < 31)
+        v = ldexp((double)(1024 + m), e - 25);     /* (1 + m/1024) * 2^(e-15) */
+    else
+        v = m ? NAN : INFINITY;
+    return sign ? -v : v;
+}
+
+/* Round a non-negative binary64 value q to an integer, ties to even.  q is at
+ * most 2^12 here, so q - floor(q) is exact. */
+static double round_half_even(double q)
+{
+    double f = floor(q);
+    double d = q - f;
+    if (d > 0.5)
+        return f + 1.0;
+    if (d < 0.5)
+        return f;
+    return fmod(f, 2.0) == 0.0 ? f : f + 1.0;
+}
+
+/* binary64 -> binary16 bit pattern, round to nearest, ties to even. */
+static uint16_t enc16(double x)
+{
+    if (isnan(x))
+        return 0x7e00;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    /* 65504 is the largest finite half; 65520 is the midpoint to 2^16 and ties
+     * to the even neighbour, which is 2^16, i.e. infinity. */
+    if (a >= 65520.0)
+        return sign | 0x7c00;
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal range: the quantum is 2^-24.  A result of 1024 is the
+         * smallest normal, whose encoding is exactly 0x0400. */
+        double q = round_half_even(ldexp(a, 24));
+        return sign | (uint16_t)q;
+    }
+    int e;
+    frexp(a, &e);                 /* a in [2^(e-1), 2^e) */
+    double q = round_half_even(ldexp(a, 11 - e));   /* in [1024, 2048] */
+    /* biased exponent of a is (e - 1) + 15; q == 2048 carries into it. */
+    uint32_t bits = ((uint32_t)(e + 14) << 10) + ((uint32_t)q - 1024u);
+    return sign | (uint16_t)bits;
+}
+
+/* ReLU on the exact accumulator, then the fp16 store. */
+static uint16_t relu_store(double s)
+{
+    double r = (s > 0.0) ? s : 0.0;
+    return enc16(r);
+}
+
+/* The K-sum for one output: a[k] * b[k], k ascending, in binary64. */
+static double dot_k(const double *a, const double *b, int64_t K, double *abs_out)
+{
+    double s = 0.0, sa = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double p = a[k] * b[k];   /* exact: two 11-bit significands */
+        s += p;
+        sa += fabs(p);
+    }
+    if (abs_out)
+        *abs_out = sa;
+    return s;
+}
+
+/* ------------------------------------------------------------------------ */
+
+void oracle_dec16_array(const uint16_t *in, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = dec16(in[i]);
+}
+
+void oracle_enc16_array(const double *in, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = enc16(in[i]);
+}
+
+void oracle_relu_store_array(const double *in, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = relu_store(in[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const uint16_t *A, *B;
+    uint16_t *C;
+    double *S, *Sabs;         /* optional, batch*M*N, contiguous */
+    int64_t M, N, K, lda, ldb, ldc, sA, sB, sC;
+    const double *Bt;         /* this batch's B decoded and laid out as (N,K) */
+    int64_t b;                /* current batch */
+    int nthreads;
+    int tid;
+} job_t;
+
+static void *row_worker(void *p)
+{
+    job_t *j = (job_t *)p;
+    double *arow = (double *)malloc(sizeof(double) * (size_t)(j->K > 0 ? j->K : 1));
+    const uint16_t *A = j->A + j->b * j->sA;
+    uint16_t *C = j->C + j->b * j->sC;
+    for (int64_t i = j->tid; i < j->M; i += j->nthreads) {
+        for (int64_t k = 0; k < j->K; ++k)
+            arow[k] = dec16(A[i * j->lda + k]);
+        for (int64_t n = 0; n < j->N; ++n) {
+            double sabs;
+            double s = dot_k(arow, j->Bt + n * j->K, j->K, &sabs);
+            C[i * j->ldc + n] = relu_store(s);
+            if (j->S) {
+                int64_t o = (j->b * j->M + i) * j->N + n;
+                j->S[o] = s;
+                j->Sabs[o] = sabs;
+            }
+        }
+    }
+    free(arow);
+    return NULL;
+}
+
+static int clamp_threads(int nthreads)
+{
+    if (nthreads <= 0) {
+        long n = sysconf(_SC_NPROCESSORS_ONLN);
+        nthreads = n > 0 ? (int)n : 1;
+    }
+    if (nthreads > 256)
+        nthreads = 256;
+    return nthreads;
+}
+
+/*
+ * Full computation of every output.  Strides and leading dimensions are in
+ * elements.  S and Sabs may be NULL; when given they receive the binary64 sum
+ * and the sum of absolute products for every (b, i, j), laid out contiguously
+ * as [batch][M][N].  Returns 0, or -1 when memory runs out.
+ */
+int oracle_gemm_relu_f16(const uint16_t *A, const uint16_t *B, uint16_t *C,
+                         int64_t M, int64_t N, int64_t K,
+                         int64_t lda, int64_t ldb, int64_t ldc,
+                         int64_t sA, int64_t sB, int64_t sC, int64_t batch,
+                         double *S, double *Sabs, int nthreads)
+{
+    nthreads = clamp_threads(nthreads);
+    if (M <= 0 || N <= 0 || batch <= 0)
+        return 0;
+    double *Bt = (double *)malloc(sizeof(double) * (size_t)N * (size_t)(K > 0 ? K : 1));
+    if (!Bt)
+        return -1;
+    pthread_t th[256];
+    job_t jobs[256];
+    for (int64_t b = 0; b < batch; ++b) {
+        const uint16_t *Bb = B + b * sB;
+        /* a copy of B in (N,K) order, so that each output's k-loop reads
+         * contiguous memory; the values and their order of use are unchanged */
+        for (int64_t k = 0; k < K; ++k)
+            for (int64_t n = 0; n < N; ++n)
+                Bt[n * K + k] = dec16(Bb[k * ldb + n]);
+        int nt = (int)(M < nthreads ? M : nthreads);
+        for (int t = 0; t < nt; ++t) {
+            job_t *j = &jobs[t];
+            j->A = A; j->B = B; j->C = C; j->S = S; j->Sabs = Sabs;
+            j->M = M; j->N = N; j->K = K; j->lda = lda; j->ldb = ldb; j->ldc = ldc;
+            j->sA = sA; j->sB = sB; j->sC = sC; j->Bt = Bt; j->b = b;
+            j->nthreads = nt; j->tid = t;
+            if (nt == 1)
+                row_worker(j);
+            else
+                pthread_create(&th[t], NULL, row_worker, j);
+        }
+        if (nt > 1)
+            for (int t = 0; t < nt; ++t)
+                pthread_join(th[t], NULL);
+    }
+    free(Bt);
+    return 0;
+}
+
+/*
+ * Sampled computation: out[q] = C[b][i][j] for the q-th triple (b, i, j) in
+ * idx (3*n int64 values).  s_out / abs_out (optional) receive the binary64 sum
+ * and the sum of absolute products.  Same arithmetic as the full version.
+ */
+typedef struct {
+    const uint16_t *A, *B;
+    int64_t K, lda, ldb, sA, sB;
+    const int64_t *idx;
+    int64_t n;
+    uint16_t *out;
+    double *s_out, *abs_out;
+    int nthreads, tid;
+} sjob_t;
+
+static void *sample_worker(void *p)
+{
+    sjob_t *j = (sjob_t *)p;
+    int64_t K = j->K;
+    double *a = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    double *bcol = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    for (int64_t q = j->tid; q < j->n; q += j->nthreads) {
+        int64_t b = j->idx[3 * q], i = j->idx[3 * q + 1], c = j->idx[3 * q + 2];
+        const uint16_t *Ar = j->A + b * j->sA + i * j->lda;
+        const uint16_t *Bc = j->B + b * j->sB + c;
+        for (int64_t k = 0; k < K; ++k) {
+            a[k] = dec16(Ar[k]);
+            bcol[k] = dec16(Bc[k * j->ldb]);
+        }
+        double sabs;
+        double s = dot_k(a, bcol, K, &sabs);
+        j->out[q] = relu_store(s);
+        if (j->s_out)
+            j->s_out[q] = s;
+        if (j->abs_out)
+            j->abs_out[q] = sabs;
+    }
+    free(a);
+    free(bcol);
+    return NULL;
+}
+
+int oracle_gemm_relu_f16_sampled(const uint16_t *A, const uint16_t *B,
+                                 int64_t K, int64_t lda, int64_t ldb,
+                                 int64_t sA, int64_t sB,
+                                 const int64_t *idx, int64_t n,
+                                 uint16_t *out, double *s_out, double *abs_out,
+                                 int nthreads)
+{
+    nthreads = clamp_threads(nthreads);
+    if (n <= 0)
+        return 0;
+    int nt = (int)(n < nthreads ? n : nthreads);
+    pthread_t th[256];
+    sjob_t jobs[256];
+    for (int t = 0; t < nt; ++t) {
+        sjob_t *j = &jobs[t];
+        j->A = A; j->B = B; j->K = K; j->lda = lda; j->ldb = ldb;
+        j->sA = sA; j->sB = sB; j->idx = idx; j->n = n; j->out = out;
+        j->s_out = s_out; j->abs_out = abs_out; j->nthreads = nt; j->tid = t;
+        if (nt == 1)
+            sample_worker(j);
+        else
+            pthread_create(&th[t], NULL, sample_worker, j);
+    }
+    if (nt > 1)
+        for (int t = 0; t < nt; ++t)
+            pthread_join(th[t], NULL);
+    return 0;
+}
