@@ -1,0 +1,117 @@
+/*
+ * tg.h -- C ABI of the MI355X (gfx950) fused fp16 GEMM + ReLU library.
+ *
+ * The operation is the GEMM+ReLU tile program of the "TileLang paper reading"
+ * page (hotelren.com), section 2: A is an (M,K) fp16 tensor, B a (K,N) fp16
+ * tensor, the product is accumulated in an fp32 fragment that starts at zero,
+ * is clamped below at zero, and is stored into the (M,N) fp16 output.  The
+ * "tilelang practitioner's notes" page (dpshk.com), sections 3.2-3.3, adds
+ * that K is a serial accumulation in a type wider than fp16 and that the
+ * compiled kernel is called on device tensors and may run asynchronously.
+ *
+ *   C[i*ldc + j] = fp16_rne( max(0, sum_k A[i*lda + k] * B[k*ldb + j]) )
+ *
+ * with the sum in fp32 (order of summation unspecified), ReLU mapping every
+ * value that is not > 0 to +0.0, and the fp32 -> fp16 conversion rounding to
+ * nearest, ties to even, with subnormals kept.
+ *
+ * Conventions shared by every entry point:
+ *  - Elements are IEEE binary16; A, B, C are DEVICE pointers (void* so that a
+ *    framework's data pointer passes straight through).  All matrices are
+ *    row-major with leading dimensions in elements.
+ *  - Ownership: the caller owns A, B and C.  The library allocates nothing per
+ *    call and keeps no pointer after it returns.
+ *  - Asynchrony: work is enqueued on `stream` (0 = the default stream) and the
+ *    call returns without waiting; the buffers must stay alive until the
+ *    stream reaches the call.  Calls are reentrant.
+ *  - Errors are returned, never thrown.  Argument errors are detected before
+ *    any HIP call.  M = 0, N = 0 or batch = 0 is a no-op returning TG_OK;
+ *    K = 0 writes +0.0 to the whole M x N window (the empty sum).
+ *  - Only the M x N window of C is written; the ldc padding is untouched.
+ *    C overlapping A or B is undefined.
+ *  - Any 2-byte-aligned pointer and any leading dimension are accepted;
+ *    16-byte-aligned pointers with leading dimensions and N, K that are
+ *    multiples of 8 take the fastest kernels.
+ *  - Results are deterministic: the same inputs, shape and device give the
+ *    same bits on every call (no floating-point atomics).
+ */
+#ifndef TG_H
+#define TG_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TG_OK = 0,
+    TG_ERR_INVALID_ARG = 1,         /* bad size, leading dimension, stride or null pointer */
+    TG_ERR_NO_DEVICE = 2,           /* no HIP device is usable from this process */
+    TG_ERR_UNSUPPORTED_DEVICE = 3,  /* the current device is not gfx950 */
+    TG_ERR_HIP = 4                  /* a HIP runtime call or kernel launch failed */
+} tg_status;
+
+/*
+ * C = ReLU(A * B) for one matrix.
+ *   A      (M,K) fp16, row-major, leading dimension lda >= max(1,K)
+ *   B      (K,N) fp16, row-major, leading dimension ldb >= max(1,N)
+ *   C      (M,N) fp16, row-major, leading dimension ldc >= max(1,N)
+ *   M,N,K  sizes, each in [0, 2^31 - 1]
+ * A and B may be NULL only when the matrix they hold is empty (M*K == 0,
+ * K*N == 0); C may be NULL only when M*N == 0.
+ * Returns a tg_status.
+ */
+int tg_gemm_relu_f16(const void *A, const void *B, void *C,
+                     int64_t M, int64_t N, int64_t K,
+                     int64_t lda, int64_t ldb, int64_t ldc,
+                     hipStream_t stream);
+
+/*
+ * Strided-batched form: for b in [0, batch),
+ *   C + b*strideC = ReLU((A + b*strideA) * (B + b*strideB))
+ * with each slice laid out as in tg_gemm_relu_f16.  Strides are in elements;
+ * strideA or strideB may be 0 (the operand is shared by every slice).  When
+ * batch > 1 the C slices must not overlap: |strideC| >= (M-1)*ldc + N.
+ * batch is in [0, 2^31 - 1].
+ */
+int tg_gemm_relu_f16_strided_batched(const void *A, const void *B, void *C,
+                                     int64_t M, int64_t N, int64_t K,
+                                     int64_t lda, int64_t ldb, int64_t ldc,
+                                     int64_t strideA, int64_t strideB, int64_t strideC,
+                                     int64_t batch, hipStream_t stream);
+
+/* A static, human-readable name for a tg_status value. */
+const char *tg_status_string(int status);
+
+/*
+ * Kernel-path selection, for tests and benchmarks.  TG_PATH_AUTO (the default)
+ * lets the library pick from the shape and alignment; any other value forces
+ * that path for every later call in the process (a path that cannot serve a
+ * call's alignment falls back to TG_PATH_GENERIC).  tg_set_path returns the
+ * previous setting, or -1 for an unknown path (the setting is unchanged).
+ */
+enum {
+    TG_PATH_AUTO = 0,
+    TG_PATH_NAIVE = 1,      /* one thread per output; a slow, plain kernel */
+    TG_PATH_GENERIC = 2,    /* 128x128 tiles, any alignment, masked loads */
+    TG_PATH_TILE128 = 3,    /* 128x128x32 tiles, 256 threads, aligned operands */
+    TG_PATH_TILE256 = 4,    /* 256x256 tiles for large shapes, aligned operands */
+    TG_PATH_SKINNY = 5,     /* M <= 64: narrow-N slices streaming B, aligned */
+    TG_PATH_COUNT = 6
+};
+int tg_set_path(int path);
+
+/* The path the most recent successful launch from this process used. */
+int tg_last_path(void);
+
+/* A static name for a path number ("auto", "naive", ...), or "unknown". */
+const char *tg_path_name(int path);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TG_H */

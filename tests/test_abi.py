@@ -1,0 +1,114 @@
+"""The C-ABI library on the CPU: it loads, exports what include/tg.h declares,
+and rejects bad arguments before touching HIP (no GPU is needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tg.h")
+
+
+@pytest.fixture(scope="module")
+def tg():
+    import tiled_dense_gemm_05_amd as tg
+    return tg
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(tg_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    assert "tg_gemm_relu_f16" in names and "tg_gemm_relu_f16_strided_batched" in names
+    assert len(names) >= 6
+
+
+def test_every_declared_symbol_is_exported(tg):
+    lib = ctypes.CDLL(tg.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert set(_declared_functions()) == set(tg.EXPORTED_SYMBOLS)
+
+
+def test_status_strings(tg):
+    assert tg.tg_status_string(0) == "TG_OK"
+    for s in range(1, 5):
+        assert tg.tg_status_string(s).startswith("TG_ERR_")
+    assert "unknown" in tg.tg_status_string(99)
+
+
+def test_path_control(tg):
+    assert tg.tg_path_name(tg.TG_PATH_TILE128) == "tile128"
+    assert tg.tg_path_name(77) == "unknown"
+    prev = tg.tg_set_path(tg.TG_PATH_NAIVE)
+    assert prev == tg.TG_PATH_AUTO
+    assert tg.tg_set_path(tg.TG_PATH_AUTO) == tg.TG_PATH_NAIVE
+    assert tg.tg_set_path(-1) == -1 and tg.tg_set_path(99) == -1
+
+
+P = 0x10000  # a fake, 16-byte aligned device address; never dereferenced here
+
+INVALID = [
+    # (M, N, K, lda, ldb, ldc)
+    (-1, 4, 4, 4, 4, 4),
+    (4, -1, 4, 4, 4, 4),
+    (4, 4, -1, 4, 4, 4),
+    (4, 4, 8, 7, 4, 4),          # lda < K
+    (4, 8, 4, 4, 7, 8),          # ldb < N
+    (4, 8, 4, 4, 8, 7),          # ldc < N
+    (2 ** 31, 4, 4, 4, 4, 4),    # too large
+    (4, 4, 4, 0, 4, 4),
+]
+
+
+@pytest.mark.parametrize("args", INVALID)
+def test_invalid_sizes(tg, args):
+    M, N, K, lda, ldb, ldc = args
+    assert tg.tg_gemm_relu_f16(P, P, P, M, N, K, lda, ldb, ldc, 0) == tg.TG_ERR_INVALID_ARG
+
+
+def test_null_pointers(tg):
+    assert tg.tg_gemm_relu_f16(0, P, P, 4, 4, 4, 4, 4, 4, 0) == tg.TG_ERR_INVALID_ARG
+    assert tg.tg_gemm_relu_f16(P, 0, P, 4, 4, 4, 4, 4, 4, 0) == tg.TG_ERR_INVALID_ARG
+    assert tg.tg_gemm_relu_f16(P, P, 0, 4, 4, 4, 4, 4, 4, 0) == tg.TG_ERR_INVALID_ARG
+
+
+def test_empty_calls_are_noops(tg):
+    # no HIP call happens for an empty problem, so these succeed without a GPU
+    assert tg.tg_gemm_relu_f16(0, 0, 0, 0, 5, 3, 3, 5, 5, 0) == tg.TG_OK
+    assert tg.tg_gemm_relu_f16(0, 0, 0, 5, 0, 3, 3, 1, 1, 0) == tg.TG_OK
+    assert tg.tg_gemm_relu_f16_strided_batched(0, 0, 0, 4, 4, 4, 4, 4, 4, 16, 16, 16, 0,
+                                               0) == tg.TG_OK
+
+
+def test_batched_validation(tg):
+    f = tg.tg_gemm_relu_f16_strided_batched
+    assert f(P, P, P, 4, 4, 4, 4, 4, 4, 16, 16, 16, -1, 0) == tg.TG_ERR_INVALID_ARG
+    # C slices would overlap
+    assert f(P, P, P, 4, 4, 4, 4, 4, 4, 16, 16, 15, 2, 0) == tg.TG_ERR_INVALID_ARG
+    assert f(P, P, P, 4, 4, 4, 4, 4, 4, 16, 16, -15, 2, 0) == tg.TG_ERR_INVALID_ARG
+    # an address range beyond 2^62 elements
+    assert f(P, P, P, 4, 4, 4, 4, 4, 4, 2 ** 62, 16, 16, 2, 0) == tg.TG_ERR_INVALID_ARG
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="checks the no-device error on a host without a GPU")
+def test_valid_call_without_device_reports_no_device(tg):
+    st = tg.tg_gemm_relu_f16(P, P, P, 4, 4, 4, 4, 4, 4, 0)
+    assert st == tg.TG_ERR_NO_DEVICE
+    # K = 0 with null operands is valid and also reaches the device check
+    st = tg.tg_gemm_relu_f16(0, 0, P, 4, 4, 0, 1, 4, 4, 0)
+    assert st == tg.TG_ERR_NO_DEVICE

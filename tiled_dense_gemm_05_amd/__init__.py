@@ -1,0 +1,175 @@
+"""Python binding of the MI355X fused fp16 GEMM + ReLU library (``libtg.so``).
+
+Argument marshalling only: every step of C = ReLU(A·B) runs in the HIP kernels
+behind the C ABI declared in ``include/tg.h``.  The functions named like the
+C entry points take raw device pointers and sizes; ``gemm_relu`` and
+``gemm_relu_strided_batched`` accept torch tensors (torch provides device
+memory and streams only).  There is no fallback: if the library is not built,
+importing this package raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtg.so")
+
+TG_OK = 0
+TG_ERR_INVALID_ARG = 1
+TG_ERR_NO_DEVICE = 2
+TG_ERR_UNSUPPORTED_DEVICE = 3
+TG_ERR_HIP = 4
+
+TG_PATH_AUTO = 0
+TG_PATH_NAIVE = 1
+TG_PATH_GENERIC = 2
+TG_PATH_TILE128 = 3
+TG_PATH_TILE256 = 4
+TG_PATH_SKINNY = 5
+TG_PATH_COUNT = 6
+
+EXPORTED_SYMBOLS = (
+    "tg_gemm_relu_f16",
+    "tg_gemm_relu_f16_strided_batched",
+    "tg_status_string",
+    "tg_set_path",
+    "tg_last_path",
+    "tg_path_name",
+)
+
+
+class TGError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(tg_status_string(status))
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m tiled_dense_gemm_05_amd.build` "
+        "(there is no CPU fallback)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_lib.tg_gemm_relu_f16.argtypes = [_vp, _vp, _vp] + [_i64] * 6 + [_vp]
+_lib.tg_gemm_relu_f16.restype = ctypes.c_int
+_lib.tg_gemm_relu_f16_strided_batched.argtypes = [_vp, _vp, _vp] + [_i64] * 10 + [_vp]
+_lib.tg_gemm_relu_f16_strided_batched.restype = ctypes.c_int
+_lib.tg_status_string.argtypes = [ctypes.c_int]
+_lib.tg_status_string.restype = ctypes.c_char_p
+_lib.tg_set_path.argtypes = [ctypes.c_int]
+_lib.tg_set_path.restype = ctypes.c_int
+_lib.tg_last_path.argtypes = []
+_lib.tg_last_path.restype = ctypes.c_int
+_lib.tg_path_name.argtypes = [ctypes.c_int]
+_lib.tg_path_name.restype = ctypes.c_char_p
+
+
+# ----------------------------------------------------------- C-ABI mirror
+
+
+def tg_gemm_relu_f16(A: int, B: int, C: int, M: int, N: int, K: int, lda: int, ldb: int,
+                     ldc: int, stream: int = 0) -> int:
+    """Raw call: device pointers as ints, returns the tg_status code."""
+    return _lib.tg_gemm_relu_f16(A, B, C, M, N, K, lda, ldb, ldc, stream)
+
+
+def tg_gemm_relu_f16_strided_batched(A: int, B: int, C: int, M: int, N: int, K: int, lda: int,
+                                     ldb: int, ldc: int, strideA: int, strideB: int,
+                                     strideC: int, batch: int, stream: int = 0) -> int:
+    """Raw strided-batched call, returns the tg_status code."""
+    return _lib.tg_gemm_relu_f16_strided_batched(A, B, C, M, N, K, lda, ldb, ldc, strideA,
+                                                 strideB, strideC, batch, stream)
+
+
+def tg_status_string(status: int) -> str:
+    return _lib.tg_status_string(status).decode()
+
+
+def tg_set_path(path: int) -> int:
+    return _lib.tg_set_path(path)
+
+
+def tg_last_path() -> int:
+    return _lib.tg_last_path()
+
+
+def tg_path_name(path: int) -> str:
+    return _lib.tg_path_name(path).decode()
+
+
+# ----------------------------------------------------------- torch helpers
+
+
+def _check(status: int) -> None:
+    if status != TG_OK:
+        raise TGError(status)
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _row_major_2d(t, name):
+    import torch
+    if t.dtype != torch.float16:
+        raise TypeError(f"{name} must be float16")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.stride(1) != 1 and t.size(1) > 1:
+        raise ValueError(f"{name} must have unit column stride (row-major)")
+    return max(t.stride(0), 1)
+
+
+def gemm_relu(A, B, out=None, stream=None):
+    """C = ReLU(A @ B) for 2-D fp16 device tensors with unit column stride.
+
+    ``out`` (optional) is an (M, N) fp16 tensor with unit column stride; its
+    leading dimension is taken from its row stride.  Enqueued on ``stream``
+    (default: torch's current stream); returns ``out``.
+    """
+    import torch
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError(f"inner sizes differ: {tuple(A.shape)} @ {tuple(B.shape)}")
+    lda = _row_major_2d(A, "A") if M and K else max(K, 1)
+    ldb = _row_major_2d(B, "B") if K and N else max(N, 1)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    ldc = _row_major_2d(out, "out") if M and N else max(N, 1)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out has the wrong shape")
+    _check(tg_gemm_relu_f16(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K,
+                            max(lda, K, 1), max(ldb, N, 1), max(ldc, N, 1),
+                            _stream_handle(stream)))
+    return out
+
+
+def gemm_relu_strided_batched(A, B, out=None, stream=None):
+    """C[b] = ReLU(A[b] @ B[b]) for 3-D fp16 device tensors (batch, rows, cols)
+    with unit column stride; batch strides come from the tensors' strides (a
+    stride of 0, e.g. from ``expand``, shares one operand across the batch)."""
+    import torch
+    bt, M, K = A.shape
+    bt2, K2, N = B.shape
+    if bt2 != bt or K2 != K:
+        raise ValueError(f"shapes do not match: {tuple(A.shape)} @ {tuple(B.shape)}")
+    if out is None:
+        out = torch.empty((bt, M, N), dtype=torch.float16, device=A.device)
+    for t, name in ((A, "A"), (B, "B"), (out, "out")):
+        if t.dtype != torch.float16:
+            raise TypeError(f"{name} must be float16")
+        if t.stride(2) != 1 and t.size(2) > 1:
+            raise ValueError(f"{name} must have unit column stride")
+    _check(tg_gemm_relu_f16_strided_batched(
+        A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K,
+        max(A.stride(1), K, 1), max(B.stride(1), N, 1), max(out.stride(1), N, 1),
+        A.stride(0), B.stride(0), out.stride(0), bt, _stream_handle(stream)))
+    return out

@@ -1,0 +1,203 @@
+// C ABI of the library: argument validation, device checks, kernel-path
+// selection and launch.  Declarations and the contract are in include/tg.h.
+#include "tg.h"
+
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+
+#include "tg_internal.h"
+
+namespace {
+
+std::atomic<int> g_forced_path{TG_PATH_AUTO};
+std::atomic<int> g_last_path{TG_PATH_AUTO};
+
+// Per-device architecture check, done once per device: 0 unknown, 1 gfx950,
+// 2 something else.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_state[kMaxDevices];
+
+constexpr int64_t kMaxDim = 0x7fffffff;
+constexpr __int128 kMaxExtent = (__int128)1 << 62;
+
+int check_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return TG_ERR_NO_DEVICE;
+    }
+    if (dev >= kMaxDevices)
+        return TG_ERR_UNSUPPORTED_DEVICE;
+    int st = g_arch_state[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return TG_ERR_NO_DEVICE;
+        }
+        st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_arch_state[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? TG_OK : TG_ERR_UNSUPPORTED_DEVICE;
+}
+
+// Largest element offset touched by a strided-batched operand, or -1 when it
+// is too large to address.
+__int128 extent(int64_t rows, int64_t cols, int64_t ld, int64_t stride, int64_t batch)
+{
+    if (rows == 0 || cols == 0 || batch == 0)
+        return 0;
+    __int128 s = stride < 0 ? -(__int128)stride : (__int128)stride;
+    return (__int128)(batch - 1) * s + (__int128)(rows - 1) * ld + cols;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int validate(const void *A, const void *B, const void *C, int64_t M, int64_t N, int64_t K,
+             int64_t lda, int64_t ldb, int64_t ldc, int64_t sA, int64_t sB, int64_t sC,
+             int64_t batch)
+{
+    if (M < 0 || N < 0 || K < 0 || batch < 0)
+        return TG_ERR_INVALID_ARG;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim || batch > kMaxDim)
+        return TG_ERR_INVALID_ARG;
+    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+        return TG_ERR_INVALID_ARG;
+    if (M == 0 || N == 0 || batch == 0)
+        return TG_OK;
+    if (C == nullptr)
+        return TG_ERR_INVALID_ARG;
+    if (K > 0 && (A == nullptr || B == nullptr))
+        return TG_ERR_INVALID_ARG;
+    if (extent(M, K, lda, sA, batch) > kMaxExtent || extent(K, N, ldb, sB, batch) > kMaxExtent ||
+        extent(M, N, ldc, sC, batch) > kMaxExtent)
+        return TG_ERR_INVALID_ARG;
+    if (batch > 1) {
+        const __int128 span = (__int128)(M - 1) * ldc + N;
+        const __int128 s = sC < 0 ? -(__int128)sC : (__int128)sC;
+        if (s < span)
+            return TG_ERR_INVALID_ARG;
+    }
+    return TG_OK;
+}
+
+// Whether the 16-byte-chunk kernels can serve this call.
+bool fast_layout(const tg::GemmArgs &p)
+{
+    if (!aligned16(p.A) || !aligned16(p.B) || !aligned16(p.C))
+        return false;
+    if ((p.lda | p.ldb | p.ldc | p.N | p.K) & 7)
+        return false;
+    if (p.batch > 1 && ((p.sA | p.sB | p.sC) & 7))
+        return false;
+    return p.K > 0;
+}
+
+int choose_path(const tg::GemmArgs &p)
+{
+    if (!fast_layout(p))
+        return TG_PATH_GENERIC;
+    const int64_t tiles256 = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
+    if (tiles256 >= 1024)
+        return TG_PATH_TILE256;
+    return TG_PATH_TILE128;
+}
+
+int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int64_t lda,
+        int64_t ldb, int64_t ldc, int64_t sA, int64_t sB, int64_t sC, int64_t batch,
+        hipStream_t stream)
+{
+    int st = validate(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch);
+    if (st != TG_OK)
+        return st;
+    if (M == 0 || N == 0 || batch == 0)
+        return TG_OK;
+    st = check_device();
+    if (st != TG_OK)
+        return st;
+
+    tg::GemmArgs p;
+    p.A = static_cast<const uint16_t *>(A);
+    p.B = static_cast<const uint16_t *>(B);
+    p.C = static_cast<uint16_t *>(C);
+    p.M = M; p.N = N; p.K = K;
+    p.lda = lda; p.ldb = ldb; p.ldc = ldc;
+    p.sA = batch > 1 ? sA : 0;
+    p.sB = batch > 1 ? sB : 0;
+    p.sC = batch > 1 ? sC : 0;
+    p.batch = batch;
+
+    int path = g_forced_path.load(std::memory_order_relaxed);
+    if (path == TG_PATH_AUTO)
+        path = choose_path(p);
+    else if (path != TG_PATH_NAIVE && path != TG_PATH_GENERIC && !fast_layout(p))
+        path = TG_PATH_GENERIC;
+
+    hipError_t e;
+    switch (path) {
+    case TG_PATH_NAIVE: e = tg::launch_naive(p, stream); break;
+    case TG_PATH_TILE128: e = tg::launch_tile128(p, stream); break;
+    case TG_PATH_TILE256: e = tg::launch_tile256(p, stream); break;
+    default: e = tg::launch_generic(p, stream); path = TG_PATH_GENERIC; break;
+    }
+    if (e != hipSuccess)
+        return TG_ERR_HIP;
+    g_last_path.store(path, std::memory_order_relaxed);
+    return TG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tg_gemm_relu_f16(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
+                     int64_t lda, int64_t ldb, int64_t ldc, hipStream_t stream)
+{
+    return run(A, B, C, M, N, K, lda, ldb, ldc, 0, 0, 0, 1, stream);
+}
+
+int tg_gemm_relu_f16_strided_batched(const void *A, const void *B, void *C, int64_t M, int64_t N,
+                                     int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                                     int64_t strideA, int64_t strideB, int64_t strideC,
+                                     int64_t batch, hipStream_t stream)
+{
+    return run(A, B, C, M, N, K, lda, ldb, ldc, strideA, strideB, strideC, batch, stream);
+}
+
+const char *tg_status_string(int status)
+{
+    switch (status) {
+    case TG_OK: return "TG_OK";
+    case TG_ERR_INVALID_ARG: return "TG_ERR_INVALID_ARG: invalid size, leading dimension, stride or pointer";
+    case TG_ERR_NO_DEVICE: return "TG_ERR_NO_DEVICE: no usable HIP device";
+    case TG_ERR_UNSUPPORTED_DEVICE: return "TG_ERR_UNSUPPORTED_DEVICE: the current device is not gfx950";
+    case TG_ERR_HIP: return "TG_ERR_HIP: a HIP call or kernel launch failed";
+    default: return "unknown tg_status";
+    }
+}
+
+int tg_set_path(int path)
+{
+    if (path < 0 || path >= TG_PATH_COUNT || path == TG_PATH_SKINNY)
+        return -1;
+    return g_forced_path.exchange(path);
+}
+
+int tg_last_path(void) { return g_last_path.load(std::memory_order_relaxed); }
+
+const char *tg_path_name(int path)
+{
+    switch (path) {
+    case TG_PATH_AUTO: return "auto";
+    case TG_PATH_NAIVE: return "naive";
+    case TG_PATH_GENERIC: return "generic";
+    case TG_PATH_TILE128: return "tile128";
+    case TG_PATH_TILE256: return "tile256";
+    case TG_PATH_SKINNY: return "skinny";
+    default: return "unknown";
+    }
+}
+
+}  // extern "C"

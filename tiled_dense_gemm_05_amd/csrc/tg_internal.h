@@ -1,0 +1,29 @@
+// Internal interface between the host dispatcher (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tg {
+
+// One strided-batched problem, sizes and strides in elements.  The host has
+// validated it; every kernel masks its own edges, so any M, N, K >= 0 is safe
+// for the layouts the ABI documents.
+struct GemmArgs {
+    const uint16_t *A;
+    const uint16_t *B;
+    uint16_t *C;
+    int64_t M, N, K;
+    int64_t lda, ldb, ldc;
+    int64_t sA, sB, sC;
+    int64_t batch;
+};
+
+// Every launcher enqueues on `stream` and returns hipGetLastError().
+hipError_t launch_naive(const GemmArgs &p, hipStream_t stream);
+hipError_t launch_generic(const GemmArgs &p, hipStream_t stream);
+hipError_t launch_tile128(const GemmArgs &p, hipStream_t stream);
+hipError_t launch_tile256(const GemmArgs &p, hipStream_t stream);
+hipError_t launch_skinny(const GemmArgs &p, hipStream_t stream);
+
+}  // namespace tg
