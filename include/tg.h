@@ -107,6 +107,16 @@ int tg_set_path(int path);
 /* The path the most recent successful launch from this process used. */
 int tg_last_path(void);
 
+/*
+ * Tuning knob for benchmarks: selects the kernel configuration (block tile,
+ * K tile, pipeline depth) that the tile paths use.  -1 restores the defaults;
+ * 0..6 are the direct-to-LDS configurations, 10 and 11 the register-staged
+ * 128x128 and 256x256 kernels.  Returns the previous setting, or -2 for an
+ * unknown variant (the setting is unchanged).  Results are identical within
+ * the accuracy contract for every variant; only speed changes.
+ */
+int tg_set_tile_variant(int variant);
+
 /* A static name for a path number ("auto", "naive", ...), or "unknown". */
 const char *tg_path_name(int path);
 

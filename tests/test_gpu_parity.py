@@ -337,3 +337,20 @@ def _workload_case(tg, oracle_lib, name, n_samples=None):
 ])
 def test_workloads_full_size(tg, oracle_lib, name, n):
     _workload_case(tg, oracle_lib, name, n)
+
+
+# ------------------------------------------------------ every tile configuration
+
+VARIANTS = [0, 1, 2, 3, 4, 5, 6, 10, 11]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("M,N,K", [(257, 264, 136), (520, 392, 1000), (64, 256, 8)])
+def test_tile_variants_match_oracle(tg, oracle_lib, variant, M, N, K):
+    assert tg.tg_set_tile_variant(variant) >= -1
+    try:
+        used, _, _ = full_case(tg, oracle_lib, M, N, K, seed=variant + 11,
+                               path=tg.TG_PATH_TILE256)
+        assert used == "tile256"
+    finally:
+        tg.tg_set_tile_variant(-1)

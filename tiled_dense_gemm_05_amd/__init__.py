@@ -37,6 +37,7 @@ EXPORTED_SYMBOLS = (
     "tg_set_path",
     "tg_last_path",
     "tg_path_name",
+    "tg_set_tile_variant",
 )
 
 
@@ -48,7 +49,7 @@ class TGError(RuntimeError):
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m tiled_dense_gemm_05_amd.build` "
+        f"{LIB_PATH} is not built; run `python tiled_dense_gemm_05_amd/build.py` "
         "(there is no CPU fallback)")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -64,6 +65,8 @@ _lib.tg_set_path.argtypes = [ctypes.c_int]
 _lib.tg_set_path.restype = ctypes.c_int
 _lib.tg_last_path.argtypes = []
 _lib.tg_last_path.restype = ctypes.c_int
+_lib.tg_set_tile_variant.argtypes = [ctypes.c_int]
+_lib.tg_set_tile_variant.restype = ctypes.c_int
 _lib.tg_path_name.argtypes = [ctypes.c_int]
 _lib.tg_path_name.restype = ctypes.c_char_p
 
@@ -99,6 +102,10 @@ def tg_last_path() -> int:
 
 def tg_path_name(path: int) -> str:
     return _lib.tg_path_name(path).decode()
+
+
+def tg_set_tile_variant(variant: int) -> int:
+    return _lib.tg_set_tile_variant(variant)
 
 
 # ----------------------------------------------------------- torch helpers

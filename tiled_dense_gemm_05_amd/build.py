@@ -2,7 +2,8 @@
 
 Every source under ``csrc/`` is compiled with hipcc into ``_build/`` and
 linked into ``tiled_dense_gemm_05_amd/libtg.so`` next to this file.  Run
-``python -m tiled_dense_gemm_05_amd.build`` (or ``__graft_entry__.build()``).
+``python tiled_dense_gemm_05_amd/build.py`` (or ``__graft_entry__.build()``);
+it is a plain script so that it never imports the package it builds.
 """
 
 from __future__ import annotations

@@ -12,6 +12,13 @@ namespace {
 
 std::atomic<int> g_forced_path{TG_PATH_AUTO};
 std::atomic<int> g_last_path{TG_PATH_AUTO};
+std::atomic<int> g_tile_variant{-1};
+
+// Default direct-to-LDS configurations of the tile paths.
+constexpr int kTile128Default = 3;   // 128x128x64, 4 stages
+constexpr int kTile256Default = 0;   // 256x256x64, 2 stages
+constexpr int kRegStaged128 = 10;    // register-staged kernels, kept for comparison
+constexpr int kRegStaged256 = 11;
 
 // Per-device architecture check, done once per device: 0 unknown, 1 gfx950,
 // 2 something else.
@@ -92,7 +99,7 @@ bool fast_layout(const tg::GemmArgs &p)
         return false;
     if (p.batch > 1 && ((p.sA | p.sB | p.sC) & 7))
         return false;
-    return p.K > 0;
+    return p.K > 0 && tg::dma_layout_ok(p);
 }
 
 int choose_path(const tg::GemmArgs &p)
@@ -138,8 +145,19 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
     hipError_t e;
     switch (path) {
     case TG_PATH_NAIVE: e = tg::launch_naive(p, stream); break;
-    case TG_PATH_TILE128: e = tg::launch_tile128(p, stream); break;
-    case TG_PATH_TILE256: e = tg::launch_tile256(p, stream); break;
+    case TG_PATH_TILE128:
+    case TG_PATH_TILE256: {
+        int v = g_tile_variant.load(std::memory_order_relaxed);
+        if (v < 0)
+            v = path == TG_PATH_TILE128 ? kTile128Default : kTile256Default;
+        if (v == kRegStaged128)
+            e = tg::launch_tile128(p, stream);
+        else if (v == kRegStaged256)
+            e = tg::launch_tile256(p, stream);
+        else
+            e = tg::launch_dma_config(v, p, stream, 8);
+        break;
+    }
     default: e = tg::launch_generic(p, stream); path = TG_PATH_GENERIC; break;
     }
     if (e != hipSuccess)
@@ -186,6 +204,14 @@ int tg_set_path(int path)
 }
 
 int tg_last_path(void) { return g_last_path.load(std::memory_order_relaxed); }
+
+int tg_set_tile_variant(int variant)
+{
+    if (!(variant == -1 || (variant >= 0 && variant < tg::kDmaConfigs) ||
+          variant == kRegStaged128 || variant == kRegStaged256))
+        return -2;
+    return g_tile_variant.exchange(variant);
+}
 
 const char *tg_path_name(int path)
 {

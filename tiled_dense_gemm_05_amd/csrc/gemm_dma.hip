@@ -1,0 +1,513 @@
+// Aligned fp16 GEMM + ReLU on gfx950 with a multi-stage direct-to-LDS
+// pipeline.
+//
+// The tile program is the GEMM+ReLU of the "TileLang paper reading" page
+// (hotelren.com), section 2: one workgroup per output tile, LDS operand tiles,
+// an fp32 accumulator cleared to zero, a K loop pipelined over STAGES buffers,
+// ReLU on the accumulator, copy to the fp16 C.  Section 3 of that page names
+// the AMD pipeline primitives used here directly: loads that write LDS
+// without passing through registers (buffer_load ... lds) and counter waits
+// (s_waitcnt vmcnt) that release a stage once its loads have landed.
+//
+// gfx950 specifics:
+//  * buffer_load_dwordx4 ... lds: each lane fetches 16 bytes and the wave
+//    writes them as one contiguous 1 KiB block of LDS (lane L at byte 16 L,
+//    block base in M0).  The XOR swizzle of the LDS tile is realised by
+//    choosing, per lane, which global chunk lands in that fixed slot.
+//  * Each operand is addressed through a buffer descriptor (SGPRs) whose base
+//    advances by one K tile per iteration and one 32-bit VGPR offset per load.
+//    Chunks outside the matrix (rows >= M, k >= K, columns >= N) get the
+//    offset 2^31, at the descriptor's record count, and the hardware range
+//    check returns zeros for them; every stage is fully written and the tails
+//    contribute exact zeros.  This needs N and K to be multiples of 8 (a
+//    16-byte chunk is wholly inside or outside) and 16-byte aligned rows.
+//  * Before tile kt is computed, tiles kt+1 .. kt+STAGES-1 are in flight.
+//    The last 16-wide k step of tile kt overlaps the switch to tile kt+1:
+//    wait until this wave's loads of tile kt+1 have landed, barrier (every
+//    wave is done reading tile kt's stage), then the matrix-core work of that
+//    last step is interleaved with the loads of tile kt+STAGES into the stage
+//    just released and with the LDS reads of tile kt+1's first fragments.
+//  * Inside a tile, the fragments of the next k step are read from LDS while
+//    the matrix cores work on the current one (two register sets).
+//  * The loads are issued as inline assembly so the compiler does not treat
+//    them as LDS stores that every LDS read must wait for; the kernel orders
+//    them itself with vmcnt waits and barriers.
+//  * Operand roles (the matrix core computes C^T = B^T A^T so a lane owns 4
+//    consecutive columns of a C row), transpose reads of the row-major B
+//    (ds_read_b64_tr_b16), the swizzles, the XCD-aware tile order and the
+//    epilogue are shared with the register-staged kernel.
+#include "tg_internal.h"
+
+namespace tg {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) f16x8 lds_f16x8;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+constexpr uint32_t kOutOfRange = 0x80000000u;   // == the descriptors' record count
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, STAGES = STAGES_;
+    static constexpr int NW = WM * WN;                // waves
+    static constexpr int NT = 64 * NW;                // threads
+    static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
+    static constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 fragments per wave
+    static constexpr int CA = BK / 8, CB = BN / 8;    // 16-byte chunks per tile row
+    static constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BN;
+    static constexpr int STAGE = A_ELEMS + B_ELEMS;   // fp16 elements per stage
+    static constexpr int A_LD = A_ELEMS / 512 / NW;   // 1 KiB loads per wave per tile
+    static constexpr int B_LD = B_ELEMS / 512 / NW;
+    static constexpr int LOADS = A_LD + B_LD;
+    static constexpr int A_RPB = 64 / CA;             // tile rows per 1 KiB block
+    static constexpr int B_RPB = 64 / CB;
+    static constexpr int KSTEPS = BK / 16;
+    static constexpr int READS = FM + 2 * FN;         // LDS reads per k step
+    // With 3+ stages the loads of tile kt+STAGES-1 are spread evenly over the
+    // k steps of tile kt (DPS per step); with 2 stages the only free stage is
+    // released at the last k step, which then issues all of them.
+    static constexpr bool SPREAD = STAGES >= 3;
+    static constexpr int DPS = SPREAD ? LOADS / KSTEPS : 0;
+    static constexpr int AHEAD = SPREAD ? STAGES - 1 : STAGES;   // tile distance of the loads
+    static constexpr int PROLOGUE = SPREAD ? STAGES - 1 : STAGES; // tiles issued up front
+    // loads of this wave issued after tile kt+1's at the wait before the last k step
+    static constexpr int WAIT_LAST = SPREAD ? (STAGES - 3) * LOADS + (KSTEPS - 1) * DPS : 0;
+    static_assert(!SPREAD || LOADS % KSTEPS == 0, "loads per k step");
+    static_assert((A_ELEMS / 512) % NW == 0 && (B_ELEMS / 512) % NW == 0, "blocks per wave");
+    static_assert(CA <= 16 && CB <= 64 && 64 % CA == 0 && 64 % CB == 0, "rows per block");
+    static_assert(TM % 32 == 0 && TN % 32 == 0 && BK % 16 == 0, "fragment shape");
+    static_assert(LOADS * (STAGES - 1) <= 63, "vmcnt range");
+    static_assert(KSTEPS <= 4, "k steps per tile");
+    static_assert(STAGE * 2 * STAGES <= 160 * 1024, "LDS size");
+    // a thread's loads of one tile share one swizzled column (see load plan)
+    static_assert((NW * A_RPB) % 16 == 0 && (NW * B_RPB) % 4 == 0, "swizzle period");
+};
+
+template <int CA>
+__device__ __forceinline__ int swz_a(int row, int c)
+{
+    constexpr int rows_per_line = 16 / CA;
+    return c ^ ((row / rows_per_line) % CA);
+}
+
+template <int CB>
+__device__ __forceinline__ int swz_b(int k, int c)
+{
+    if constexpr (CB >= 16)
+        return c ^ ((k & 3) << 2);
+    else if constexpr (CB == 8)
+        return c ^ (((k >> 1) & 1) << 2);
+    else
+        return c;
+}
+
+__device__ __forceinline__ void tile_coords(int pid, int tilesM, int tilesN, int groupM, int &tm,
+                                            int &tn)
+{
+    const int T = tilesM * tilesN;
+    const int q = T >> 3, r = T & 7;
+    const int xcd = pid & 7, local = pid >> 3;
+    const int id = (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+    const int per_group = groupM * tilesN;
+    const int g = id / per_group;
+    const int first_m = g * groupM;
+    const int gsz = min(tilesM - first_m, groupM);
+    const int in = id - g * per_group;
+    tm = first_m + in % gsz;
+    tn = in / gsz;
+}
+
+// s_waitcnt vmcnt(N), other counters untouched, fenced against compiler
+// reordering of memory operations.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt");
+    constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(imm);
+    asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier once this wave's LDS reads have completed (the lgkmcnt
+// wait is a builtin so the compiler's own wait tracking sees it).
+__device__ __forceinline__ void block_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((3 << 14) | (0 << 8) | (7 << 4) | 15);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Raw buffer descriptor over `base`: record count 2^31 (offsets at or past it
+// read as zero), 32-bit data format as the gfx9 family requires.
+__device__ __forceinline__ i32x4 make_rsrc(const void *base)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+    r.z = (int)kOutOfRange;
+    r.w = 0x00020000;
+    return r;
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane from rsrc + voff into the 1 KiB LDS block at lds_addr.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %2\n\t"
+                 "s_nop 0\n\t"
+                 "buffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(lds_addr)
+                 : "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t pack_relu_f16x2(float a, float b)
+{
+    const _Float16 ha = (_Float16)(a > 0.0f ? a : 0.0f);
+    const _Float16 hb = (_Float16)(b > 0.0f ? b : 0.0f);
+    return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+// Scheduling hint: alternate one MFMA with one LDS read, then the rest.
+template <int MFMAS, int READS>
+__device__ __forceinline__ void interleave_mfma_lds()
+{
+    constexpr int pairs = MFMAS < READS ? MFMAS : READS;
+#pragma unroll
+    for (int i = 0; i < pairs; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+    }
+    if constexpr (MFMAS > pairs)
+        __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - pairs, 0);
+    if constexpr (READS > pairs)
+        __builtin_amdgcn_sched_group_barrier(0x100, READS - pairs, 0);
+}
+
+// Piece r of the fragments of k step kk: r < FM is the A^T fragment r (lane
+// holds A[row][8 consecutive k], one 16-byte read); FM + 2 fn + hh is half hh
+// of the B^T fragment fn (a transpose read: source lane s of each 16-lane
+// group points at row s / 4, columns 4 (s % 4) .. + 3 of a 4 x 16 block and
+// receives one column's 4 consecutive k).
+template <class T, int r>
+__device__ __forceinline__ void read_piece(const lds_u16 *As, const lds_u16 *Bs, int kk, int wm,
+                                           int wn, int lane, f16x8 (&af)[T::FM],
+                                           s16x4 (&bh)[T::FN][2])
+{
+    if constexpr (r < T::FM) {
+        const int row = wm * T::TM + r * 32 + (lane & 31);
+        const int c = kk * 2 + (lane >> 5);
+        af[r] = *reinterpret_cast<const lds_f16x8 *>(As + row * T::BK + swz_a<T::CA>(row, c) * 8);
+    } else {
+        constexpr int fn = (r - T::FM) / 2, hh = (r - T::FM) % 2;
+        const int k = kk * 16 + 8 * (lane >> 5) + 4 * hh + ((lane & 15) >> 2);
+        const int n = wn * T::TN + fn * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        const lds_u16 *src = Bs + k * T::BN + swz_b<T::CB>(k, n >> 3) * 8 + (n & 7);
+        bh[fn][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src);
+    }
+}
+
+template <class T, int r = 0>
+__device__ __forceinline__ void read_all(const lds_u16 *As, const lds_u16 *Bs, int kk, int wm,
+                                         int wn, int lane, f16x8 (&af)[T::FM],
+                                         s16x4 (&bh)[T::FN][2])
+{
+    if constexpr (r < T::READS) {
+        read_piece<T, r>(As, Bs, kk, wm, wn, lane, af, bh);
+        read_all<T, r + 1>(As, Bs, kk, wm, wn, lane, af, bh);
+    }
+}
+
+template <class T>
+__device__ __forceinline__ void join_b(const s16x4 (&bh)[T::FN][2], f16x8 (&bf)[T::FN])
+{
+#pragma unroll
+    for (int fn = 0; fn < T::FN; ++fn)
+        bf[fn] = __builtin_bit_cast(f16x8,
+                                    __builtin_shufflevector(bh[fn][0], bh[fn][1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <class T>
+__device__ __forceinline__ void mma_all(f32x16 (&acc)[T::FM][T::FN], const f16x8 (&af)[T::FM],
+                                        const f16x8 (&bf)[T::FN])
+{
+#pragma unroll
+    for (int fm = 0; fm < T::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < T::FN; ++fn)
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[fn], af[fm], acc[fm][fn], 0, 0, 0);
+}
+
+// Everything a thread needs to issue its loads of one tile.
+template <class T>
+struct LoadPlan {
+    uint32_t a_voff[T::A_LD];   // byte offsets from the A descriptor, or out of range
+    uint32_t b_voff[T::B_LD];
+    int a_kcol;                 // the thread's column inside the K tile (A)
+    int b_row0;                 // the thread's first row inside the K tile (B)
+};
+
+template <class T, int I>
+__device__ __forceinline__ void issue_one(const LoadPlan<T> &lp, const i32x4 &ra, const i32x4 &rb,
+                                          bool a_kok, int b_rows_left, uint32_t stage_addr,
+                                          int wave)
+{
+    if constexpr (I < T::A_LD) {
+        const uint32_t v = a_kok ? lp.a_voff[I] : kOutOfRange;
+        dma16(ra, v, stage_addr + (uint32_t)((wave + I * T::NW) * 1024));
+    } else {
+        constexpr int J = I - T::A_LD;
+        const bool ok = (lp.b_row0 + J * T::NW * T::B_RPB) < b_rows_left;
+        const uint32_t v = ok ? lp.b_voff[J] : kOutOfRange;
+        dma16(rb, v, stage_addr + (uint32_t)(T::A_ELEMS * 2 + (wave + J * T::NW) * 1024));
+    }
+}
+
+// One k step: the MFMAs on fragments (af, bf), with loads D0 .. D1-1 of a
+// tile and the LDS reads of the next fragments (k step kkn of As/Bs) placed
+// between them in program order: MFMA i is followed by load D0 + i and read i.
+template <class T, int D0, int D1, int I = 0>
+__device__ __forceinline__ void step(f32x16 (&acc)[T::FM][T::FN], const f16x8 (&af)[T::FM],
+                                     const f16x8 (&bf)[T::FN], const LoadPlan<T> &lp,
+                                     const i32x4 &ra, const i32x4 &rb, bool a_kok, int b_rows_left,
+                                     uint32_t stage_addr, int wave, const lds_u16 *As,
+                                     const lds_u16 *Bs, int kkn, int wm, int wn, int lane,
+                                     f16x8 (&afn)[T::FM], s16x4 (&bhn)[T::FN][2])
+{
+    constexpr int MF = T::FM * T::FN;
+    constexpr int ND = D1 - D0;
+    constexpr int STEPS = MF > ND ? (MF > T::READS ? MF : T::READS) : (ND > T::READS ? ND : T::READS);
+    if constexpr (I < STEPS) {
+        if constexpr (I < MF) {
+            constexpr int fm = I / T::FN, fn = I % T::FN;
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[fn], af[fm], acc[fm][fn], 0, 0, 0);
+        }
+        if constexpr (I < ND)
+            issue_one<T, D0 + I>(lp, ra, rb, a_kok, b_rows_left, stage_addr, wave);
+        if constexpr (I < T::READS)
+            read_piece<T, I>(As, Bs, kkn, wm, wn, lane, afn, bhn);
+        step<T, D0, D1, I + 1>(acc, af, bf, lp, ra, rb, a_kok, b_rows_left, stage_addr, wave, As,
+                               Bs, kkn, wm, wn, lane, afn, bhn);
+    }
+}
+
+template <class T, int I = 0>
+__device__ __forceinline__ void issue_tile(const LoadPlan<T> &lp, const i32x4 &ra, const i32x4 &rb,
+                                           bool a_kok, int b_rows_left, uint32_t stage_addr,
+                                           int wave)
+{
+    if constexpr (I < T::LOADS) {
+        issue_one<T, I>(lp, ra, rb, a_kok, b_rows_left, stage_addr, wave);
+        issue_tile<T, I + 1>(lp, ra, rb, a_kok, b_rows_left, stage_addr, wave);
+    }
+}
+
+template <class T>
+__global__ void __launch_bounds__(T::NT) gemm_relu_dma_kernel(GemmArgs p, int tilesM, int tilesN,
+                                                              int groupM)
+{
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[T::STAGES * T::STAGE];
+    const lds_u16 *lds = (const lds_u16 *)smem;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / T::WN, wn = wave % T::WN;
+    int tm, tn;
+    tile_coords(blockIdx.x, tilesM, tilesN, groupM, tm, tn);
+    const int64_t bidx = blockIdx.y;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int64_t m0 = (int64_t)tm * T::BM, n0 = (int64_t)tn * T::BN;
+    // operand panels of this tile; the descriptors advance along K
+    const uint16_t *Ab = p.A + bidx * p.sA + m0 * p.lda;
+    const uint16_t *Bb = p.B + bidx * p.sB + n0;
+    uint16_t *C = p.C + bidx * p.sC;
+
+    // Load plan.  Wave w moves 1 KiB blocks w, w + NW, ... of each operand
+    // tile; lane L of a block covers its LDS bytes 16 L .. 16 L + 15, i.e.
+    // physical chunk L % C of row L / C; the logical chunk stored there is the
+    // XOR-swizzled one.  Every block of a thread has the same swizzle.
+    LoadPlan<T> lp;
+    {
+        const int r0 = wave * T::A_RPB + lane / T::CA;
+        const int c = swz_a<T::CA>(r0, lane % T::CA);
+        lp.a_kcol = c * 8;
+#pragma unroll
+        for (int i = 0; i < T::A_LD; ++i) {
+            const int row = r0 + i * T::NW * T::A_RPB;
+            lp.a_voff[i] = (m0 + row < M) ? (uint32_t)((row * p.lda + c * 8) * 2) : kOutOfRange;
+        }
+    }
+    {
+        const int r0 = wave * T::B_RPB + lane / T::CB;
+        const int c = swz_b<T::CB>(r0, lane % T::CB);
+        lp.b_row0 = r0;
+        const bool col_ok = n0 + c * 8 < N;
+#pragma unroll
+        for (int j = 0; j < T::B_LD; ++j) {
+            const int row = r0 + j * T::NW * T::B_RPB;
+            lp.b_voff[j] = col_ok ? (uint32_t)((row * p.ldb + c * 8) * 2) : kOutOfRange;
+        }
+    }
+    auto rsrc_a = [&](int kt) { return make_rsrc(Ab + (int64_t)kt * T::BK); };
+    auto rsrc_b = [&](int kt) { return make_rsrc(Bb + (int64_t)kt * T::BK * p.ldb); };
+    auto a_kok = [&](int kt) { return (int64_t)kt * T::BK + lp.a_kcol < K; };
+    auto b_left = [&](int kt) {
+        const int64_t r = K - (int64_t)kt * T::BK;
+        return (int)(r < 0 ? 0 : (r > T::BK ? T::BK : r));
+    };
+
+    f32x16 acc[T::FM][T::FN];
+#pragma unroll
+    for (int fm = 0; fm < T::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < T::FN; ++fn)
+            acc[fm][fn] = f32x16{};
+
+    const int KT = (int)((K + T::BK - 1) / T::BK);
+    f16x8 af[2][T::FM], bf[2][T::FN];
+    if (KT > 0) {
+        // Issue the first tiles (tiles past the end of K load zeros and never
+        // touch memory), then wait for tile 0.
+#pragma unroll
+        for (int s = 0; s < T::PROLOGUE; ++s)
+            issue_tile<T>(lp, rsrc_a(s), rsrc_b(s), a_kok(s), b_left(s),
+                          lds_base + (uint32_t)(s * T::STAGE * 2), wave);
+        wait_vmcnt<(T::PROLOGUE - 1) * T::LOADS>();
+        block_barrier();
+        s16x4 bh[T::FN][2];
+        read_all<T>(lds, lds + T::A_ELEMS, 0, wm, wn, lane, af[0], bh);
+        join_b<T>(bh, bf[0]);
+    }
+
+    for (int kt = 0; kt < KT; ++kt) {
+        const int stage = kt % T::STAGES;
+        const lds_u16 *As = lds + stage * T::STAGE;
+        const lds_u16 *Bs = As + T::A_ELEMS;
+        // loads of tile kt + AHEAD go to the stage that tile held
+        const int kl = kt + T::AHEAD;
+        const int lstage = kl % T::STAGES;
+        const uint32_t laddr = lds_base + (uint32_t)(lstage * T::STAGE * 2);
+        const i32x4 ra = rsrc_a(kl), rb = rsrc_b(kl);
+        const bool akok = a_kok(kl);
+        const int bleft = b_left(kl);
+#pragma unroll
+        for (int kk = 0; kk + 1 < T::KSTEPS; ++kk) {
+            s16x4 bh[T::FN][2];
+            // compile-time DMA range of this k step
+            if (kk == 0)
+                step<T, 0, T::DPS>(acc, af[0], bf[0], lp, ra, rb, akok, bleft, laddr, wave, As, Bs,
+                                   kk + 1, wm, wn, lane, af[1], bh);
+            else if (kk == 1)
+                step<T, T::DPS, 2 * T::DPS>(acc, af[1], bf[1], lp, ra, rb, akok, bleft, laddr, wave,
+                                            As, Bs, kk + 1, wm, wn, lane, af[0], bh);
+            else
+                step<T, 2 * T::DPS, 3 * T::DPS>(acc, af[0], bf[0], lp, ra, rb, akok, bleft, laddr,
+                                                wave, As, Bs, kk + 1, wm, wn, lane, af[1], bh);
+            join_b<T>(bh, bf[(kk + 1) & 1]);
+        }
+        constexpr int cur = (T::KSTEPS - 1) & 1, nxt = T::KSTEPS & 1;
+        // Tile kt+1 has landed once at most WAIT_LAST later loads of this wave
+        // are outstanding.  On the last tile this step still runs (one MFMA
+        // chain for the register allocator): its loads are past the end of K
+        // and read nothing, its fragment reads are never used.
+        wait_vmcnt<T::WAIT_LAST>();
+        block_barrier();
+        {
+            const int nstage = (kt + 1) % T::STAGES;
+            const lds_u16 *An = lds + nstage * T::STAGE;
+            s16x4 bh[T::FN][2];
+            constexpr int D0 = T::SPREAD ? (T::KSTEPS - 1) * T::DPS : 0;
+            step<T, D0, T::LOADS>(acc, af[cur], bf[cur], lp, ra, rb, akok, bleft, laddr, wave, An,
+                                  An + T::A_ELEMS, 0, wm, wn, lane, af[nxt], bh);
+            join_b<T>(bh, bf[nxt]);
+        }
+    }
+    // loads issued past the end of K must land before the LDS is released
+    wait_vmcnt<0>();
+
+    // Epilogue: ReLU, round to nearest even, 8-byte stores (N % 8 == 0 and
+    // 16-byte aligned rows make every 4-column group wholly in or out).
+#pragma unroll
+    for (int fm = 0; fm < T::FM; ++fm) {
+        const int64_t m = m0 + wm * T::TM + fm * 32 + (lane & 31);
+        if (m >= M)
+            continue;
+        uint16_t *crow = C + m * p.ldc;
+#pragma unroll
+        for (int fn = 0; fn < T::FN; ++fn) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t n = n0 + wn * T::TN + fn * 32 + 8 * g + 4 * (lane >> 5);
+                const f32x16 &v = acc[fm][fn];
+                u32x2 w;
+                w.x = pack_relu_f16x2(v[4 * g + 0], v[4 * g + 1]);
+                w.y = pack_relu_f16x2(v[4 * g + 2], v[4 * g + 3]);
+                if (n < N)
+                    *reinterpret_cast<u32x2 *>(crow + n) = w;
+            }
+        }
+    }
+}
+
+template <class T>
+hipError_t launch_dma(const GemmArgs &p, hipStream_t stream, int groupM)
+{
+    const int64_t tilesM = (p.M + T::BM - 1) / T::BM;
+    const int64_t tilesN = (p.N + T::BN - 1) / T::BN;
+    const int64_t tiles = tilesM * tilesN;
+    if (tiles > 0x7fffffff)
+        return hipErrorInvalidValue;
+    GemmArgs q = p;
+    for (int64_t b0 = 0; b0 < p.batch; b0 += 65535) {
+        const int64_t nb = (p.batch - b0) < 65535 ? (p.batch - b0) : 65535;
+        q.A = p.A + b0 * p.sA;
+        q.B = p.B + b0 * p.sB;
+        q.C = p.C + b0 * p.sC;
+        q.batch = nb;
+        hipLaunchKernelGGL((gemm_relu_dma_kernel<T>), dim3((unsigned)tiles, (unsigned)nb), dim3(T::NT),
+                           0, stream, q, (int)tilesM, (int)tilesN, groupM);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+bool dma_layout_ok(const GemmArgs &p)
+{
+    // 32-bit buffer offsets: a 256-row A panel and a 64-row B tile must stay
+    // below 2^31 bytes from their descriptors
+    return p.lda <= (1 << 21) && p.ldb <= (1 << 21);
+}
+
+hipError_t launch_dma_config(int cfg, const GemmArgs &p, hipStream_t stream, int groupM)
+{
+    switch (cfg) {
+    case 0: return launch_dma<Cfg<256, 256, 32, 2, 2, 4>>(p, stream, groupM);
+    case 1: return launch_dma<Cfg<256, 256, 32, 2, 2, 3>>(p, stream, groupM);
+    case 2: return launch_dma<Cfg<256, 256, 64, 2, 2, 2>>(p, stream, groupM);
+    case 3: return launch_dma<Cfg<128, 128, 64, 2, 2, 4>>(p, stream, groupM);
+    case 4: return launch_dma<Cfg<128, 128, 32, 2, 2, 4>>(p, stream, groupM);
+    case 5: return launch_dma<Cfg<128, 128, 64, 2, 2, 3>>(p, stream, groupM);
+    case 6: return launch_dma<Cfg<256, 128, 64, 2, 2, 3>>(p, stream, groupM);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace tg

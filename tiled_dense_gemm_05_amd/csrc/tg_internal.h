@@ -26,4 +26,11 @@ hipError_t launch_tile128(const GemmArgs &p, hipStream_t stream);
 hipError_t launch_tile256(const GemmArgs &p, hipStream_t stream);
 hipError_t launch_skinny(const GemmArgs &p, hipStream_t stream);
 
+// Direct-to-LDS pipelined kernels (aligned layouts only).  `cfg` selects the
+// block tile / K tile / stage count; see gemm_dma.hip.
+constexpr int kDmaConfigs = 7;
+hipError_t launch_dma_config(int cfg, const GemmArgs &p, hipStream_t stream, int groupM);
+// Whether the leading dimensions fit the kernels' 32-bit buffer offsets.
+bool dma_layout_ok(const GemmArgs &p);
+
 }  // namespace tg
