@@ -99,7 +99,7 @@ enum {
     TG_PATH_GENERIC = 2,    /* 128x128 tiles, any alignment, masked loads */
     TG_PATH_TILE128 = 3,    /* 128x128x32 tiles, 256 threads, aligned operands */
     TG_PATH_TILE256 = 4,    /* 256x256 tiles for large shapes, aligned operands */
-    TG_PATH_SKINNY = 5,     /* M <= 64: narrow-N slices streaming B, aligned */
+    TG_PATH_SKINNY = 5,     /* M <= 64: column slices streaming B, K split over waves */
     TG_PATH_COUNT = 6
 };
 int tg_set_path(int path);
@@ -110,12 +110,19 @@ int tg_last_path(void);
 /*
  * Tuning knob for benchmarks: selects the kernel configuration (block tile,
  * K tile, pipeline depth) that the tile paths use.  -1 restores the defaults;
- * 0..6 are the direct-to-LDS configurations, 10 and 11 the register-staged
+ * 0..9 are the direct-to-LDS configurations, 10 and 11 the register-staged
  * 128x128 and 256x256 kernels.  Returns the previous setting, or -2 for an
  * unknown variant (the setting is unchanged).  Results are identical within
  * the accuracy contract for every variant; only speed changes.
  */
 int tg_set_tile_variant(int variant);
+
+/*
+ * The same for the skinny path (M <= 64): 0..3 select the column-slice width,
+ * wave count and pipeline depth; -1 restores the default.  Returns the
+ * previous setting, or -2 for an unknown variant.
+ */
+int tg_set_skinny_variant(int variant);
 
 /* A static name for a path number ("auto", "naive", ...), or "unknown". */
 const char *tg_path_name(int path);

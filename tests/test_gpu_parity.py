@@ -122,7 +122,7 @@ def test_auto_path_matches_oracle(tg, oracle_lib, M, N, K):
     full_case(tg, oracle_lib, M, N, K, seed=M + N + K)
 
 
-FORCED = ["naive", "generic", "tile128", "tile256"]
+FORCED = ["naive", "generic", "tile128", "tile256", "skinny"]
 
 
 @pytest.mark.parametrize("path", FORCED)
@@ -131,7 +131,9 @@ FORCED = ["naive", "generic", "tile128", "tile256"]
 def test_forced_paths_match_oracle(tg, oracle_lib, path, M, N, K):
     used, _, _ = full_case(tg, oracle_lib, M, N, K, seed=3, path=getattr(
         tg, "TG_PATH_" + path.upper()))
-    if (N % 8 == 0 and K % 8 == 0) or path in ("naive", "generic"):
+    if path == "skinny" and M > 64:
+        assert used == ("tile128" if (N % 8 == 0 and K % 8 == 0) else "generic")
+    elif (N % 8 == 0 and K % 8 == 0) or path in ("naive", "generic"):
         assert used == path
 
 
@@ -165,10 +167,10 @@ def _bits(x):
     return np.asarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
 
 
-@pytest.mark.parametrize("path", ["auto", "naive", "generic", "tile128", "tile256"])
+@pytest.mark.parametrize("path", ["auto", "naive", "generic", "tile128", "tile256", "skinny"])
 @pytest.mark.parametrize("K", [1000, 2048, 8192])
 def test_ones_give_K_exactly(tg, path, K):
-    M, N = 256, 256
+    M, N = (64, 256) if path == "skinny" else (256, 256)
     if path != "auto":
         tg.tg_set_path(getattr(tg, "TG_PATH_" + path.upper()))
     a_d = dev(np.full(M * K, 0x3C00, np.uint16))
@@ -213,7 +215,7 @@ def _probe(tg, M, N, K, A, B):
     return host(c_d)
 
 
-@pytest.mark.parametrize("path", ["auto", "naive", "generic", "tile128", "tile256"])
+@pytest.mark.parametrize("path", ["auto", "naive", "generic", "tile128", "tile256", "skinny"])
 def test_rounding_and_subnormal_probes(tg, path):
     if path != "auto":
         tg.tg_set_path(getattr(tg, "TG_PATH_" + path.upper()))
@@ -341,7 +343,7 @@ def test_workloads_full_size(tg, oracle_lib, name, n):
 
 # ------------------------------------------------------ every tile configuration
 
-VARIANTS = [0, 1, 2, 3, 4, 5, 6, 10, 11]
+VARIANTS = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11]
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -354,3 +356,27 @@ def test_tile_variants_match_oracle(tg, oracle_lib, variant, M, N, K):
         assert used == "tile256"
     finally:
         tg.tg_set_tile_variant(-1)
+
+
+# ------------------------------------------------------------------ skinny M
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
+@pytest.mark.parametrize("M,N,K", [(16, 1024, 8192), (1, 264, 520), (7, 1000, 136),
+                                   (17, 512, 1000), (33, 96, 64), (64, 520, 2056),
+                                   (48, 8, 8)])
+def test_skinny_variants_match_oracle(tg, oracle_lib, variant, M, N, K):
+    assert tg.tg_set_skinny_variant(variant) >= -1
+    try:
+        used, _, _ = full_case(tg, oracle_lib, M, N, K, dist="uniform", seed=variant + M,
+                               path=tg.TG_PATH_SKINNY)
+        assert used == "skinny"
+    finally:
+        tg.tg_set_skinny_variant(-1)
+
+
+def test_skinny_is_auto_for_small_m(tg, oracle_lib):
+    used, _, _ = full_case(tg, oracle_lib, 16, 4096, 4096, seed=5)
+    assert used == "skinny"
+    used, _, _ = full_case(tg, oracle_lib, 65, 512, 256, seed=6)
+    assert used != "skinny"

@@ -38,6 +38,7 @@ EXPORTED_SYMBOLS = (
     "tg_last_path",
     "tg_path_name",
     "tg_set_tile_variant",
+    "tg_set_skinny_variant",
 )
 
 
@@ -67,6 +68,8 @@ _lib.tg_last_path.argtypes = []
 _lib.tg_last_path.restype = ctypes.c_int
 _lib.tg_set_tile_variant.argtypes = [ctypes.c_int]
 _lib.tg_set_tile_variant.restype = ctypes.c_int
+_lib.tg_set_skinny_variant.argtypes = [ctypes.c_int]
+_lib.tg_set_skinny_variant.restype = ctypes.c_int
 _lib.tg_path_name.argtypes = [ctypes.c_int]
 _lib.tg_path_name.restype = ctypes.c_char_p
 
@@ -106,6 +109,10 @@ def tg_path_name(path: int) -> str:
 
 def tg_set_tile_variant(variant: int) -> int:
     return _lib.tg_set_tile_variant(variant)
+
+
+def tg_set_skinny_variant(variant: int) -> int:
+    return _lib.tg_set_skinny_variant(variant)
 
 
 # ----------------------------------------------------------- torch helpers

@@ -19,6 +19,8 @@ constexpr int kTile128Default = 3;   // 128x128x64, 4 stages
 constexpr int kTile256Default = 0;   // 256x256x64, 2 stages
 constexpr int kRegStaged128 = 10;    // register-staged kernels, kept for comparison
 constexpr int kRegStaged256 = 11;
+constexpr int kSkinnyDefault = 0;
+std::atomic<int> g_skinny_variant{-1};
 
 // Per-device architecture check, done once per device: 0 unknown, 1 gfx950,
 // 2 something else.
@@ -106,8 +108,14 @@ int choose_path(const tg::GemmArgs &p)
 {
     if (!fast_layout(p))
         return TG_PATH_GENERIC;
-    const int64_t tiles256 = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
-    if (tiles256 >= 1024)
+    if (p.M <= 64 && tg::skinny_layout_ok(p))
+        return TG_PATH_SKINNY;
+    // 256x256 tiles once there are enough of them to fill the chip and the
+    // padding they add to ragged edges is small; 128x128 tiles otherwise
+    const int64_t tm = (p.M + 255) / 256, tn = (p.N + 255) / 256;
+    const int64_t tiles256 = tm * tn * p.batch;
+    const double fill = (double)p.M * (double)p.N / ((double)tm * 256.0 * (double)tn * 256.0);
+    if (tiles256 >= 256 && fill >= 0.85)
         return TG_PATH_TILE256;
     return TG_PATH_TILE128;
 }
@@ -141,6 +149,8 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
         path = choose_path(p);
     else if (path != TG_PATH_NAIVE && path != TG_PATH_GENERIC && !fast_layout(p))
         path = TG_PATH_GENERIC;
+    else if (path == TG_PATH_SKINNY && !tg::skinny_layout_ok(p))
+        path = TG_PATH_TILE128;
 
     hipError_t e;
     switch (path) {
@@ -156,6 +166,11 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
             e = tg::launch_tile256(p, stream);
         else
             e = tg::launch_dma_config(v, p, stream, 8);
+        break;
+    }
+    case TG_PATH_SKINNY: {
+        int v = g_skinny_variant.load(std::memory_order_relaxed);
+        e = tg::launch_skinny_config(v < 0 ? kSkinnyDefault : v, p, stream);
         break;
     }
     default: e = tg::launch_generic(p, stream); path = TG_PATH_GENERIC; break;
@@ -198,12 +213,19 @@ const char *tg_status_string(int status)
 
 int tg_set_path(int path)
 {
-    if (path < 0 || path >= TG_PATH_COUNT || path == TG_PATH_SKINNY)
+    if (path < 0 || path >= TG_PATH_COUNT)
         return -1;
     return g_forced_path.exchange(path);
 }
 
 int tg_last_path(void) { return g_last_path.load(std::memory_order_relaxed); }
+
+int tg_set_skinny_variant(int variant)
+{
+    if (!(variant == -1 || (variant >= 0 && variant < tg::kSkinnyConfigs)))
+        return -2;
+    return g_skinny_variant.exchange(variant);
+}
 
 int tg_set_tile_variant(int variant)
 {

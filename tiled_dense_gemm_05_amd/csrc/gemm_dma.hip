@@ -303,6 +303,27 @@ __device__ __forceinline__ void step(f32x16 (&acc)[T::FM][T::FN], const f16x8 (&
     }
 }
 
+// The k steps 0 .. KSTEPS-2 of a tile: step kk works on fragment set kk & 1,
+// reads set (kk+1) & 1 and issues loads kk*DPS .. (kk+1)*DPS-1.
+template <class T, int KK = 0>
+__device__ __forceinline__ void inner_steps(f32x16 (&acc)[T::FM][T::FN], f16x8 (&af)[2][T::FM],
+                                            f16x8 (&bf)[2][T::FN], const LoadPlan<T> &lp,
+                                            const i32x4 &ra, const i32x4 &rb, bool a_kok,
+                                            int b_rows_left, uint32_t stage_addr, int wave,
+                                            const lds_u16 *As, const lds_u16 *Bs, int wm, int wn,
+                                            int lane)
+{
+    if constexpr (KK + 1 < T::KSTEPS) {
+        s16x4 bh[T::FN][2];
+        step<T, KK * T::DPS, (KK + 1) * T::DPS>(acc, af[KK & 1], bf[KK & 1], lp, ra, rb, a_kok,
+                                                 b_rows_left, stage_addr, wave, As, Bs, KK + 1, wm,
+                                                 wn, lane, af[(KK + 1) & 1], bh);
+        join_b<T>(bh, bf[(KK + 1) & 1]);
+        inner_steps<T, KK + 1>(acc, af, bf, lp, ra, rb, a_kok, b_rows_left, stage_addr, wave, As,
+                               Bs, wm, wn, lane);
+    }
+}
+
 template <class T, int I = 0>
 __device__ __forceinline__ void issue_tile(const LoadPlan<T> &lp, const i32x4 &ra, const i32x4 &rb,
                                            bool a_kok, int b_rows_left, uint32_t stage_addr,
@@ -404,21 +425,7 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_dma_kernel(GemmArgs p, int ti
         const i32x4 ra = rsrc_a(kl), rb = rsrc_b(kl);
         const bool akok = a_kok(kl);
         const int bleft = b_left(kl);
-#pragma unroll
-        for (int kk = 0; kk + 1 < T::KSTEPS; ++kk) {
-            s16x4 bh[T::FN][2];
-            // compile-time DMA range of this k step
-            if (kk == 0)
-                step<T, 0, T::DPS>(acc, af[0], bf[0], lp, ra, rb, akok, bleft, laddr, wave, As, Bs,
-                                   kk + 1, wm, wn, lane, af[1], bh);
-            else if (kk == 1)
-                step<T, T::DPS, 2 * T::DPS>(acc, af[1], bf[1], lp, ra, rb, akok, bleft, laddr, wave,
-                                            As, Bs, kk + 1, wm, wn, lane, af[0], bh);
-            else
-                step<T, 2 * T::DPS, 3 * T::DPS>(acc, af[0], bf[0], lp, ra, rb, akok, bleft, laddr,
-                                                wave, As, Bs, kk + 1, wm, wn, lane, af[1], bh);
-            join_b<T>(bh, bf[(kk + 1) & 1]);
-        }
+        inner_steps<T>(acc, af, bf, lp, ra, rb, akok, bleft, laddr, wave, As, Bs, wm, wn, lane);
         constexpr int cur = (T::KSTEPS - 1) & 1, nxt = T::KSTEPS & 1;
         // Tile kt+1 has landed once at most WAIT_LAST later loads of this wave
         // are outstanding.  On the last tile this step still runs (one MFMA
@@ -506,6 +513,10 @@ hipError_t launch_dma_config(int cfg, const GemmArgs &p, hipStream_t stream, int
     case 4: return launch_dma<Cfg<128, 128, 32, 2, 2, 4>>(p, stream, groupM);
     case 5: return launch_dma<Cfg<128, 128, 64, 2, 2, 3>>(p, stream, groupM);
     case 6: return launch_dma<Cfg<256, 128, 64, 2, 2, 3>>(p, stream, groupM);
+    // eight waves: two per SIMD, 128x64 or 64x128 wave tiles
+    case 7: return launch_dma<Cfg<256, 256, 32, 2, 4, 4>>(p, stream, groupM);
+    case 8: return launch_dma<Cfg<256, 256, 64, 2, 4, 2>>(p, stream, groupM);
+    case 9: return launch_dma<Cfg<256, 256, 32, 4, 2, 4>>(p, stream, groupM);
     default: return hipErrorInvalidValue;
     }
 }

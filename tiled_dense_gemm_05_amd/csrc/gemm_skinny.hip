@@ -1,0 +1,325 @@
+// Skinny-M fp16 GEMM + ReLU (M <= 64) on gfx950: a memory-bound stream of B.
+//
+// Same operation as the GEMM+ReLU tile program of the "TileLang paper
+// reading" page (hotelren.com), section 2, for the shape where A has a
+// handful of rows (decode-like): each element of B is used by at most 64
+// output rows, so the time is the time to stream B from HBM once.  The
+// "tilelang practitioner's notes" page (dpshk.com), section 1.1, names such
+// long, thin GEMMs as a case vendor libraries handle poorly; section 3.2 of
+// that page fixes K as a serial accumulation, so a K split must be summed
+// before the ReLU (done here in registers and LDS, in a fixed order).
+//
+// Design:
+//  * One workgroup per NB-column slice of C (grid = ceil(N / NB)), NW waves.
+//    The K range is split evenly over the waves; each wave streams its own
+//    part of the B slice through a private S-stage LDS ring with
+//    buffer_load_dwordx4 ... lds (one 1 KiB block per instruction) and never
+//    waits for the other waves until the end.  The A rows of the same K step
+//    ride along in the same stage (A is small and stays in L2).
+//  * Per 32-wide k step: v_mfma_f32_16x16x32_f16 with the operand roles
+//    swapped as in the tile kernels (C^T = B^T A^T): B^T fragments come from
+//    transpose reads (ds_read_b64_tr_b16) of the row-major B block, A^T
+//    fragments from one 16-byte LDS read per lane; a lane ends up owning 4
+//    consecutive columns of one C row.
+//  * Out-of-range chunks (k >= K, columns >= N, rows >= M) get a buffer
+//    offset at the descriptor's record count and read as zeros.
+//  * At the end each wave's fp32 partial sums go to LDS; after one barrier
+//    every output fragment is summed over the waves in wave order (the result
+//    is deterministic), clamped at zero, rounded to fp16 (nearest even) and
+//    stored.
+// Requirements (checked by the dispatcher): 16-byte aligned A, B, C; lda,
+// ldb, ldc, N, K multiples of 8; M <= 16 * MB.
+#include "tg_internal.h"
+
+namespace tg {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) f16x8 lds_f16x8;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+template <int MB_, int NB_, int NW_, int S_>
+struct Skinny {
+    static constexpr int MB = MB_;               // 16-row blocks of A / C
+    static constexpr int NB = NB_;               // columns of C per workgroup
+    static constexpr int NW = NW_;               // waves (K split)
+    static constexpr int S = S_;                 // LDS stages per wave
+    static constexpr int NT = 64 * NW;
+    static constexpr int NF = NB / 16;           // 16-column fragments
+    static constexpr int KS = 32;                // k per step
+    static constexpr int A_BYTES = MB * 16 * KS * 2;      // A rows of one step
+    static constexpr int B_BYTES = KS * NB * 2;           // B block of one step
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int A_LD = A_BYTES / 1024, B_LD = B_BYTES / 1024;
+    static constexpr int LOADS = A_LD + B_LD;
+    static constexpr int CB = NB / 8;            // 16-byte chunks per B row
+    static constexpr int B_RPB = 64 / CB;        // B rows per 1 KiB block
+    static constexpr int RING = NW * S * STAGE;
+    static constexpr int RED = NW * MB * NF * 64 * 16;    // partial sums
+    static constexpr int LDS = RING > RED ? RING : RED;
+    static_assert(NB == 32 || NB == 64, "slice width");
+    static_assert(LOADS * (S - 1) <= 63, "vmcnt range");
+    static_assert(LDS <= 160 * 1024, "LDS size");
+};
+
+// A block (MB*16 rows x 32 k, 64-byte rows): a 16-byte read of 16 rows at the
+// same chunk is spread over the bank line by XOR-ing the chunk with row / 4.
+__device__ __forceinline__ int swz_a(int row, int c) { return c ^ ((row >> 2) & 3); }
+
+// B block (32 rows x NB columns): a transpose read touches rows
+// {4h..4h+3} and {8+4h..8+4h+3} (32 bytes each) per half-wave; XOR the
+// 32-byte window of the row so those eight rows hit distinct windows.
+template <int CB>
+__device__ __forceinline__ int swz_b(int k, int c)
+{
+    if constexpr (CB == 8)
+        return c ^ ((((k >> 1) & 1) | (((k >> 3) & 1) << 1)) << 1);
+    else
+        return c ^ (((k >> 3) & 1) << 1);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt");
+    constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(imm);
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void wait_lgkm0()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((3 << 14) | (0 << 8) | (7 << 4) | 15);
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ i32x4 make_rsrc(const void *base)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+    r.z = (int)kOutOfRange;
+    r.w = 0x00020000;
+    return r;
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %2\n\t"
+                 "s_nop 0\n\t"
+                 "buffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(lds_addr)
+                 : "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t pack_relu_f16x2(float a, float b)
+{
+    const _Float16 ha = (_Float16)(a > 0.0f ? a : 0.0f);
+    const _Float16 hb = (_Float16)(b > 0.0f ? b : 0.0f);
+    return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+template <class T>
+__global__ void __launch_bounds__(T::NT) gemm_relu_skinny_kernel(GemmArgs p, int steps_per_wave)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS];
+    const lds_u16 *lds = (const lds_u16 *)smem;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t bidx = blockIdx.y;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int64_t n0 = (int64_t)blockIdx.x * T::NB;
+    const int64_t kw0 = (int64_t)wave * steps_per_wave * T::KS;   // this wave's first k
+    const uint16_t *Ab = p.A + bidx * p.sA + kw0;
+    const uint16_t *Bb = p.B + bidx * p.sB + kw0 * p.ldb + n0;
+    uint16_t *C = p.C + bidx * p.sC;
+    const uint32_t ring = lds_base + (uint32_t)(wave * T::S * T::STAGE);
+
+    // Load plan.  A block j (16 rows of 64 bytes): lane L -> row 16 j + L / 4,
+    // physical chunk L % 4.  B block j: lane L -> row j * B_RPB + L / CB,
+    // physical chunk L % CB.  The logical chunk is the swizzled one.
+    uint32_t a_voff[T::A_LD];
+    int a_col[T::A_LD];
+#pragma unroll
+    for (int j = 0; j < T::A_LD; ++j) {
+        const int row = 16 * j + lane / 4;
+        const int c = swz_a(row, lane % 4);
+        a_col[j] = c * 8;
+        a_voff[j] = row < M ? (uint32_t)((row * p.lda + c * 8) * 2) : kOutOfRange;
+    }
+    uint32_t b_voff[T::B_LD];
+    int b_row[T::B_LD];
+#pragma unroll
+    for (int j = 0; j < T::B_LD; ++j) {
+        const int row = j * T::B_RPB + lane / T::CB;
+        const int c = swz_b<T::CB>(row, lane % T::CB);
+        b_row[j] = row;
+        b_voff[j] = (n0 + c * 8 < N) ? (uint32_t)((row * p.ldb + c * 8) * 2) : kOutOfRange;
+    }
+
+    auto issue = [&](int st) {
+        const int64_t k0 = (int64_t)st * T::KS;          // relative to kw0
+        const int64_t kleft = K - kw0 - k0;               // valid k from here
+        const i32x4 ra = make_rsrc(Ab + k0);
+        const i32x4 rb = make_rsrc(Bb + k0 * p.ldb);
+        const uint32_t base = ring + (uint32_t)((st % T::S) * T::STAGE);
+#pragma unroll
+        for (int j = 0; j < T::A_LD; ++j)
+            dma16(ra, a_col[j] < kleft ? a_voff[j] : kOutOfRange, base + j * 1024);
+#pragma unroll
+        for (int j = 0; j < T::B_LD; ++j)
+            dma16(rb, b_row[j] < kleft ? b_voff[j] : kOutOfRange, base + T::A_BYTES + j * 1024);
+    };
+
+    f32x4 acc[T::MB][T::NF];
+#pragma unroll
+    for (int mb = 0; mb < T::MB; ++mb)
+#pragma unroll
+        for (int f = 0; f < T::NF; ++f)
+            acc[mb][f] = f32x4{};
+
+    // Every wave runs the same number of steps; steps past the end of K load
+    // zeros (no memory access) so the wait counts stay constant.
+#pragma unroll
+    for (int s = 0; s < T::S - 1; ++s)
+        issue(s);
+    for (int st = 0; st < steps_per_wave; ++st) {
+        // Refill the stage read one step ago (its reads completed before that
+        // step's MFMAs; the wait makes the order explicit), then wait until
+        // step st has landed: the S-1 later steps may still be in flight.
+        wait_lgkm0();
+        issue(st + T::S - 1);
+        wait_vmcnt<(T::S - 1) * T::LOADS>();
+        const lds_u16 *As = lds + (wave * T::S + st % T::S) * (T::STAGE / 2);
+        const lds_u16 *Bs = As + T::A_BYTES / 2;
+        f16x8 af[T::MB], bf[T::NF];
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb) {
+            const int row = mb * 16 + (lane & 15);
+            const int c = lane >> 4;
+            af[mb] = *reinterpret_cast<const lds_f16x8 *>(As + row * 32 + swz_a(row, c) * 8);
+        }
+#pragma unroll
+        for (int f = 0; f < T::NF; ++f) {
+            s16x4 h[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int k = 8 * (lane >> 4) + 4 * hh + ((lane & 15) >> 2);
+                const int n = f * 16 + 4 * (lane & 3);
+                const lds_u16 *src = Bs + k * T::NB + swz_b<T::CB>(k, n >> 3) * 8 + (n & 7);
+                h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src);
+            }
+            bf[f] = __builtin_bit_cast(f16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb)
+#pragma unroll
+            for (int f = 0; f < T::NF; ++f)
+                acc[mb][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[f], af[mb], acc[mb][f], 0, 0, 0);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();   // every wave is done with its ring before it is reused
+
+    // Partial sums: [wave][mb][f][lane] of 4 floats.
+    lds_f32x4 *part = (lds_f32x4 *)smem;
+#pragma unroll
+    for (int mb = 0; mb < T::MB; ++mb)
+#pragma unroll
+        for (int f = 0; f < T::NF; ++f)
+            part[((wave * T::MB + mb) * T::NF + f) * 64 + lane] = acc[mb][f];
+    __syncthreads();
+
+    // Fragment q = (mb, f) is finished by wave q % NW: sum over the waves in
+    // order, ReLU, fp16, store.  Lane owns C[m][n .. n+3].
+    for (int q = wave; q < T::MB * T::NF; q += T::NW) {
+        f32x4 s = part[q * 64 + lane];
+        for (int w = 1; w < T::NW; ++w)
+            s += part[(w * T::MB * T::NF + q) * 64 + lane];
+        const int mb = q / T::NF, f = q % T::NF;
+        const int64_t m = mb * 16 + (lane & 15);
+        const int64_t n = n0 + f * 16 + 4 * (lane >> 4);
+        if (m < M && n < N) {
+            u32x2 w2;
+            w2.x = pack_relu_f16x2(s[0], s[1]);
+            w2.y = pack_relu_f16x2(s[2], s[3]);
+            *reinterpret_cast<u32x2 *>(C + m * p.ldc + n) = w2;
+        }
+    }
+}
+
+template <class T>
+hipError_t launch(const GemmArgs &p, hipStream_t stream)
+{
+    const int64_t slices = (p.N + T::NB - 1) / T::NB;
+    const int64_t ksteps = (p.K + T::KS - 1) / T::KS;
+    const int64_t per_wave = (ksteps + T::NW - 1) / T::NW;
+    if (slices > 0x7fffffff || per_wave > 0x7fffffff)
+        return hipErrorInvalidValue;
+    GemmArgs q = p;
+    for (int64_t b0 = 0; b0 < p.batch; b0 += 65535) {
+        const int64_t nb = (p.batch - b0) < 65535 ? (p.batch - b0) : 65535;
+        q.A = p.A + b0 * p.sA;
+        q.B = p.B + b0 * p.sB;
+        q.C = p.C + b0 * p.sC;
+        q.batch = nb;
+        hipLaunchKernelGGL((gemm_relu_skinny_kernel<T>), dim3((unsigned)slices, (unsigned)nb),
+                           dim3(T::NT), 0, stream, q, (int)per_wave);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+bool skinny_layout_ok(const GemmArgs &p)
+{
+    // M <= 64; 32-bit buffer offsets: 64 A rows and 32 B rows per step
+    return p.M <= 64 && p.lda <= (1 << 24) && p.ldb <= (1 << 24);
+}
+
+hipError_t launch_skinny_config(int cfg, const GemmArgs &p, hipStream_t stream)
+{
+    const int mb = (int)((p.M + 15) / 16);
+    switch (cfg) {
+    case 0:   // 64-column slices, 4 waves, 6 stages
+        if (mb <= 1) return launch<Skinny<1, 64, 4, 6>>(p, stream);
+        if (mb <= 2) return launch<Skinny<2, 64, 4, 5>>(p, stream);
+        return launch<Skinny<4, 64, 4, 4>>(p, stream);
+    case 1:   // 32-column slices, 4 waves, 8 stages
+        if (mb <= 1) return launch<Skinny<1, 32, 4, 8>>(p, stream);
+        if (mb <= 2) return launch<Skinny<2, 32, 4, 6>>(p, stream);
+        return launch<Skinny<4, 32, 4, 5>>(p, stream);
+    case 2:   // 64-column slices, 8 waves, 3 stages
+        if (mb <= 1) return launch<Skinny<1, 64, 8, 3>>(p, stream);
+        if (mb <= 2) return launch<Skinny<2, 64, 8, 3>>(p, stream);
+        return launch<Skinny<4, 64, 8, 2>>(p, stream);
+    case 3:   // 32-column slices, 8 waves, 4 stages
+        if (mb <= 1) return launch<Skinny<1, 32, 8, 4>>(p, stream);
+        if (mb <= 2) return launch<Skinny<2, 32, 8, 4>>(p, stream);
+        return launch<Skinny<4, 32, 8, 3>>(p, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace tg

@@ -24,12 +24,16 @@ hipError_t launch_naive(const GemmArgs &p, hipStream_t stream);
 hipError_t launch_generic(const GemmArgs &p, hipStream_t stream);
 hipError_t launch_tile128(const GemmArgs &p, hipStream_t stream);
 hipError_t launch_tile256(const GemmArgs &p, hipStream_t stream);
-hipError_t launch_skinny(const GemmArgs &p, hipStream_t stream);
 
 // Direct-to-LDS pipelined kernels (aligned layouts only).  `cfg` selects the
 // block tile / K tile / stage count; see gemm_dma.hip.
-constexpr int kDmaConfigs = 7;
+constexpr int kDmaConfigs = 10;
 hipError_t launch_dma_config(int cfg, const GemmArgs &p, hipStream_t stream, int groupM);
+// Skinny-M kernels (M <= 64, aligned layouts); `cfg` selects slice width,
+// waves and stages; see gemm_skinny.hip.
+constexpr int kSkinnyConfigs = 4;
+hipError_t launch_skinny_config(int cfg, const GemmArgs &p, hipStream_t stream);
+bool skinny_layout_ok(const GemmArgs &p);
 // Whether the leading dimensions fit the kernels' 32-bit buffer offsets.
 bool dma_layout_ok(const GemmArgs &p);
 
