@@ -29,7 +29,9 @@ import workloads as wl  # noqa: E402
 METRIC = "TFLOP/s fp16 GEMM+ReLU at 8192^3 (% of FP16 MFMA peak); GB/s at M=16"
 PEAK_F16_TFLOPS = 2516.6     # 256 CU x 4096 flop/clk x 2.4 GHz, dense
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic.txt")
+COPY_BYTES = 1 << 30          # the calibration copy: 1 GiB read + 1 GiB written
 CSRC = os.path.join(ROOT, "tiled_dense_gemm_05_amd", "csrc")
 
 
@@ -45,18 +47,38 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def read_traffic_file() -> dict:
+    """profiles/traffic.txt: one line per workload,
+    `workload source_hash fetch_bytes write_bytes` (per launch, calibrated)."""
+    out = {}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                parts = line.split()
+                if len(parts) == 4 and not line.startswith("#"):
+                    out[parts[0]] = (parts[1], float(parts[2]), float(parts[3]))
+    except OSError:
+        pass
+    return out
+
+
 def measured_traffic(workload: str):
     """HBM bytes per launch from the committed counter runs, only while the
     kernel sources are unchanged since those counters were taken."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+    e = read_traffic_file().get(workload)
+    if not e or e[0] != kernel_source_hash():
         return None
-    e = t.get(workload)
-    if not e or e.get("source_hash") != kernel_source_hash():
-        return None
-    return e.get("bytes_per_launch")
+    return e[1] + e[2]
+
+
+def calibration_copy(torch):
+    """A plain 1 GiB device-to-device copy, twice, for counter calibration."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def run_workload(tg, torch, w: wl.Workload, steps: int, warmup: int):
@@ -116,11 +138,13 @@ def cpu_baseline(w: wl.Workload, target_s: float = 12.0):
         oracle.gemm_relu(a[: r * w.lda_], b, r, N, K, w.lda_, w.ldb_, w.ldc_, threads=threads)
         return time.perf_counter() - t
 
-    r = max(threads, 16)
-    dt = timed(r)
-    r2 = int(min(w.M, max(r, r * target_s / max(dt, 1e-3))))
-    r2 = max(threads, (r2 // threads) * threads)
-    dt2 = timed(r2)
+    r2, dt2 = max(threads, 16), 0.0
+    for _ in range(4):
+        dt2 = timed(r2)
+        if dt2 >= 0.6 * target_s or r2 >= w.M:
+            break
+        r2 = int(min(w.M, r2 * target_s / max(dt2, 1e-3)))
+        r2 = max(threads, (r2 // threads) * threads)
     tflops = 2.0 * r2 * N * K / dt2 / 1e12
     return {
         "value": tflops,
@@ -128,11 +152,98 @@ def cpu_baseline(w: wl.Workload, target_s: float = 12.0):
         "cores": threads,
         "kind": "oracle",
         "sample": (f"rows 0..{r2 - 1} of the {w.M}x{w.N}x{w.K} workload's C ({r2}x{N}x{K} "
-                   f"multiply-adds, binary64 C oracle, {threads} threads), {dt2:.1f} s"),
+                   f"multiply-adds, binary64 C oracle, {threads} threads), {dt2:.1f} s, "
+                   f"rate scaled to the whole workload"),
     }
 
 
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(d, suffix):
+    for root, _, files in os.walk(d):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def summarize(workload: str, stats_dir: str, fetch_dir: str, write_dir: str, commands: list[str]):
+    """Writes profiles/<kernel-workload>.md from rocprofv3 output directories
+    (kernel-trace --stats run, then one --pmc FETCH_SIZE and one --pmc
+    WRITE_SIZE run of `bench.py --calibrate-copy`), and records the
+    calibrated HBM bytes per launch in profiles/traffic.txt."""
+    import collections
+    stats = _csv_rows(_find(stats_dir, "kernel_stats.csv"))
+    stats.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    top = stats[0]
+
+    def per_kernel(d, counter):
+        acc = collections.defaultdict(list)
+        per_dispatch = collections.defaultdict(float)
+        names = {}
+        for r in _csv_rows(_find(d, "counter_collection.csv")):
+            if r["Counter_Name"] != counter:
+                continue
+            per_dispatch[r["Dispatch_Id"]] += float(r["Counter_Value"])
+            names[r["Dispatch_Id"]] = r["Kernel_Name"]
+        for k, v in per_dispatch.items():
+            acc[names[k]].append(v)
+        return acc
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    copy_name = next(n for n in fetch if "copyBuffer" in n or "copy" in n.lower())
+    gemm_name = max(fetch, key=lambda n: sum(fetch[n]) if "tg::" in n else -1)
+    kib = 1024.0
+    copy_fetch = sum(fetch[copy_name]) / len(fetch[copy_name]) * kib
+    copy_write = sum(write[copy_name]) / len(write[copy_name]) * kib
+    f_fetch = COPY_BYTES / copy_fetch
+    f_write = COPY_BYTES / copy_write
+    g_fetch = sum(fetch[gemm_name]) / len(fetch[gemm_name]) * kib * f_fetch
+    g_write = sum(write[gemm_name]) / len(write[gemm_name]) * kib * f_write
+    w = wl.WORKLOADS[workload]
+    family = ("gemm_relu_dma_kernel" if "dma_kernel" in top["Name"] else
+              "gemm_relu_skinny_kernel" if "skinny_kernel" in top["Name"] else "kernel")
+    md = os.path.join(PROFILES, f"{family}-{workload}.md")
+    with open(md, "w") as f:
+        f.write(f"# {top['Name']} on {workload}\n\n")
+        f.write("Commands (from the repository root on the GPU box):\n\n")
+        for c in commands:
+            f.write(f"    {c}\n")
+        f.write("\nKernel trace (rocprofv3 --kernel-trace --stats), top kernels:\n\n")
+        f.write("| kernel | calls | average ns | min ns | max ns |\n|---|---|---|---|---|\n")
+        for r in stats[:4]:
+            f.write(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                    f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} |\n")
+        f.write(f"\nAlgorithmic work per launch: {w.flops:.4e} flop, "
+                f"{w.compulsory_bytes:.4e} compulsory HBM bytes.\n")
+        f.write(f"\nCounters (rocprofv3 --pmc, one counter set per run), per launch:\n\n")
+        f.write(f"* calibration copy of {COPY_BYTES} bytes: FETCH_SIZE {copy_fetch:.4e} B, "
+                f"WRITE_SIZE {copy_write:.4e} B -> factors {f_fetch:.3f} (fetch), "
+                f"{f_write:.3f} (write)\n")
+        reads = 2 * (w.M * w.K + w.K * w.N) * w.batch
+        writes = 2 * w.M * w.N * w.batch
+        f.write(f"* GEMM: HBM read {g_fetch:.4e} B ({g_fetch / reads:.2f} x the {reads:.4e} B of A and B), "
+                f"HBM write {g_write:.4e} B ({g_write / writes:.2f} x the {writes:.4e} B of C)\n")
+        f.write(f"* kernel source hash {kernel_source_hash()}\n")
+    lines = {k: v for k, v in read_traffic_file().items()}
+    lines[workload] = (kernel_source_hash(), g_fetch, g_write)
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("# workload source_hash hbm_read_bytes hbm_write_bytes (per launch, calibrated)\n")
+        for k, (h, r_, w_) in sorted(lines.items()):
+            f.write(f"{k} {h} {r_:.6e} {w_:.6e}\n")
+    print(f"wrote {md} and {TRAFFIC_FILE}")
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize":
+        # bench.py --summarize WORKLOAD STATS_DIR FETCH_DIR WRITE_DIR "cmd1" "cmd2" ...
+        summarize(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6:])
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -140,6 +251,8 @@ def main():
     ap.add_argument("--workload", default="large_8192", choices=sorted(wl.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a 1 GiB copy first (counter calibration runs only)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -154,6 +267,8 @@ def main():
         sys.exit(1)
     import tiled_dense_gemm_05_amd as tg
 
+    if args.calibrate_copy:
+        calibration_copy(torch)
     w = wl.WORKLOADS[args.workload]
     log(f"workload {w.name}: M={w.M} N={w.N} K={w.K} batch={w.batch}")
     ms, path, nbuf = run_workload(tg, torch, w, args.steps, args.warmup)

@@ -110,16 +110,16 @@ int tg_last_path(void);
 /*
  * Tuning knob for benchmarks: selects the kernel configuration (block tile,
  * K tile, pipeline depth) that the tile paths use.  -1 restores the defaults;
- * 0..9 are the direct-to-LDS configurations, 10 and 11 the register-staged
- * 128x128 and 256x256 kernels.  Returns the previous setting, or -2 for an
+ * 0..11 are the direct-to-LDS configurations, 100 and 101 the
+ * register-staged 128x128 and 256x256 kernels.  Returns the previous setting, or -2 for an
  * unknown variant (the setting is unchanged).  Results are identical within
  * the accuracy contract for every variant; only speed changes.
  */
 int tg_set_tile_variant(int variant);
 
 /*
- * The same for the skinny path (M <= 64): 0..3 select the column-slice width,
- * wave count and pipeline depth; -1 restores the default.  Returns the
+ * The same for the skinny path (M <= 64): 0..6 select the column-slice width,
+ * wave count, pipeline depth and cache hint; -1 restores the default.  Returns the
  * previous setting, or -2 for an unknown variant.
  */
 int tg_set_skinny_variant(int variant);

@@ -16,10 +16,11 @@ std::atomic<int> g_tile_variant{-1};
 
 // Default direct-to-LDS configurations of the tile paths.
 constexpr int kTile128Default = 3;   // 128x128x64, 4 stages
-constexpr int kTile256Default = 0;   // 256x256x64, 2 stages
-constexpr int kRegStaged128 = 10;    // register-staged kernels, kept for comparison
-constexpr int kRegStaged256 = 11;
-constexpr int kSkinnyDefault = 0;
+constexpr int kTile256Default = 0;   // 256x256x32, 4 stages
+constexpr int kTile128ShortK = 10;   // 128x128x32, 2 stages: several workgroups per CU
+constexpr int kRegStaged128 = 100;   // register-staged kernels, kept for comparison
+constexpr int kRegStaged256 = 101;
+constexpr int kSkinnyDefault = 4;   // 64-column slices, 4 waves, 6 stages, non-temporal B
 std::atomic<int> g_skinny_variant{-1};
 
 // Per-device architecture check, done once per device: 0 unknown, 1 gfx950,
@@ -159,7 +160,8 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
     case TG_PATH_TILE256: {
         int v = g_tile_variant.load(std::memory_order_relaxed);
         if (v < 0)
-            v = path == TG_PATH_TILE128 ? kTile128Default : kTile256Default;
+            v = path == TG_PATH_TILE256 ? kTile256Default
+                : (p.K <= 64 ? kTile128ShortK : kTile128Default);
         if (v == kRegStaged128)
             e = tg::launch_tile128(p, stream);
         else if (v == kRegStaged256)

@@ -517,6 +517,9 @@ hipError_t launch_dma_config(int cfg, const GemmArgs &p, hipStream_t stream, int
     case 7: return launch_dma<Cfg<256, 256, 32, 2, 4, 4>>(p, stream, groupM);
     case 8: return launch_dma<Cfg<256, 256, 64, 2, 4, 2>>(p, stream, groupM);
     case 9: return launch_dma<Cfg<256, 256, 32, 4, 2, 4>>(p, stream, groupM);
+    // small LDS footprint: several workgroups per CU for short K
+    case 10: return launch_dma<Cfg<128, 128, 32, 2, 2, 2>>(p, stream, groupM);
+    case 11: return launch_dma<Cfg<128, 128, 64, 2, 2, 2>>(p, stream, groupM);
     default: return hipErrorInvalidValue;
     }
 }

@@ -46,8 +46,9 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-template <int MB_, int NB_, int NW_, int S_>
+template <int MB_, int NB_, int NW_, int S_, bool NTB_ = false>
 struct Skinny {
+    static constexpr bool NTB = NTB_;            // stream B with non-temporal loads
     static constexpr int MB = MB_;               // 16-row blocks of A / C
     static constexpr int NB = NB_;               // columns of C per workgroup
     static constexpr int NW = NW_;               // waves (K split)
@@ -65,7 +66,7 @@ struct Skinny {
     static constexpr int RING = NW * S * STAGE;
     static constexpr int RED = NW * MB * NF * 64 * 16;    // partial sums
     static constexpr int LDS = RING > RED ? RING : RED;
-    static_assert(NB == 32 || NB == 64, "slice width");
+    static_assert(NB == 32 || NB == 64 || NB == 128, "slice width");
     static_assert(LOADS * (S - 1) <= 63, "vmcnt range");
     static_assert(LDS <= 160 * 1024, "LDS size");
 };
@@ -80,7 +81,9 @@ __device__ __forceinline__ int swz_a(int row, int c) { return c ^ ((row >> 2) & 
 template <int CB>
 __device__ __forceinline__ int swz_b(int k, int c)
 {
-    if constexpr (CB == 8)
+    if constexpr (CB == 16)
+        return c ^ (((k & 3) | (((k >> 3) & 1) << 2)) << 1);
+    else if constexpr (CB == 8)
         return c ^ ((((k >> 1) & 1) | (((k >> 3) & 1) << 1)) << 1);
     else
         return c ^ (((k >> 3) & 1) << 1);
@@ -121,6 +124,18 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_ad
     asm volatile("s_mov_b32 m0, %2\n\t"
                  "s_nop 0\n\t"
                  "buffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(lds_addr)
+                 : "m0");
+}
+
+// The same with the non-temporal hint: data streamed once is not kept in the
+// caches.
+__device__ __forceinline__ void dma16_nt(i32x4 rsrc, uint32_t voff, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %2\n\t"
+                 "s_nop 0\n\t"
+                 "buffer_load_dwordx4 %0, %1, 0 offen nt lds"
                  :
                  : "v"(voff), "s"(rsrc), "s"(lds_addr)
                  : "m0");
@@ -186,8 +201,13 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_skinny_kernel(GemmArgs p, int
         for (int j = 0; j < T::A_LD; ++j)
             dma16(ra, a_col[j] < kleft ? a_voff[j] : kOutOfRange, base + j * 1024);
 #pragma unroll
-        for (int j = 0; j < T::B_LD; ++j)
-            dma16(rb, b_row[j] < kleft ? b_voff[j] : kOutOfRange, base + T::A_BYTES + j * 1024);
+        for (int j = 0; j < T::B_LD; ++j) {
+            const uint32_t v = b_row[j] < kleft ? b_voff[j] : kOutOfRange;
+            if constexpr (T::NTB)
+                dma16_nt(rb, v, base + T::A_BYTES + j * 1024);
+            else
+                dma16(rb, v, base + T::A_BYTES + j * 1024);
+        }
     };
 
     f32x4 acc[T::MB][T::NF];
@@ -318,6 +338,18 @@ hipError_t launch_skinny_config(int cfg, const GemmArgs &p, hipStream_t stream)
         if (mb <= 1) return launch<Skinny<1, 32, 8, 4>>(p, stream);
         if (mb <= 2) return launch<Skinny<2, 32, 8, 4>>(p, stream);
         return launch<Skinny<4, 32, 8, 3>>(p, stream);
+    case 4:   // 64-column slices, 4 waves, 6 stages, non-temporal B
+        if (mb <= 1) return launch<Skinny<1, 64, 4, 6, true>>(p, stream);
+        if (mb <= 2) return launch<Skinny<2, 64, 4, 5, true>>(p, stream);
+        return launch<Skinny<4, 64, 4, 4, true>>(p, stream);
+    case 5:   // 128-column slices, 8 waves, 2 stages
+        if (mb <= 1) return launch<Skinny<1, 128, 8, 2>>(p, stream);
+        if (mb <= 2) return launch<Skinny<2, 128, 8, 2>>(p, stream);
+        return launch<Skinny<4, 128, 4, 2>>(p, stream);
+    case 6:   // 128-column slices, 4 waves, 4 stages, non-temporal B
+        if (mb <= 1) return launch<Skinny<1, 128, 4, 4, true>>(p, stream);
+        if (mb <= 2) return launch<Skinny<2, 128, 4, 3, true>>(p, stream);
+        return launch<Skinny<4, 128, 4, 2, true>>(p, stream);
     default: return hipErrorInvalidValue;
     }
 }
