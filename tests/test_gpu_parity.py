@@ -343,7 +343,7 @@ def test_workloads_full_size(tg, oracle_lib, name, n):
 
 # ------------------------------------------------------ every tile configuration
 
-VARIANTS = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 100, 101]
+VARIANTS = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 100, 101]
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -380,3 +380,60 @@ def test_skinny_is_auto_for_small_m(tg, oracle_lib):
     assert used == "skinny"
     used, _, _ = full_case(tg, oracle_lib, 65, 512, 256, seed=6)
     assert used != "skinny"
+
+
+# ------------------------------------------------------------ random shapes
+
+
+def _random_case(rng):
+    """Random small strided-batched problem: sizes 1..300 with a bias towards
+    tile edges, aligned or not, padded leading dimensions, a few batches."""
+    def dim(hi):
+        r = rng.random()
+        if r < 0.3:
+            return int(rng.integers(1, 17))
+        if r < 0.6:
+            base = int(rng.choice([32, 64, 128, 256]))
+            return max(1, base + int(rng.integers(-2, 3)))
+        return int(rng.integers(1, hi))
+    M, N, K = dim(300), dim(300), dim(300)
+    if rng.random() < 0.5:      # aligned layouts (fast paths)
+        N = (N + 7) // 8 * 8
+        K = (K + 7) // 8 * 8
+        lda = K + 8 * int(rng.integers(0, 3))
+        ldb = N + 8 * int(rng.integers(0, 3))
+        ldc = N + 8 * int(rng.integers(0, 3))
+    else:
+        lda = K + int(rng.integers(0, 5))
+        ldb = N + int(rng.integers(0, 5))
+        ldc = N + int(rng.integers(0, 5))
+    batch = int(rng.choice([1, 1, 2, 3]))
+    return M, N, K, lda, ldb, ldc, batch
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_shapes_match_oracle(tg, oracle_lib, seed):
+    rng = np.random.default_rng(9000 + seed)
+    M, N, K, lda, ldb, ldc, batch = _random_case(rng)
+    sA = M * lda + 8 * int(rng.integers(0, 2))
+    sB = K * ldb + 8 * int(rng.integers(0, 2))
+    sC = (M - 1) * ldc + N + 8 * int(rng.integers(0, 3))
+    a, b = wl.generate_dense(M, N, K, "uniform", seed, batch=batch)
+    ab = np.full(batch * sA, SENTINEL, np.uint16)
+    bb = np.full(batch * sB, SENTINEL, np.uint16)
+    for i in range(batch):
+        ab[i * sA:i * sA + M * lda] = wl.pad_rows(a[i * M * K:(i + 1) * M * K], M, K, lda)
+        bb[i * sB:i * sB + K * ldb] = wl.pad_rows(b[i * K * N:(i + 1) * K * N], K, N, ldb)
+    csize = (batch - 1) * sC + (M - 1) * ldc + N
+    ref = np.full(csize + 32, SENTINEL, np.uint16)
+    ref, S, Sa = oracle_lib.gemm_relu(ab, bb, M, N, K, lda, ldb, ldc, batch, sA, sB, sC, C=ref,
+                                      want_sums=True)
+    c_d = dev(np.full(csize + 32, SENTINEL, np.uint16))
+    say(f"random seed={seed} M={M} N={N} K={K} ld=({lda},{ldb},{ldc}) batch={batch} "
+        f"strides=({sA},{sB},{sC})")
+    used = run_batched(tg, dev(ab), dev(bb), c_d, M, N, K, lda, ldb, ldc, sA, sB, sC, batch)
+    out = host(c_d)
+    assert np.array_equal(out == SENTINEL, ref == SENTINEL), f"{used}: wrote outside the windows"
+    win = ref != SENTINEL
+    rep = gate(out[win], ref[win], K, Sa.reshape(-1))
+    assert rep.ok, f"{used}: {rep}"

@@ -17,7 +17,7 @@ std::atomic<int> g_tile_variant{-1};
 // Default direct-to-LDS configurations of the tile paths.
 constexpr int kTile128Default = 3;   // 128x128x64, 4 stages
 constexpr int kTile256Default = 0;   // 256x256x32, 4 stages
-constexpr int kTile128ShortK = 10;   // 128x128x32, 2 stages: several workgroups per CU
+constexpr int kTile128ShortK = 12;   // 128x128x32, 2 stages, 4 waves/SIMD: several workgroups per CU
 constexpr int kRegStaged128 = 100;   // register-staged kernels, kept for comparison
 constexpr int kRegStaged256 = 101;
 constexpr int kSkinnyDefault = 4;   // 64-column slices, 4 waves, 6 stages, non-temporal B

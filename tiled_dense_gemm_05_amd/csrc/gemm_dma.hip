@@ -52,11 +52,13 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 constexpr uint32_t kOutOfRange = 0x80000000u;   // == the descriptors' record count
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int OCC_ = 1, int KG_ = 1>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, STAGES = STAGES_;
-    static constexpr int NW = WM * WN;                // waves
-    static constexpr int NT = 64 * NW;                // threads
+    static constexpr int OCC = OCC_;                  // waves per SIMD the registers must allow
+    static constexpr int KG = KG_;                    // K groups: wave groups on alternate K tiles
+    static constexpr int NW = WM * WN;                // waves per K group
+    static constexpr int NT = 64 * NW * KG;           // threads
     static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
     static constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 fragments per wave
     static constexpr int CA = BK / 8, CB = BN / 8;    // 16-byte chunks per tile row
@@ -84,7 +86,10 @@ struct Cfg {
     static_assert(TM % 32 == 0 && TN % 32 == 0 && BK % 16 == 0, "fragment shape");
     static_assert(LOADS * (STAGES - 1) <= 63, "vmcnt range");
     static_assert(KSTEPS <= 4, "k steps per tile");
-    static_assert(STAGE * 2 * STAGES <= 160 * 1024, "LDS size");
+    static constexpr int RING = KG * STAGES * STAGE * 2;        // bytes of LDS rings
+    static constexpr int RED = (KG - 1) * NW * FM * FN * 64 * 64; // partial sums of groups > 0
+    static constexpr int LDS = RING > RED ? RING : RED;
+    static_assert(LDS <= 160 * 1024, "LDS size");
     // a thread's loads of one tile share one swizzled column (see load plan)
     static_assert((NW * A_RPB) % 16 == 0 && (NW * B_RPB) % 4 == 0, "swizzle period");
 };
@@ -336,16 +341,20 @@ __device__ __forceinline__ void issue_tile(const LoadPlan<T> &lp, const i32x4 &r
 }
 
 template <class T>
-__global__ void __launch_bounds__(T::NT) gemm_relu_dma_kernel(GemmArgs p, int tilesM, int tilesN,
-                                                              int groupM)
+__global__ void __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(T::OCC)))
+gemm_relu_dma_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
 {
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[T::STAGES * T::STAGE];
-    const lds_u16 *lds = (const lds_u16 *)smem;
-    const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[T::LDS / 2];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // K group kg works on K tiles kg, kg + KG, ... with its own LDS ring;
+    // `wave` is the wave's index inside its group
+    const int kg = wave_all / T::NW;
+    const int wave = wave_all % T::NW;
+    const lds_u16 *lds = (const lds_u16 *)smem + kg * T::STAGES * T::STAGE;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
     const int wm = wave / T::WN, wn = wave % T::WN;
     int tm, tn;
     tile_coords(blockIdx.x, tilesM, tilesN, groupM, tm, tn);
@@ -383,11 +392,12 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_dma_kernel(GemmArgs p, int ti
             lp.b_voff[j] = col_ok ? (uint32_t)((row * p.ldb + c * 8) * 2) : kOutOfRange;
         }
     }
-    auto rsrc_a = [&](int kt) { return make_rsrc(Ab + (int64_t)kt * T::BK); };
-    auto rsrc_b = [&](int kt) { return make_rsrc(Bb + (int64_t)kt * T::BK * p.ldb); };
-    auto a_kok = [&](int kt) { return (int64_t)kt * T::BK + lp.a_kcol < K; };
-    auto b_left = [&](int kt) {
-        const int64_t r = K - (int64_t)kt * T::BK;
+    // the group's t-th K tile is K tile t * KG + kg
+    auto rsrc_a = [&](int t) { return make_rsrc(Ab + ((int64_t)t * T::KG + kg) * T::BK); };
+    auto rsrc_b = [&](int t) { return make_rsrc(Bb + ((int64_t)t * T::KG + kg) * T::BK * p.ldb); };
+    auto a_kok = [&](int t) { return ((int64_t)t * T::KG + kg) * T::BK + lp.a_kcol < K; };
+    auto b_left = [&](int t) {
+        const int64_t r = K - ((int64_t)t * T::KG + kg) * T::BK;
         return (int)(r < 0 ? 0 : (r > T::BK ? T::BK : r));
     };
 
@@ -398,7 +408,9 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_dma_kernel(GemmArgs p, int ti
         for (int fn = 0; fn < T::FN; ++fn)
             acc[fm][fn] = f32x16{};
 
-    const int KT = (int)((K + T::BK - 1) / T::BK);
+    // every group runs the same number of tiles (a group past the end of K
+    // loads zeros) so that the workgroup barriers line up
+    const int KT = (int)(((K + T::BK - 1) / T::BK + T::KG - 1) / T::KG);
     f16x8 af[2][T::FM], bf[2][T::FN];
     if (KT > 0) {
         // Issue the first tiles (tiles past the end of K load zeros and never
@@ -445,6 +457,31 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_dma_kernel(GemmArgs p, int ti
     }
     // loads issued past the end of K must land before the LDS is released
     wait_vmcnt<0>();
+
+    if constexpr (T::KG > 1) {
+        // Groups 1 .. KG-1 hand their partial sums to group 0 through LDS;
+        // group 0 adds them in group order (deterministic) and stores.
+        block_barrier();
+        typedef __attribute__((address_space(3))) f32x16 lds_f32x16;
+        lds_f32x16 *part = (lds_f32x16 *)smem;
+        if (kg > 0) {
+#pragma unroll
+            for (int fm = 0; fm < T::FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < T::FN; ++fn)
+                    part[(((kg - 1) * T::NW + wave) * T::FM * T::FN + fm * T::FN + fn) * 64 + lane] =
+                        acc[fm][fn];
+        }
+        block_barrier();
+        if (kg > 0)
+            return;
+        for (int g = 1; g < T::KG; ++g)
+#pragma unroll
+            for (int fm = 0; fm < T::FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < T::FN; ++fn)
+                    acc[fm][fn] += part[(((g - 1) * T::NW + wave) * T::FM * T::FN + fm * T::FN + fn) * 64 + lane];
+    }
 
     // Epilogue: ReLU, round to nearest even, 8-byte stores (N % 8 == 0 and
     // 16-byte aligned rows make every 4-column group wholly in or out).
@@ -520,6 +557,15 @@ hipError_t launch_dma_config(int cfg, const GemmArgs &p, hipStream_t stream, int
     // small LDS footprint: several workgroups per CU for short K
     case 10: return launch_dma<Cfg<128, 128, 32, 2, 2, 2>>(p, stream, groupM);
     case 11: return launch_dma<Cfg<128, 128, 64, 2, 2, 2>>(p, stream, groupM);
+    case 12: return launch_dma<Cfg<128, 128, 32, 2, 2, 2, 4>>(p, stream, groupM);
+    case 13: return launch_dma<Cfg<128, 128, 64, 2, 2, 2, 2>>(p, stream, groupM);
+    // two K groups of four waves (two waves per SIMD on alternate K tiles)
+    case 14: return launch_dma<Cfg<128, 128, 64, 2, 2, 2, 2, 2>>(p, stream, groupM);
+    case 15: return launch_dma<Cfg<128, 128, 32, 2, 2, 4, 2, 2>>(p, stream, groupM);
+    case 16: return launch_dma<Cfg<128, 128, 32, 2, 2, 3, 2, 2>>(p, stream, groupM);
+    // deep rings for latency-bound mid-size shapes
+    case 17: return launch_dma<Cfg<128, 128, 32, 2, 2, 8>>(p, stream, groupM);
+    case 18: return launch_dma<Cfg<128, 128, 64, 2, 2, 5>>(p, stream, groupM);
     default: return hipErrorInvalidValue;
     }
 }

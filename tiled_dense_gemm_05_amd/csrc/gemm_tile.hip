@@ -36,6 +36,10 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// the same vectors at 4-byte alignment: gfx950 vector memory instructions
+// need only dword alignment
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) f16x8 lds_f16x8;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -113,12 +117,29 @@ __device__ __forceinline__ u32x4 pack8(const uint16_t (&e)[8])
 }
 
 // Eight consecutive elements p[0..7] of a row whose valid length from p is
-// `avail` (elements past it read as zero).  The vector form needs 16-byte
-// alignment; otherwise elements are read one by one.
-__device__ __forceinline__ u32x4 load8_masked(const uint16_t *p, int64_t avail)
+// `avail` (elements past it read as zero).  Whole chunks at a 4-byte aligned
+// address are one dword-aligned vector load.  Chunks at 2 mod 4 read the
+// dword-aligned window starting one element earlier plus one more dword and
+// shift by 16 bits; `window_ok` says that p[-1] and p[8] lie inside the
+// operand's extent.  Everything else is read element by element.
+__device__ __forceinline__ u32x4 load8_masked(const uint16_t *p, int64_t avail, bool window_ok)
 {
-    if (avail >= 8 && (reinterpret_cast<uintptr_t>(p) & 15) == 0)
-        return *reinterpret_cast<const u32x4 *>(p);
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    if (avail >= 8) {
+        if ((a & 3) == 0)
+            return *reinterpret_cast<const u32x4_a4 *>(p);
+        if (window_ok) {
+            const uint32_t *q = reinterpret_cast<const uint32_t *>(a - 2);
+            const u32x4 w = *reinterpret_cast<const u32x4_a4 *>(q);
+            const uint32_t w4 = q[4];
+            u32x4 r;
+            r.x = __builtin_amdgcn_alignbit(w.y, w.x, 16);
+            r.y = __builtin_amdgcn_alignbit(w.z, w.y, 16);
+            r.z = __builtin_amdgcn_alignbit(w.w, w.z, 16);
+            r.w = __builtin_amdgcn_alignbit(w4, w.w, 16);
+            return r;
+        }
+    }
     uint16_t e[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -201,11 +222,14 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_tile_kernel(GemmArgs p, int t
     const uint16_t *pa[T::A_LD];
     int a_col[T::A_LD], a_dst[T::A_LD];
     bool a_ok[T::A_LD];
+    bool a_first[T::A_LD], a_last[T::A_LD];   // first / last row of A
 #pragma unroll
     for (int i = 0; i < T::A_LD; ++i) {
         const int q = tid + i * T::NT;
         const int r = q / T::CA, c = q % T::CA;
         a_ok[i] = (m0 + r) < M;
+        a_first[i] = (m0 + r) == 0;
+        a_last[i] = (m0 + r) == M - 1;
         a_col[i] = c * 8;
         pa[i] = A + (a_ok[i] ? (m0 + r) : 0) * p.lda + c * 8;
         a_dst[i] = r * T::BK + swz_a<T::CA>(r, c) * 8;
@@ -213,12 +237,14 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_tile_kernel(GemmArgs p, int t
     const uint16_t *pb[T::B_LD];
     int b_row[T::B_LD], b_dst[T::B_LD];
     int64_t b_avail[T::B_LD];
+    bool b_col0[T::B_LD];   // chunk starts at column 0 of B
 #pragma unroll
     for (int i = 0; i < T::B_LD; ++i) {
         const int q = tid + i * T::NT;
         const int r = q / T::CB, c = q % T::CB;
         b_row[i] = r;
         b_avail[i] = N - (n0 + c * 8);
+        b_col0[i] = (n0 + c * 8) == 0;
         pb[i] = B + r * p.ldb + (b_avail[i] > 0 ? n0 + c * 8 : 0);
         b_dst[i] = T::A_ELEMS + r * T::BN + swz_b<T::CB>(r, c) * 8;
     }
@@ -231,9 +257,11 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_tile_kernel(GemmArgs p, int t
             const int64_t kavail = K - (k0 + a_col[i]);
             ra[i] = u32x4{0, 0, 0, 0};
             if (a_ok[i] && kavail > 0) {
-                if constexpr (GENERIC)
-                    ra[i] = load8_masked(pa[i] + k0, kavail);
-                else
+                if constexpr (GENERIC) {
+                    const int64_t col = k0 + a_col[i];
+                    const bool wok = !(a_first[i] && col == 0) && !(a_last[i] && kavail <= 8);
+                    ra[i] = load8_masked(pa[i] + k0, kavail, wok);
+                } else
                     ra[i] = *reinterpret_cast<const u32x4 *>(pa[i] + k0);
             }
         }
@@ -242,9 +270,11 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_tile_kernel(GemmArgs p, int t
             rb[i] = u32x4{0, 0, 0, 0};
             if (b_avail[i] > 0 && k0 + b_row[i] < K) {
                 const uint16_t *src = pb[i] + k0 * p.ldb;
-                if constexpr (GENERIC)
-                    rb[i] = load8_masked(src, b_avail[i]);
-                else
+                if constexpr (GENERIC) {
+                    const int64_t row = k0 + b_row[i];
+                    const bool wok = !(row == 0 && b_col0[i]) && !(row == K - 1 && b_avail[i] <= 8);
+                    rb[i] = load8_masked(src, b_avail[i], wok);
+                } else
                     rb[i] = *reinterpret_cast<const u32x4 *>(src);
             }
         }
@@ -304,8 +334,14 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_tile_kernel(GemmArgs p, int t
                     if (n < N)
                         *reinterpret_cast<u32x2 *>(dst) = w;
                 } else {
-                    if (n + 4 <= N && (reinterpret_cast<uintptr_t>(dst) & 7) == 0) {
-                        *reinterpret_cast<u32x2 *>(dst) = w;
+                    const uintptr_t da = reinterpret_cast<uintptr_t>(dst);
+                    if (n + 4 <= N && (da & 3) == 0) {
+                        *reinterpret_cast<u32x2_a4 *>(dst) = w;
+                    } else if (n + 4 <= N) {
+                        // 2 mod 4: one element, one aligned pair, one element
+                        dst[0] = (uint16_t)(w.x & 0xffff);
+                        *reinterpret_cast<uint32_t *>(dst + 1) = (w.x >> 16) | (w.y << 16);
+                        dst[3] = (uint16_t)(w.y >> 16);
                     } else {
                         const uint16_t e[4] = {(uint16_t)(w.x & 0xffff), (uint16_t)(w.x >> 16),
                                                (uint16_t)(w.y & 0xffff), (uint16_t)(w.y >> 16)};
