@@ -118,7 +118,7 @@ int tg_last_path(void);
 int tg_set_tile_variant(int variant);
 
 /*
- * The same for the skinny path (M <= 64): 0..6 select the column-slice width,
+ * The same for the skinny path (M <= 64): 0..9 select the column-slice width,
  * wave count, pipeline depth and cache hint; -1 restores the default.  Returns the
  * previous setting, or -2 for an unknown variant.
  */

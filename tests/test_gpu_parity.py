@@ -361,7 +361,7 @@ def test_tile_variants_match_oracle(tg, oracle_lib, variant, M, N, K):
 # ------------------------------------------------------------------ skinny M
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5, 6, 7, 8, 9])
 @pytest.mark.parametrize("M,N,K", [(16, 1024, 8192), (1, 264, 520), (7, 1000, 136),
                                    (17, 512, 1000), (33, 96, 64), (64, 520, 2056),
                                    (48, 8, 8)])

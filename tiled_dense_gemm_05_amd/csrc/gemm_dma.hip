@@ -46,6 +46,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) f16x8 lds_f16x8;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
@@ -88,7 +89,9 @@ struct Cfg {
     static_assert(KSTEPS <= 4, "k steps per tile");
     static constexpr int RING = KG * STAGES * STAGE * 2;        // bytes of LDS rings
     static constexpr int RED = (KG - 1) * NW * FM * FN * 64 * 64; // partial sums of groups > 0
-    static constexpr int LDS = RING > RED ? RING : RED;
+    static constexpr int CST = BM * BN * 2;                      // the fp16 C tile (epilogue)
+    static constexpr int LDS0 = RING > RED ? RING : RED;
+    static constexpr int LDS = LDS0 > CST ? LDS0 : CST;
     static_assert(LDS <= 160 * 1024, "LDS size");
     // a thread's loads of one tile share one swizzled column (see load plan)
     static_assert((NW * A_RPB) % 16 == 0 && (NW * B_RPB) % 4 == 0, "swizzle period");
@@ -460,7 +463,7 @@ gemm_relu_dma_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
 
     if constexpr (T::KG > 1) {
         // Groups 1 .. KG-1 hand their partial sums to group 0 through LDS;
-        // group 0 adds them in group order (deterministic) and stores.
+        // group 0 adds them in group order (deterministic).
         block_barrier();
         typedef __attribute__((address_space(3))) f32x16 lds_f32x16;
         lds_f32x16 *part = (lds_f32x16 *)smem;
@@ -473,36 +476,53 @@ gemm_relu_dma_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
                         acc[fm][fn];
         }
         block_barrier();
-        if (kg > 0)
-            return;
-        for (int g = 1; g < T::KG; ++g)
+        if (kg == 0) {
+            for (int g = 1; g < T::KG; ++g)
 #pragma unroll
-            for (int fm = 0; fm < T::FM; ++fm)
+                for (int fm = 0; fm < T::FM; ++fm)
 #pragma unroll
-                for (int fn = 0; fn < T::FN; ++fn)
-                    acc[fm][fn] += part[(((g - 1) * T::NW + wave) * T::FM * T::FN + fm * T::FN + fn) * 64 + lane];
+                    for (int fn = 0; fn < T::FN; ++fn)
+                        acc[fm][fn] +=
+                            part[(((g - 1) * T::NW + wave) * T::FM * T::FN + fm * T::FN + fn) * 64 + lane];
+        }
     }
 
-    // Epilogue: ReLU, round to nearest even, 8-byte stores (N % 8 == 0 and
-    // 16-byte aligned rows make every 4-column group wholly in or out).
+    // Epilogue: ReLU, round to nearest even, and the fp16 tile staged in LDS
+    // (16-byte chunks of each row XOR-swizzled by the row) so that the global
+    // stores are whole 16-byte chunks per lane, a wave writing contiguous
+    // runs of rows instead of 8 bytes into 32 different rows.
+    block_barrier();   // every wave is done with the LDS ring / partial sums
+    lds_u16 *cst = (lds_u16 *)smem;
+    if (kg == 0) {
 #pragma unroll
-    for (int fm = 0; fm < T::FM; ++fm) {
-        const int64_t m = m0 + wm * T::TM + fm * 32 + (lane & 31);
-        if (m >= M)
-            continue;
-        uint16_t *crow = C + m * p.ldc;
+        for (int fm = 0; fm < T::FM; ++fm) {
+            const int row = wm * T::TM + fm * 32 + (lane & 31);
 #pragma unroll
-        for (int fn = 0; fn < T::FN; ++fn) {
+            for (int fn = 0; fn < T::FN; ++fn) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int64_t n = n0 + wn * T::TN + fn * 32 + 8 * g + 4 * (lane >> 5);
-                const f32x16 &v = acc[fm][fn];
-                u32x2 w;
-                w.x = pack_relu_f16x2(v[4 * g + 0], v[4 * g + 1]);
-                w.y = pack_relu_f16x2(v[4 * g + 2], v[4 * g + 3]);
-                if (n < N)
-                    *reinterpret_cast<u32x2 *>(crow + n) = w;
+                for (int g = 0; g < 4; ++g) {
+                    const int col = wn * T::TN + fn * 32 + 8 * g + 4 * (lane >> 5);
+                    const f32x16 &v = acc[fm][fn];
+                    u32x2 w;
+                    w.x = pack_relu_f16x2(v[4 * g + 0], v[4 * g + 1]);
+                    w.y = pack_relu_f16x2(v[4 * g + 2], v[4 * g + 3]);
+                    const int phys = (col >> 3) ^ (row % T::CB);
+                    *reinterpret_cast<__attribute__((address_space(3))) u32x2 *>(
+                        cst + row * T::BN + phys * 8 + (col & 4)) = w;
+                }
             }
+        }
+    }
+    block_barrier();
+    // N % 8 == 0 and 16-byte aligned rows: every chunk is wholly in or out
+    for (int q = tid; q < T::BM * T::CB; q += T::NT) {
+        const int row = q / T::CB, c = q % T::CB;
+        const int64_t gm = m0 + row, gn = n0 + c * 8;
+        if (gm < M && gn < N) {
+            const int phys = c ^ (row % T::CB);
+            const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(
+                cst + row * T::BN + phys * 8);
+            *reinterpret_cast<u32x4 *>(C + gm * p.ldc + gn) = v;
         }
     }
 }

@@ -350,6 +350,18 @@ hipError_t launch_skinny_config(int cfg, const GemmArgs &p, hipStream_t stream)
         if (mb <= 1) return launch<Skinny<1, 128, 4, 4, true>>(p, stream);
         if (mb <= 2) return launch<Skinny<2, 128, 4, 3, true>>(p, stream);
         return launch<Skinny<4, 128, 4, 2, true>>(p, stream);
+    case 7:   // 64-column slices, 8 waves, 3 stages, non-temporal B
+        if (mb <= 1) return launch<Skinny<1, 64, 8, 3, true>>(p, stream);
+        if (mb <= 2) return launch<Skinny<2, 64, 8, 3, true>>(p, stream);
+        return launch<Skinny<4, 64, 8, 2, true>>(p, stream);
+    case 8:   // 64-column slices, 4 waves, 8 stages, non-temporal B
+        if (mb <= 1) return launch<Skinny<1, 64, 4, 8, true>>(p, stream);
+        if (mb <= 2) return launch<Skinny<2, 64, 4, 6, true>>(p, stream);
+        return launch<Skinny<4, 64, 4, 4, true>>(p, stream);
+    case 9:   // 32-column slices, 8 waves, 4 stages, non-temporal B
+        if (mb <= 1) return launch<Skinny<1, 32, 8, 4, true>>(p, stream);
+        if (mb <= 2) return launch<Skinny<2, 32, 8, 4, true>>(p, stream);
+        return launch<Skinny<4, 32, 8, 3, true>>(p, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -31,7 +31,7 @@ constexpr int kDmaConfigs = 19;
 hipError_t launch_dma_config(int cfg, const GemmArgs &p, hipStream_t stream, int groupM);
 // Skinny-M kernels (M <= 64, aligned layouts); `cfg` selects slice width,
 // waves and stages; see gemm_skinny.hip.
-constexpr int kSkinnyConfigs = 7;
+constexpr int kSkinnyConfigs = 10;
 hipError_t launch_skinny_config(int cfg, const GemmArgs &p, hipStream_t stream);
 bool skinny_layout_ok(const GemmArgs &p);
 // Whether the leading dimensions fit the kernels' 32-bit buffer offsets.
