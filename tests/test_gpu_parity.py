@@ -343,7 +343,7 @@ def test_workloads_full_size(tg, oracle_lib, name, n):
 
 # ------------------------------------------------------ every tile configuration
 
-VARIANTS = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 100, 101]
+VARIANTS = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 100, 101]
 
 
 @pytest.mark.parametrize("variant", VARIANTS)

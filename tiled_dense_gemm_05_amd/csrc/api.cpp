@@ -18,6 +18,7 @@ std::atomic<int> g_tile_variant{-1};
 constexpr int kTile128Default = 3;   // 128x128x64, 4 stages
 constexpr int kTile256Default = 0;   // 256x256x32, 4 stages
 constexpr int kTile128ShortK = 12;   // 128x128x32, 2 stages, 4 waves/SIMD: several workgroups per CU
+constexpr int kTile64 = 20;          // 64x64x64, 4 stages, two K groups: grids with few tiles
 constexpr int kRegStaged128 = 100;   // register-staged kernels, kept for comparison
 constexpr int kRegStaged256 = 101;
 constexpr int kSkinnyDefault = 4;   // 64-column slices, 4 waves, 6 stages, non-temporal B
@@ -159,9 +160,13 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
     case TG_PATH_TILE128:
     case TG_PATH_TILE256: {
         int v = g_tile_variant.load(std::memory_order_relaxed);
-        if (v < 0)
+        if (v < 0) {
+            const int64_t tiles128 = ((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch;
             v = path == TG_PATH_TILE256 ? kTile256Default
-                : (p.K <= 64 ? kTile128ShortK : kTile128Default);
+                : p.K <= 64         ? kTile128ShortK
+                : tiles128 < 128    ? kTile64
+                                    : kTile128Default;
+        }
         if (v == kRegStaged128)
             e = tg::launch_tile128(p, stream);
         else if (v == kRegStaged256)

@@ -586,6 +586,11 @@ hipError_t launch_dma_config(int cfg, const GemmArgs &p, hipStream_t stream, int
     // deep rings for latency-bound mid-size shapes
     case 17: return launch_dma<Cfg<128, 128, 32, 2, 2, 8>>(p, stream, groupM);
     case 18: return launch_dma<Cfg<128, 128, 64, 2, 2, 5>>(p, stream, groupM);
+    // 64x64 tiles for problems with few 128x128 tiles
+    case 19: return launch_dma<Cfg<64, 64, 64, 2, 2, 4>>(p, stream, groupM);
+    case 20: return launch_dma<Cfg<64, 64, 64, 2, 2, 4, 1, 2>>(p, stream, groupM);
+    // the tile the pages start from: 128 x 128 x 32, 3 stages, 4 waves
+    case 21: return launch_dma<Cfg<128, 128, 32, 2, 2, 3>>(p, stream, groupM);
     default: return hipErrorInvalidValue;
     }
 }
