@@ -8,6 +8,11 @@ is reported alongside as a secondary figure.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--no-secondary]
+                    [--tile-variant V] [--skinny-variant V] [--raster G]
+
+The last three select non-default kernel configurations and tile orders for
+ablations; a line measured with any of them carries them in `config` and no
+`traffic` figure (the counters are taken at the defaults).
 """
 
 from __future__ import annotations
@@ -239,7 +244,72 @@ def summarize(workload: str, stats_dir: str, fetch_dir: str, write_dir: str, com
     print(f"wrote {md} and {TRAFFIC_FILE}")
 
 
+def _dispatch_counters(d):
+    """Counter values per dispatch of the library's kernels under directory d:
+    {dispatch id: {"name", "us", counter: value summed over its instances}}."""
+    out = {}
+    for r in _csv_rows(_find(d, "counter_collection.csv")):
+        e = out.setdefault(r["Dispatch_Id"], {
+            "name": r["Kernel_Name"],
+            "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def summarize_ablation(out_md: str, root: str, title: str):
+    """Writes a table of ablation runs.  root/labels.txt holds one line per
+    run, `label<TAB>description`; root/<label>/bench.json is that run's bench
+    line, root/<label>/pmc one counter run (SQ_CYCLES, SQ_VALU_MFMA_BUSY_CYCLES,
+    SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE, TCC_HIT_sum, TCC_MISS_sum) and
+    root/<label>/fetch one FETCH_SIZE run with the calibration copy;
+    root/commands.txt the commands, copied into the summary."""
+    with open(os.path.join(root, "labels.txt")) as f:
+        labels = [ln.rstrip("\n").split("\t", 1) for ln in f if ln.strip()]
+    with open(os.path.join(root, "commands.txt")) as f:
+        commands = f.read().rstrip()
+    rows = []
+    for label, desc in labels:
+        d = os.path.join(root, label)
+        with open(os.path.join(d, "bench.json")) as f:
+            b = json.loads(f.read().strip().splitlines()[-1])
+        w = wl.WORKLOADS[b["config"]["workload"]]
+        pmc = [v for v in _dispatch_counters(os.path.join(d, "pmc")).values() if "tg::" in v["name"]]
+        n = len(pmc)
+        avg = lambda key: sum(v[key] for v in pmc) / n
+        clock = sum(v["SQ_CYCLES"] / 32 / v["us"] / 1e3 for v in pmc) / n
+        mfma = sum(v["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * v["SQ_CYCLES"] / 32) for v in pmc) / n
+        lds_conf = avg("SQ_LDS_BANK_CONFLICT") / max(avg("SQ_LDS_IDX_ACTIVE"), 1.0)
+        l2_hit = avg("TCC_HIT_sum") / max(avg("TCC_HIT_sum") + avg("TCC_MISS_sum"), 1.0)
+        fe = _dispatch_counters(os.path.join(d, "fetch"))
+        copy = [v["FETCH_SIZE"] for v in fe.values() if "copy" in v["name"].lower()]
+        gem = [v["FETCH_SIZE"] for v in fe.values() if "tg::" in v["name"]]
+        factor = COPY_BYTES / (sum(copy) / len(copy) * 1024.0)
+        read = sum(gem) / len(gem) * 1024.0 * factor
+        ab = 2.0 * (w.M * w.K + w.K * w.N) * w.batch
+        rows.append((label, desc, b["ms_per_step"] * 1e3, b["value"], b["unit"], clock, mfma,
+                     lds_conf, l2_hit, read / ab, n))
+    with open(out_md, "w") as f:
+        f.write(f"# {title}\n\nCommands (from the repository root on the GPU box; "
+                f"<label> and <args> per row):\n\n")
+        for c in commands.splitlines():
+            f.write(f"    {c}\n")
+        f.write("\nRate and time from the bench line; clock, MFMA-busy fraction, LDS bank-conflict "
+                "cycles per LDS-active cycle and L2 hit rate averaged over the profiled "
+                "dispatches; HBM read = FETCH_SIZE x the factor a 1 GiB copy gives, per launch, "
+                "over the bytes of A and B.\n\n")
+        f.write("| run | setting | us / call | rate | clock GHz | MFMA busy | LDS conflict | "
+                "L2 hit | HBM read / (A+B) |\n|---|---|---|---|---|---|---|---|---|\n")
+        for (label, desc, us, val, unit, clock, mfma, lc, l2, rd, n) in rows:
+            f.write(f"| {label} | {desc} | {us:.1f} | {val:.0f} {unit} | {clock:.2f} | "
+                    f"{mfma:.1%} | {lc:.3f} | {l2:.1%} | {rd:.2f} |\n")
+    print(f"wrote {out_md}")
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-ablation":
+        # bench.py --summarize-ablation OUT_MD ROOT_DIR TITLE
+        summarize_ablation(sys.argv[2], sys.argv[3], sys.argv[4])
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize":
         # bench.py --summarize WORKLOAD STATS_DIR FETCH_DIR WRITE_DIR "cmd1" "cmd2" ...
         summarize(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6:])
@@ -253,6 +323,12 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a 1 GiB copy first (counter calibration runs only)")
+    ap.add_argument("--tile-variant", type=int, default=-1,
+                    help="tile-kernel configuration (tg_set_tile_variant), -1 = default")
+    ap.add_argument("--skinny-variant", type=int, default=-1,
+                    help="skinny-kernel configuration (tg_set_skinny_variant), -1 = default")
+    ap.add_argument("--raster", type=int, default=-1,
+                    help="tile order (tg_set_raster): panel height, 0 = row-major, -1 = default")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -267,6 +343,15 @@ def main():
         sys.exit(1)
     import tiled_dense_gemm_05_amd as tg
 
+    knobs = {}
+    for name, value, setter in (("tile_variant", args.tile_variant, tg.tg_set_tile_variant),
+                                ("skinny_variant", args.skinny_variant, tg.tg_set_skinny_variant),
+                                ("raster", args.raster, tg.tg_set_raster)):
+        if value != -1:
+            if setter(value) < -1:
+                print(f"invalid --{name.replace('_', '-')} {value}", file=sys.stderr)
+                sys.exit(2)
+            knobs[name] = value
     if args.calibrate_copy:
         calibration_copy(torch)
     w = wl.WORKLOADS[args.workload]
@@ -285,7 +370,7 @@ def main():
         value, unit = gbs, "GB/s"
         roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": gbs / PEAK_HBM_GBS}
-    roof["traffic"] = measured_traffic(w.name)
+    roof["traffic"] = None if knobs else measured_traffic(w.name)
 
     out = {
         "metric": METRIC,
@@ -302,7 +387,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "batch": w.batch,
                    "inputs": f"{w.dist}, seed {w.seed}", "accumulate": "fp32", "path": path,
-                   "input_copies": nbuf},
+                   "input_copies": nbuf, **knobs},
         "roofline": roof,
     }
 
@@ -315,7 +400,8 @@ def main():
             "workload": s.name, "value": sgbs, "unit": "GB/s", "ms_per_step": sms, "path": spath,
             "input_copies": snbuf,
             "roofline": {"bound": "hbm", "achieved": sgbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": sgbs / PEAK_HBM_GBS, "traffic": measured_traffic(s.name)},
+                         "frac": sgbs / PEAK_HBM_GBS,
+                         "traffic": None if knobs else measured_traffic(s.name)},
         }
 
     if not args.no_cpu_baseline:

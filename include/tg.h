@@ -110,10 +110,12 @@ int tg_last_path(void);
 /*
  * Tuning knob for benchmarks: selects the kernel configuration (block tile,
  * K tile, pipeline depth) that the tile paths use.  -1 restores the defaults;
- * 0..21 are the direct-to-LDS configurations, 100 and 101 the
+ * 0..23 are the direct-to-LDS configurations, 100 and 101 the
  * register-staged 128x128 and 256x256 kernels.  Returns the previous setting, or -2 for an
  * unknown variant (the setting is unchanged).  Results are identical within
- * the accuracy contract for every variant; only speed changes.
+ * the accuracy contract for every variant; only speed changes.  22 and 23 are
+ * ablations of configuration 0 (operand tiles without the XOR swizzle; a
+ * 2-stage ring).
  */
 int tg_set_tile_variant(int variant);
 
@@ -123,6 +125,22 @@ int tg_set_tile_variant(int variant);
  * previous setting, or -2 for an unknown variant.
  */
 int tg_set_skinny_variant(int variant);
+
+/*
+ * Tuning knob for benchmarks: the order in which the tile kernels (generic,
+ * tile128, tile256) walk their output tiles.  group_m in 1..64: the workgroup
+ * ids are renumbered so that each of the eight XCDs (each with its own L2)
+ * takes a contiguous run of tiles, walked in panels of group_m tile rows,
+ * column by column, so that tiles resident together share operand rows and
+ * columns (the L2-friendly rasterisation primitive of the "TileLang paper
+ * reading" page (hotelren.com), section 4, and of the primitive list of the
+ * "TileLang DSL explainer" page (lzwjava.github.io), adapted to one L2 per
+ * XCD).  0: plain row-major order of the workgroup ids, no renumbering.  -1
+ * restores the default (8).  Returns the previous setting, or -2 for a value
+ * outside -1..64 (unchanged).  Results are bitwise identical for every
+ * setting.
+ */
+int tg_set_raster(int group_m);
 
 /* A static name for a path number ("auto", "naive", ...), or "unknown". */
 const char *tg_path_name(int path);

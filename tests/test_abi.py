@@ -52,6 +52,17 @@ def test_path_control(tg):
     assert tg.tg_set_path(-1) == -1 and tg.tg_set_path(99) == -1
 
 
+def test_tuning_knobs(tg):
+    assert tg.tg_set_tile_variant(23) == -1
+    assert tg.tg_set_tile_variant(24) == -2
+    assert tg.tg_set_tile_variant(-1) == 23
+    assert tg.tg_set_skinny_variant(10) == -2
+    assert tg.tg_set_raster(0) == 8          # default: panels of 8 tile rows
+    assert tg.tg_set_raster(65) == -2 and tg.tg_set_raster(-3) == -2
+    assert tg.tg_set_raster(-1) == 0
+    assert tg.tg_set_raster(-1) == 8
+
+
 P = 0x10000  # a fake, 16-byte aligned device address; never dereferenced here
 
 INVALID = [

@@ -39,6 +39,7 @@ EXPORTED_SYMBOLS = (
     "tg_path_name",
     "tg_set_tile_variant",
     "tg_set_skinny_variant",
+    "tg_set_raster",
 )
 
 
@@ -70,6 +71,8 @@ _lib.tg_set_tile_variant.argtypes = [ctypes.c_int]
 _lib.tg_set_tile_variant.restype = ctypes.c_int
 _lib.tg_set_skinny_variant.argtypes = [ctypes.c_int]
 _lib.tg_set_skinny_variant.restype = ctypes.c_int
+_lib.tg_set_raster.argtypes = [ctypes.c_int]
+_lib.tg_set_raster.restype = ctypes.c_int
 _lib.tg_path_name.argtypes = [ctypes.c_int]
 _lib.tg_path_name.restype = ctypes.c_char_p
 
@@ -113,6 +116,10 @@ def tg_set_tile_variant(variant: int) -> int:
 
 def tg_set_skinny_variant(variant: int) -> int:
     return _lib.tg_set_skinny_variant(variant)
+
+
+def tg_set_raster(group_m: int) -> int:
+    return _lib.tg_set_raster(group_m)
 
 
 # ----------------------------------------------------------- torch helpers

@@ -23,6 +23,10 @@ constexpr int kRegStaged128 = 100;   // register-staged kernels, kept for compar
 constexpr int kRegStaged256 = 101;
 constexpr int kSkinnyDefault = 4;   // 64-column slices, 4 waves, 6 stages, non-temporal B
 std::atomic<int> g_skinny_variant{-1};
+// tile order of the tile kernels: panels of this many tile rows after the XCD
+// renumbering (0: plain row-major order)
+constexpr int kGroupMDefault = 8;
+std::atomic<int> g_group_m{kGroupMDefault};
 
 // Per-device architecture check, done once per device: 0 unknown, 1 gfx950,
 // 2 something else.
@@ -167,12 +171,13 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
                 : tiles128 < 128    ? kTile64
                                     : kTile128Default;
         }
+        const int gm = g_group_m.load(std::memory_order_relaxed);
         if (v == kRegStaged128)
-            e = tg::launch_tile128(p, stream);
+            e = tg::launch_tile128(p, stream, gm);
         else if (v == kRegStaged256)
-            e = tg::launch_tile256(p, stream);
+            e = tg::launch_tile256(p, stream, gm);
         else
-            e = tg::launch_dma_config(v, p, stream, 8);
+            e = tg::launch_dma_config(v, p, stream, gm);
         break;
     }
     case TG_PATH_SKINNY: {
@@ -180,7 +185,10 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
         e = tg::launch_skinny_config(v < 0 ? kSkinnyDefault : v, p, stream);
         break;
     }
-    default: e = tg::launch_generic(p, stream); path = TG_PATH_GENERIC; break;
+    default:
+        e = tg::launch_generic(p, stream, g_group_m.load(std::memory_order_relaxed));
+        path = TG_PATH_GENERIC;
+        break;
     }
     if (e != hipSuccess)
         return TG_ERR_HIP;
@@ -240,6 +248,15 @@ int tg_set_tile_variant(int variant)
           variant == kRegStaged128 || variant == kRegStaged256))
         return -2;
     return g_tile_variant.exchange(variant);
+}
+
+int tg_set_raster(int group_m)
+{
+    if (group_m == -1)
+        group_m = kGroupMDefault;
+    if (group_m < 0 || group_m > 64)
+        return -2;
+    return g_group_m.exchange(group_m);
 }
 
 const char *tg_path_name(int path)

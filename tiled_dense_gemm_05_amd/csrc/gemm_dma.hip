@@ -53,11 +53,13 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 constexpr uint32_t kOutOfRange = 0x80000000u;   // == the descriptors' record count
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int OCC_ = 1, int KG_ = 1>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int OCC_ = 1, int KG_ = 1,
+          bool SWZ_ = true>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, STAGES = STAGES_;
     static constexpr int OCC = OCC_;                  // waves per SIMD the registers must allow
     static constexpr int KG = KG_;                    // K groups: wave groups on alternate K tiles
+    static constexpr bool SWZ = SWZ_;                 // XOR-swizzled operand tiles (off: ablation)
     static constexpr int NW = WM * WN;                // waves per K group
     static constexpr int NT = 64 * NW * KG;           // threads
     static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
@@ -97,38 +99,26 @@ struct Cfg {
     static_assert((NW * A_RPB) % 16 == 0 && (NW * B_RPB) % 4 == 0, "swizzle period");
 };
 
-template <int CA>
+template <int CA, bool ON = true>
 __device__ __forceinline__ int swz_a(int row, int c)
 {
     constexpr int rows_per_line = 16 / CA;
+    if constexpr (!ON)
+        return c;
     return c ^ ((row / rows_per_line) % CA);
 }
 
-template <int CB>
+template <int CB, bool ON = true>
 __device__ __forceinline__ int swz_b(int k, int c)
 {
-    if constexpr (CB >= 16)
+    if constexpr (!ON)
+        return c;
+    else if constexpr (CB >= 16)
         return c ^ ((k & 3) << 2);
     else if constexpr (CB == 8)
         return c ^ (((k >> 1) & 1) << 2);
     else
         return c;
-}
-
-__device__ __forceinline__ void tile_coords(int pid, int tilesM, int tilesN, int groupM, int &tm,
-                                            int &tn)
-{
-    const int T = tilesM * tilesN;
-    const int q = T >> 3, r = T & 7;
-    const int xcd = pid & 7, local = pid >> 3;
-    const int id = (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
-    const int per_group = groupM * tilesN;
-    const int g = id / per_group;
-    const int first_m = g * groupM;
-    const int gsz = min(tilesM - first_m, groupM);
-    const int in = id - g * per_group;
-    tm = first_m + in % gsz;
-    tn = in / gsz;
 }
 
 // s_waitcnt vmcnt(N), other counters untouched, fenced against compiler
@@ -217,12 +207,13 @@ __device__ __forceinline__ void read_piece(const lds_u16 *As, const lds_u16 *Bs,
     if constexpr (r < T::FM) {
         const int row = wm * T::TM + r * 32 + (lane & 31);
         const int c = kk * 2 + (lane >> 5);
-        af[r] = *reinterpret_cast<const lds_f16x8 *>(As + row * T::BK + swz_a<T::CA>(row, c) * 8);
+        const int ca = swz_a<T::CA, T::SWZ>(row, c);
+        af[r] = *reinterpret_cast<const lds_f16x8 *>(As + row * T::BK + ca * 8);
     } else {
         constexpr int fn = (r - T::FM) / 2, hh = (r - T::FM) % 2;
         const int k = kk * 16 + 8 * (lane >> 5) + 4 * hh + ((lane & 15) >> 2);
         const int n = wn * T::TN + fn * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        const lds_u16 *src = Bs + k * T::BN + swz_b<T::CB>(k, n >> 3) * 8 + (n & 7);
+        const lds_u16 *src = Bs + k * T::BN + swz_b<T::CB, T::SWZ>(k, n >> 3) * 8 + (n & 7);
         bh[fn][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src);
     }
 }
@@ -376,7 +367,7 @@ gemm_relu_dma_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
     LoadPlan<T> lp;
     {
         const int r0 = wave * T::A_RPB + lane / T::CA;
-        const int c = swz_a<T::CA>(r0, lane % T::CA);
+        const int c = swz_a<T::CA, T::SWZ>(r0, lane % T::CA);
         lp.a_kcol = c * 8;
 #pragma unroll
         for (int i = 0; i < T::A_LD; ++i) {
@@ -386,7 +377,7 @@ gemm_relu_dma_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
     }
     {
         const int r0 = wave * T::B_RPB + lane / T::CB;
-        const int c = swz_b<T::CB>(r0, lane % T::CB);
+        const int c = swz_b<T::CB, T::SWZ>(r0, lane % T::CB);
         lp.b_row0 = r0;
         const bool col_ok = n0 + c * 8 < N;
 #pragma unroll
@@ -591,6 +582,10 @@ hipError_t launch_dma_config(int cfg, const GemmArgs &p, hipStream_t stream, int
     case 20: return launch_dma<Cfg<64, 64, 64, 2, 2, 4, 1, 2>>(p, stream, groupM);
     // the tile the pages start from: 128 x 128 x 32, 3 stages, 4 waves
     case 21: return launch_dma<Cfg<128, 128, 32, 2, 2, 3>>(p, stream, groupM);
+    // ablations of the large-shape tile: operand tiles without the XOR
+    // swizzle, and a 2-stage ring
+    case 22: return launch_dma<Cfg<256, 256, 32, 2, 2, 4, 1, 1, false>>(p, stream, groupM);
+    case 23: return launch_dma<Cfg<256, 256, 32, 2, 2, 2>>(p, stream, groupM);
     default: return hipErrorInvalidValue;
     }
 }

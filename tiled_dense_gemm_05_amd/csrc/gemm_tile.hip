@@ -88,24 +88,6 @@ __device__ __forceinline__ int swz_b(int k, int c)
         return c;
 }
 
-// Tile coordinates of workgroup `pid` (XCD-contiguous renumbering, then
-// panels of groupM tile rows walked column by column).
-__device__ __forceinline__ void tile_coords(int pid, int tilesM, int tilesN, int groupM,
-                                            int &tm, int &tn)
-{
-    const int T = tilesM * tilesN;
-    const int q = T >> 3, r = T & 7;
-    const int xcd = pid & 7, local = pid >> 3;
-    const int id = (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
-    const int per_group = groupM * tilesN;
-    const int g = id / per_group;
-    const int first_m = g * groupM;
-    const int gsz = min(tilesM - first_m, groupM);
-    const int in = id - g * per_group;
-    tm = first_m + in % gsz;
-    tn = in / gsz;
-}
-
 __device__ __forceinline__ u32x4 pack8(const uint16_t (&e)[8])
 {
     u32x4 v;
@@ -385,19 +367,19 @@ using Tile256 = Tile<256, 256, 32, 2, 2>;
 
 }  // namespace
 
-hipError_t launch_generic(const GemmArgs &p, hipStream_t stream)
+hipError_t launch_generic(const GemmArgs &p, hipStream_t stream, int groupM)
 {
-    return launch_tiles<Tile128, true>(p, stream, 8);
+    return launch_tiles<Tile128, true>(p, stream, groupM);
 }
 
-hipError_t launch_tile128(const GemmArgs &p, hipStream_t stream)
+hipError_t launch_tile128(const GemmArgs &p, hipStream_t stream, int groupM)
 {
-    return launch_tiles<Tile128, false>(p, stream, 8);
+    return launch_tiles<Tile128, false>(p, stream, groupM);
 }
 
-hipError_t launch_tile256(const GemmArgs &p, hipStream_t stream)
+hipError_t launch_tile256(const GemmArgs &p, hipStream_t stream, int groupM)
 {
-    return launch_tiles<Tile256, false>(p, stream, 8);
+    return launch_tiles<Tile256, false>(p, stream, groupM);
 }
 
 }  // namespace tg

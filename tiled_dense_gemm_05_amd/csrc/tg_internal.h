@@ -19,15 +19,44 @@ struct GemmArgs {
     int64_t batch;
 };
 
-// Every launcher enqueues on `stream` and returns hipGetLastError().
+// Tile coordinates of workgroup `pid` of a tilesM x tilesN grid.  The
+// hardware hands consecutive workgroup ids to the eight XCDs in turn, and
+// each XCD has its own L2; the ids are first renumbered so that each XCD
+// receives a contiguous run of tiles, then that run is walked in panels of
+// `groupM` tile rows, column by column, so that the tiles resident on one XCD
+// at a time share A rows and B columns.  groupM <= 0 turns both off: plain
+// row-major order of the workgroup ids (the ablation baseline).
+__device__ __forceinline__ void tile_coords(int pid, int tilesM, int tilesN, int groupM, int &tm,
+                                            int &tn)
+{
+    if (groupM <= 0) {
+        tm = pid / tilesN;
+        tn = pid - tm * tilesN;
+        return;
+    }
+    const int T = tilesM * tilesN;
+    const int q = T >> 3, r = T & 7;
+    const int xcd = pid & 7, local = pid >> 3;
+    const int id = (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+    const int per_group = groupM * tilesN;
+    const int g = id / per_group;
+    const int first_m = g * groupM;
+    const int gsz = min(tilesM - first_m, groupM);
+    const int in = id - g * per_group;
+    tm = first_m + in % gsz;
+    tn = in / gsz;
+}
+
+// Every launcher enqueues on `stream` and returns hipGetLastError().  The
+// tile launchers take the raster setting of tile_coords.
 hipError_t launch_naive(const GemmArgs &p, hipStream_t stream);
-hipError_t launch_generic(const GemmArgs &p, hipStream_t stream);
-hipError_t launch_tile128(const GemmArgs &p, hipStream_t stream);
-hipError_t launch_tile256(const GemmArgs &p, hipStream_t stream);
+hipError_t launch_generic(const GemmArgs &p, hipStream_t stream, int groupM);
+hipError_t launch_tile128(const GemmArgs &p, hipStream_t stream, int groupM);
+hipError_t launch_tile256(const GemmArgs &p, hipStream_t stream, int groupM);
 
 // Direct-to-LDS pipelined kernels (aligned layouts only).  `cfg` selects the
 // block tile / K tile / stage count; see gemm_dma.hip.
-constexpr int kDmaConfigs = 22;
+constexpr int kDmaConfigs = 24;
 hipError_t launch_dma_config(int cfg, const GemmArgs &p, hipStream_t stream, int groupM);
 // Skinny-M kernels (M <= 64, aligned layouts); `cfg` selects slice width,
 // waves and stages; see gemm_skinny.hip.
