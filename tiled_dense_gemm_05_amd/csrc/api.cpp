@@ -15,8 +15,8 @@ std::atomic<int> g_last_path{TG_PATH_AUTO};
 std::atomic<int> g_tile_variant{-1};
 
 // Default direct-to-LDS configurations of the tile paths.
-constexpr int kTile128Default = 3;   // 128x128x64, 4 stages
-constexpr int kTile256Default = 0;   // 256x256x32, 4 stages
+constexpr int kTile128Default = 29;  // 128x128x64, 4 stages, 8 waves (4x2, 32x64 wave tiles)
+constexpr int kTile256Default = 8;   // 256x256x64, 2 stages, 8 waves (2 per SIMD)
 constexpr int kTile128ShortK = 12;   // 128x128x32, 2 stages, 4 waves/SIMD: several workgroups per CU
 constexpr int kTile64 = 20;          // 64x64x64, 4 stages, two K groups: grids with few tiles
 constexpr int kRegStaged128 = 100;   // register-staged kernels, kept for comparison
@@ -116,14 +116,19 @@ int choose_path(const tg::GemmArgs &p)
         return TG_PATH_GENERIC;
     if (p.M <= 64 && tg::skinny_layout_ok(p))
         return TG_PATH_SKINNY;
-    // 256x256 tiles once there are enough of them to fill the chip and the
-    // padding they add to ragged edges is small; 128x128 tiles otherwise
-    const int64_t tm = (p.M + 255) / 256, tn = (p.N + 255) / 256;
-    const int64_t tiles256 = tm * tn * p.batch;
-    const double fill = (double)p.M * (double)p.N / ((double)tm * 256.0 * (double)tn * 256.0);
-    if (tiles256 >= 256 && fill >= 0.85)
-        return TG_PATH_TILE256;
-    return TG_PATH_TILE128;
+    // Both tile kernels run one workgroup per CU, so a launch takes
+    // ceil(tiles / 256) rounds.  A round of 256x256 tiles does four times the
+    // work of a round of 128x128 tiles and takes about 2.6 times as long
+    // (measured from 2048^2 to 8192^2, K >= 1000); pick the cheaper estimate.
+    // Short K (the batched shapes) stays on the 128x128 kernel, which then
+    // runs several workgroups per CU.
+    if (p.K <= 64)
+        return TG_PATH_TILE128;
+    const int64_t tiles256 = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
+    const int64_t tiles128 = ((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch;
+    const double rounds256 = (double)((tiles256 + 255) / 256) * 2.6;
+    const double rounds128 = (double)((tiles128 + 255) / 256);
+    return rounds256 < rounds128 ? TG_PATH_TILE256 : TG_PATH_TILE128;
 }
 
 int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int64_t lda,

@@ -586,6 +586,15 @@ hipError_t launch_dma_config(int cfg, const GemmArgs &p, hipStream_t stream, int
     // swizzle, and a 2-stage ring
     case 22: return launch_dma<Cfg<256, 256, 32, 2, 2, 4, 1, 1, false>>(p, stream, groupM);
     case 23: return launch_dma<Cfg<256, 256, 32, 2, 2, 2>>(p, stream, groupM);
+    // more eight-wave large tiles
+    case 24: return launch_dma<Cfg<256, 256, 64, 4, 2, 2>>(p, stream, groupM);
+    case 25: return launch_dma<Cfg<256, 256, 32, 2, 4, 3>>(p, stream, groupM);
+    // sixteen waves, 64x64 wave tiles
+    case 26: return launch_dma<Cfg<256, 256, 64, 4, 4, 2>>(p, stream, groupM);
+    case 27: return launch_dma<Cfg<256, 256, 32, 4, 4, 4>>(p, stream, groupM);
+    // eight-wave 128x128 tiles
+    case 28: return launch_dma<Cfg<128, 128, 64, 2, 4, 4>>(p, stream, groupM);
+    case 29: return launch_dma<Cfg<128, 128, 64, 4, 2, 4>>(p, stream, groupM);
     default: return hipErrorInvalidValue;
     }
 }

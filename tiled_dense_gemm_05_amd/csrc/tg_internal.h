@@ -56,7 +56,7 @@ hipError_t launch_tile256(const GemmArgs &p, hipStream_t stream, int groupM);
 
 // Direct-to-LDS pipelined kernels (aligned layouts only).  `cfg` selects the
 // block tile / K tile / stage count; see gemm_dma.hip.
-constexpr int kDmaConfigs = 24;
+constexpr int kDmaConfigs = 30;
 hipError_t launch_dma_config(int cfg, const GemmArgs &p, hipStream_t stream, int groupM);
 // Skinny-M kernels (M <= 64, aligned layouts); `cfg` selects slice width,
 // waves and stages; see gemm_skinny.hip.
