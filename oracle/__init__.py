@@ -1,4 +1,6 @@
-"""CPU oracle for C = ReLU(A·B) with fp16 storage (binary64 accumulation).
+"""CPU oracle for C = ReLU(A·B) with fp16 storage (binary64 accumulation),
+and for its variants C = act(A·B + bias) with fp16 or bf16 storage and B
+stored as (K,N) or (N,K).
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
 CPU-baseline leg may import this package.  It shares no code with the HIP
@@ -12,7 +14,8 @@ section 2 of the "TileLang paper reading" page (hotelren.com) and the serial,
 fp32-or-wider K accumulation in section 3.2 of the "tilelang practitioner's
 notes" page (dpshk.com).
 
-Every fp16 array here is passed as its raw bit patterns (``numpy.uint16``).
+Every fp16 / bf16 array here is passed as its raw bit patterns
+(``numpy.uint16``).
 """
 
 from __future__ import annotations
@@ -63,6 +66,16 @@ def _load():
     lib.oracle_gemm_relu_f16_sampled.argtypes = [vp, vp] + [i64] * 5 + [vp, i64, vp, vp, vp,
                                                                         ctypes.c_int]
     lib.oracle_gemm_relu_f16_sampled.restype = ctypes.c_int
+    lib.oracle_decbf16_array.argtypes = [vp, vp, i64]
+    lib.oracle_decbf16_array.restype = None
+    lib.oracle_encbf16_array.argtypes = [vp, vp, i64]
+    lib.oracle_encbf16_array.restype = None
+    ci = ctypes.c_int
+    lib.oracle_gemm_ex.argtypes = [ci, ci, ci, vp, vp, vp, vp] + [i64] * 10 + [vp, vp, ci]
+    lib.oracle_gemm_ex.restype = ctypes.c_int
+    lib.oracle_gemm_ex_sampled.argtypes = [ci, ci, ci, vp, vp, vp] + [i64] * 5 + [vp, i64, vp,
+                                                                                  vp, vp, ci]
+    lib.oracle_gemm_ex_sampled.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -101,6 +114,22 @@ def enc16(x) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float64)
     out = np.empty(x.shape, dtype=np.uint16)
     _load().oracle_enc16_array(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def decbf16(bits) -> np.ndarray:
+    """Exact bfloat16 -> binary64 decode of an array of bit patterns."""
+    b = _u16(bits)
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().oracle_decbf16_array(_ptr(b), _ptr(out), b.size)
+    return out
+
+
+def encbf16(x) -> np.ndarray:
+    """binary64 -> bfloat16 bit patterns, round to nearest, ties to even."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().oracle_encbf16_array(_ptr(x), _ptr(out), x.size)
     return out
 
 
@@ -194,4 +223,99 @@ def gemm_relu_sampled(A, B, K: int, lda: int, ldb: int, idx, sA: int = 0, sB: in
     _load().oracle_gemm_relu_f16_sampled(
         _ptr(A), _ptr(B), K, lda, ldb, sA, sB, _ptr(idx), n, _ptr(out), _ptr(s), _ptr(sa),
         host_threads() if threads is None else threads)
+    return out, s, sa
+
+
+DTYPES = {"f16": 0, "bf16": 1}
+B_LAYOUTS = {"kn": 0, "nk": 1}
+ACTS = {"none": 0, "relu": 1}
+
+
+def gemm_ex(A, B, M: int, N: int, K: int, lda: int | None = None, ldb: int | None = None,
+            ldc: int | None = None, batch: int = 1, sA: int | None = None,
+            sB: int | None = None, sC: int | None = None, C=None, bias=None,
+            dtype: str = "f16", b_layout: str = "kn", act: str = "relu",
+            want_sums: bool = False, threads: int | None = None):
+    """Every output of C = act(A·B + bias), strided-batched.
+
+    As ``gemm_relu``, plus: ``dtype`` "f16" or "bf16" (the element type of A,
+    B, bias and C, all passed as uint16 bit patterns); ``b_layout`` "kn" (B
+    is (K,N) row-major, B(k,j) at k*ldb + j) or "nk" (B is (N,K) row-major,
+    B(k,j) at j*ldb + k); ``act`` "none" or "relu"; ``bias`` None or N values
+    added to every row before the activation.  The sums returned with
+    ``want_sums`` include the bias.
+    """
+    layout = B_LAYOUTS[b_layout]
+    lda = K if lda is None else lda
+    ldb = (N if layout == 0 else K) if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    sA = M * lda if sA is None else sA
+    sB = (K * ldb if layout == 0 else N * ldb) if sB is None else sB
+    sC = M * ldc if sC is None else sC
+    A = _u16(A).reshape(-1)
+    B = _u16(B).reshape(-1)
+    if M > 0 and N > 0:
+        _check_extent(A, M, K, lda, sA, batch, "A")
+        if layout == 0:
+            _check_extent(B, K, N, ldb, sB, batch, "B")
+        else:
+            _check_extent(B, N, K, ldb, sB, batch, "B")
+    if bias is not None:
+        bias = _u16(bias).reshape(-1)
+        if bias.size < N:
+            raise ValueError(f"bias holds {bias.size} values, N = {N}")
+    if C is None:
+        size = 0 if (M == 0 or N == 0 or batch == 0) else (batch - 1) * sC + (M - 1) * ldc + N
+        C = np.zeros(size, dtype=np.uint16)
+    else:
+        if C.dtype != np.uint16 or not C.flags.c_contiguous:
+            raise TypeError("C must be a contiguous uint16 array")
+        C = C.reshape(-1)
+    _check_extent(C, M, N, ldc, sC, batch, "C")
+    S = Sa = None
+    if want_sums:
+        S = np.zeros((batch, M, N), dtype=np.float64)
+        Sa = np.zeros((batch, M, N), dtype=np.float64)
+    rc = _load().oracle_gemm_ex(
+        DTYPES[dtype], layout, ACTS[act], _ptr(A), _ptr(B), _ptr(C),
+        _ptr(bias) if bias is not None else None, M, N, K, lda, ldb, ldc, sA, sB, sC, batch,
+        _ptr(S) if S is not None else None, _ptr(Sa) if Sa is not None else None,
+        host_threads() if threads is None else threads)
+    if rc != 0:
+        raise MemoryError("oracle ran out of memory") if rc == -1 else ValueError("bad mode")
+    if want_sums:
+        return C, S, Sa
+    return C
+
+
+def gemm_ex_sampled(A, B, K: int, lda: int, ldb: int, idx, sA: int = 0, sB: int = 0,
+                    bias=None, dtype: str = "f16", b_layout: str = "kn", act: str = "relu",
+                    threads: int | None = None):
+    """``gemm_relu_sampled`` for the variants of ``gemm_ex``."""
+    layout = B_LAYOUTS[b_layout]
+    A = _u16(A).reshape(-1)
+    B = _u16(B).reshape(-1)
+    idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int64).reshape(-1, 3))
+    n = idx.shape[0]
+    if n:
+        bmax, imax, jmax = idx.max(axis=0)
+        if idx.min() < 0:
+            raise ValueError("negative index")
+        if K > 0:
+            if bmax * sA + imax * lda + K > A.size:
+                raise ValueError("sample outside A")
+            last = (K - 1) * ldb + jmax if layout == 0 else jmax * ldb + K - 1
+            if bmax * sB + last >= B.size:
+                raise ValueError("sample outside B")
+        if bias is not None and jmax >= np.asarray(bias).size:
+            raise ValueError("sample outside bias")
+    if bias is not None:
+        bias = _u16(bias).reshape(-1)
+    out = np.zeros(n, dtype=np.uint16)
+    s = np.zeros(n, dtype=np.float64)
+    sa = np.zeros(n, dtype=np.float64)
+    _load().oracle_gemm_ex_sampled(
+        DTYPES[dtype], layout, ACTS[act], _ptr(A), _ptr(B),
+        _ptr(bias) if bias is not None else None, K, lda, ldb, sA, sB, _ptr(idx), n, _ptr(out),
+        _ptr(s), _ptr(sa), host_threads() if threads is None else threads)
     return out, s, sa

@@ -1,5 +1,6 @@
 /*
- * CPU oracle for the fused GEMM + ReLU with fp16 storage.
+ * CPU oracle for the fused GEMM + ReLU with fp16 storage, and for its
+ * variants: bf16 storage, B stored as (N,K), a per-column bias, no activation.
  *
  * TEST INFRASTRUCTURE ONLY. Nothing on the product path may include, link or
  * call this file: only the test suite, the smoke check and the benchmark's
@@ -35,9 +36,22 @@
  *  - The fp16 store rounds to nearest even (the IEEE default conversion).
  *  - Subnormal fp16 inputs and outputs are exact (no flushing).
  *
+ * Variants (oracle_gemm_ex), each a plain generalisation of the definition:
+ *  - element type bf16 instead of fp16: dec and enc use the bfloat16 format
+ *    (8 exponent bits, 7 stored significand bits); bf16 products are exact in
+ *    binary64 too (two 8-bit significands).
+ *  - B stored as an (N,K) row-major array: B(k,j) is read at B[j*ldb + k]
+ *    (the (BN,BK) B tile of section 3.2 of the practitioner's notes page).
+ *  - a bias vector of N values of the element type, added to every row's sum
+ *    before the activation: r = act(s + bias[j]).  The fusion of neighbouring
+ *    operators into the GEMM's epilogue is what section 2.2 of that page
+ *    describes; the bias-add is the plainest such neighbour.
+ *  - activation none (r = s) or ReLU.
+ *
  * Also exported: dec/enc on arrays (for the pins in the tests), a sampled
  * variant that computes chosen (b, i, j) outputs one by one, and the optional
- * per-element s and sum_k |A_ik * B_kj| used by the fp32 error-bound gate.
+ * per-element s and sum_k |A_ik * B_kj| (+ |bias_j|) used by the fp32
+ * error-bound gate.
  */
 #include <math.h>
 #include <pthread.h>
@@ -100,11 +114,66 @@ static uint16_t enc16(double x)
     return sign | (uint16_t)bits;
 }
 
+/* bfloat16 bit pattern -> exact binary64 value. */
+static double decbf16(uint16_t h)
+{
+    int sign = h >> 15;
+    int e = (h >> 7) & 0xff;
+    int m = h & 0x7f;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -133);                /* subnormal: m * 2^-133 */
+    else if (e < 255)
+        v = ldexp((double)(128 + m), e - 134);     /* (1 + m/128) * 2^(e-127) */
+    else
+        v = m ? NAN : INFINITY;
+    return sign ? -v : v;
+}
+
+/* binary64 -> bfloat16 bit pattern, round to nearest, ties to even (directly
+ * from binary64: no intermediate binary32 rounding). */
+static uint16_t encbf16(double x)
+{
+    if (isnan(x))
+        return 0x7fc0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (a < ldexp(1.0, -126)) {
+        /* subnormal range: the quantum is 2^-133; 128 quanta are the smallest
+         * normal, encoded 0x0080 */
+        double q = round_half_even(ldexp(a, 133));
+        return sign | (uint16_t)q;
+    }
+    if (isinf(a))
+        return sign | 0x7f80;
+    int e;
+    frexp(a, &e);                 /* a in [2^(e-1), 2^e) */
+    double q = round_half_even(ldexp(a, 8 - e));    /* in [128, 256] */
+    /* biased exponent of a is (e - 1) + 127; q == 256 carries into it, and a
+     * carry out of the largest finite binade gives 0x7f80, infinity */
+    uint32_t bits = ((uint32_t)(e + 126) << 7) + ((uint32_t)q - 128u);
+    if (bits >= 0x7f80u)
+        return sign | 0x7f80;
+    return sign | (uint16_t)bits;
+}
+
+enum { DT_F16 = 0, DT_BF16 = 1 };
+enum { B_KN = 0, B_NK = 1 };
+enum { ACT_NONE = 0, ACT_RELU = 1 };
+
+static double dec(int dtype, uint16_t h) { return dtype == DT_BF16 ? decbf16(h) : dec16(h); }
+
+/* The activation on the exact value, then the store in the element type. */
+static uint16_t act_store(int dtype, int act, double s)
+{
+    double r = (act == ACT_RELU) ? ((s > 0.0) ? s : 0.0) : s;
+    return dtype == DT_BF16 ? encbf16(r) : enc16(r);
+}
+
 /* ReLU on the exact accumulator, then the fp16 store. */
 static uint16_t relu_store(double s)
 {
-    double r = (s > 0.0) ? s : 0.0;
-    return enc16(r);
+    return act_store(DT_F16, ACT_RELU, s);
 }
 
 /* The K-sum for one output: a[k] * b[k], k ascending, in binary64. */
@@ -141,6 +210,18 @@ void oracle_relu_store_array(const double *in, uint16_t *out, int64_t n)
         out[i] = relu_store(in[i]);
 }
 
+void oracle_decbf16_array(const uint16_t *in, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = decbf16(in[i]);
+}
+
+void oracle_encbf16_array(const double *in, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = encbf16(in[i]);
+}
+
 /* ------------------------------------------------------------------------ */
 
 typedef struct {
@@ -148,6 +229,8 @@ typedef struct {
     uint16_t *C;
     double *S, *Sabs;         /* optional, batch*M*N, contiguous */
     int64_t M, N, K, lda, ldb, ldc, sA, sB, sC;
+    int dtype, act;
+    const double *bias;       /* decoded bias (N values) or NULL */
     const double *Bt;         /* this batch's B decoded and laid out as (N,K) */
     int64_t b;                /* current batch */
     int nthreads;
@@ -162,11 +245,15 @@ static void *row_worker(void *p)
     uint16_t *C = j->C + j->b * j->sC;
     for (int64_t i = j->tid; i < j->M; i += j->nthreads) {
         for (int64_t k = 0; k < j->K; ++k)
-            arow[k] = dec16(A[i * j->lda + k]);
+            arow[k] = dec(j->dtype, A[i * j->lda + k]);
         for (int64_t n = 0; n < j->N; ++n) {
             double sabs;
             double s = dot_k(arow, j->Bt + n * j->K, j->K, &sabs);
-            C[i * j->ldc + n] = relu_store(s);
+            if (j->bias) {
+                s += j->bias[n];
+                sabs += fabs(j->bias[n]);
+            }
+            C[i * j->ldc + n] = act_store(j->dtype, j->act, s);
             if (j->S) {
                 int64_t o = (j->b * j->M + i) * j->N + n;
                 j->S[o] = s;
@@ -191,22 +278,36 @@ static int clamp_threads(int nthreads)
 
 /*
  * Full computation of every output.  Strides and leading dimensions are in
- * elements.  S and Sabs may be NULL; when given they receive the binary64 sum
- * and the sum of absolute products for every (b, i, j), laid out contiguously
- * as [batch][M][N].  Returns 0, or -1 when memory runs out.
+ * elements.  dtype: 0 fp16, 1 bf16; b_layout: 0 B is (K,N) row-major, 1 B is
+ * (N,K) row-major; act: 0 none, 1 ReLU; bias: N values of the element type
+ * shared by every row and batch, or NULL.  S and Sabs may be NULL; when given
+ * they receive the binary64 value before the activation (sum plus bias) and
+ * the sum of absolute products (plus |bias|) for every (b, i, j), laid out
+ * contiguously as [batch][M][N].  Returns 0, -1 when memory runs out, -2 for
+ * an unknown dtype, layout or activation.
  */
-int oracle_gemm_relu_f16(const uint16_t *A, const uint16_t *B, uint16_t *C,
-                         int64_t M, int64_t N, int64_t K,
-                         int64_t lda, int64_t ldb, int64_t ldc,
-                         int64_t sA, int64_t sB, int64_t sC, int64_t batch,
-                         double *S, double *Sabs, int nthreads)
+int oracle_gemm_ex(int dtype, int b_layout, int act,
+                   const uint16_t *A, const uint16_t *B, uint16_t *C, const uint16_t *bias,
+                   int64_t M, int64_t N, int64_t K,
+                   int64_t lda, int64_t ldb, int64_t ldc,
+                   int64_t sA, int64_t sB, int64_t sC, int64_t batch,
+                   double *S, double *Sabs, int nthreads)
 {
+    if ((dtype != DT_F16 && dtype != DT_BF16) || (b_layout != B_KN && b_layout != B_NK) ||
+        (act != ACT_NONE && act != ACT_RELU))
+        return -2;
     nthreads = clamp_threads(nthreads);
     if (M <= 0 || N <= 0 || batch <= 0)
         return 0;
     double *Bt = (double *)malloc(sizeof(double) * (size_t)N * (size_t)(K > 0 ? K : 1));
-    if (!Bt)
+    double *biasd = bias ? (double *)malloc(sizeof(double) * (size_t)N) : NULL;
+    if (!Bt || (bias && !biasd)) {
+        free(Bt);
+        free(biasd);
         return -1;
+    }
+    for (int64_t n = 0; bias && n < N; ++n)
+        biasd[n] = dec(dtype, bias[n]);
     pthread_t th[256];
     job_t jobs[256];
     for (int64_t b = 0; b < batch; ++b) {
@@ -215,13 +316,14 @@ int oracle_gemm_relu_f16(const uint16_t *A, const uint16_t *B, uint16_t *C,
          * contiguous memory; the values and their order of use are unchanged */
         for (int64_t k = 0; k < K; ++k)
             for (int64_t n = 0; n < N; ++n)
-                Bt[n * K + k] = dec16(Bb[k * ldb + n]);
+                Bt[n * K + k] = dec(dtype, b_layout == B_KN ? Bb[k * ldb + n] : Bb[n * ldb + k]);
         int nt = (int)(M < nthreads ? M : nthreads);
         for (int t = 0; t < nt; ++t) {
             job_t *j = &jobs[t];
             j->A = A; j->B = B; j->C = C; j->S = S; j->Sabs = Sabs;
             j->M = M; j->N = N; j->K = K; j->lda = lda; j->ldb = ldb; j->ldc = ldc;
             j->sA = sA; j->sB = sB; j->sC = sC; j->Bt = Bt; j->b = b;
+            j->dtype = dtype; j->act = act; j->bias = biasd;
             j->nthreads = nt; j->tid = t;
             if (nt == 1)
                 row_worker(j);
@@ -233,17 +335,31 @@ int oracle_gemm_relu_f16(const uint16_t *A, const uint16_t *B, uint16_t *C,
                 pthread_join(th[t], NULL);
     }
     free(Bt);
+    free(biasd);
     return 0;
+}
+
+/* The fp16 GEMM + ReLU itself: oracle_gemm_ex with fp16, (K,N) B, no bias. */
+int oracle_gemm_relu_f16(const uint16_t *A, const uint16_t *B, uint16_t *C,
+                         int64_t M, int64_t N, int64_t K,
+                         int64_t lda, int64_t ldb, int64_t ldc,
+                         int64_t sA, int64_t sB, int64_t sC, int64_t batch,
+                         double *S, double *Sabs, int nthreads)
+{
+    return oracle_gemm_ex(DT_F16, B_KN, ACT_RELU, A, B, C, NULL, M, N, K, lda, ldb, ldc, sA, sB,
+                          sC, batch, S, Sabs, nthreads);
 }
 
 /*
  * Sampled computation: out[q] = C[b][i][j] for the q-th triple (b, i, j) in
- * idx (3*n int64 values).  s_out / abs_out (optional) receive the binary64 sum
- * and the sum of absolute products.  Same arithmetic as the full version.
+ * idx (3*n int64 values).  s_out / abs_out (optional) receive the binary64
+ * value before the activation and the sum of absolute products (plus |bias|).
+ * Same arithmetic as the full version.
  */
 typedef struct {
-    const uint16_t *A, *B;
+    const uint16_t *A, *B, *bias;
     int64_t K, lda, ldb, sA, sB;
+    int dtype, b_layout, act;
     const int64_t *idx;
     int64_t n;
     uint16_t *out;
@@ -260,14 +376,19 @@ static void *sample_worker(void *p)
     for (int64_t q = j->tid; q < j->n; q += j->nthreads) {
         int64_t b = j->idx[3 * q], i = j->idx[3 * q + 1], c = j->idx[3 * q + 2];
         const uint16_t *Ar = j->A + b * j->sA + i * j->lda;
-        const uint16_t *Bc = j->B + b * j->sB + c;
+        const uint16_t *Bb = j->B + b * j->sB;
         for (int64_t k = 0; k < K; ++k) {
-            a[k] = dec16(Ar[k]);
-            bcol[k] = dec16(Bc[k * j->ldb]);
+            a[k] = dec(j->dtype, Ar[k]);
+            bcol[k] = dec(j->dtype, j->b_layout == B_KN ? Bb[k * j->ldb + c] : Bb[c * j->ldb + k]);
         }
         double sabs;
         double s = dot_k(a, bcol, K, &sabs);
-        j->out[q] = relu_store(s);
+        if (j->bias) {
+            double bv = dec(j->dtype, j->bias[c]);
+            s += bv;
+            sabs += fabs(bv);
+        }
+        j->out[q] = act_store(j->dtype, j->act, s);
         if (j->s_out)
             j->s_out[q] = s;
         if (j->abs_out)
@@ -278,13 +399,17 @@ static void *sample_worker(void *p)
     return NULL;
 }
 
-int oracle_gemm_relu_f16_sampled(const uint16_t *A, const uint16_t *B,
-                                 int64_t K, int64_t lda, int64_t ldb,
-                                 int64_t sA, int64_t sB,
-                                 const int64_t *idx, int64_t n,
-                                 uint16_t *out, double *s_out, double *abs_out,
-                                 int nthreads)
+int oracle_gemm_ex_sampled(int dtype, int b_layout, int act,
+                           const uint16_t *A, const uint16_t *B, const uint16_t *bias,
+                           int64_t K, int64_t lda, int64_t ldb,
+                           int64_t sA, int64_t sB,
+                           const int64_t *idx, int64_t n,
+                           uint16_t *out, double *s_out, double *abs_out,
+                           int nthreads)
 {
+    if ((dtype != DT_F16 && dtype != DT_BF16) || (b_layout != B_KN && b_layout != B_NK) ||
+        (act != ACT_NONE && act != ACT_RELU))
+        return -2;
     nthreads = clamp_threads(nthreads);
     if (n <= 0)
         return 0;
@@ -293,8 +418,9 @@ int oracle_gemm_relu_f16_sampled(const uint16_t *A, const uint16_t *B,
     sjob_t jobs[256];
     for (int t = 0; t < nt; ++t) {
         sjob_t *j = &jobs[t];
-        j->A = A; j->B = B; j->K = K; j->lda = lda; j->ldb = ldb;
-        j->sA = sA; j->sB = sB; j->idx = idx; j->n = n; j->out = out;
+        j->A = A; j->B = B; j->bias = bias; j->K = K; j->lda = lda; j->ldb = ldb;
+        j->sA = sA; j->sB = sB; j->dtype = dtype; j->b_layout = b_layout; j->act = act;
+        j->idx = idx; j->n = n; j->out = out;
         j->s_out = s_out; j->abs_out = abs_out; j->nthreads = nt; j->tid = t;
         if (nt == 1)
             sample_worker(j);
@@ -305,4 +431,15 @@ int oracle_gemm_relu_f16_sampled(const uint16_t *A, const uint16_t *B,
         for (int t = 0; t < nt; ++t)
             pthread_join(th[t], NULL);
     return 0;
+}
+
+int oracle_gemm_relu_f16_sampled(const uint16_t *A, const uint16_t *B,
+                                 int64_t K, int64_t lda, int64_t ldb,
+                                 int64_t sA, int64_t sB,
+                                 const int64_t *idx, int64_t n,
+                                 uint16_t *out, double *s_out, double *abs_out,
+                                 int nthreads)
+{
+    return oracle_gemm_ex_sampled(DT_F16, B_KN, ACT_RELU, A, B, NULL, K, lda, ldb, sA, sB, idx,
+                                  n, out, s_out, abs_out, nthreads);
 }
