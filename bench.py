@@ -9,10 +9,12 @@ is reported alongside as a secondary figure.  Prints one JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--no-secondary]
                     [--tile-variant V] [--skinny-variant V] [--raster G]
+                    [--act relu|none] [--bias]
 
-The last three select non-default kernel configurations and tile orders for
-ablations; a line measured with any of them carries them in `config` and no
-`traffic` figure (the counters are taken at the defaults).
+--tile-variant, --skinny-variant and --raster select non-default kernel
+configurations and tile orders for ablations; --act and --bias measure the
+extended epilogue (tg_gemm_ex).  A line measured with any of them carries them
+in `config` and no `traffic` figure (the counters are taken at the defaults).
 """
 
 from __future__ import annotations
@@ -86,7 +88,9 @@ def calibration_copy(torch):
     del src, dst
 
 
-def run_workload(tg, torch, w: wl.Workload, steps: int, warmup: int):
+def run_workload(tg, torch, w: wl.Workload, steps: int, warmup: int, epilogue=None):
+    """Times `steps` calls after `warmup`.  epilogue = (activation, with_bias)
+    routes the calls through tg_gemm_ex; None uses the GEMM+ReLU entry points."""
     a, b = wl.generate(w)
     dev = torch.device("cuda:0")
     nbuf = 1
@@ -100,10 +104,18 @@ def run_workload(tg, torch, w: wl.Workload, steps: int, warmup: int):
     C = [torch.empty(csize, dtype=torch.int16, device=dev) for _ in range(nbuf)]
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
+    bias = None
+    if epilogue is not None and epilogue[1]:
+        bias = torch.from_numpy(wl.generate_bias(w.N, w.seed, scale=0.05).view(np.int16)).to(dev)
 
     def call(i):
         j = i % nbuf
-        if w.batch == 1:
+        if epilogue is not None:
+            st = tg.tg_gemm_ex(tg.TG_DTYPE_F16, tg.TG_B_KN, epilogue[0], A[j].data_ptr(),
+                               B[j].data_ptr(), C[j].data_ptr(),
+                               bias.data_ptr() if bias is not None else 0, w.M, w.N, w.K, w.lda_,
+                               w.ldb_, w.ldc_, w.sA, w.sB, w.sC, w.batch, sh)
+        elif w.batch == 1:
             st = tg.tg_gemm_relu_f16(A[j].data_ptr(), B[j].data_ptr(), C[j].data_ptr(), w.M, w.N,
                                      w.K, w.lda_, w.ldb_, w.ldc_, sh)
         else:
@@ -329,6 +341,10 @@ def main():
                     help="skinny-kernel configuration (tg_set_skinny_variant), -1 = default")
     ap.add_argument("--raster", type=int, default=-1,
                     help="tile order (tg_set_raster): panel height, 0 = row-major, -1 = default")
+    ap.add_argument("--act", choices=["relu", "none"], default="relu",
+                    help="epilogue activation (none: through tg_gemm_ex)")
+    ap.add_argument("--bias", action="store_true",
+                    help="add a per-column bias in the epilogue (through tg_gemm_ex)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -352,11 +368,15 @@ def main():
                 print(f"invalid --{name.replace('_', '-')} {value}", file=sys.stderr)
                 sys.exit(2)
             knobs[name] = value
+    epilogue = None
+    if args.bias or args.act != "relu":
+        epilogue = (tg.TG_ACT_RELU if args.act == "relu" else tg.TG_ACT_NONE, args.bias)
+        knobs["epilogue"] = ("bias+" if args.bias else "") + args.act
     if args.calibrate_copy:
         calibration_copy(torch)
     w = wl.WORKLOADS[args.workload]
     log(f"workload {w.name}: M={w.M} N={w.N} K={w.K} batch={w.batch}")
-    ms, path, nbuf = run_workload(tg, torch, w, args.steps, args.warmup)
+    ms, path, nbuf = run_workload(tg, torch, w, args.steps, args.warmup, epilogue)
     tflops = w.flops / (ms * 1e-3) / 1e12
     gbs = w.compulsory_bytes / (ms * 1e-3) / 1e9
     compute_bound = w.flops / w.compulsory_bytes > PEAK_F16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
@@ -393,7 +413,8 @@ def main():
 
     if not args.no_secondary and w.name != "skinny_16x16384x8192":
         s = wl.WORKLOADS["skinny_16x16384x8192"]
-        sms, spath, snbuf = run_workload(tg, torch, s, max(args.steps, 20), args.warmup)
+        sms, spath, snbuf = run_workload(tg, torch, s, max(args.steps, 20), args.warmup,
+                                         epilogue)
         sgbs = s.compulsory_bytes / (sms * 1e-3) / 1e9
         log(f"{s.name}: {sms * 1e3:.1f} us/call, {sgbs:.0f} GB/s, path={spath}")
         out["secondary"] = {

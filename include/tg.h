@@ -83,6 +83,41 @@ int tg_gemm_relu_f16_strided_batched(const void *A, const void *B, void *C,
                                      int64_t strideA, int64_t strideB, int64_t strideC,
                                      int64_t batch, hipStream_t stream);
 
+/*
+ * Extended form: C = act(A * B + bias), strided-batched, with a choice of
+ * element type and B layout.
+ *
+ * The bias-add and activation are the epilogue of the same tile program (the
+ * "TileLang paper reading" page, section 2, whose epilogue is the ReLU), with
+ * the neighbouring element-wise operator fused into the GEMM as section 2.2 of
+ * the "tilelang practitioner's notes" page describes for fused kernels:
+ *
+ *   C[b][i*ldc + j] = rne( act( sum_k A[b][i*lda + k] * B(b, k, j) + bias[j] ) )
+ *
+ *   dtype       TG_DTYPE_F16: A, B, bias and C are IEEE binary16.
+ *   b_layout    TG_B_KN: B is (K,N) row-major, B(b,k,j) = B[b*strideB + k*ldb + j],
+ *               ldb >= max(1,N).
+ *   activation  TG_ACT_NONE: act(x) = x;  TG_ACT_RELU: x if x > 0 else +0.0.
+ *   bias        DEVICE pointer to N elements shared by every row and batch
+ *               slice, or NULL for no bias (the sum alone).  The bias is added
+ *               to the fp32 sum before the activation, in fp32.
+ * Everything else (sizes, leading dimensions, strides, batch, NULL rules,
+ * errors, asynchrony, determinism) is as for tg_gemm_relu_f16_strided_batched;
+ * batch = 1 is the single-matrix form (strides ignored).  With
+ * TG_ACT_RELU and a NULL bias this is exactly tg_gemm_relu_f16[_strided_batched].
+ * An unknown dtype, layout or activation returns TG_ERR_INVALID_ARG.  A bias
+ * that is not 16-byte aligned takes the any-alignment kernel.
+ */
+enum { TG_DTYPE_F16 = 0 };
+enum { TG_B_KN = 0 };
+enum { TG_ACT_NONE = 0, TG_ACT_RELU = 1 };
+int tg_gemm_ex(int dtype, int b_layout, int activation,
+               const void *A, const void *B, void *C, const void *bias,
+               int64_t M, int64_t N, int64_t K,
+               int64_t lda, int64_t ldb, int64_t ldc,
+               int64_t strideA, int64_t strideB, int64_t strideC,
+               int64_t batch, hipStream_t stream);
+
 /* A static, human-readable name for a tg_status value. */
 const char *tg_status_string(int status);
 

@@ -108,6 +108,26 @@ def test_batched_validation(tg):
     assert f(P, P, P, 4, 4, 4, 4, 4, 4, 2 ** 62, 16, 16, 2, 0) == tg.TG_ERR_INVALID_ARG
 
 
+def test_ex_validation(tg):
+    f = tg.tg_gemm_ex
+    ok = dict(dtype=tg.TG_DTYPE_F16, b_layout=tg.TG_B_KN, activation=tg.TG_ACT_NONE)
+
+    def call(dtype, b_layout, activation, M=4, N=4, K=4, lda=4, ldb=4, ldc=4, batch=1, bias=P):
+        return f(dtype, b_layout, activation, P, P, P, bias, M, N, K, lda, ldb, ldc, 16, 16, 16,
+                 batch, 0)
+
+    assert call(9, ok["b_layout"], ok["activation"]) == tg.TG_ERR_INVALID_ARG
+    assert call(ok["dtype"], 9, ok["activation"]) == tg.TG_ERR_INVALID_ARG
+    assert call(ok["dtype"], ok["b_layout"], 7) == tg.TG_ERR_INVALID_ARG
+    assert call(ok["dtype"], ok["b_layout"], -1) == tg.TG_ERR_INVALID_ARG
+    # the shared size checks apply
+    assert call(ok["dtype"], ok["b_layout"], ok["activation"], lda=3) == tg.TG_ERR_INVALID_ARG
+    assert call(ok["dtype"], ok["b_layout"], ok["activation"], batch=-1) == tg.TG_ERR_INVALID_ARG
+    # empty problems are no-ops, bias or not
+    assert call(ok["dtype"], ok["b_layout"], ok["activation"], M=0) == tg.TG_OK
+    assert call(ok["dtype"], ok["b_layout"], tg.TG_ACT_RELU, N=0, bias=0) == tg.TG_OK
+
+
 def _gpu_visible():
     try:
         import torch
@@ -122,4 +142,7 @@ def test_valid_call_without_device_reports_no_device(tg):
     assert st == tg.TG_ERR_NO_DEVICE
     # K = 0 with null operands is valid and also reaches the device check
     st = tg.tg_gemm_relu_f16(0, 0, P, 4, 4, 0, 1, 4, 4, 0)
+    assert st == tg.TG_ERR_NO_DEVICE
+    st = tg.tg_gemm_ex(tg.TG_DTYPE_F16, tg.TG_B_KN, tg.TG_ACT_NONE, P, P, P, 0, 4, 4, 4, 4, 4, 4,
+                       0, 0, 0, 1, 0)
     assert st == tg.TG_ERR_NO_DEVICE

@@ -40,7 +40,13 @@ EXPORTED_SYMBOLS = (
     "tg_set_tile_variant",
     "tg_set_skinny_variant",
     "tg_set_raster",
+    "tg_gemm_ex",
 )
+
+TG_DTYPE_F16 = 0
+TG_B_KN = 0
+TG_ACT_NONE = 0
+TG_ACT_RELU = 1
 
 
 class TGError(RuntimeError):
@@ -61,6 +67,8 @@ _lib.tg_gemm_relu_f16.argtypes = [_vp, _vp, _vp] + [_i64] * 6 + [_vp]
 _lib.tg_gemm_relu_f16.restype = ctypes.c_int
 _lib.tg_gemm_relu_f16_strided_batched.argtypes = [_vp, _vp, _vp] + [_i64] * 10 + [_vp]
 _lib.tg_gemm_relu_f16_strided_batched.restype = ctypes.c_int
+_lib.tg_gemm_ex.argtypes = [ctypes.c_int] * 3 + [_vp] * 4 + [_i64] * 10 + [_vp]
+_lib.tg_gemm_ex.restype = ctypes.c_int
 _lib.tg_status_string.argtypes = [ctypes.c_int]
 _lib.tg_status_string.restype = ctypes.c_char_p
 _lib.tg_set_path.argtypes = [ctypes.c_int]
@@ -92,6 +100,14 @@ def tg_gemm_relu_f16_strided_batched(A: int, B: int, C: int, M: int, N: int, K: 
     """Raw strided-batched call, returns the tg_status code."""
     return _lib.tg_gemm_relu_f16_strided_batched(A, B, C, M, N, K, lda, ldb, ldc, strideA,
                                                  strideB, strideC, batch, stream)
+
+
+def tg_gemm_ex(dtype: int, b_layout: int, activation: int, A: int, B: int, C: int, bias: int,
+               M: int, N: int, K: int, lda: int, ldb: int, ldc: int, strideA: int, strideB: int,
+               strideC: int, batch: int, stream: int = 0) -> int:
+    """Raw extended call (bias may be 0 for none), returns the tg_status code."""
+    return _lib.tg_gemm_ex(dtype, b_layout, activation, A, B, C, bias or None, M, N, K, lda, ldb,
+                           ldc, strideA, strideB, strideC, batch, stream)
 
 
 def tg_status_string(status: int) -> str:

@@ -103,6 +103,8 @@ bool fast_layout(const tg::GemmArgs &p)
 {
     if (!aligned16(p.A) || !aligned16(p.B) || !aligned16(p.C))
         return false;
+    if (p.bias != nullptr && !aligned16(p.bias))
+        return false;
     if ((p.lda | p.ldb | p.ldc | p.N | p.K) & 7)
         return false;
     if (p.batch > 1 && ((p.sA | p.sB | p.sC) & 7))
@@ -131,9 +133,9 @@ int choose_path(const tg::GemmArgs &p)
     return rounds256 < rounds128 ? TG_PATH_TILE256 : TG_PATH_TILE128;
 }
 
-int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int64_t lda,
-        int64_t ldb, int64_t ldc, int64_t sA, int64_t sB, int64_t sC, int64_t batch,
-        hipStream_t stream)
+int run(const void *A, const void *B, void *C, const void *bias, bool relu, int64_t M, int64_t N,
+        int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int64_t sA, int64_t sB, int64_t sC,
+        int64_t batch, hipStream_t stream)
 {
     int st = validate(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch);
     if (st != TG_OK)
@@ -154,6 +156,8 @@ int run(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, 
     p.sB = batch > 1 ? sB : 0;
     p.sC = batch > 1 ? sC : 0;
     p.batch = batch;
+    p.bias = static_cast<const uint16_t *>(bias);
+    p.relu = relu ? 1 : 0;
 
     int path = g_forced_path.load(std::memory_order_relaxed);
     if (path == TG_PATH_AUTO)
@@ -208,7 +212,7 @@ extern "C" {
 int tg_gemm_relu_f16(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
                      int64_t lda, int64_t ldb, int64_t ldc, hipStream_t stream)
 {
-    return run(A, B, C, M, N, K, lda, ldb, ldc, 0, 0, 0, 1, stream);
+    return run(A, B, C, nullptr, true, M, N, K, lda, ldb, ldc, 0, 0, 0, 1, stream);
 }
 
 int tg_gemm_relu_f16_strided_batched(const void *A, const void *B, void *C, int64_t M, int64_t N,
@@ -216,7 +220,21 @@ int tg_gemm_relu_f16_strided_batched(const void *A, const void *B, void *C, int6
                                      int64_t strideA, int64_t strideB, int64_t strideC,
                                      int64_t batch, hipStream_t stream)
 {
-    return run(A, B, C, M, N, K, lda, ldb, ldc, strideA, strideB, strideC, batch, stream);
+    return run(A, B, C, nullptr, true, M, N, K, lda, ldb, ldc, strideA, strideB, strideC, batch,
+               stream);
+}
+
+int tg_gemm_ex(int dtype, int b_layout, int activation, const void *A, const void *B, void *C,
+               const void *bias, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+               int64_t ldc, int64_t strideA, int64_t strideB, int64_t strideC, int64_t batch,
+               hipStream_t stream)
+{
+    if (dtype != TG_DTYPE_F16 || b_layout != TG_B_KN)
+        return TG_ERR_INVALID_ARG;
+    if (activation != TG_ACT_NONE && activation != TG_ACT_RELU)
+        return TG_ERR_INVALID_ARG;
+    return run(A, B, C, bias, activation == TG_ACT_RELU, M, N, K, lda, ldb, ldc, strideA, strideB,
+               strideC, batch, stream);
 }
 
 const char *tg_status_string(int status)

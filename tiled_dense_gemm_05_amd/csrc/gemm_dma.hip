@@ -170,14 +170,6 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_ad
 }
 #pragma clang diagnostic pop
 
-__device__ __forceinline__ uint32_t pack_relu_f16x2(float a, float b)
-{
-    const _Float16 ha = (_Float16)(a > 0.0f ? a : 0.0f);
-    const _Float16 hb = (_Float16)(b > 0.0f ? b : 0.0f);
-    return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
-}
-
 // Scheduling hint: alternate one MFMA with one LDS read, then the rest.
 template <int MFMAS, int READS>
 __device__ __forceinline__ void interleave_mfma_lds()
@@ -478,25 +470,29 @@ gemm_relu_dma_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
         }
     }
 
-    // Epilogue: ReLU, round to nearest even, and the fp16 tile staged in LDS
-    // (16-byte chunks of each row XOR-swizzled by the row) so that the global
-    // stores are whole 16-byte chunks per lane, a wave writing contiguous
-    // runs of rows instead of 8 bytes into 32 different rows.
+    // Epilogue: bias, ReLU, round to nearest even, and the fp16 tile staged
+    // in LDS (16-byte chunks of each row XOR-swizzled by the row) so that the
+    // global stores are whole 16-byte chunks per lane, a wave writing
+    // contiguous runs of rows instead of 8 bytes into 32 different rows.
     block_barrier();   // every wave is done with the LDS ring / partial sums
     lds_u16 *cst = (lds_u16 *)smem;
     if (kg == 0) {
+        const bool relu = p.relu != 0;
 #pragma unroll
-        for (int fm = 0; fm < T::FM; ++fm) {
-            const int row = wm * T::TM + fm * 32 + (lane & 31);
+        for (int fn = 0; fn < T::FN; ++fn) {
 #pragma unroll
-            for (int fn = 0; fn < T::FN; ++fn) {
+            for (int g = 0; g < 4; ++g) {
+                // the lane's four columns of this group, the same in every row
+                const int col = wn * T::TN + fn * 32 + 8 * g + 4 * (lane >> 5);
+                float bv[4];
+                load_bias4(p.bias, n0 + col, N, bv);
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int col = wn * T::TN + fn * 32 + 8 * g + 4 * (lane >> 5);
+                for (int fm = 0; fm < T::FM; ++fm) {
+                    const int row = wm * T::TM + fm * 32 + (lane & 31);
                     const f32x16 &v = acc[fm][fn];
                     u32x2 w;
-                    w.x = pack_relu_f16x2(v[4 * g + 0], v[4 * g + 1]);
-                    w.y = pack_relu_f16x2(v[4 * g + 2], v[4 * g + 3]);
+                    w.x = epi_pack_f16x2(v[4 * g + 0] + bv[0], v[4 * g + 1] + bv[1], relu);
+                    w.y = epi_pack_f16x2(v[4 * g + 2] + bv[2], v[4 * g + 3] + bv[3], relu);
                     const int phys = (col >> 3) ^ (row % T::CB);
                     *reinterpret_cast<__attribute__((address_space(3))) u32x2 *>(
                         cst + row * T::BN + phys * 8 + (col & 4)) = w;

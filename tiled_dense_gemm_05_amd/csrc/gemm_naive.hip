@@ -1,7 +1,8 @@
 // The plain kernel: one thread per output element, fp32 fused multiply-add
-// over k in ascending order, ReLU, round-to-nearest-even fp16 store.  It is the
-// literal reading of the GEMM+ReLU program of the "TileLang paper reading"
-// page, section 2, without tiles; it serves as a slow cross-check path.
+// over k in ascending order, bias, ReLU, round-to-nearest-even fp16 store.
+// It is the literal reading of the GEMM+ReLU program of the "TileLang paper
+// reading" page, section 2, without tiles; it serves as a slow cross-check
+// path.
 #include "tg_internal.h"
 
 namespace tg {
@@ -22,7 +23,9 @@ __global__ void __launch_bounds__(256) gemm_relu_naive_kernel(GemmArgs p)
         float s = 0.0f;
         for (int64_t k = 0; k < p.K; ++k)
             s = __builtin_fmaf((float)a[k], (float)bc[k * p.ldb], s);
-        const float r0 = s > 0.0f ? s : 0.0f;
+        if (p.bias != nullptr)
+            s += (float)__builtin_bit_cast(_Float16, p.bias[j]);
+        const float r0 = (p.relu == 0 || s > 0.0f) ? s : 0.0f;
         reinterpret_cast<_Float16 *>(p.C)[b * p.sC + i * p.ldc + j] = (_Float16)r0;
     }
 }

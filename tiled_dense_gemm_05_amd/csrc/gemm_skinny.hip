@@ -142,14 +142,6 @@ __device__ __forceinline__ void dma16_nt(i32x4 rsrc, uint32_t voff, uint32_t lds
 }
 #pragma clang diagnostic pop
 
-__device__ __forceinline__ uint32_t pack_relu_f16x2(float a, float b)
-{
-    const _Float16 ha = (_Float16)(a > 0.0f ? a : 0.0f);
-    const _Float16 hb = (_Float16)(b > 0.0f ? b : 0.0f);
-    return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
-}
-
 template <class T>
 __global__ void __launch_bounds__(T::NT) gemm_relu_skinny_kernel(GemmArgs p, int steps_per_wave)
 {
@@ -269,7 +261,8 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_skinny_kernel(GemmArgs p, int
     __syncthreads();
 
     // Fragment q = (mb, f) is finished by wave q % NW: sum over the waves in
-    // order, ReLU, fp16, store.  Lane owns C[m][n .. n+3].
+    // order, bias, ReLU, fp16, store.  Lane owns C[m][n .. n+3].
+    const bool relu = p.relu != 0;
     for (int q = wave; q < T::MB * T::NF; q += T::NW) {
         f32x4 s = part[q * 64 + lane];
         for (int w = 1; w < T::NW; ++w)
@@ -278,9 +271,11 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_skinny_kernel(GemmArgs p, int
         const int64_t m = mb * 16 + (lane & 15);
         const int64_t n = n0 + f * 16 + 4 * (lane >> 4);
         if (m < M && n < N) {
+            float bv[4];
+            load_bias4(p.bias, n, N, bv);
             u32x2 w2;
-            w2.x = pack_relu_f16x2(s[0], s[1]);
-            w2.y = pack_relu_f16x2(s[2], s[3]);
+            w2.x = epi_pack_f16x2(s[0] + bv[0], s[1] + bv[1], relu);
+            w2.y = epi_pack_f16x2(s[2] + bv[2], s[3] + bv[3], relu);
             *reinterpret_cast<u32x2 *>(C + m * p.ldc + n) = w2;
         }
     }

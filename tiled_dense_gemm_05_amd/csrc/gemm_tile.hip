@@ -129,14 +129,6 @@ __device__ __forceinline__ u32x4 load8_masked(const uint16_t *p, int64_t avail, 
     return pack8(e);
 }
 
-__device__ __forceinline__ uint32_t pack_relu_f16x2(float a, float b)
-{
-    const _Float16 ha = (_Float16)(a > 0.0f ? a : 0.0f);
-    const _Float16 hb = (_Float16)(b > 0.0f ? b : 0.0f);
-    return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
-}
-
 // One K-tile of matrix-core work on LDS stage (As, Bs).
 template <class T>
 __device__ __forceinline__ void mma_stage(const lds_u16 *As, const lds_u16 *Bs,
@@ -294,8 +286,9 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_tile_kernel(GemmArgs p, int t
         }
     }
 
-    // Epilogue: ReLU on the fp32 accumulator, round to nearest even fp16,
-    // masked store.  Lane owns C[m][n .. n+3] of each 4-register group.
+    // Epilogue: bias and ReLU on the fp32 accumulator, round to nearest even
+    // fp16, masked store.  Lane owns C[m][n .. n+3] of each 4-register group.
+    const bool relu = p.relu != 0;
 #pragma unroll
     for (int fm = 0; fm < T::FM; ++fm) {
         const int64_t m = m0 + wm * T::TM + fm * 32 + (lane & 31);
@@ -308,9 +301,19 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_tile_kernel(GemmArgs p, int t
             for (int g = 0; g < 4; ++g) {
                 const int64_t n = n0 + wn * T::TN + fn * 32 + 8 * g + 4 * (lane >> 5);
                 const f32x16 &v = acc[fm][fn];
+                float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if constexpr (!GENERIC) {
+                    load_bias4(p.bias, n, N, bv);
+                } else if (p.bias != nullptr) {
+                    // any alignment: one element at a time, inside the row only
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        if (n + t < N)
+                            bv[t] = (float)__builtin_bit_cast(_Float16, p.bias[n + t]);
+                }
                 u32x2 w;
-                w.x = pack_relu_f16x2(v[4 * g + 0], v[4 * g + 1]);
-                w.y = pack_relu_f16x2(v[4 * g + 2], v[4 * g + 3]);
+                w.x = epi_pack_f16x2(v[4 * g + 0] + bv[0], v[4 * g + 1] + bv[1], relu);
+                w.y = epi_pack_f16x2(v[4 * g + 2] + bv[2], v[4 * g + 3] + bv[3], relu);
                 uint16_t *dst = crow + n;
                 if constexpr (!GENERIC) {
                     if (n < N)

@@ -8,7 +8,9 @@ namespace tg {
 
 // One strided-batched problem, sizes and strides in elements.  The host has
 // validated it; every kernel masks its own edges, so any M, N, K >= 0 is safe
-// for the layouts the ABI documents.
+// for the layouts the ABI documents.  The epilogue adds bias[n] (N values
+// shared by every row and batch; none when null) and applies the ReLU when
+// `relu` is set.
 struct GemmArgs {
     const uint16_t *A;
     const uint16_t *B;
@@ -17,7 +19,40 @@ struct GemmArgs {
     int64_t lda, ldb, ldc;
     int64_t sA, sB, sC;
     int64_t batch;
+    const uint16_t *bias;
+    int relu;
 };
+
+// Epilogue of two outputs: ReLU (x if x > 0 else +0) when `relu`, then fp16
+// round to nearest even; packed low | high << 16.
+__device__ __forceinline__ uint32_t epi_pack_f16x2(float a, float b, bool relu)
+{
+    if (relu) {
+        a = a > 0.0f ? a : 0.0f;
+        b = b > 0.0f ? b : 0.0f;
+    }
+    const _Float16 ha = (_Float16)a;
+    const _Float16 hb = (_Float16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+// bias[n .. n+3] as floats, from an 8-byte aligned address; zeros without a
+// bias or past the last column (N is a multiple of 4 on the paths that use
+// this, so a group of four columns is wholly inside or outside).
+__device__ __forceinline__ void load_bias4(const uint16_t *bias, int64_t n, int64_t N,
+                                           float (&b)[4])
+{
+    b[0] = b[1] = b[2] = b[3] = 0.0f;
+    if (bias != nullptr && n < N) {
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t w = *reinterpret_cast<const u32x2_t *>(bias + n);
+        b[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w.x & 0xffff));
+        b[1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w.x >> 16));
+        b[2] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w.y & 0xffff));
+        b[3] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w.y >> 16));
+    }
+}
 
 // Tile coordinates of workgroup `pid` of a tilesM x tilesN grid.  The
 // hardware hands consecutive workgroup ids to the eight XCDs in turn, and

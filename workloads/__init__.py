@@ -114,12 +114,44 @@ def to_f16_bits(x: np.ndarray) -> np.ndarray:
     return np.asarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
 
 
-def generate_dense(M: int, N: int, K: int, dist: str, seed: int, batch: int = 1):
-    """(A_bits, B_bits): dense row-major operands, A drawn before B."""
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """binary64 values -> bfloat16 bit patterns (rounded to binary32 by numpy,
+    then to bfloat16 by torch's round-to-nearest-even cast)."""
+    import torch
+    x32 = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    t = torch.from_numpy(x32).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def to_bits(x: np.ndarray, dtype: str = "f16") -> np.ndarray:
+    if dtype == "f16":
+        return to_f16_bits(x)
+    if dtype == "bf16":
+        return to_bf16_bits(x)
+    raise ValueError(f"unknown element type {dtype!r}")
+
+
+def generate_dense(M: int, N: int, K: int, dist: str, seed: int, batch: int = 1,
+                   dtype: str = "f16"):
+    """(A_bits, B_bits): dense row-major operands, A drawn before B, as fp16
+    (default) or bf16 bit patterns.  B is (K,N) row-major; its (N,K) form is
+    the transpose of the same values."""
     rng = np.random.default_rng(seed)
-    a = to_f16_bits(_draw(rng, dist, K, batch * M * K))
-    b = to_f16_bits(_draw(rng, dist, K, batch * K * N))
+    a = to_bits(_draw(rng, dist, K, batch * M * K), dtype)
+    b = to_bits(_draw(rng, dist, K, batch * K * N), dtype)
     return a, b
+
+
+def generate_bias(N: int, seed: int, dtype: str = "f16", scale: float = 1.0) -> np.ndarray:
+    """N bias values, uniform(-scale, scale), from their own seeded stream."""
+    rng = np.random.default_rng(10_000 + seed)
+    return to_bits(rng.uniform(-scale, scale, N), dtype)
+
+
+def transpose_bits(b: np.ndarray, K: int, N: int, batch: int = 1) -> np.ndarray:
+    """(K,N) row-major slices -> (N,K) row-major slices (a copy)."""
+    return np.ascontiguousarray(
+        np.asarray(b).reshape(batch, K, N).transpose(0, 2, 1)).reshape(-1)
 
 
 def pad_rows(x: np.ndarray, rows: int, cols: int, ld: int, batch: int = 1,
