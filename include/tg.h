@@ -94,9 +94,14 @@ int tg_gemm_relu_f16_strided_batched(const void *A, const void *B, void *C,
  *
  *   C[b][i*ldc + j] = rne( act( sum_k A[b][i*lda + k] * B(b, k, j) + bias[j] ) )
  *
- *   dtype       TG_DTYPE_F16: A, B, bias and C are IEEE binary16.
+ *   dtype       TG_DTYPE_F16: A, B, bias and C are IEEE binary16;
+ *               TG_DTYPE_BF16: they are bfloat16 (8 exponent, 7 stored
+ *               significand bits), stored with round to nearest even.
  *   b_layout    TG_B_KN: B is (K,N) row-major, B(b,k,j) = B[b*strideB + k*ldb + j],
- *               ldb >= max(1,N).
+ *               ldb >= max(1,N);
+ *               TG_B_NK: B is (N,K) row-major (a transposed weight, the (BN,BK)
+ *               B tile of section 3.2 of the practitioner's notes page),
+ *               B(b,k,j) = B[b*strideB + j*ldb + k], ldb >= max(1,K).
  *   activation  TG_ACT_NONE: act(x) = x;  TG_ACT_RELU: x if x > 0 else +0.0.
  *   bias        DEVICE pointer to N elements shared by every row and batch
  *               slice, or NULL for no bias (the sum alone).  The bias is added
@@ -106,10 +111,12 @@ int tg_gemm_relu_f16_strided_batched(const void *A, const void *B, void *C,
  * batch = 1 is the single-matrix form (strides ignored).  With
  * TG_ACT_RELU and a NULL bias this is exactly tg_gemm_relu_f16[_strided_batched].
  * An unknown dtype, layout or activation returns TG_ERR_INVALID_ARG.  A bias
- * that is not 16-byte aligned takes the any-alignment kernel.
+ * that is not 16-byte aligned takes the any-alignment kernel.  The tuning
+ * knobs tg_set_tile_variant / tg_set_skinny_variant apply to bf16 and (N,K) B
+ * only for the default configurations (others fall back to the default).
  */
-enum { TG_DTYPE_F16 = 0 };
-enum { TG_B_KN = 0 };
+enum { TG_DTYPE_F16 = 0, TG_DTYPE_BF16 = 1 };
+enum { TG_B_KN = 0, TG_B_NK = 1 };
 enum { TG_ACT_NONE = 0, TG_ACT_RELU = 1 };
 int tg_gemm_ex(int dtype, int b_layout, int activation,
                const void *A, const void *B, void *C, const void *bias,

@@ -123,6 +123,11 @@ def test_ex_validation(tg):
     # the shared size checks apply
     assert call(ok["dtype"], ok["b_layout"], ok["activation"], lda=3) == tg.TG_ERR_INVALID_ARG
     assert call(ok["dtype"], ok["b_layout"], ok["activation"], batch=-1) == tg.TG_ERR_INVALID_ARG
+    # an (N,K) B needs ldb >= K, a (K,N) B ldb >= N
+    assert f(0, tg.TG_B_NK, 0, P, P, P, 0, 4, 8, 16, 16, 12, 8, 0, 0, 0, 1,
+             0) == tg.TG_ERR_INVALID_ARG
+    assert f(0, tg.TG_B_KN, 0, P, P, P, 0, 4, 16, 8, 8, 12, 16, 0, 0, 0, 1,
+             0) == tg.TG_ERR_INVALID_ARG
     # empty problems are no-ops, bias or not
     assert call(ok["dtype"], ok["b_layout"], ok["activation"], M=0) == tg.TG_OK
     assert call(ok["dtype"], ok["b_layout"], tg.TG_ACT_RELU, N=0, bias=0) == tg.TG_OK
@@ -143,6 +148,8 @@ def test_valid_call_without_device_reports_no_device(tg):
     # K = 0 with null operands is valid and also reaches the device check
     st = tg.tg_gemm_relu_f16(0, 0, P, 4, 4, 0, 1, 4, 4, 0)
     assert st == tg.TG_ERR_NO_DEVICE
-    st = tg.tg_gemm_ex(tg.TG_DTYPE_F16, tg.TG_B_KN, tg.TG_ACT_NONE, P, P, P, 0, 4, 4, 4, 4, 4, 4,
-                       0, 0, 0, 1, 0)
-    assert st == tg.TG_ERR_NO_DEVICE
+    for dtype in (tg.TG_DTYPE_F16, tg.TG_DTYPE_BF16):
+        for layout in (tg.TG_B_KN, tg.TG_B_NK):
+            st = tg.tg_gemm_ex(dtype, layout, tg.TG_ACT_NONE, P, P, P, 0, 4, 4, 4, 4, 4, 4, 0, 0,
+                               0, 1, 0)
+            assert st == tg.TG_ERR_NO_DEVICE

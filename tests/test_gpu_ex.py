@@ -1,5 +1,5 @@
-"""GPU parity of the extended entry point tg_gemm_ex (bias and activation)
-against the CPU oracle, through the C ABI.
+"""GPU parity of the extended entry point tg_gemm_ex (bias, activation, bf16
+elements, B stored as (N,K)) against the CPU oracle, through the C ABI.
 
 Every case prints its name before touching the GPU.  Inputs come from the
 seeded generators; expected values come only from the oracle.
@@ -17,8 +17,11 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-SENTINEL = 0x7E00   # quiet NaN in cells the kernel must not write
+SENTINEL = 0x7E00   # cells the kernel must not write (an fp16 NaN; compared as bits)
 ACTS = {"none": 0, "relu": 1}
+DTYPES = {"f16": 0, "bf16": 1}
+LAYOUTS = {"kn": 0, "nk": 1}
+MODES = [("f16", "kn"), ("bf16", "kn"), ("f16", "nk"), ("bf16", "nk")]
 
 
 def say(*a):
@@ -50,22 +53,33 @@ def host(t) -> np.ndarray:
     return t.cpu().numpy().view(np.uint16)
 
 
+def operands(M, N, K, dist, seed, batch, dtype, layout, lda, ldb):
+    """Seeded A and B bits in the requested element type and B layout, rows
+    padded to the leading dimensions (padding holds NaN)."""
+    a, b = wl.generate_dense(M, N, K, dist, seed, batch=batch, dtype=dtype)
+    a = wl.pad_rows(a, M, K, lda, batch)
+    if layout == "nk":
+        b = wl.pad_rows(wl.transpose_bits(b, K, N, batch), N, K, ldb, batch)
+    else:
+        b = wl.pad_rows(b, K, N, ldb, batch)
+    return a, b
+
+
 def ex_case(tg, oracle_lib, M, N, K, act, bias_mode, path=None, batch=1, dist="uniform",
-            seed=0, lda=None, ldb=None, ldc=None, guard=64):
+            seed=0, lda=None, ldb=None, ldc=None, guard=64, dtype="f16", layout="kn"):
     """One strided-batched call against the oracle: bias_mode None, "aligned"
     (16-byte aligned) or "offset" (2 bytes past an aligned address)."""
     lda = K if lda is None else lda
-    ldb = N if ldb is None else ldb
+    ldb = (N if layout == "kn" else K) if ldb is None else ldb
     ldc = N if ldc is None else ldc
-    sA, sB, sC = M * lda, K * ldb, M * ldc
-    a, b = wl.generate_dense(M, N, K, dist, seed, batch=batch)
-    a = wl.pad_rows(a, M, K, lda, batch)
-    b = wl.pad_rows(b, K, N, ldb, batch)
-    bias = wl.generate_bias(N, seed) if bias_mode else None
+    sA, sB, sC = M * lda, (K if layout == "kn" else N) * ldb, M * ldc
+    a, b = operands(M, N, K, dist, seed, batch, dtype, layout, lda, ldb)
+    bias = wl.generate_bias(N, seed, dtype=dtype) if bias_mode else None
     csize = (batch - 1) * sC + (M - 1) * ldc + N
     ref = np.full(csize, SENTINEL, np.uint16)
     ref, S, Sa = oracle_lib.gemm_ex(a, b, M, N, K, lda, ldb, ldc, batch, sA, sB, sC, C=ref,
-                                    bias=bias, act=act, want_sums=True)
+                                    bias=bias, act=act, dtype=dtype, b_layout=layout,
+                                    want_sums=True)
     if path is not None:
         assert tg.tg_set_path(path) >= 0
     a_d, b_d = dev(a), dev(b)
@@ -73,9 +87,9 @@ def ex_case(tg, oracle_lib, M, N, K, act, bias_mode, path=None, batch=1, dist="u
     off = 1 if bias_mode == "offset" else 0
     bias_d = dev(np.concatenate([np.zeros(off, np.uint16), bias])) if bias_mode else None
     bias_ptr = bias_d.data_ptr() + 2 * off if bias_mode else 0
-    say(f"ex M={M} N={N} K={K} act={act} bias={bias_mode} batch={batch} "
+    say(f"ex {dtype}/{layout} M={M} N={N} K={K} act={act} bias={bias_mode} batch={batch} "
         f"ld=({lda},{ldb},{ldc}) forced={path}")
-    st = tg.tg_gemm_ex(tg.TG_DTYPE_F16, tg.TG_B_KN, ACTS[act], a_d.data_ptr(), b_d.data_ptr(),
+    st = tg.tg_gemm_ex(DTYPES[dtype], LAYOUTS[layout], ACTS[act], a_d.data_ptr(), b_d.data_ptr(),
                        c_d.data_ptr(), bias_ptr, M, N, K, lda, ldb, ldc, sA, sB, sC, batch,
                        torch.cuda.current_stream().cuda_stream)
     assert st == tg.TG_OK, tg.tg_status_string(st)
@@ -89,7 +103,7 @@ def ex_case(tg, oracle_lib, M, N, K, act, bias_mode, path=None, batch=1, dist="u
            + np.arange(N)[None, None, :]).reshape(-1)
     win[idx] = True
     assert np.all(out[~win] == SENTINEL), "wrote outside the M x N windows"
-    rep = gate(out[idx], ref[idx], K, Sa.reshape(-1), relu=(act == "relu"))
+    rep = gate(out[idx], ref[idx], K, Sa.reshape(-1), dtype=dtype, relu=(act == "relu"))
     assert rep.ok, f"{used}: {rep}"
     return used, out[idx], ref[idx]
 
@@ -97,13 +111,16 @@ def ex_case(tg, oracle_lib, M, N, K, act, bias_mode, path=None, batch=1, dist="u
 PATHS = ["auto", "naive", "generic", "tile128", "tile256", "skinny"]
 
 
+@pytest.mark.parametrize("dtype,layout", MODES)
 @pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("act", ["none", "relu"])
 @pytest.mark.parametrize("bias_mode", [None, "aligned", "offset"])
 @pytest.mark.parametrize("M,N,K", [(257, 264, 136), (48, 520, 1000), (129, 131, 33)])
-def test_bias_and_activation_on_every_path(tg, oracle_lib, path, act, bias_mode, M, N, K):
+def test_bias_and_activation_on_every_path(tg, oracle_lib, dtype, layout, path, act, bias_mode,
+                                           M, N, K):
     forced = None if path == "auto" else getattr(tg, f"TG_PATH_{path.upper()}")
-    used, _, _ = ex_case(tg, oracle_lib, M, N, K, act, bias_mode, path=forced, seed=M + K)
+    used, _, _ = ex_case(tg, oracle_lib, M, N, K, act, bias_mode, path=forced, seed=M + K,
+                         dtype=dtype, layout=layout)
     aligned = N % 8 == 0 and K % 8 == 0 and bias_mode != "offset"
     if path in ("naive", "generic"):
         assert used == path
@@ -115,16 +132,33 @@ def test_bias_and_activation_on_every_path(tg, oracle_lib, path, act, bias_mode,
         assert used == path
 
 
+@pytest.mark.parametrize("dtype,layout", MODES)
 @pytest.mark.parametrize("act", ["none", "relu"])
-@pytest.mark.parametrize("M,N,K,batch", [(128, 128, 64, 6), (100, 72, 40, 3), (16, 256, 512, 4)])
-def test_batched_with_shared_bias(tg, oracle_lib, act, M, N, K, batch):
-    ex_case(tg, oracle_lib, M, N, K, act, "aligned", batch=batch, seed=batch)
+@pytest.mark.parametrize("M,N,K,batch", [(128, 128, 64, 6), (100, 72, 40, 3), (16, 256, 512, 4),
+                                         (520, 264, 136, 2)])
+def test_batched_with_shared_bias(tg, oracle_lib, dtype, layout, act, M, N, K, batch):
+    ex_case(tg, oracle_lib, M, N, K, act, "aligned", batch=batch, seed=batch, dtype=dtype,
+            layout=layout)
 
 
+@pytest.mark.parametrize("dtype,layout", MODES)
 @pytest.mark.parametrize("act", ["none", "relu"])
-def test_padded_leading_dimensions(tg, oracle_lib, act):
-    ex_case(tg, oracle_lib, 300, 264, 200, act, "aligned", lda=216, ldb=280, ldc=272, seed=3)
-    ex_case(tg, oracle_lib, 300, 261, 203, act, "offset", lda=205, ldb=263, ldc=267, seed=4)
+def test_padded_leading_dimensions(tg, oracle_lib, dtype, layout, act):
+    ldb_a, ldb_b = (280, 263) if layout == "kn" else (216, 205)
+    ex_case(tg, oracle_lib, 300, 264, 200, act, "aligned", lda=216, ldb=ldb_a, ldc=272, seed=3,
+            dtype=dtype, layout=layout)
+    ex_case(tg, oracle_lib, 300, 261, 203, act, "offset", lda=205, ldb=ldb_b, ldc=267, seed=4,
+            dtype=dtype, layout=layout)
+
+
+@pytest.mark.parametrize("dtype,layout", MODES)
+@pytest.mark.parametrize("path", ["tile128", "tile256", "skinny", "generic"])
+@pytest.mark.parametrize("M,N,K", [(1, 8, 8), (64, 64, 64), (33, 1000, 2056), (700, 520, 72),
+                                   (65, 136, 4104)])
+def test_modes_across_shapes(tg, oracle_lib, dtype, layout, path, M, N, K):
+    forced = getattr(tg, f"TG_PATH_{path.upper()}")
+    ex_case(tg, oracle_lib, M, N, K, "relu", "aligned", path=forced, seed=N + K, dtype=dtype,
+            layout=layout, dist="uniform_invsqrtk")
 
 
 def test_relu_without_bias_equals_the_plain_entry_point(tg, oracle_lib):
@@ -144,23 +178,26 @@ def test_relu_without_bias_equals_the_plain_entry_point(tg, oracle_lib):
     assert np.array_equal(host(c1), host(c2))
 
 
-@pytest.mark.parametrize("path", ["tile128", "tile256", "skinny", "generic"])
-def test_integer_inputs_are_bit_exact_without_relu(tg, oracle_lib, path):
+@pytest.mark.parametrize("dtype,layout", MODES)
+@pytest.mark.parametrize("path", ["tile128", "tile256", "skinny", "generic", "naive"])
+def test_integer_inputs_are_bit_exact_without_relu(tg, oracle_lib, dtype, layout, path):
     # integer operands and bias: every fp32 partial sum is exact, so the GPU
-    # must equal the oracle bit for bit, negative outputs included
+    # and the oracle round the same exact value and agree bit for bit,
+    # negative outputs included
     M, N, K = (32, 256, 1024) if path == "skinny" else (264, 256, 520)
     if path == "generic":
         N += 3
-    a, b = wl.generate_dense(M, N, K, "int3", 17)
-    bias = wl.to_f16_bits(np.round(np.random.default_rng(5).uniform(-40, 40, N)))
-    ref = oracle_lib.gemm_ex(a, b, M, N, K, bias=bias, act="none")
+    a, b = operands(M, N, K, "int3", 17, 1, dtype, layout, K, N if layout == "kn" else K)
+    bias = wl.to_bits(np.round(np.random.default_rng(5).uniform(-40, 40, N)), dtype)
+    ref = oracle_lib.gemm_ex(a, b, M, N, K, bias=bias, act="none", dtype=dtype, b_layout=layout)
     assert tg.tg_set_path(getattr(tg, f"TG_PATH_{path.upper()}")) >= 0
     a_d, b_d, bias_d = dev(a), dev(b), dev(bias)
     c_d = dev(np.zeros(M * N, np.uint16))
-    say(f"ex integer M={M} N={N} K={K} path={path}")
-    st = tg.tg_gemm_ex(tg.TG_DTYPE_F16, tg.TG_B_KN, tg.TG_ACT_NONE, a_d.data_ptr(),
-                       b_d.data_ptr(), c_d.data_ptr(), bias_d.data_ptr(), M, N, K, K, N, N, 0, 0,
-                       0, 1, torch.cuda.current_stream().cuda_stream)
+    say(f"ex integer {dtype}/{layout} M={M} N={N} K={K} path={path}")
+    st = tg.tg_gemm_ex(DTYPES[dtype], LAYOUTS[layout], tg.TG_ACT_NONE, a_d.data_ptr(),
+                       b_d.data_ptr(), c_d.data_ptr(), bias_d.data_ptr(), M, N, K, K,
+                       N if layout == "kn" else K, N, 0, 0, 0, 1,
+                       torch.cuda.current_stream().cuda_stream)
     assert st == tg.TG_OK
     torch.cuda.synchronize()
     got = host(c_d)
@@ -169,31 +206,39 @@ def test_integer_inputs_are_bit_exact_without_relu(tg, oracle_lib, path):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("dtype,layout", MODES)
 @pytest.mark.parametrize("name,n", [("large_8192", 20000), ("skinny_16x16384x8192", None),
                                     ("batched_1024x128x128x64", None)])
-def test_full_size_with_bias_no_activation(tg, oracle_lib, name, n):
+def test_full_size_with_bias_no_activation(tg, oracle_lib, dtype, layout, name, n):
     w = wl.WORKLOADS[name]
-    a, b = wl.generate(w)
-    bias = wl.generate_bias(w.N, w.seed, scale=0.05)
+    a, b = wl.generate_dense(w.M, w.N, w.K, w.dist, w.seed, batch=w.batch, dtype=dtype)
+    ldb = w.N if layout == "kn" else w.K
+    sB = w.K * w.N
+    if layout == "nk":
+        b = wl.transpose_bits(b, w.K, w.N, w.batch)
+    bias = wl.generate_bias(w.N, w.seed, dtype=dtype, scale=0.05)
     csize = (w.batch - 1) * w.sC + (w.M - 1) * w.ldc_ + w.N
     a_d, b_d, bias_d = dev(a), dev(b), dev(bias)
     c_d = torch.empty(csize, dtype=torch.int16, device="cuda")
-    say(f"ex full-size {name} bias, no activation")
-    st = tg.tg_gemm_ex(tg.TG_DTYPE_F16, tg.TG_B_KN, tg.TG_ACT_NONE, a_d.data_ptr(),
-                       b_d.data_ptr(), c_d.data_ptr(), bias_d.data_ptr(), w.M, w.N, w.K, w.lda_,
-                       w.ldb_, w.ldc_, w.sA, w.sB, w.sC, w.batch,
+    say(f"ex full-size {name} {dtype}/{layout} bias, no activation")
+    st = tg.tg_gemm_ex(DTYPES[dtype], LAYOUTS[layout], tg.TG_ACT_NONE, a_d.data_ptr(),
+                       b_d.data_ptr(), c_d.data_ptr(), bias_d.data_ptr(), w.M, w.N, w.K, w.K,
+                       ldb, w.N, w.M * w.K, sB, w.M * w.N, w.batch,
                        torch.cuda.current_stream().cuda_stream)
     assert st == tg.TG_OK
     torch.cuda.synchronize()
     out = host(c_d)
+    sC = w.M * w.N
     if n is None:
-        ref, _, Sa = oracle_lib.gemm_ex(a, b, w.M, w.N, w.K, w.lda_, w.ldb_, w.ldc_, w.batch,
-                                        w.sA, w.sB, w.sC, bias=bias, act="none", want_sums=True)
-        rep = gate(out, ref, w.K, Sa.reshape(-1), relu=False)
+        ref, _, Sa = oracle_lib.gemm_ex(a, b, w.M, w.N, w.K, w.K, ldb, w.N, w.batch, w.M * w.K,
+                                        sB, sC, bias=bias, act="none", dtype=dtype,
+                                        b_layout=layout, want_sums=True)
+        rep = gate(out, ref, w.K, Sa.reshape(-1), dtype=dtype, relu=False)
     else:
         idx = wl.sample_positions(w, n)
-        ref, _, Sa = oracle_lib.gemm_ex_sampled(a, b, w.K, w.lda_, w.ldb_, idx, w.sA, w.sB,
-                                                bias=bias, act="none")
-        got = np.array([out[bb * w.sC + i * w.ldc_ + j] for bb, i, j in idx], dtype=np.uint16)
-        rep = gate(got, ref, w.K, Sa, relu=False)
+        ref, _, Sa = oracle_lib.gemm_ex_sampled(a, b, w.K, w.K, ldb, idx, w.M * w.K, sB,
+                                                bias=bias, dtype=dtype, b_layout=layout,
+                                                act="none")
+        got = np.array([out[bb * sC + i * w.N + j] for bb, i, j in idx], dtype=np.uint16)
+        rep = gate(got, ref, w.K, Sa, dtype=dtype, relu=False)
     assert rep.ok, str(rep)

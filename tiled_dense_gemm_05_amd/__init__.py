@@ -44,7 +44,9 @@ EXPORTED_SYMBOLS = (
 )
 
 TG_DTYPE_F16 = 0
+TG_DTYPE_BF16 = 1
 TG_B_KN = 0
+TG_B_NK = 1
 TG_ACT_NONE = 0
 TG_ACT_RELU = 1
 

@@ -70,15 +70,17 @@ __int128 extent(int64_t rows, int64_t cols, int64_t ld, int64_t stride, int64_t 
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// b_nk: B is stored (N,K) (leading dimension over k) instead of (K,N).
 int validate(const void *A, const void *B, const void *C, int64_t M, int64_t N, int64_t K,
              int64_t lda, int64_t ldb, int64_t ldc, int64_t sA, int64_t sB, int64_t sC,
-             int64_t batch)
+             int64_t batch, bool b_nk)
 {
     if (M < 0 || N < 0 || K < 0 || batch < 0)
         return TG_ERR_INVALID_ARG;
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim || batch > kMaxDim)
         return TG_ERR_INVALID_ARG;
-    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+    const int64_t ldb_min = b_nk ? (K > 1 ? K : 1) : (N > 1 ? N : 1);
+    if (lda < (K > 1 ? K : 1) || ldb < ldb_min || ldc < (N > 1 ? N : 1))
         return TG_ERR_INVALID_ARG;
     if (M == 0 || N == 0 || batch == 0)
         return TG_OK;
@@ -86,7 +88,8 @@ int validate(const void *A, const void *B, const void *C, int64_t M, int64_t N, 
         return TG_ERR_INVALID_ARG;
     if (K > 0 && (A == nullptr || B == nullptr))
         return TG_ERR_INVALID_ARG;
-    if (extent(M, K, lda, sA, batch) > kMaxExtent || extent(K, N, ldb, sB, batch) > kMaxExtent ||
+    const __int128 b_ext = b_nk ? extent(N, K, ldb, sB, batch) : extent(K, N, ldb, sB, batch);
+    if (extent(M, K, lda, sA, batch) > kMaxExtent || b_ext > kMaxExtent ||
         extent(M, N, ldc, sC, batch) > kMaxExtent)
         return TG_ERR_INVALID_ARG;
     if (batch > 1) {
@@ -133,11 +136,11 @@ int choose_path(const tg::GemmArgs &p)
     return rounds256 < rounds128 ? TG_PATH_TILE256 : TG_PATH_TILE128;
 }
 
-int run(const void *A, const void *B, void *C, const void *bias, bool relu, int64_t M, int64_t N,
-        int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int64_t sA, int64_t sB, int64_t sC,
-        int64_t batch, hipStream_t stream)
+int run(const void *A, const void *B, void *C, const void *bias, bool relu, bool bf16, bool b_nk,
+        int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int64_t sA,
+        int64_t sB, int64_t sC, int64_t batch, hipStream_t stream)
 {
-    int st = validate(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch);
+    int st = validate(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, b_nk);
     if (st != TG_OK)
         return st;
     if (M == 0 || N == 0 || batch == 0)
@@ -158,6 +161,9 @@ int run(const void *A, const void *B, void *C, const void *bias, bool relu, int6
     p.batch = batch;
     p.bias = static_cast<const uint16_t *>(bias);
     p.relu = relu ? 1 : 0;
+    p.bf16 = bf16 ? 1 : 0;
+    p.b_nk = b_nk ? 1 : 0;
+    const int mode = p.bf16 | (p.b_nk << 1);
 
     int path = g_forced_path.load(std::memory_order_relaxed);
     if (path == TG_PATH_AUTO)
@@ -173,6 +179,9 @@ int run(const void *A, const void *B, void *C, const void *bias, bool relu, int6
     case TG_PATH_TILE128:
     case TG_PATH_TILE256: {
         int v = g_tile_variant.load(std::memory_order_relaxed);
+        // bf16 and (N,K) B exist in the default configurations only
+        if (v >= 0 && (v >= tg::kDmaConfigs ? mode != 0 : !tg::dma_config_has_mode(v, mode)))
+            v = -1;
         if (v < 0) {
             const int64_t tiles128 = ((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch;
             v = path == TG_PATH_TILE256 ? kTile256Default
@@ -191,7 +200,9 @@ int run(const void *A, const void *B, void *C, const void *bias, bool relu, int6
     }
     case TG_PATH_SKINNY: {
         int v = g_skinny_variant.load(std::memory_order_relaxed);
-        e = tg::launch_skinny_config(v < 0 ? kSkinnyDefault : v, p, stream);
+        if (v < 0 || !tg::skinny_config_has_mode(v, mode))
+            v = kSkinnyDefault;
+        e = tg::launch_skinny_config(v, p, stream);
         break;
     }
     default:
@@ -212,7 +223,7 @@ extern "C" {
 int tg_gemm_relu_f16(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
                      int64_t lda, int64_t ldb, int64_t ldc, hipStream_t stream)
 {
-    return run(A, B, C, nullptr, true, M, N, K, lda, ldb, ldc, 0, 0, 0, 1, stream);
+    return run(A, B, C, nullptr, true, false, false, M, N, K, lda, ldb, ldc, 0, 0, 0, 1, stream);
 }
 
 int tg_gemm_relu_f16_strided_batched(const void *A, const void *B, void *C, int64_t M, int64_t N,
@@ -220,8 +231,8 @@ int tg_gemm_relu_f16_strided_batched(const void *A, const void *B, void *C, int6
                                      int64_t strideA, int64_t strideB, int64_t strideC,
                                      int64_t batch, hipStream_t stream)
 {
-    return run(A, B, C, nullptr, true, M, N, K, lda, ldb, ldc, strideA, strideB, strideC, batch,
-               stream);
+    return run(A, B, C, nullptr, true, false, false, M, N, K, lda, ldb, ldc, strideA, strideB,
+               strideC, batch, stream);
 }
 
 int tg_gemm_ex(int dtype, int b_layout, int activation, const void *A, const void *B, void *C,
@@ -229,12 +240,15 @@ int tg_gemm_ex(int dtype, int b_layout, int activation, const void *A, const voi
                int64_t ldc, int64_t strideA, int64_t strideB, int64_t strideC, int64_t batch,
                hipStream_t stream)
 {
-    if (dtype != TG_DTYPE_F16 || b_layout != TG_B_KN)
+    if (dtype != TG_DTYPE_F16 && dtype != TG_DTYPE_BF16)
+        return TG_ERR_INVALID_ARG;
+    if (b_layout != TG_B_KN && b_layout != TG_B_NK)
         return TG_ERR_INVALID_ARG;
     if (activation != TG_ACT_NONE && activation != TG_ACT_RELU)
         return TG_ERR_INVALID_ARG;
-    return run(A, B, C, bias, activation == TG_ACT_RELU, M, N, K, lda, ldb, ldc, strideA, strideB,
-               strideC, batch, stream);
+    return run(A, B, C, bias, activation == TG_ACT_RELU, dtype == TG_DTYPE_BF16,
+               b_layout == TG_B_NK, M, N, K, lda, ldb, ldc, strideA, strideB, strideC, batch,
+               stream);
 }
 
 const char *tg_status_string(int status)

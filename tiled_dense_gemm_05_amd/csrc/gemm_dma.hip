@@ -42,7 +42,9 @@ namespace tg {
 namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -97,6 +99,19 @@ struct Cfg {
     static_assert(LDS <= 160 * 1024, "LDS size");
     // a thread's loads of one tile share one swizzled column (see load plan)
     static_assert((NW * A_RPB) % 16 == 0 && (NW * B_RPB) % 4 == 0, "swizzle period");
+};
+
+// Element type and B layout of a configuration.  MODE bit 0: bf16 elements
+// (fp16 otherwise); bit 1: B stored as (N,K) row-major, whose tile is BN rows
+// of BK contiguous k, staged and read exactly like the A tile (no transpose
+// read needed).
+template <class C, int MODE>
+struct Mode : C {
+    static constexpr bool BF16 = (MODE & 1) != 0;
+    static constexpr bool BT = (MODE & 2) != 0;
+    static constexpr int B_RPB = BT ? 64 / C::CA : 64 / C::CB;   // B tile rows per 1 KiB
+    static constexpr int READS = C::FM + (BT ? C::FN : 2 * C::FN);
+    static_assert(!BT || (C::NW * (64 / C::CA)) % 16 == 0, "swizzle period");
 };
 
 template <int CA, bool ON = true>
@@ -201,6 +216,16 @@ __device__ __forceinline__ void read_piece(const lds_u16 *As, const lds_u16 *Bs,
         const int c = kk * 2 + (lane >> 5);
         const int ca = swz_a<T::CA, T::SWZ>(row, c);
         af[r] = *reinterpret_cast<const lds_f16x8 *>(As + row * T::BK + ca * 8);
+    } else if constexpr (T::BT) {
+        // (N,K) B: the fragment is one 16-byte read of a B^T row, like A's
+        constexpr int fn = r - T::FM;
+        const int row = wn * T::TN + fn * 32 + (lane & 31);
+        const int c = kk * 2 + (lane >> 5);
+        const int cb = swz_a<T::CA, T::SWZ>(row, c);
+        const s16x8 v = *reinterpret_cast<const __attribute__((address_space(3))) s16x8 *>(
+            Bs + row * T::BK + cb * 8);
+        bh[fn][0] = __builtin_shufflevector(v, v, 0, 1, 2, 3);
+        bh[fn][1] = __builtin_shufflevector(v, v, 4, 5, 6, 7);
     } else {
         constexpr int fn = (r - T::FM) / 2, hh = (r - T::FM) % 2;
         const int k = kk * 16 + 8 * (lane >> 5) + 4 * hh + ((lane & 15) >> 2);
@@ -230,15 +255,16 @@ __device__ __forceinline__ void join_b(const s16x4 (&bh)[T::FN][2], f16x8 (&bf)[
                                     __builtin_shufflevector(bh[fn][0], bh[fn][1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// One 32x32x16 matrix-core product in the configuration's element type (the
+// fragments hold raw 16-bit patterns either way).
 template <class T>
-__device__ __forceinline__ void mma_all(f32x16 (&acc)[T::FM][T::FN], const f16x8 (&af)[T::FM],
-                                        const f16x8 (&bf)[T::FN])
+__device__ __forceinline__ f32x16 mfma32(const f16x8 &b, const f16x8 &a, const f32x16 &c)
 {
-#pragma unroll
-    for (int fm = 0; fm < T::FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < T::FN; ++fn)
-            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[fn], af[fm], acc[fm][fn], 0, 0, 0);
+    if constexpr (T::BF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b),
+                                                       __builtin_bit_cast(bf16x8, a), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c, 0, 0, 0);
 }
 
 // Everything a thread needs to issue its loads of one tile.
@@ -247,9 +273,12 @@ struct LoadPlan {
     uint32_t a_voff[T::A_LD];   // byte offsets from the A descriptor, or out of range
     uint32_t b_voff[T::B_LD];
     int a_kcol;                 // the thread's column inside the K tile (A)
-    int b_row0;                 // the thread's first row inside the K tile (B)
+    int b_row0;                 // the thread's first row inside the K tile ((K,N) B)
+    int b_kcol;                 // the thread's column inside the K tile ((N,K) B)
 };
 
+// b_rows_left: for a (K,N) B the rows of this K tile inside K; for an (N,K)
+// B, 1 when the thread's k columns are inside K, else 0.
 template <class T, int I>
 __device__ __forceinline__ void issue_one(const LoadPlan<T> &lp, const i32x4 &ra, const i32x4 &rb,
                                           bool a_kok, int b_rows_left, uint32_t stage_addr,
@@ -260,7 +289,8 @@ __device__ __forceinline__ void issue_one(const LoadPlan<T> &lp, const i32x4 &ra
         dma16(ra, v, stage_addr + (uint32_t)((wave + I * T::NW) * 1024));
     } else {
         constexpr int J = I - T::A_LD;
-        const bool ok = (lp.b_row0 + J * T::NW * T::B_RPB) < b_rows_left;
+        const bool ok = T::BT ? b_rows_left != 0
+                              : (lp.b_row0 + J * T::NW * T::B_RPB) < b_rows_left;
         const uint32_t v = ok ? lp.b_voff[J] : kOutOfRange;
         dma16(rb, v, stage_addr + (uint32_t)(T::A_ELEMS * 2 + (wave + J * T::NW) * 1024));
     }
@@ -283,7 +313,7 @@ __device__ __forceinline__ void step(f32x16 (&acc)[T::FM][T::FN], const f16x8 (&
     if constexpr (I < STEPS) {
         if constexpr (I < MF) {
             constexpr int fm = I / T::FN, fn = I % T::FN;
-            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[fn], af[fm], acc[fm][fn], 0, 0, 0);
+            acc[fm][fn] = mfma32<T>(bf[fn], af[fm], acc[fm][fn]);
         }
         if constexpr (I < ND)
             issue_one<T, D0 + I>(lp, ra, rb, a_kok, b_rows_left, stage_addr, wave);
@@ -349,7 +379,7 @@ gemm_relu_dma_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
     const int64_t m0 = (int64_t)tm * T::BM, n0 = (int64_t)tn * T::BN;
     // operand panels of this tile; the descriptors advance along K
     const uint16_t *Ab = p.A + bidx * p.sA + m0 * p.lda;
-    const uint16_t *Bb = p.B + bidx * p.sB + n0;
+    const uint16_t *Bb = p.B + bidx * p.sB + (T::BT ? n0 * p.ldb : n0);
     uint16_t *C = p.C + bidx * p.sC;
 
     // Load plan.  Wave w moves 1 KiB blocks w, w + NW, ... of each operand
@@ -367,10 +397,22 @@ gemm_relu_dma_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
             lp.a_voff[i] = (m0 + row < M) ? (uint32_t)((row * p.lda + c * 8) * 2) : kOutOfRange;
         }
     }
-    {
+    if constexpr (T::BT) {
+        // (N,K) B: rows are output columns n0 + row, chunks run along K
+        const int r0 = wave * T::B_RPB + lane / T::CA;
+        const int c = swz_a<T::CA, T::SWZ>(r0, lane % T::CA);
+        lp.b_kcol = c * 8;
+        lp.b_row0 = 0;
+#pragma unroll
+        for (int j = 0; j < T::B_LD; ++j) {
+            const int row = r0 + j * T::NW * T::B_RPB;
+            lp.b_voff[j] = (n0 + row < N) ? (uint32_t)((row * p.ldb + c * 8) * 2) : kOutOfRange;
+        }
+    } else {
         const int r0 = wave * T::B_RPB + lane / T::CB;
         const int c = swz_b<T::CB, T::SWZ>(r0, lane % T::CB);
         lp.b_row0 = r0;
+        lp.b_kcol = 0;
         const bool col_ok = n0 + c * 8 < N;
 #pragma unroll
         for (int j = 0; j < T::B_LD; ++j) {
@@ -380,10 +422,16 @@ gemm_relu_dma_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
     }
     // the group's t-th K tile is K tile t * KG + kg
     auto rsrc_a = [&](int t) { return make_rsrc(Ab + ((int64_t)t * T::KG + kg) * T::BK); };
-    auto rsrc_b = [&](int t) { return make_rsrc(Bb + ((int64_t)t * T::KG + kg) * T::BK * p.ldb); };
+    auto rsrc_b = [&](int t) {
+        const int64_t k0 = ((int64_t)t * T::KG + kg) * T::BK;
+        return make_rsrc(Bb + (T::BT ? k0 : k0 * p.ldb));
+    };
     auto a_kok = [&](int t) { return ((int64_t)t * T::KG + kg) * T::BK + lp.a_kcol < K; };
     auto b_left = [&](int t) {
-        const int64_t r = K - ((int64_t)t * T::KG + kg) * T::BK;
+        const int64_t k0 = ((int64_t)t * T::KG + kg) * T::BK;
+        if constexpr (T::BT)
+            return (int)(k0 + lp.b_kcol < K);
+        const int64_t r = K - k0;
         return (int)(r < 0 ? 0 : (r > T::BK ? T::BK : r));
     };
 
@@ -485,14 +533,14 @@ gemm_relu_dma_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
                 // the lane's four columns of this group, the same in every row
                 const int col = wn * T::TN + fn * 32 + 8 * g + 4 * (lane >> 5);
                 float bv[4];
-                load_bias4(p.bias, n0 + col, N, bv);
+                load_bias4<T::BF16>(p.bias, n0 + col, N, bv);
 #pragma unroll
                 for (int fm = 0; fm < T::FM; ++fm) {
                     const int row = wm * T::TM + fm * 32 + (lane & 31);
                     const f32x16 &v = acc[fm][fn];
                     u32x2 w;
-                    w.x = epi_pack_f16x2(v[4 * g + 0] + bv[0], v[4 * g + 1] + bv[1], relu);
-                    w.y = epi_pack_f16x2(v[4 * g + 2] + bv[2], v[4 * g + 3] + bv[3], relu);
+                    w.x = epi_pack2<T::BF16>(v[4 * g + 0] + bv[0], v[4 * g + 1] + bv[1], relu);
+                    w.y = epi_pack2<T::BF16>(v[4 * g + 2] + bv[2], v[4 * g + 3] + bv[3], relu);
                     const int phys = (col >> 3) ^ (row % T::CB);
                     *reinterpret_cast<__attribute__((address_space(3))) u32x2 *>(
                         cst + row * T::BN + phys * 8 + (col & 4)) = w;
@@ -538,6 +586,69 @@ hipError_t launch_dma(const GemmArgs &p, hipStream_t stream, int groupM)
     return hipSuccess;
 }
 
+hipError_t launch_all_configs(int cfg, const GemmArgs &p, hipStream_t stream, int groupM)
+{
+    switch (cfg) {
+    case 0: return launch_dma<Mode<Cfg<256, 256, 32, 2, 2, 4>, 0>>(p, stream, groupM);
+    case 1: return launch_dma<Mode<Cfg<256, 256, 32, 2, 2, 3>, 0>>(p, stream, groupM);
+    case 2: return launch_dma<Mode<Cfg<256, 256, 64, 2, 2, 2>, 0>>(p, stream, groupM);
+    case 3: return launch_dma<Mode<Cfg<128, 128, 64, 2, 2, 4>, 0>>(p, stream, groupM);
+    case 4: return launch_dma<Mode<Cfg<128, 128, 32, 2, 2, 4>, 0>>(p, stream, groupM);
+    case 5: return launch_dma<Mode<Cfg<128, 128, 64, 2, 2, 3>, 0>>(p, stream, groupM);
+    case 6: return launch_dma<Mode<Cfg<256, 128, 64, 2, 2, 3>, 0>>(p, stream, groupM);
+    // eight waves: two per SIMD, 128x64 or 64x128 wave tiles
+    case 7: return launch_dma<Mode<Cfg<256, 256, 32, 2, 4, 4>, 0>>(p, stream, groupM);
+    case 8: return launch_dma<Mode<Cfg<256, 256, 64, 2, 4, 2>, 0>>(p, stream, groupM);
+    case 9: return launch_dma<Mode<Cfg<256, 256, 32, 4, 2, 4>, 0>>(p, stream, groupM);
+    // small LDS footprint: several workgroups per CU for short K
+    case 10: return launch_dma<Mode<Cfg<128, 128, 32, 2, 2, 2>, 0>>(p, stream, groupM);
+    case 11: return launch_dma<Mode<Cfg<128, 128, 64, 2, 2, 2>, 0>>(p, stream, groupM);
+    case 12: return launch_dma<Mode<Cfg<128, 128, 32, 2, 2, 2, 4>, 0>>(p, stream, groupM);
+    case 13: return launch_dma<Mode<Cfg<128, 128, 64, 2, 2, 2, 2>, 0>>(p, stream, groupM);
+    // two K groups of four waves (two waves per SIMD on alternate K tiles)
+    case 14: return launch_dma<Mode<Cfg<128, 128, 64, 2, 2, 2, 2, 2>, 0>>(p, stream, groupM);
+    case 15: return launch_dma<Mode<Cfg<128, 128, 32, 2, 2, 4, 2, 2>, 0>>(p, stream, groupM);
+    case 16: return launch_dma<Mode<Cfg<128, 128, 32, 2, 2, 3, 2, 2>, 0>>(p, stream, groupM);
+    // deep rings for latency-bound mid-size shapes
+    case 17: return launch_dma<Mode<Cfg<128, 128, 32, 2, 2, 8>, 0>>(p, stream, groupM);
+    case 18: return launch_dma<Mode<Cfg<128, 128, 64, 2, 2, 5>, 0>>(p, stream, groupM);
+    // 64x64 tiles for problems with few 128x128 tiles
+    case 19: return launch_dma<Mode<Cfg<64, 64, 64, 2, 2, 4>, 0>>(p, stream, groupM);
+    case 20: return launch_dma<Mode<Cfg<64, 64, 64, 2, 2, 4, 1, 2>, 0>>(p, stream, groupM);
+    // the tile the pages start from: 128 x 128 x 32, 3 stages, 4 waves
+    case 21: return launch_dma<Mode<Cfg<128, 128, 32, 2, 2, 3>, 0>>(p, stream, groupM);
+    // ablations of the large-shape tile: operand tiles without the XOR
+    // swizzle, and a 2-stage ring
+    case 22: return launch_dma<Mode<Cfg<256, 256, 32, 2, 2, 4, 1, 1, false>, 0>>(p, stream, groupM);
+    case 23: return launch_dma<Mode<Cfg<256, 256, 32, 2, 2, 2>, 0>>(p, stream, groupM);
+    // more eight-wave large tiles
+    case 24: return launch_dma<Mode<Cfg<256, 256, 64, 4, 2, 2>, 0>>(p, stream, groupM);
+    case 25: return launch_dma<Mode<Cfg<256, 256, 32, 2, 4, 3>, 0>>(p, stream, groupM);
+    // sixteen waves, 64x64 wave tiles
+    case 26: return launch_dma<Mode<Cfg<256, 256, 64, 4, 4, 2>, 0>>(p, stream, groupM);
+    case 27: return launch_dma<Mode<Cfg<256, 256, 32, 4, 4, 4>, 0>>(p, stream, groupM);
+    // eight-wave 128x128 tiles
+    case 28: return launch_dma<Mode<Cfg<128, 128, 64, 2, 4, 4>, 0>>(p, stream, groupM);
+    case 29: return launch_dma<Mode<Cfg<128, 128, 64, 4, 2, 4>, 0>>(p, stream, groupM);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+
+// bf16 and (N,K)-B instances exist for the configurations the dispatcher
+// picks by default: 256x256 (8), 128x128 (29), short K (12) and few tiles (20).
+template <int MODE>
+hipError_t launch_default_configs(int cfg, const GemmArgs &p, hipStream_t stream, int groupM)
+{
+    switch (cfg) {
+    case 8: return launch_dma<Mode<Cfg<256, 256, 64, 2, 4, 2>, MODE>>(p, stream, groupM);
+    case 29: return launch_dma<Mode<Cfg<128, 128, 64, 4, 2, 4>, MODE>>(p, stream, groupM);
+    case 12: return launch_dma<Mode<Cfg<128, 128, 32, 2, 2, 2, 4>, MODE>>(p, stream, groupM);
+    case 20: return launch_dma<Mode<Cfg<64, 64, 64, 2, 2, 4, 1, 2>, MODE>>(p, stream, groupM);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
 bool dma_layout_ok(const GemmArgs &p)
@@ -547,51 +658,19 @@ bool dma_layout_ok(const GemmArgs &p)
     return p.lda <= (1 << 21) && p.ldb <= (1 << 21);
 }
 
+bool dma_config_has_mode(int cfg, int mode)
+{
+    return mode == 0 ? (cfg >= 0 && cfg < kDmaConfigs)
+                     : (cfg == 8 || cfg == 29 || cfg == 12 || cfg == 20);
+}
+
 hipError_t launch_dma_config(int cfg, const GemmArgs &p, hipStream_t stream, int groupM)
 {
-    switch (cfg) {
-    case 0: return launch_dma<Cfg<256, 256, 32, 2, 2, 4>>(p, stream, groupM);
-    case 1: return launch_dma<Cfg<256, 256, 32, 2, 2, 3>>(p, stream, groupM);
-    case 2: return launch_dma<Cfg<256, 256, 64, 2, 2, 2>>(p, stream, groupM);
-    case 3: return launch_dma<Cfg<128, 128, 64, 2, 2, 4>>(p, stream, groupM);
-    case 4: return launch_dma<Cfg<128, 128, 32, 2, 2, 4>>(p, stream, groupM);
-    case 5: return launch_dma<Cfg<128, 128, 64, 2, 2, 3>>(p, stream, groupM);
-    case 6: return launch_dma<Cfg<256, 128, 64, 2, 2, 3>>(p, stream, groupM);
-    // eight waves: two per SIMD, 128x64 or 64x128 wave tiles
-    case 7: return launch_dma<Cfg<256, 256, 32, 2, 4, 4>>(p, stream, groupM);
-    case 8: return launch_dma<Cfg<256, 256, 64, 2, 4, 2>>(p, stream, groupM);
-    case 9: return launch_dma<Cfg<256, 256, 32, 4, 2, 4>>(p, stream, groupM);
-    // small LDS footprint: several workgroups per CU for short K
-    case 10: return launch_dma<Cfg<128, 128, 32, 2, 2, 2>>(p, stream, groupM);
-    case 11: return launch_dma<Cfg<128, 128, 64, 2, 2, 2>>(p, stream, groupM);
-    case 12: return launch_dma<Cfg<128, 128, 32, 2, 2, 2, 4>>(p, stream, groupM);
-    case 13: return launch_dma<Cfg<128, 128, 64, 2, 2, 2, 2>>(p, stream, groupM);
-    // two K groups of four waves (two waves per SIMD on alternate K tiles)
-    case 14: return launch_dma<Cfg<128, 128, 64, 2, 2, 2, 2, 2>>(p, stream, groupM);
-    case 15: return launch_dma<Cfg<128, 128, 32, 2, 2, 4, 2, 2>>(p, stream, groupM);
-    case 16: return launch_dma<Cfg<128, 128, 32, 2, 2, 3, 2, 2>>(p, stream, groupM);
-    // deep rings for latency-bound mid-size shapes
-    case 17: return launch_dma<Cfg<128, 128, 32, 2, 2, 8>>(p, stream, groupM);
-    case 18: return launch_dma<Cfg<128, 128, 64, 2, 2, 5>>(p, stream, groupM);
-    // 64x64 tiles for problems with few 128x128 tiles
-    case 19: return launch_dma<Cfg<64, 64, 64, 2, 2, 4>>(p, stream, groupM);
-    case 20: return launch_dma<Cfg<64, 64, 64, 2, 2, 4, 1, 2>>(p, stream, groupM);
-    // the tile the pages start from: 128 x 128 x 32, 3 stages, 4 waves
-    case 21: return launch_dma<Cfg<128, 128, 32, 2, 2, 3>>(p, stream, groupM);
-    // ablations of the large-shape tile: operand tiles without the XOR
-    // swizzle, and a 2-stage ring
-    case 22: return launch_dma<Cfg<256, 256, 32, 2, 2, 4, 1, 1, false>>(p, stream, groupM);
-    case 23: return launch_dma<Cfg<256, 256, 32, 2, 2, 2>>(p, stream, groupM);
-    // more eight-wave large tiles
-    case 24: return launch_dma<Cfg<256, 256, 64, 4, 2, 2>>(p, stream, groupM);
-    case 25: return launch_dma<Cfg<256, 256, 32, 2, 4, 3>>(p, stream, groupM);
-    // sixteen waves, 64x64 wave tiles
-    case 26: return launch_dma<Cfg<256, 256, 64, 4, 4, 2>>(p, stream, groupM);
-    case 27: return launch_dma<Cfg<256, 256, 32, 4, 4, 4>>(p, stream, groupM);
-    // eight-wave 128x128 tiles
-    case 28: return launch_dma<Cfg<128, 128, 64, 2, 4, 4>>(p, stream, groupM);
-    case 29: return launch_dma<Cfg<128, 128, 64, 4, 2, 4>>(p, stream, groupM);
-    default: return hipErrorInvalidValue;
+    switch ((p.bf16 ? 1 : 0) | (p.b_nk ? 2 : 0)) {
+    case 0: return launch_all_configs(cfg, p, stream, groupM);
+    case 1: return launch_default_configs<1>(cfg, p, stream, groupM);
+    case 2: return launch_default_configs<2>(cfg, p, stream, groupM);
+    default: return launch_default_configs<3>(cfg, p, stream, groupM);
     }
 }
 

@@ -1,5 +1,6 @@
 // The plain kernel: one thread per output element, fp32 fused multiply-add
-// over k in ascending order, bias, ReLU, round-to-nearest-even fp16 store.
+// over k in ascending order, bias, ReLU, round-to-nearest-even store; element
+// type (fp16 or bf16) and B layout ((K,N) or (N,K)) are read at run time.
 // It is the literal reading of the GEMM+ReLU program of the "TileLang paper
 // reading" page, section 2, without tiles; it serves as a slow cross-check
 // path.
@@ -18,15 +19,20 @@ __global__ void __launch_bounds__(256) gemm_relu_naive_kernel(GemmArgs p)
         const int64_t r = e - b * per_batch;
         const int64_t i = r / p.N;
         const int64_t j = r - i * p.N;
-        const _Float16 *a = reinterpret_cast<const _Float16 *>(p.A) + b * p.sA + i * p.lda;
-        const _Float16 *bc = reinterpret_cast<const _Float16 *>(p.B) + b * p.sB + j;
+        const uint16_t *a = p.A + b * p.sA + i * p.lda;
+        // B(k, j) at bc[k * kstride]
+        const uint16_t *bc = p.B + b * p.sB + (p.b_nk ? j * p.ldb : j);
+        const int64_t kstride = p.b_nk ? 1 : p.ldb;
+        const bool bf = p.bf16 != 0;
+        auto val = [bf](uint16_t h) { return bf ? bits_to_float<true>(h) : bits_to_float<false>(h); };
         float s = 0.0f;
         for (int64_t k = 0; k < p.K; ++k)
-            s = __builtin_fmaf((float)a[k], (float)bc[k * p.ldb], s);
+            s = __builtin_fmaf(val(a[k]), val(bc[k * kstride]), s);
         if (p.bias != nullptr)
-            s += (float)__builtin_bit_cast(_Float16, p.bias[j]);
+            s += val(p.bias[j]);
         const float r0 = (p.relu == 0 || s > 0.0f) ? s : 0.0f;
-        reinterpret_cast<_Float16 *>(p.C)[b * p.sC + i * p.ldc + j] = (_Float16)r0;
+        p.C[b * p.sC + i * p.ldc + j] = bf ? __builtin_bit_cast(uint16_t, (__bf16)r0)
+                                           : __builtin_bit_cast(uint16_t, (_Float16)r0);
     }
 }
 

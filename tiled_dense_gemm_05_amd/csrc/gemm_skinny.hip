@@ -27,6 +27,9 @@
 //    every output fragment is summed over the waves in wave order (the result
 //    is deterministic), clamped at zero, rounded to fp16 (nearest even) and
 //    stored.
+//  * MODE bit 0: bf16 elements (v_mfma_f32_16x16x32_bf16, bf16 store); bit 1:
+//    B stored (N,K): the slice is NB rows of B^T, staged like the A rows
+//    (64-byte rows of 32 k) and read with one 16-byte read per fragment.
 // Requirements (checked by the dispatcher): 16-byte aligned A, B, C; lda,
 // ldb, ldc, N, K multiples of 8; M <= 16 * MB.
 #include "tg_internal.h"
@@ -35,6 +38,7 @@ namespace tg {
 namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
@@ -46,9 +50,11 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-template <int MB_, int NB_, int NW_, int S_, bool NTB_ = false>
+template <int MB_, int NB_, int NW_, int S_, bool NTB_ = false, int MODE_ = 0>
 struct Skinny {
     static constexpr bool NTB = NTB_;            // stream B with non-temporal loads
+    static constexpr bool BF16 = (MODE_ & 1) != 0;
+    static constexpr bool BT = (MODE_ & 2) != 0;  // B stored (N,K)
     static constexpr int MB = MB_;               // 16-row blocks of A / C
     static constexpr int NB = NB_;               // columns of C per workgroup
     static constexpr int NW = NW_;               // waves (K split)
@@ -62,7 +68,7 @@ struct Skinny {
     static constexpr int A_LD = A_BYTES / 1024, B_LD = B_BYTES / 1024;
     static constexpr int LOADS = A_LD + B_LD;
     static constexpr int CB = NB / 8;            // 16-byte chunks per B row
-    static constexpr int B_RPB = 64 / CB;        // B rows per 1 KiB block
+    static constexpr int B_RPB = BT ? 16 : 64 / CB;   // B rows per 1 KiB block
     static constexpr int RING = NW * S * STAGE;
     static constexpr int RED = NW * MB * NF * 64 * 16;    // partial sums
     static constexpr int LDS = RING > RED ? RING : RED;
@@ -157,7 +163,7 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_skinny_kernel(GemmArgs p, int
     const int64_t n0 = (int64_t)blockIdx.x * T::NB;
     const int64_t kw0 = (int64_t)wave * steps_per_wave * T::KS;   // this wave's first k
     const uint16_t *Ab = p.A + bidx * p.sA + kw0;
-    const uint16_t *Bb = p.B + bidx * p.sB + kw0 * p.ldb + n0;
+    const uint16_t *Bb = p.B + bidx * p.sB + (T::BT ? n0 * p.ldb + kw0 : kw0 * p.ldb + n0);
     uint16_t *C = p.C + bidx * p.sC;
     const uint32_t ring = lds_base + (uint32_t)(wave * T::S * T::STAGE);
 
@@ -173,21 +179,30 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_skinny_kernel(GemmArgs p, int
         a_col[j] = c * 8;
         a_voff[j] = row < M ? (uint32_t)((row * p.lda + c * 8) * 2) : kOutOfRange;
     }
+    // (N,K) B: block j is rows 16 j .. 16 j + 15 of the B^T slice, laid out
+    // like an A block; b_row then holds the chunk's k column.
     uint32_t b_voff[T::B_LD];
     int b_row[T::B_LD];
 #pragma unroll
     for (int j = 0; j < T::B_LD; ++j) {
-        const int row = j * T::B_RPB + lane / T::CB;
-        const int c = swz_b<T::CB>(row, lane % T::CB);
-        b_row[j] = row;
-        b_voff[j] = (n0 + c * 8 < N) ? (uint32_t)((row * p.ldb + c * 8) * 2) : kOutOfRange;
+        if constexpr (T::BT) {
+            const int row = 16 * j + lane / 4;
+            const int c = swz_a(row, lane % 4);
+            b_row[j] = c * 8;
+            b_voff[j] = (n0 + row < N) ? (uint32_t)((row * p.ldb + c * 8) * 2) : kOutOfRange;
+        } else {
+            const int row = j * T::B_RPB + lane / T::CB;
+            const int c = swz_b<T::CB>(row, lane % T::CB);
+            b_row[j] = row;
+            b_voff[j] = (n0 + c * 8 < N) ? (uint32_t)((row * p.ldb + c * 8) * 2) : kOutOfRange;
+        }
     }
 
     auto issue = [&](int st) {
         const int64_t k0 = (int64_t)st * T::KS;          // relative to kw0
         const int64_t kleft = K - kw0 - k0;               // valid k from here
         const i32x4 ra = make_rsrc(Ab + k0);
-        const i32x4 rb = make_rsrc(Bb + k0 * p.ldb);
+        const i32x4 rb = make_rsrc(Bb + (T::BT ? k0 : k0 * p.ldb));
         const uint32_t base = ring + (uint32_t)((st % T::S) * T::STAGE);
 #pragma unroll
         for (int j = 0; j < T::A_LD; ++j)
@@ -232,6 +247,12 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_skinny_kernel(GemmArgs p, int
         }
 #pragma unroll
         for (int f = 0; f < T::NF; ++f) {
+            if constexpr (T::BT) {
+                const int row = f * 16 + (lane & 15);
+                const int c = lane >> 4;
+                bf[f] = *reinterpret_cast<const lds_f16x8 *>(Bs + row * 32 + swz_a(row, c) * 8);
+                continue;
+            }
             s16x4 h[2];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
@@ -246,7 +267,13 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_skinny_kernel(GemmArgs p, int
         for (int mb = 0; mb < T::MB; ++mb)
 #pragma unroll
             for (int f = 0; f < T::NF; ++f)
-                acc[mb][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[f], af[mb], acc[mb][f], 0, 0, 0);
+                if constexpr (T::BF16)
+                    acc[mb][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, bf[f]), __builtin_bit_cast(bf16x8, af[mb]),
+                        acc[mb][f], 0, 0, 0);
+                else
+                    acc[mb][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[f], af[mb], acc[mb][f],
+                                                                        0, 0, 0);
     }
     wait_vmcnt<0>();
     __syncthreads();   // every wave is done with its ring before it is reused
@@ -272,10 +299,10 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_skinny_kernel(GemmArgs p, int
         const int64_t n = n0 + f * 16 + 4 * (lane >> 4);
         if (m < M && n < N) {
             float bv[4];
-            load_bias4(p.bias, n, N, bv);
+            load_bias4<T::BF16>(p.bias, n, N, bv);
             u32x2 w2;
-            w2.x = epi_pack_f16x2(s[0] + bv[0], s[1] + bv[1], relu);
-            w2.y = epi_pack_f16x2(s[2] + bv[2], s[3] + bv[3], relu);
+            w2.x = epi_pack2<T::BF16>(s[0] + bv[0], s[1] + bv[1], relu);
+            w2.y = epi_pack2<T::BF16>(s[2] + bv[2], s[3] + bv[3], relu);
             *reinterpret_cast<u32x2 *>(C + m * p.ldc + n) = w2;
         }
     }
@@ -309,12 +336,46 @@ hipError_t launch(const GemmArgs &p, hipStream_t stream)
 
 bool skinny_layout_ok(const GemmArgs &p)
 {
-    // M <= 64; 32-bit buffer offsets: 64 A rows and 32 B rows per step
-    return p.M <= 64 && p.lda <= (1 << 24) && p.ldb <= (1 << 24);
+    // M <= 64; 32-bit buffer offsets: 64 A rows and 32 (K,N) B rows, or 64
+    // (N,K) B rows, per step
+    return p.M <= 64 && p.lda <= (1 << 24) && p.ldb <= (p.b_nk ? (1 << 22) : (1 << 24));
+}
+
+namespace {
+
+// bf16 and (N,K)-B instances of configurations 0 and 4 (the default).
+template <int MODE>
+hipError_t launch_mode(int cfg, const GemmArgs &p, hipStream_t stream)
+{
+    const int mb = (int)((p.M + 15) / 16);
+    switch (cfg) {
+    case 0:
+        if (mb <= 1) return launch<Skinny<1, 64, 4, 6, false, MODE>>(p, stream);
+        if (mb <= 2) return launch<Skinny<2, 64, 4, 5, false, MODE>>(p, stream);
+        return launch<Skinny<4, 64, 4, 4, false, MODE>>(p, stream);
+    case 4:
+        if (mb <= 1) return launch<Skinny<1, 64, 4, 6, true, MODE>>(p, stream);
+        if (mb <= 2) return launch<Skinny<2, 64, 4, 5, true, MODE>>(p, stream);
+        return launch<Skinny<4, 64, 4, 4, true, MODE>>(p, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool skinny_config_has_mode(int cfg, int mode)
+{
+    return mode == 0 ? (cfg >= 0 && cfg < kSkinnyConfigs) : (cfg == 0 || cfg == 4);
 }
 
 hipError_t launch_skinny_config(int cfg, const GemmArgs &p, hipStream_t stream)
 {
+    switch ((p.bf16 ? 1 : 0) | (p.b_nk ? 2 : 0)) {
+    case 1: return launch_mode<1>(cfg, p, stream);
+    case 2: return launch_mode<2>(cfg, p, stream);
+    case 3: return launch_mode<3>(cfg, p, stream);
+    default: break;
+    }
     const int mb = (int)((p.M + 15) / 16);
     switch (cfg) {
     case 0:   // 64-column slices, 4 waves, 6 stages

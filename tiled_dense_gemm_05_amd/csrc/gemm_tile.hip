@@ -26,12 +26,16 @@
 //  * Two LDS stages with register prefetch: the next K-tile's global loads
 //    are in flight while the matrix cores work on the current one; one
 //    barrier per K-tile.
+//  * MODE bit 0 selects bf16 elements (the bf16 matrix-core instruction and
+//    a bf16 store), bit 1 a B stored as (N,K): its tile is BN rows of BK
+//    contiguous k, loaded, stored and read exactly like the A tile.
 #include "tg_internal.h"
 
 namespace tg {
 namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -47,9 +51,11 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 // Block tile BM x BN x BK computed by WM x WN waves; every wave owns a
 // (BM/WM) x (BN/WN) sub-tile made of 32 x 32 MFMA fragments.
-template <int BM_, int BN_, int BK_, int WM_, int WN_>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int MODE_ = 0>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+    static constexpr bool BF16 = (MODE_ & 1) != 0;    // bf16 elements (fp16 otherwise)
+    static constexpr bool BT = (MODE_ & 2) != 0;      // B stored (N,K)
     static constexpr int NT = 64 * WM * WN;           // threads per workgroup
     static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
     static constexpr int FM = TM / 32, FN = TN / 32;  // MFMA fragments per wave
@@ -58,8 +64,9 @@ struct Tile {
     static constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BN;
     static constexpr int STAGE = A_ELEMS + B_ELEMS;   // fp16 elements per LDS stage
     static constexpr int A_LD = BM * CA / NT;         // A chunks per thread per K-tile
-    static constexpr int B_LD = BK * CB / NT;         // B chunks per thread per K-tile
-    static_assert((BM * CA) % NT == 0 && (BK * CB) % NT == 0, "tile not divisible by threads");
+    static constexpr int B_CHUNKS = BT ? BN * CA : BK * CB;
+    static constexpr int B_LD = B_CHUNKS / NT;        // B chunks per thread per K-tile
+    static_assert((BM * CA) % NT == 0 && B_CHUNKS % NT == 0, "tile not divisible by threads");
     static_assert(TM % 32 == 0 && TN % 32 == 0 && BK % 16 == 0, "fragment shape");
 };
 
@@ -145,11 +152,20 @@ __device__ __forceinline__ void mma_stage(const lds_u16 *As, const lds_u16 *Bs,
             const int c = kk * 2 + (lane >> 5);
             af[fm] = *reinterpret_cast<const lds_f16x8 *>(As + row * T::BK + swz_a<T::CA>(row, c) * 8);
         }
-        // B^T operand: lane needs B[8 consecutive k][one n]; two transpose
-        // reads of 4 k each.  Source lane s of each 16-lane group points at
-        // row (s / 4) and columns 4 * (s % 4) .. + 3 of a 4 x 16 block.
+        // B^T operand: lane needs B[8 consecutive k][one n].  An (N,K) B
+        // tile holds them contiguously (one 16-byte read, as for A); a (K,N)
+        // tile takes two transpose reads of 4 k each: source lane s of each
+        // 16-lane group points at row (s / 4) and columns 4 * (s % 4) .. + 3
+        // of a 4 x 16 block.
 #pragma unroll
         for (int fn = 0; fn < T::FN; ++fn) {
+            if constexpr (T::BT) {
+                const int row = wn * T::TN + fn * 32 + (lane & 31);
+                const int c = kk * 2 + (lane >> 5);
+                bf[fn] = *reinterpret_cast<const lds_f16x8 *>(Bs + row * T::BK +
+                                                              swz_a<T::CA>(row, c) * 8);
+                continue;
+            }
             s16x4 h[2];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
@@ -164,7 +180,13 @@ __device__ __forceinline__ void mma_stage(const lds_u16 *As, const lds_u16 *Bs,
         for (int fm = 0; fm < T::FM; ++fm)
 #pragma unroll
             for (int fn = 0; fn < T::FN; ++fn)
-                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[fn], af[fm], acc[fm][fn], 0, 0, 0);
+                if constexpr (T::BF16)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, bf[fn]), __builtin_bit_cast(bf16x8, af[fm]),
+                        acc[fm][fn], 0, 0, 0);
+                else
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[fn], af[fm],
+                                                                         acc[fm][fn], 0, 0, 0);
     }
 }
 
@@ -208,19 +230,35 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_tile_kernel(GemmArgs p, int t
         pa[i] = A + (a_ok[i] ? (m0 + r) : 0) * p.lda + c * 8;
         a_dst[i] = r * T::BK + swz_a<T::CA>(r, c) * 8;
     }
+    // (K,N) B: chunk (r, c) is row k0 + r, columns n0 + 8c ..; (N,K) B: chunk
+    // (r, c) is row n0 + r, k columns k0 + 8c .. (the A plan, on B^T).
     const uint16_t *pb[T::B_LD];
     int b_row[T::B_LD], b_dst[T::B_LD];
     int64_t b_avail[T::B_LD];
-    bool b_col0[T::B_LD];   // chunk starts at column 0 of B
+    bool b_col0[T::B_LD];   // (K,N): chunk starts at column 0 of B
+    bool b_ok[T::B_LD], b_first[T::B_LD], b_last[T::B_LD];   // (N,K): row n in range / first / last
 #pragma unroll
     for (int i = 0; i < T::B_LD; ++i) {
         const int q = tid + i * T::NT;
-        const int r = q / T::CB, c = q % T::CB;
-        b_row[i] = r;
-        b_avail[i] = N - (n0 + c * 8);
-        b_col0[i] = (n0 + c * 8) == 0;
-        pb[i] = B + r * p.ldb + (b_avail[i] > 0 ? n0 + c * 8 : 0);
-        b_dst[i] = T::A_ELEMS + r * T::BN + swz_b<T::CB>(r, c) * 8;
+        if constexpr (T::BT) {
+            const int r = q / T::CA, c = q % T::CA;
+            b_ok[i] = (n0 + r) < N;
+            b_first[i] = (n0 + r) == 0;
+            b_last[i] = (n0 + r) == N - 1;
+            b_row[i] = c * 8;                       // the chunk's k column in the tile
+            b_avail[i] = 0;
+            b_col0[i] = false;
+            pb[i] = B + (b_ok[i] ? (n0 + r) : 0) * p.ldb + c * 8;
+            b_dst[i] = T::A_ELEMS + r * T::BK + swz_a<T::CA>(r, c) * 8;
+        } else {
+            const int r = q / T::CB, c = q % T::CB;
+            b_row[i] = r;
+            b_avail[i] = N - (n0 + c * 8);
+            b_col0[i] = (n0 + c * 8) == 0;
+            b_ok[i] = b_first[i] = b_last[i] = false;
+            pb[i] = B + r * p.ldb + (b_avail[i] > 0 ? n0 + c * 8 : 0);
+            b_dst[i] = T::A_ELEMS + r * T::BN + swz_b<T::CB>(r, c) * 8;
+        }
     }
 
     u32x4 ra[T::A_LD], rb[T::B_LD];
@@ -242,6 +280,18 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_tile_kernel(GemmArgs p, int t
 #pragma unroll
         for (int i = 0; i < T::B_LD; ++i) {
             rb[i] = u32x4{0, 0, 0, 0};
+            if constexpr (T::BT) {
+                const int64_t kavail = K - (k0 + b_row[i]);
+                if (b_ok[i] && kavail > 0) {
+                    if constexpr (GENERIC) {
+                        const int64_t col = k0 + b_row[i];
+                        const bool wok = !(b_first[i] && col == 0) && !(b_last[i] && kavail <= 8);
+                        rb[i] = load8_masked(pb[i] + k0, kavail, wok);
+                    } else
+                        rb[i] = *reinterpret_cast<const u32x4 *>(pb[i] + k0);
+                }
+                continue;
+            }
             if (b_avail[i] > 0 && k0 + b_row[i] < K) {
                 const uint16_t *src = pb[i] + k0 * p.ldb;
                 if constexpr (GENERIC) {
@@ -303,17 +353,17 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_tile_kernel(GemmArgs p, int t
                 const f32x16 &v = acc[fm][fn];
                 float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
                 if constexpr (!GENERIC) {
-                    load_bias4(p.bias, n, N, bv);
+                    load_bias4<T::BF16>(p.bias, n, N, bv);
                 } else if (p.bias != nullptr) {
                     // any alignment: one element at a time, inside the row only
 #pragma unroll
                     for (int t = 0; t < 4; ++t)
                         if (n + t < N)
-                            bv[t] = (float)__builtin_bit_cast(_Float16, p.bias[n + t]);
+                            bv[t] = bits_to_float<T::BF16>(p.bias[n + t]);
                 }
                 u32x2 w;
-                w.x = epi_pack_f16x2(v[4 * g + 0] + bv[0], v[4 * g + 1] + bv[1], relu);
-                w.y = epi_pack_f16x2(v[4 * g + 2] + bv[2], v[4 * g + 3] + bv[3], relu);
+                w.x = epi_pack2<T::BF16>(v[4 * g + 0] + bv[0], v[4 * g + 1] + bv[1], relu);
+                w.y = epi_pack2<T::BF16>(v[4 * g + 2] + bv[2], v[4 * g + 3] + bv[3], relu);
                 uint16_t *dst = crow + n;
                 if constexpr (!GENERIC) {
                     if (n < N)
@@ -365,23 +415,36 @@ hipError_t launch_tiles(const GemmArgs &p, hipStream_t stream, int groupM)
     return hipSuccess;
 }
 
-using Tile128 = Tile<128, 128, 32, 2, 2>;
+template <int MODE>
+using Tile128 = Tile<128, 128, 32, 2, 2, MODE>;
 using Tile256 = Tile<256, 256, 32, 2, 2>;
 
 }  // namespace
 
+// The any-layout kernel exists for every element type and B layout; the
+// aligned register-staged kernels (kept for comparison) for fp16 with a
+// (K,N) B only.
 hipError_t launch_generic(const GemmArgs &p, hipStream_t stream, int groupM)
 {
-    return launch_tiles<Tile128, true>(p, stream, groupM);
+    switch ((p.bf16 ? 1 : 0) | (p.b_nk ? 2 : 0)) {
+    case 0: return launch_tiles<Tile128<0>, true>(p, stream, groupM);
+    case 1: return launch_tiles<Tile128<1>, true>(p, stream, groupM);
+    case 2: return launch_tiles<Tile128<2>, true>(p, stream, groupM);
+    default: return launch_tiles<Tile128<3>, true>(p, stream, groupM);
+    }
 }
 
 hipError_t launch_tile128(const GemmArgs &p, hipStream_t stream, int groupM)
 {
-    return launch_tiles<Tile128, false>(p, stream, groupM);
+    if (p.bf16 || p.b_nk)
+        return hipErrorInvalidValue;
+    return launch_tiles<Tile128<0>, false>(p, stream, groupM);
 }
 
 hipError_t launch_tile256(const GemmArgs &p, hipStream_t stream, int groupM)
 {
+    if (p.bf16 || p.b_nk)
+        return hipErrorInvalidValue;
     return launch_tiles<Tile256, false>(p, stream, groupM);
 }
 

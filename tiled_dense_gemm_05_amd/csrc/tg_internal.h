@@ -10,7 +10,9 @@ namespace tg {
 // validated it; every kernel masks its own edges, so any M, N, K >= 0 is safe
 // for the layouts the ABI documents.  The epilogue adds bias[n] (N values
 // shared by every row and batch; none when null) and applies the ReLU when
-// `relu` is set.
+// `relu` is set.  Elements are bf16 when `bf16` is set (fp16 otherwise) and B
+// is stored (N,K) when `b_nk` is set ((K,N) otherwise); the tile kernels take
+// these two as template parameters and the launcher picks the instance.
 struct GemmArgs {
     const uint16_t *A;
     const uint16_t *B;
@@ -21,25 +23,44 @@ struct GemmArgs {
     int64_t batch;
     const uint16_t *bias;
     int relu;
+    int bf16;
+    int b_nk;
 };
 
-// Epilogue of two outputs: ReLU (x if x > 0 else +0) when `relu`, then fp16
-// round to nearest even; packed low | high << 16.
-__device__ __forceinline__ uint32_t epi_pack_f16x2(float a, float b, bool relu)
+// Epilogue of two outputs: ReLU (x if x > 0 else +0) when `relu`, then round
+// to nearest even into fp16 (or bf16 when BF16); packed low | high << 16.
+template <bool BF16 = false>
+__device__ __forceinline__ uint32_t epi_pack2(float a, float b, bool relu)
 {
     if (relu) {
         a = a > 0.0f ? a : 0.0f;
         b = b > 0.0f ? b : 0.0f;
     }
-    const _Float16 ha = (_Float16)a;
-    const _Float16 hb = (_Float16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+    uint16_t ha, hb;
+    if constexpr (BF16) {
+        ha = __builtin_bit_cast(uint16_t, (__bf16)a);
+        hb = __builtin_bit_cast(uint16_t, (__bf16)b);
+    } else {
+        ha = __builtin_bit_cast(uint16_t, (_Float16)a);
+        hb = __builtin_bit_cast(uint16_t, (_Float16)b);
+    }
+    return (uint32_t)ha | ((uint32_t)hb << 16);
+}
+
+// One element's bit pattern (fp16, or bf16 when BF16) as a float.
+template <bool BF16 = false>
+__device__ __forceinline__ float bits_to_float(uint16_t h)
+{
+    if constexpr (BF16)
+        return __builtin_bit_cast(float, (uint32_t)h << 16);
+    else
+        return (float)__builtin_bit_cast(_Float16, h);
 }
 
 // bias[n .. n+3] as floats, from an 8-byte aligned address; zeros without a
 // bias or past the last column (N is a multiple of 4 on the paths that use
 // this, so a group of four columns is wholly inside or outside).
+template <bool BF16 = false>
 __device__ __forceinline__ void load_bias4(const uint16_t *bias, int64_t n, int64_t N,
                                            float (&b)[4])
 {
@@ -47,10 +68,10 @@ __device__ __forceinline__ void load_bias4(const uint16_t *bias, int64_t n, int6
     if (bias != nullptr && n < N) {
         typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
         const u32x2_t w = *reinterpret_cast<const u32x2_t *>(bias + n);
-        b[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w.x & 0xffff));
-        b[1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w.x >> 16));
-        b[2] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w.y & 0xffff));
-        b[3] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w.y >> 16));
+        b[0] = bits_to_float<BF16>((uint16_t)(w.x & 0xffff));
+        b[1] = bits_to_float<BF16>((uint16_t)(w.x >> 16));
+        b[2] = bits_to_float<BF16>((uint16_t)(w.y & 0xffff));
+        b[3] = bits_to_float<BF16>((uint16_t)(w.y >> 16));
     }
 }
 
@@ -91,12 +112,17 @@ hipError_t launch_tile256(const GemmArgs &p, hipStream_t stream, int groupM);
 
 // Direct-to-LDS pipelined kernels (aligned layouts only).  `cfg` selects the
 // block tile / K tile / stage count; see gemm_dma.hip.
+// Every configuration exists for fp16 with a (K,N) B (mode 0); bf16 and (N,K)
+// B (mode bits 1 and 2) exist for the default configurations only.
 constexpr int kDmaConfigs = 30;
 hipError_t launch_dma_config(int cfg, const GemmArgs &p, hipStream_t stream, int groupM);
+bool dma_config_has_mode(int cfg, int mode);
 // Skinny-M kernels (M <= 64, aligned layouts); `cfg` selects slice width,
 // waves and stages; see gemm_skinny.hip.
+// bf16 and (N,K) B exist for configurations 0 and 4 only.
 constexpr int kSkinnyConfigs = 10;
 hipError_t launch_skinny_config(int cfg, const GemmArgs &p, hipStream_t stream);
+bool skinny_config_has_mode(int cfg, int mode);
 bool skinny_layout_ok(const GemmArgs &p);
 // Whether the leading dimensions fit the kernels' 32-bit buffer offsets.
 bool dma_layout_ok(const GemmArgs &p);
