@@ -9,11 +9,11 @@ is reported alongside as a secondary figure.  Prints one JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--no-secondary]
                     [--tile-variant V] [--skinny-variant V] [--raster G]
-                    [--act relu|none] [--bias]
+                    [--act relu|none] [--bias] [--dtype f16|bf16] [--layout kn|nk]
 
 --tile-variant, --skinny-variant and --raster select non-default kernel
-configurations and tile orders for ablations; --act and --bias measure the
-extended epilogue (tg_gemm_ex).  A line measured with any of them carries them
+configurations and tile orders for ablations; --act, --bias, --dtype and
+--layout measure the extended entry point tg_gemm_ex.  A line measured with any of them carries them
 in `config` and no `traffic` figure (the counters are taken at the defaults).
 """
 
@@ -88,10 +88,21 @@ def calibration_copy(torch):
     del src, dst
 
 
-def run_workload(tg, torch, w: wl.Workload, steps: int, warmup: int, epilogue=None):
+def run_workload(tg, torch, w: wl.Workload, steps: int, warmup: int, epilogue=None,
+                 dtype: str = "f16", layout: str = "kn"):
     """Times `steps` calls after `warmup`.  epilogue = (activation, with_bias)
-    routes the calls through tg_gemm_ex; None uses the GEMM+ReLU entry points."""
-    a, b = wl.generate(w)
+    routes the calls through tg_gemm_ex, as do a bf16 element type and an
+    (N,K) B; otherwise the GEMM+ReLU entry points are timed."""
+    a, b = wl.generate_dense(w.M, w.N, w.K, w.dist, w.seed, batch=w.batch, dtype=dtype)
+    ex = epilogue is not None or dtype != "f16" or layout != "kn"
+    if epilogue is None:
+        epilogue = (tg.TG_ACT_RELU, False)
+    ldb = w.ldb_
+    if layout == "nk":
+        # the workloads are dense (lda = K, ldb = N); the (N,K) form is the
+        # transposed B with ldb = K
+        b = wl.transpose_bits(b, w.K, w.N, w.batch)
+        ldb = w.K
     dev = torch.device("cuda:0")
     nbuf = 1
     # skinny and batched workloads are HBM-bound: rotate input copies so a
@@ -105,16 +116,18 @@ def run_workload(tg, torch, w: wl.Workload, steps: int, warmup: int, epilogue=No
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     bias = None
-    if epilogue is not None and epilogue[1]:
-        bias = torch.from_numpy(wl.generate_bias(w.N, w.seed, scale=0.05).view(np.int16)).to(dev)
+    if epilogue[1]:
+        bias = torch.from_numpy(
+            wl.generate_bias(w.N, w.seed, dtype=dtype, scale=0.05).view(np.int16)).to(dev)
+    dt = tg.TG_DTYPE_BF16 if dtype == "bf16" else tg.TG_DTYPE_F16
+    lay = tg.TG_B_NK if layout == "nk" else tg.TG_B_KN
 
     def call(i):
         j = i % nbuf
-        if epilogue is not None:
-            st = tg.tg_gemm_ex(tg.TG_DTYPE_F16, tg.TG_B_KN, epilogue[0], A[j].data_ptr(),
-                               B[j].data_ptr(), C[j].data_ptr(),
-                               bias.data_ptr() if bias is not None else 0, w.M, w.N, w.K, w.lda_,
-                               w.ldb_, w.ldc_, w.sA, w.sB, w.sC, w.batch, sh)
+        if ex:
+            st = tg.tg_gemm_ex(dt, lay, epilogue[0], A[j].data_ptr(), B[j].data_ptr(),
+                               C[j].data_ptr(), bias.data_ptr() if bias is not None else 0, w.M,
+                               w.N, w.K, w.lda_, ldb, w.ldc_, w.sA, w.sB, w.sC, w.batch, sh)
         elif w.batch == 1:
             st = tg.tg_gemm_relu_f16(A[j].data_ptr(), B[j].data_ptr(), C[j].data_ptr(), w.M, w.N,
                                      w.K, w.lda_, w.ldb_, w.ldc_, sh)
@@ -345,6 +358,10 @@ def main():
                     help="epilogue activation (none: through tg_gemm_ex)")
     ap.add_argument("--bias", action="store_true",
                     help="add a per-column bias in the epilogue (through tg_gemm_ex)")
+    ap.add_argument("--dtype", choices=["f16", "bf16"], default="f16",
+                    help="element type (bf16: through tg_gemm_ex)")
+    ap.add_argument("--layout", choices=["kn", "nk"], default="kn",
+                    help="B stored (K,N) or (N,K) (nk: through tg_gemm_ex)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -372,11 +389,14 @@ def main():
     if args.bias or args.act != "relu":
         epilogue = (tg.TG_ACT_RELU if args.act == "relu" else tg.TG_ACT_NONE, args.bias)
         knobs["epilogue"] = ("bias+" if args.bias else "") + args.act
+    if args.layout != "kn":
+        knobs["b_layout"] = args.layout
     if args.calibrate_copy:
         calibration_copy(torch)
     w = wl.WORKLOADS[args.workload]
     log(f"workload {w.name}: M={w.M} N={w.N} K={w.K} batch={w.batch}")
-    ms, path, nbuf = run_workload(tg, torch, w, args.steps, args.warmup, epilogue)
+    ms, path, nbuf = run_workload(tg, torch, w, args.steps, args.warmup, epilogue, args.dtype,
+                                  args.layout)
     tflops = w.flops / (ms * 1e-3) / 1e12
     gbs = w.compulsory_bytes / (ms * 1e-3) / 1e9
     compute_bound = w.flops / w.compulsory_bytes > PEAK_F16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
@@ -390,6 +410,8 @@ def main():
         value, unit = gbs, "GB/s"
         roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": gbs / PEAK_HBM_GBS}
+    if args.dtype != "f16":
+        knobs["element"] = args.dtype
     roof["traffic"] = None if knobs else measured_traffic(w.name)
 
     out = {
@@ -403,7 +425,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "batch": w.batch,
                    "inputs": f"{w.dist}, seed {w.seed}", "accumulate": "fp32", "path": path,
@@ -414,7 +436,7 @@ def main():
     if not args.no_secondary and w.name != "skinny_16x16384x8192":
         s = wl.WORKLOADS["skinny_16x16384x8192"]
         sms, spath, snbuf = run_workload(tg, torch, s, max(args.steps, 20), args.warmup,
-                                         epilogue)
+                                         epilogue, args.dtype, args.layout)
         sgbs = s.compulsory_bytes / (sms * 1e-3) / 1e9
         log(f"{s.name}: {sms * 1e3:.1f} us/call, {sgbs:.0f} GB/s, path={spath}")
         out["secondary"] = {

@@ -61,7 +61,11 @@ struct Skinny {
     static constexpr int S = S_;                 // LDS stages per wave
     static constexpr int NT = 64 * NW;
     static constexpr int NF = NB / 16;           // 16-column fragments
-    static constexpr int KS = 32;                // k per step
+    // k per step: 32 for a (K,N) B (32 rows of NB columns); 64 for an (N,K)
+    // B, so that each B^T row contributes a whole 128-byte line per step
+    static constexpr int KS = BT ? 64 : 32;
+    static constexpr int CR = KS / 8;            // 16-byte chunks per A (and B^T) row
+    static constexpr int RPB = 64 / CR;          // A (and B^T) rows per 1 KiB block
     static constexpr int A_BYTES = MB * 16 * KS * 2;      // A rows of one step
     static constexpr int B_BYTES = KS * NB * 2;           // B block of one step
     static constexpr int STAGE = A_BYTES + B_BYTES;
@@ -77,9 +81,17 @@ struct Skinny {
     static_assert(LDS <= 160 * 1024, "LDS size");
 };
 
-// A block (MB*16 rows x 32 k, 64-byte rows): a 16-byte read of 16 rows at the
-// same chunk is spread over the bank line by XOR-ing the chunk with row / 4.
-__device__ __forceinline__ int swz_a(int row, int c) { return c ^ ((row >> 2) & 3); }
+// A block (MB*16 rows x KS k): a 16-byte read of 16 rows at the same chunk
+// is spread over the bank line by XOR-ing the chunk with the row's position
+// in it (64-byte rows: row / 4; 128-byte rows: row / 2).
+template <int CR>
+__device__ __forceinline__ int swz_a(int row, int c)
+{
+    if constexpr (CR == 4)
+        return c ^ ((row >> 2) & 3);
+    else
+        return c ^ ((row >> 1) & 7);
+}
 
 // B block (32 rows x NB columns): a transpose read touches rows
 // {4h..4h+3} and {8+4h..8+4h+3} (32 bytes each) per half-wave; XOR the
@@ -174,8 +186,8 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_skinny_kernel(GemmArgs p, int
     int a_col[T::A_LD];
 #pragma unroll
     for (int j = 0; j < T::A_LD; ++j) {
-        const int row = 16 * j + lane / 4;
-        const int c = swz_a(row, lane % 4);
+        const int row = T::RPB * j + lane / T::CR;
+        const int c = swz_a<T::CR>(row, lane % T::CR);
         a_col[j] = c * 8;
         a_voff[j] = row < M ? (uint32_t)((row * p.lda + c * 8) * 2) : kOutOfRange;
     }
@@ -186,8 +198,8 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_skinny_kernel(GemmArgs p, int
 #pragma unroll
     for (int j = 0; j < T::B_LD; ++j) {
         if constexpr (T::BT) {
-            const int row = 16 * j + lane / 4;
-            const int c = swz_a(row, lane % 4);
+            const int row = T::RPB * j + lane / T::CR;
+            const int c = swz_a<T::CR>(row, lane % T::CR);
             b_row[j] = c * 8;
             b_voff[j] = (n0 + row < N) ? (uint32_t)((row * p.ldb + c * 8) * 2) : kOutOfRange;
         } else {
@@ -238,42 +250,48 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_skinny_kernel(GemmArgs p, int
         wait_vmcnt<(T::S - 1) * T::LOADS>();
         const lds_u16 *As = lds + (wave * T::S + st % T::S) * (T::STAGE / 2);
         const lds_u16 *Bs = As + T::A_BYTES / 2;
-        f16x8 af[T::MB], bf[T::NF];
 #pragma unroll
-        for (int mb = 0; mb < T::MB; ++mb) {
-            const int row = mb * 16 + (lane & 15);
-            const int c = lane >> 4;
-            af[mb] = *reinterpret_cast<const lds_f16x8 *>(As + row * 32 + swz_a(row, c) * 8);
-        }
+        for (int ks = 0; ks < T::KS / 32; ++ks) {
+            f16x8 af[T::MB], bf[T::NF];
 #pragma unroll
-        for (int f = 0; f < T::NF; ++f) {
-            if constexpr (T::BT) {
-                const int row = f * 16 + (lane & 15);
-                const int c = lane >> 4;
-                bf[f] = *reinterpret_cast<const lds_f16x8 *>(Bs + row * 32 + swz_a(row, c) * 8);
-                continue;
+            for (int mb = 0; mb < T::MB; ++mb) {
+                const int row = mb * 16 + (lane & 15);
+                const int c = ks * 4 + (lane >> 4);
+                af[mb] = *reinterpret_cast<const lds_f16x8 *>(As + row * T::KS +
+                                                              swz_a<T::CR>(row, c) * 8);
             }
-            s16x4 h[2];
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int k = 8 * (lane >> 4) + 4 * hh + ((lane & 15) >> 2);
-                const int n = f * 16 + 4 * (lane & 3);
-                const lds_u16 *src = Bs + k * T::NB + swz_b<T::CB>(k, n >> 3) * 8 + (n & 7);
-                h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src);
+            for (int f = 0; f < T::NF; ++f) {
+                if constexpr (T::BT) {
+                    const int row = f * 16 + (lane & 15);
+                    const int c = ks * 4 + (lane >> 4);
+                    bf[f] = *reinterpret_cast<const lds_f16x8 *>(Bs + row * T::KS +
+                                                                 swz_a<T::CR>(row, c) * 8);
+                    continue;
+                }
+                s16x4 h[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int k = 8 * (lane >> 4) + 4 * hh + ((lane & 15) >> 2);
+                    const int n = f * 16 + 4 * (lane & 3);
+                    const lds_u16 *src = Bs + k * T::NB + swz_b<T::CB>(k, n >> 3) * 8 + (n & 7);
+                    h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src);
+                }
+                bf[f] = __builtin_bit_cast(
+                    f16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
             }
-            bf[f] = __builtin_bit_cast(f16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int mb = 0; mb < T::MB; ++mb)
+#pragma unroll
+                for (int f = 0; f < T::NF; ++f)
+                    if constexpr (T::BF16)
+                        acc[mb][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, bf[f]), __builtin_bit_cast(bf16x8, af[mb]),
+                            acc[mb][f], 0, 0, 0);
+                    else
+                        acc[mb][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[f], af[mb],
+                                                                            acc[mb][f], 0, 0, 0);
         }
-#pragma unroll
-        for (int mb = 0; mb < T::MB; ++mb)
-#pragma unroll
-            for (int f = 0; f < T::NF; ++f)
-                if constexpr (T::BF16)
-                    acc[mb][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, bf[f]), __builtin_bit_cast(bf16x8, af[mb]),
-                        acc[mb][f], 0, 0, 0);
-                else
-                    acc[mb][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[f], af[mb], acc[mb][f],
-                                                                        0, 0, 0);
     }
     wait_vmcnt<0>();
     __syncthreads();   // every wave is done with its ring before it is reused
@@ -337,26 +355,30 @@ hipError_t launch(const GemmArgs &p, hipStream_t stream)
 bool skinny_layout_ok(const GemmArgs &p)
 {
     // M <= 64; 32-bit buffer offsets: 64 A rows and 32 (K,N) B rows, or 64
-    // (N,K) B rows, per step
+    // (N,K) B rows, per step (an (N,K) slice spans 64 rows of ldb)
     return p.M <= 64 && p.lda <= (1 << 24) && p.ldb <= (p.b_nk ? (1 << 22) : (1 << 24));
 }
 
 namespace {
 
-// bf16 and (N,K)-B instances of configurations 0 and 4 (the default).
+// bf16 and (N,K)-B instances of configurations 0 and 4 (the default).  An
+// (N,K) B stages 64 k per step, twice the bytes per stage, so its rings are
+// shallower to fit the LDS.
 template <int MODE>
 hipError_t launch_mode(int cfg, const GemmArgs &p, hipStream_t stream)
 {
+    constexpr bool bt = (MODE & 2) != 0;
+    constexpr int s1 = bt ? 3 : 6, s2 = bt ? 3 : 5, s4 = bt ? 2 : 4;
     const int mb = (int)((p.M + 15) / 16);
     switch (cfg) {
     case 0:
-        if (mb <= 1) return launch<Skinny<1, 64, 4, 6, false, MODE>>(p, stream);
-        if (mb <= 2) return launch<Skinny<2, 64, 4, 5, false, MODE>>(p, stream);
-        return launch<Skinny<4, 64, 4, 4, false, MODE>>(p, stream);
+        if (mb <= 1) return launch<Skinny<1, 64, 4, s1, false, MODE>>(p, stream);
+        if (mb <= 2) return launch<Skinny<2, 64, 4, s2, false, MODE>>(p, stream);
+        return launch<Skinny<4, 64, 4, s4, false, MODE>>(p, stream);
     case 4:
-        if (mb <= 1) return launch<Skinny<1, 64, 4, 6, true, MODE>>(p, stream);
-        if (mb <= 2) return launch<Skinny<2, 64, 4, 5, true, MODE>>(p, stream);
-        return launch<Skinny<4, 64, 4, 4, true, MODE>>(p, stream);
+        if (mb <= 1) return launch<Skinny<1, 64, 4, s1, true, MODE>>(p, stream);
+        if (mb <= 2) return launch<Skinny<2, 64, 4, s2, true, MODE>>(p, stream);
+        return launch<Skinny<4, 64, 4, s4, true, MODE>>(p, stream);
     default: return hipErrorInvalidValue;
     }
 }
