@@ -242,3 +242,35 @@ def test_full_size_with_bias_no_activation(tg, oracle_lib, dtype, layout, name, 
         got = np.array([out[bb * sC + i * w.N + j] for bb, i, j in idx], dtype=np.uint16)
         rep = gate(got, ref, w.K, Sa, dtype=dtype, relu=False)
     assert rep.ok, str(rep)
+
+
+@pytest.mark.parametrize("tdtype", ["float16", "bfloat16"])
+def test_torch_helpers(tg, oracle_lib, tdtype):
+    dtype = "f16" if tdtype == "float16" else "bf16"
+    td = getattr(torch, tdtype)
+    M, N, K = 77, 136, 200
+    a, b = wl.generate_dense(M, N, K, "uniform", 41, dtype=dtype)
+    bias = wl.generate_bias(N, 41, dtype=dtype)
+    A = torch.from_numpy(a.view(np.int16).reshape(M, K)).to("cuda").view(td)
+    B = torch.from_numpy(b.view(np.int16).reshape(K, N)).to("cuda").view(td)
+    Bt = B.t().contiguous()
+    bias_t = torch.from_numpy(bias.view(np.int16)).to("cuda").view(td)
+    say(f"ex torch helpers {tdtype}")
+    ref, _, Sa = oracle_lib.gemm_ex(a, b, M, N, K, bias=bias, act="relu", dtype=dtype,
+                                    want_sums=True)
+    c1 = tg.gemm_ex(A, B, bias=bias_t, activation="relu")
+    c2 = tg.linear(A, Bt, bias=bias_t, activation="relu")
+    torch.cuda.synchronize()
+    for c in (c1, c2):
+        got = c.view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
+        rep = gate(got, ref, K, Sa.reshape(-1), dtype=dtype)
+        assert rep.ok, str(rep)
+    ref_none = oracle_lib.gemm_ex(a, b, M, N, K, act="none", dtype=dtype)
+    c3 = tg.linear(A, Bt)
+    torch.cuda.synchronize()
+    got = c3.view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
+    assert gate(got, ref_none, K, dtype=dtype, relu=False).contract_fail == 0
+    with pytest.raises(TypeError):
+        tg.gemm_ex(A, B.float())
+    with pytest.raises(ValueError):
+        tg.gemm_ex(A, B, b_layout="nk")

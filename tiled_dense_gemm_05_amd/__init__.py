@@ -212,3 +212,55 @@ def gemm_relu_strided_batched(A, B, out=None, stream=None):
         max(A.stride(1), K, 1), max(B.stride(1), N, 1), max(out.stride(1), N, 1),
         A.stride(0), B.stride(0), out.stride(0), bt, _stream_handle(stream)))
     return out
+
+
+def gemm_ex(A, B, bias=None, activation="relu", b_layout="kn", out=None, stream=None):
+    """C = act(A @ B' + bias) through tg_gemm_ex for 2-D device tensors.
+
+    A is (M, K); B is (K, N) for ``b_layout="kn"`` or (N, K) for "nk" (then
+    B' = B^T, as a linear layer's weight); both float16 or both bfloat16 with
+    unit column stride; ``bias`` (optional) is a contiguous 1-D tensor of N
+    elements of the same type; ``activation`` is "relu" or "none".  ``out``
+    (optional) is an (M, N) tensor of that type with unit column stride.
+    Enqueued on ``stream`` (default: torch's current stream); returns ``out``.
+    """
+    import torch
+    dtypes = {torch.float16: TG_DTYPE_F16, torch.bfloat16: TG_DTYPE_BF16}
+    if A.dtype not in dtypes or B.dtype != A.dtype:
+        raise TypeError("A and B must both be float16 or both bfloat16")
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D")
+    acts = {"relu": TG_ACT_RELU, "none": TG_ACT_NONE}
+    layouts = {"kn": TG_B_KN, "nk": TG_B_NK}
+    if activation not in acts or b_layout not in layouts:
+        raise ValueError("activation is 'relu' or 'none'; b_layout is 'kn' or 'nk'")
+    M, K = A.shape
+    N, K2 = (B.shape[1], B.shape[0]) if b_layout == "kn" else (B.shape[0], B.shape[1])
+    if K2 != K:
+        raise ValueError(f"inner sizes differ: {tuple(A.shape)} and {tuple(B.shape)} ({b_layout})")
+    for t, name in ((A, "A"), (B, "B")):
+        if t.numel() and t.stride(1) != 1 and t.size(1) > 1:
+            raise ValueError(f"{name} must have unit column stride (row-major)")
+    if bias is not None:
+        if bias.dtype != A.dtype or bias.dim() != 1 or bias.numel() != N or \
+                (N > 1 and bias.stride(0) != 1):
+            raise ValueError("bias must be a contiguous 1-D tensor of N elements of A's type")
+    if out is None:
+        out = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    if tuple(out.shape) != (M, N) or out.dtype != A.dtype:
+        raise ValueError("out has the wrong shape or type")
+    if out.numel() and out.stride(1) != 1 and out.size(1) > 1:
+        raise ValueError("out must have unit column stride")
+    inner = K if b_layout == "nk" else N
+    _check(tg_gemm_ex(dtypes[A.dtype], layouts[b_layout], acts[activation], A.data_ptr(),
+                      B.data_ptr(), out.data_ptr(), bias.data_ptr() if bias is not None else 0,
+                      M, N, K, max(A.stride(0), K, 1), max(B.stride(0), inner, 1),
+                      max(out.stride(0), N, 1), 0, 0, 0, 1, _stream_handle(stream)))
+    return out
+
+
+def linear(x, weight, bias=None, activation="none", out=None, stream=None):
+    """A linear layer, x @ weight^T + bias, with an optional fused ReLU: x is
+    (M, K), weight (N, K) (the (N,K) B layout), bias N elements."""
+    return gemm_ex(x, weight, bias=bias, activation=activation, b_layout="nk", out=out,
+                   stream=stream)
