@@ -46,9 +46,18 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+# The sources that decide the kernel a workload's launch runs: the dispatcher,
+# the shared internal header and the kernel's own file.
+KERNEL_SOURCES = {
+    "skinny_16x16384x8192": ("api.cpp", "tg_internal.h", "gemm_skinny.hip"),
+    "ragged_3001x5003x1000": ("api.cpp", "tg_internal.h", "gemm_tile.hip"),
+}
+DEFAULT_SOURCES = ("api.cpp", "tg_internal.h", "gemm_dma.hip")
+
+
+def kernel_source_hash(workload: str) -> str:
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in KERNEL_SOURCES.get(workload, DEFAULT_SOURCES):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -73,7 +82,7 @@ def measured_traffic(workload: str):
     """HBM bytes per launch from the committed counter runs, only while the
     kernel sources are unchanged since those counters were taken."""
     e = read_traffic_file().get(workload)
-    if not e or e[0] != kernel_source_hash():
+    if not e or e[0] != kernel_source_hash(workload):
         return None
     return e[1] + e[2]
 
@@ -240,14 +249,15 @@ def summarize(workload: str, stats_dir: str, fetch_dir: str, write_dir: str, com
               "gemm_relu_skinny_kernel" if "skinny_kernel" in top["Name"] else "kernel")
     md = os.path.join(PROFILES, f"{family}-{workload}.md")
     with open(md, "w") as f:
-        f.write(f"# {top['Name']} on {workload}\n\n")
+        f.write(f"# {top['Name'].replace('tg::(anonymous namespace)::', '')} on {workload}\n\n")
         f.write("Commands (from the repository root on the GPU box):\n\n")
         for c in commands:
             f.write(f"    {c}\n")
         f.write("\nKernel trace (rocprofv3 --kernel-trace --stats), top kernels:\n\n")
         f.write("| kernel | calls | average ns | min ns | max ns |\n|---|---|---|---|---|\n")
         for r in stats[:4]:
-            f.write(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+            name = r["Name"].replace("tg::(anonymous namespace)::", "")
+            f.write(f"| {name[:120]} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
                     f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} |\n")
         f.write(f"\nAlgorithmic work per launch: {w.flops:.4e} flop, "
                 f"{w.compulsory_bytes:.4e} compulsory HBM bytes.\n")
@@ -259,9 +269,10 @@ def summarize(workload: str, stats_dir: str, fetch_dir: str, write_dir: str, com
         writes = 2 * w.M * w.N * w.batch
         f.write(f"* GEMM: HBM read {g_fetch:.4e} B ({g_fetch / reads:.2f} x the {reads:.4e} B of A and B), "
                 f"HBM write {g_write:.4e} B ({g_write / writes:.2f} x the {writes:.4e} B of C)\n")
-        f.write(f"* kernel source hash {kernel_source_hash()}\n")
+        f.write(f"* kernel source hash {kernel_source_hash(workload)} "
+                f"({', '.join(KERNEL_SOURCES.get(workload, DEFAULT_SOURCES))})\n")
     lines = {k: v for k, v in read_traffic_file().items()}
-    lines[workload] = (kernel_source_hash(), g_fetch, g_write)
+    lines[workload] = (kernel_source_hash(workload), g_fetch, g_write)
     with open(TRAFFIC_FILE, "w") as f:
         f.write("# workload source_hash hbm_read_bytes hbm_write_bytes (per launch, calibrated)\n")
         for k, (h, r_, w_) in sorted(lines.items()):
