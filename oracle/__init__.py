@@ -76,6 +76,10 @@ def _load():
     lib.oracle_gemm_ex_sampled.argtypes = [ci, ci, ci, vp, vp, vp] + [i64] * 5 + [vp, i64, vp,
                                                                                   vp, vp, ci]
     lib.oracle_gemm_ex_sampled.restype = ctypes.c_int
+    lib.oracle_s4_decode_array.argtypes = [vp, vp, vp, i64]
+    lib.oracle_s4_decode_array.restype = None
+    lib.oracle_gemm_w4.argtypes = [ci, ci, vp, vp, vp, vp, vp] + [i64] * 8 + [vp, vp, ci]
+    lib.oracle_gemm_w4.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -319,3 +323,58 @@ def gemm_ex_sampled(A, B, K: int, lda: int, ldb: int, idx, sA: int = 0, sB: int 
         _ptr(bias) if bias is not None else None, K, lda, ldb, sA, sB, _ptr(idx), n, _ptr(out),
         _ptr(s), _ptr(sa), host_threads() if threads is None else threads)
     return out, s, sa
+
+
+def s4_decode(packed) -> tuple[np.ndarray, np.ndarray]:
+    """Signed values (-8..7) of the low and high nibbles of each byte."""
+    b = np.ascontiguousarray(packed, dtype=np.uint8)
+    lo = np.empty(b.shape, dtype=np.int8)
+    hi = np.empty(b.shape, dtype=np.int8)
+    _load().oracle_s4_decode_array(_ptr(b), _ptr(lo), _ptr(hi), b.size)
+    return lo, hi
+
+
+def gemm_w4(A, Wq, S, M: int, N: int, K: int, G: int, lda: int | None = None,
+            ldw: int | None = None, lds: int | None = None, ldc: int | None = None, C=None,
+            bias=None, dtype: str = "f16", act: str = "relu", want_sums: bool = False,
+            threads: int | None = None):
+    """C = act(A · W + bias) with W(k, n) = S[n*lds + k//G] * q(n, k), q the
+    signed nibble k%2 of byte Wq[n*ldw + k//2] (see the C source).  A, S,
+    bias, C are uint16 bit patterns of ``dtype``; Wq is uint8.  Sums come
+    back shaped (M, N)."""
+    lda = K if lda is None else lda
+    ldw = (K + 1) // 2 if ldw is None else ldw
+    lds = (K + G - 1) // G if lds is None else lds
+    ldc = N if ldc is None else ldc
+    A = _u16(A).reshape(-1)
+    S = _u16(S).reshape(-1)
+    Wq = np.ascontiguousarray(Wq, dtype=np.uint8).reshape(-1)
+    if M > 0 and N > 0:
+        _check_extent(A, M, K, lda, 0, 1, "A")
+        if K > 0:
+            if Wq.size < (N - 1) * ldw + (K + 1) // 2:
+                raise ValueError("Wq too small")
+            if S.size < (N - 1) * lds + (K - 1) // G + 1:
+                raise ValueError("S too small")
+    if bias is not None:
+        bias = _u16(bias).reshape(-1)
+        if bias.size < N:
+            raise ValueError("bias too small")
+    if C is None:
+        C = np.zeros(0 if (M == 0 or N == 0) else (M - 1) * ldc + N, dtype=np.uint16)
+    C = C.reshape(-1)
+    _check_extent(C, M, N, ldc, 0, 1, "C")
+    Sm = Sa = None
+    if want_sums:
+        Sm = np.zeros((M, N), dtype=np.float64)
+        Sa = np.zeros((M, N), dtype=np.float64)
+    rc = _load().oracle_gemm_w4(
+        DTYPES[dtype], ACTS[act], _ptr(A), _ptr(Wq), _ptr(S), _ptr(C),
+        _ptr(bias) if bias is not None else None, M, N, K, G, lda, ldw, lds, ldc,
+        _ptr(Sm) if Sm is not None else None, _ptr(Sa) if Sa is not None else None,
+        host_threads() if threads is None else threads)
+    if rc != 0:
+        raise MemoryError("oracle ran out of memory") if rc == -1 else ValueError("bad mode")
+    if want_sums:
+        return C, Sm, Sa
+    return C

@@ -48,6 +48,15 @@
  *    describes; the bias-add is the plainest such neighbour.
  *  - activation none (r = s) or ReLU.
  *
+ * Weight-only int4 variant (oracle_gemm_w4), the W_INT4/A_FP16 dequantize
+ * GEMM named in section 5 of the "TileLang paper reading" page.  The page
+ * gives no format; the reading taken: the weight is an (N,K) array of signed
+ * 4-bit integers q in [-8, 7] (two's complement), two per byte along k (even
+ * k in the low nibble, row n at Wq[n*ldw], ldw in bytes); each group of G
+ * consecutive k of row n has one scale s[n][k/G] of the element type (row n
+ * at S[n*lds]); the weight's value is s * q, exactly; then
+ *     C[i][j] = store(act(sum_k A[i][k] * s[j][k/G] * q[j][k] + bias[j])).
+ *
  * Also exported: dec/enc on arrays (for the pins in the tests), a sampled
  * variant that computes chosen (b, i, j) outputs one by one, and the optional
  * per-element s and sum_k |A_ik * B_kj| (+ |bias_j|) used by the fp32
@@ -442,4 +451,99 @@ int oracle_gemm_relu_f16_sampled(const uint16_t *A, const uint16_t *B,
 {
     return oracle_gemm_ex_sampled(DT_F16, B_KN, ACT_RELU, A, B, NULL, K, lda, ldb, sA, sB, idx,
                                   n, out, s_out, abs_out, nthreads);
+}
+
+/* ------------------------------------------------------------------------ */
+
+/* The signed value of nibble `hi` (0: bits 0-3, 1: bits 4-7) of a byte. */
+static int nibble_s4(uint8_t b, int hi)
+{
+    int v = hi ? (b >> 4) : (b & 15);
+    return v >= 8 ? v - 16 : v;
+}
+
+void oracle_s4_decode_array(const uint8_t *in, int8_t *lo, int8_t *hi, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        lo[i] = (int8_t)nibble_s4(in[i], 0);
+        hi[i] = (int8_t)nibble_s4(in[i], 1);
+    }
+}
+
+typedef struct {
+    const uint16_t *A, *S, *bias;
+    const uint8_t *W;
+    uint16_t *C;
+    double *Sum, *Sabs;
+    int64_t M, N, K, G, lda, ldw, lds, ldc;
+    int dtype, act, nthreads, tid;
+} w4job_t;
+
+static void *w4_worker(void *p)
+{
+    w4job_t *j = (w4job_t *)p;
+    int64_t K = j->K;
+    double *a = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    double *w = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    /* threads take columns: each dequantizes its weight rows once */
+    for (int64_t n = j->tid; n < j->N; n += j->nthreads) {
+        for (int64_t k = 0; k < K; ++k) {
+            int q = nibble_s4(j->W[n * j->ldw + k / 2], (int)(k & 1));
+            w[k] = dec(j->dtype, j->S[n * j->lds + k / j->G]) * (double)q;   /* exact */
+        }
+        double bv = j->bias ? dec(j->dtype, j->bias[n]) : 0.0;
+        for (int64_t i = 0; i < j->M; ++i) {
+            for (int64_t k = 0; k < K; ++k)
+                a[k] = dec(j->dtype, j->A[i * j->lda + k]);
+            double sabs;
+            double s = dot_k(a, w, K, &sabs);
+            if (j->bias) {
+                s += bv;
+                sabs += fabs(bv);
+            }
+            j->C[i * j->ldc + n] = act_store(j->dtype, j->act, s);
+            if (j->Sum) {
+                j->Sum[i * j->N + n] = s;
+                j->Sabs[i * j->N + n] = sabs;
+            }
+        }
+    }
+    free(a);
+    free(w);
+    return NULL;
+}
+
+/*
+ * Weight-only int4 GEMM (see the header): A (M,K) of the element type dtype,
+ * Wq the (N, ldw-byte) packed weight, S the (N, lds) scales, group size G
+ * (K a multiple of G), optional bias, act 0 none / 1 ReLU.  Sum and Sabs as
+ * for oracle_gemm_ex, laid out [M][N].  Returns 0, -1 (memory), -2 (mode).
+ */
+int oracle_gemm_w4(int dtype, int act, const uint16_t *A, const uint8_t *Wq, const uint16_t *S,
+                   uint16_t *C, const uint16_t *bias, int64_t M, int64_t N, int64_t K, int64_t G,
+                   int64_t lda, int64_t ldw, int64_t lds, int64_t ldc, double *Sum, double *Sabs,
+                   int nthreads)
+{
+    if ((dtype != DT_F16 && dtype != DT_BF16) || (act != ACT_NONE && act != ACT_RELU) || G <= 0)
+        return -2;
+    nthreads = clamp_threads(nthreads);
+    if (M <= 0 || N <= 0)
+        return 0;
+    int nt = (int)(N < nthreads ? N : nthreads);
+    pthread_t th[256];
+    w4job_t jobs[256];
+    for (int t = 0; t < nt; ++t) {
+        w4job_t *j = &jobs[t];
+        j->A = A; j->S = S; j->bias = bias; j->W = Wq; j->C = C; j->Sum = Sum; j->Sabs = Sabs;
+        j->M = M; j->N = N; j->K = K; j->G = G; j->lda = lda; j->ldw = ldw; j->lds = lds;
+        j->ldc = ldc; j->dtype = dtype; j->act = act; j->nthreads = nt; j->tid = t;
+        if (nt == 1)
+            w4_worker(j);
+        else
+            pthread_create(&th[t], NULL, w4_worker, j);
+    }
+    if (nt > 1)
+        for (int t = 0; t < nt; ++t)
+            pthread_join(th[t], NULL);
+    return 0;
 }

@@ -205,3 +205,17 @@ def sample_positions(w: Workload, n: int, seed: int = 1234) -> np.ndarray:
     jj[q:2 * q] = N - 1 - rng.integers(0, min(N, 128), q)
     pts.extend(zip(bb.tolist(), ii.tolist(), jj.tolist()))
     return np.asarray(pts, dtype=np.int64)
+
+
+def generate_w4(N: int, K: int, G: int, seed: int, dtype: str = "f16"):
+    """A packed int4 weight and its group scales for an (N,K) weight: q
+    uniform on -8..7, two per byte along k (even k in the low nibble), and one
+    scale per group of G k per row, uniform in [0.5, 1.5] / (8 sqrt(K)) (so
+    the dequantized weights have the magnitude of uniform(-1,1)/sqrt(K)).
+    Returns (Wq uint8 (N, K/2) flattened, S bits (N, K/G) flattened)."""
+    rng = np.random.default_rng(20_000 + seed)
+    q = rng.integers(-8, 8, (N, K))
+    u = (q & 15).astype(np.uint8)
+    wq = (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+    s = rng.uniform(0.5, 1.5, (N, K // G)) / (8.0 * np.sqrt(K))
+    return wq.reshape(-1), to_bits(s.reshape(-1), dtype)
