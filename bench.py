@@ -163,6 +163,42 @@ def run_workload(tg, torch, w: wl.Workload, steps: int, warmup: int, epilogue=No
     return ms, path, nbuf
 
 
+def run_w4(tg, torch, M: int, N: int, K: int, G: int, steps: int, warmup: int, dtype: str):
+    """Times the weight-only int4 GEMM (tg_gemm_w4) on an (N,K) int4 weight with
+    group scales; several weight copies rotate so reruns come from HBM."""
+    a, _ = wl.generate_dense(M, 8, K, "uniform_invsqrtk", 3, dtype=dtype)
+    wq, s = wl.generate_w4(N, K, G, 3, dtype=dtype)
+    wbytes = wq.size + 2 * s.size
+    nbuf = max(2, int(np.ceil(600e6 / wbytes)))
+    dev = torch.device("cuda:0")
+    A = torch.from_numpy(a.view(np.int16)).to(dev)
+    W = [torch.from_numpy(wq).to(dev) for _ in range(nbuf)]
+    S = [torch.from_numpy(s.view(np.int16)).to(dev) for _ in range(nbuf)]
+    C = torch.empty(M * N, dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+    dt = tg.TG_DTYPE_BF16 if dtype == "bf16" else tg.TG_DTYPE_F16
+
+    def call(i):
+        j = i % nbuf
+        st = tg.tg_gemm_w4(dt, tg.TG_ACT_RELU, A.data_ptr(), W[j].data_ptr(), S[j].data_ptr(),
+                           C.data_ptr(), 0, M, N, K, G, K, K // 2, K // G, N, stream.cuda_stream)
+        if st != tg.TG_OK:
+            raise RuntimeError(tg.tg_status_string(st))
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        call(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    return ms, tg.tg_path_name(tg.tg_last_path()), nbuf, wbytes + 2 * (M * K + M * N)
+
+
 def cpu_baseline(w: wl.Workload, target_s: float = 12.0):
     """The oracle, as it stands, on the host cores: rows 0..r-1 of the
     workload's C (all N columns, full K), r sized for about target_s seconds."""
@@ -373,6 +409,9 @@ def main():
                     help="element type (bf16: through tg_gemm_ex)")
     ap.add_argument("--layout", choices=["kn", "nk"], default="kn",
                     help="B stored (K,N) or (N,K) (nk: through tg_gemm_ex)")
+    ap.add_argument("--w4", action="store_true",
+                    help="time the weight-only int4 GEMM on the decode shape "
+                         "16 x 16384 x 8192, groups of 128 (tg_gemm_w4) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -404,6 +443,22 @@ def main():
         knobs["b_layout"] = args.layout
     if args.calibrate_copy:
         calibration_copy(torch)
+    if args.w4:
+        M, N, K, G = 16, 16384, 8192, 128
+        ms, path, nbuf, nbytes = run_w4(tg, torch, M, N, K, G, args.steps, args.warmup,
+                                        args.dtype)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        log(f"w4 {M}x{N}x{K} g{G}: {ms * 1e3:.1f} us/call, {gbs:.0f} GB/s, path={path}")
+        print(json.dumps({
+            "metric": "GB/s weight-only int4 GEMM+ReLU (decode shape)", "value": gbs,
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": args.dtype, "data": "synthetic",
+            "config": {"workload": f"w4_{M}x{N}x{K}_g{G}", "M": M, "N": N, "K": K,
+                       "group_size": G, "path": path, "weight_copies": nbuf},
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "traffic": None}}), flush=True)
+        return
     w = wl.WORKLOADS[args.workload]
     log(f"workload {w.name}: M={w.M} N={w.N} K={w.K} batch={w.batch}")
     ms, path, nbuf = run_workload(tg, torch, w, args.steps, args.warmup, epilogue, args.dtype,

@@ -125,6 +125,41 @@ int tg_gemm_ex(int dtype, int b_layout, int activation,
                int64_t strideA, int64_t strideB, int64_t strideC,
                int64_t batch, hipStream_t stream);
 
+/*
+ * Weight-only int4 GEMM (W_INT4 / A_FP16 or A_BF16): the dequantize GEMM that
+ * section 5 of the "TileLang paper reading" page measures, with the
+ * epilogue of tg_gemm_ex:
+ *
+ *   C[i*ldc + j] = rne( act( sum_k A[i*lda + k] * W(k, j) + bias[j] ) )
+ *   W(k, j)      = scales[j*lds + k/group_size] * q(j, k)   (exactly)
+ *   q(j, k)      = the signed 4-bit value (two's complement, -8..7) in bits
+ *                  4*(k%2) .. 4*(k%2)+3 of the byte Wq[j*ldw + k/2]
+ *
+ * i.e. the weight is stored (N,K) like a linear layer's, two values per byte
+ * along k (even k in the low nibble), ldw in BYTES (>= ceil(K/2)); one scale
+ * of the element type per group of group_size consecutive k of each weight
+ * row, row j at scales + j*lds elements (lds >= K/group_size).  The pages
+ * name the configuration but not its format: this layout is the reading
+ * taken.  A (M,K), bias (N values or NULL) and C (M,N) have element type
+ * dtype (TG_DTYPE_F16 or TG_DTYPE_BF16); A, Wq, scales, bias and C are DEVICE
+ * pointers.  activation is TG_ACT_NONE or TG_ACT_RELU.  The products of A with
+ * q are exact; each group's sum is formed in fp32 and multiplied by its
+ * scale in fp32.
+ *
+ * Requirements: sizes in [0, 2^31 - 1]; group_size > 0 and K % group_size
+ * == 0; lda >= max(1,K), ldc >= max(1,N).  Fast kernel (any M; rows of A
+ * beyond 64 stream the weight once per 64 rows): A and Wq 16-byte aligned,
+ * lda % 8 == 0, ldw % 16 == 0, group_size a multiple of 32, C and bias
+ * 8-byte aligned, ldc and N multiples of 4, and (K/group_size) * 128 bytes of
+ * scales per 64 weight rows within the LDS the kernel leaves free (e.g.
+ * K/group_size <= 512 for M <= 16); other calls take a plain one-thread-per-
+ * output kernel.  Errors, asynchrony and determinism as for the other entry
+ * points; M = 0 or N = 0 is a no-op, K = 0 writes act(bias) (or +0).
+ */
+int tg_gemm_w4(int dtype, int activation, const void *A, const void *Wq, const void *scales,
+               void *C, const void *bias, int64_t M, int64_t N, int64_t K, int64_t group_size,
+               int64_t lda, int64_t ldw, int64_t lds, int64_t ldc, hipStream_t stream);
+
 /* A static, human-readable name for a tg_status value. */
 const char *tg_status_string(int status);
 
@@ -142,7 +177,8 @@ enum {
     TG_PATH_TILE128 = 3,    /* 128x128x32 tiles, 256 threads, aligned operands */
     TG_PATH_TILE256 = 4,    /* 256x256 tiles for large shapes, aligned operands */
     TG_PATH_SKINNY = 5,     /* M <= 64: column slices streaming B, K split over waves */
-    TG_PATH_COUNT = 6
+    TG_PATH_W4 = 6,         /* tg_gemm_w4's int4-weight kernel (reported, not forced) */
+    TG_PATH_COUNT = 7
 };
 int tg_set_path(int path);
 

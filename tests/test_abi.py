@@ -133,6 +133,26 @@ def test_ex_validation(tg):
     assert call(ok["dtype"], ok["b_layout"], tg.TG_ACT_RELU, N=0, bias=0) == tg.TG_OK
 
 
+def test_w4_validation(tg):
+    f = tg.tg_gemm_w4
+
+    def call(M=4, N=8, K=128, G=64, lda=128, ldw=64, lds=2, ldc=8, dtype=0, act=1, A=P):
+        return f(dtype, act, A, P, P, P, 0, M, N, K, G, lda, ldw, lds, ldc, 0)
+
+    assert call(dtype=5) == tg.TG_ERR_INVALID_ARG
+    assert call(act=3) == tg.TG_ERR_INVALID_ARG
+    assert call(G=0) == tg.TG_ERR_INVALID_ARG
+    assert call(G=48) == tg.TG_ERR_INVALID_ARG          # K % G != 0
+    assert call(lda=127) == tg.TG_ERR_INVALID_ARG
+    assert call(ldw=63) == tg.TG_ERR_INVALID_ARG        # ldw counts bytes: >= K / 2
+    assert call(lds=1) == tg.TG_ERR_INVALID_ARG         # one scale per group
+    assert call(ldc=7) == tg.TG_ERR_INVALID_ARG
+    assert call(M=-1) == tg.TG_ERR_INVALID_ARG
+    assert call(A=0) == tg.TG_ERR_INVALID_ARG
+    assert call(M=0) == tg.TG_OK and call(N=0, ldc=1) == tg.TG_OK
+    assert tg.tg_path_name(tg.TG_PATH_W4) == "w4"
+
+
 def _gpu_visible():
     try:
         import torch
@@ -148,6 +168,8 @@ def test_valid_call_without_device_reports_no_device(tg):
     # K = 0 with null operands is valid and also reaches the device check
     st = tg.tg_gemm_relu_f16(0, 0, P, 4, 4, 0, 1, 4, 4, 0)
     assert st == tg.TG_ERR_NO_DEVICE
+    assert tg.tg_gemm_w4(0, 1, P, P, P, P, 0, 4, 8, 128, 64, 128, 64, 2, 8,
+                         0) == tg.TG_ERR_NO_DEVICE
     for dtype in (tg.TG_DTYPE_F16, tg.TG_DTYPE_BF16):
         for layout in (tg.TG_B_KN, tg.TG_B_NK):
             st = tg.tg_gemm_ex(dtype, layout, tg.TG_ACT_NONE, P, P, P, 0, 4, 4, 4, 4, 4, 4, 0, 0,

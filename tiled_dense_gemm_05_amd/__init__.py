@@ -28,7 +28,8 @@ TG_PATH_GENERIC = 2
 TG_PATH_TILE128 = 3
 TG_PATH_TILE256 = 4
 TG_PATH_SKINNY = 5
-TG_PATH_COUNT = 6
+TG_PATH_W4 = 6
+TG_PATH_COUNT = 7
 
 EXPORTED_SYMBOLS = (
     "tg_gemm_relu_f16",
@@ -41,6 +42,7 @@ EXPORTED_SYMBOLS = (
     "tg_set_skinny_variant",
     "tg_set_raster",
     "tg_gemm_ex",
+    "tg_gemm_w4",
 )
 
 TG_DTYPE_F16 = 0
@@ -71,6 +73,8 @@ _lib.tg_gemm_relu_f16_strided_batched.argtypes = [_vp, _vp, _vp] + [_i64] * 10 +
 _lib.tg_gemm_relu_f16_strided_batched.restype = ctypes.c_int
 _lib.tg_gemm_ex.argtypes = [ctypes.c_int] * 3 + [_vp] * 4 + [_i64] * 10 + [_vp]
 _lib.tg_gemm_ex.restype = ctypes.c_int
+_lib.tg_gemm_w4.argtypes = [ctypes.c_int] * 2 + [_vp] * 5 + [_i64] * 8 + [_vp]
+_lib.tg_gemm_w4.restype = ctypes.c_int
 _lib.tg_status_string.argtypes = [ctypes.c_int]
 _lib.tg_status_string.restype = ctypes.c_char_p
 _lib.tg_set_path.argtypes = [ctypes.c_int]
@@ -110,6 +114,14 @@ def tg_gemm_ex(dtype: int, b_layout: int, activation: int, A: int, B: int, C: in
     """Raw extended call (bias may be 0 for none), returns the tg_status code."""
     return _lib.tg_gemm_ex(dtype, b_layout, activation, A, B, C, bias or None, M, N, K, lda, ldb,
                            ldc, strideA, strideB, strideC, batch, stream)
+
+
+def tg_gemm_w4(dtype: int, activation: int, A: int, Wq: int, scales: int, C: int, bias: int,
+               M: int, N: int, K: int, group_size: int, lda: int, ldw: int, lds: int, ldc: int,
+               stream: int = 0) -> int:
+    """Raw weight-only int4 call (bias may be 0 for none), returns the tg_status code."""
+    return _lib.tg_gemm_w4(dtype, activation, A, Wq, scales, C, bias or None, M, N, K,
+                           group_size, lda, ldw, lds, ldc, stream)
 
 
 def tg_status_string(status: int) -> str:

@@ -166,7 +166,7 @@ int run(const void *A, const void *B, void *C, const void *bias, bool relu, bool
     const int mode = p.bf16 | (p.b_nk << 1);
 
     int path = g_forced_path.load(std::memory_order_relaxed);
-    if (path == TG_PATH_AUTO)
+    if (path == TG_PATH_AUTO || path == TG_PATH_W4)
         path = choose_path(p);
     else if (path != TG_PATH_NAIVE && path != TG_PATH_GENERIC && !fast_layout(p))
         path = TG_PATH_GENERIC;
@@ -251,6 +251,53 @@ int tg_gemm_ex(int dtype, int b_layout, int activation, const void *A, const voi
                stream);
 }
 
+int tg_gemm_w4(int dtype, int activation, const void *A, const void *Wq, const void *scales,
+               void *C, const void *bias, int64_t M, int64_t N, int64_t K, int64_t group_size,
+               int64_t lda, int64_t ldw, int64_t lds, int64_t ldc, hipStream_t stream)
+{
+    if (dtype != TG_DTYPE_F16 && dtype != TG_DTYPE_BF16)
+        return TG_ERR_INVALID_ARG;
+    if (activation != TG_ACT_NONE && activation != TG_ACT_RELU)
+        return TG_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return TG_ERR_INVALID_ARG;
+    if (group_size <= 0 || group_size > kMaxDim || K % group_size != 0)
+        return TG_ERR_INVALID_ARG;
+    const int64_t groups = K / group_size;
+    if (lda < (K > 1 ? K : 1) || ldw < ((K + 1) / 2 > 1 ? (K + 1) / 2 : 1) ||
+        lds < (groups > 1 ? groups : 1) || ldc < (N > 1 ? N : 1))
+        return TG_ERR_INVALID_ARG;
+    if (M == 0 || N == 0)
+        return TG_OK;
+    if (C == nullptr || (K > 0 && (A == nullptr || Wq == nullptr || scales == nullptr)))
+        return TG_ERR_INVALID_ARG;
+    if (extent(M, K, lda, 0, 1) > kMaxExtent || extent(N, (K + 1) / 2, ldw, 0, 1) > kMaxExtent ||
+        extent(N, groups, lds, 0, 1) > kMaxExtent || extent(M, N, ldc, 0, 1) > kMaxExtent)
+        return TG_ERR_INVALID_ARG;
+    int st = check_device();
+    if (st != TG_OK)
+        return st;
+
+    tg::W4Args p;
+    p.A = static_cast<const uint16_t *>(A);
+    p.Wq = static_cast<const uint8_t *>(Wq);
+    p.S = static_cast<const uint16_t *>(scales);
+    p.C = static_cast<uint16_t *>(C);
+    p.bias = static_cast<const uint16_t *>(bias);
+    p.M = M; p.N = N; p.K = K; p.G = group_size;
+    p.lda = lda; p.ldw = ldw; p.lds = lds; p.ldc = ldc;
+    p.relu = activation == TG_ACT_RELU ? 1 : 0;
+    p.bf16 = dtype == TG_DTYPE_BF16 ? 1 : 0;
+
+    const int forced = g_forced_path.load(std::memory_order_relaxed);
+    const bool plain = forced == TG_PATH_NAIVE || forced == TG_PATH_GENERIC || !tg::w4_layout_ok(p);
+    const hipError_t e = plain ? tg::launch_w4_naive(p, stream) : tg::launch_w4(p, stream);
+    if (e != hipSuccess)
+        return TG_ERR_HIP;
+    g_last_path.store(plain ? TG_PATH_NAIVE : TG_PATH_W4, std::memory_order_relaxed);
+    return TG_OK;
+}
+
 const char *tg_status_string(int status)
 {
     switch (status) {
@@ -305,6 +352,7 @@ const char *tg_path_name(int path)
     case TG_PATH_TILE128: return "tile128";
     case TG_PATH_TILE256: return "tile256";
     case TG_PATH_SKINNY: return "skinny";
+    case TG_PATH_W4: return "w4";
     default: return "unknown";
     }
 }

@@ -103,6 +103,25 @@ __device__ __forceinline__ void tile_coords(int pid, int tilesM, int tilesN, int
     tn = in / gsz;
 }
 
+// One weight-only int4 problem: C = act(A * W + bias), W(k, n) =
+// S[n*lds + k/G] * q, q the signed nibble (k odd: high) of Wq[n*ldw + k/2]
+// (ldw in bytes, the rest in elements).
+struct W4Args {
+    const uint16_t *A;
+    const uint8_t *Wq;
+    const uint16_t *S;
+    uint16_t *C;
+    const uint16_t *bias;
+    int64_t M, N, K, G;
+    int64_t lda, ldw, lds, ldc;
+    int relu;
+    int bf16;
+    int scales_vec;   // set by launch_w4: scale rows 16-byte aligned, groups % 8 == 0
+};
+hipError_t launch_w4(const W4Args &p, hipStream_t stream);
+hipError_t launch_w4_naive(const W4Args &p, hipStream_t stream);
+bool w4_layout_ok(const W4Args &p);
+
 // Every launcher enqueues on `stream` and returns hipGetLastError().  The
 // tile launchers take the raster setting of tile_coords.
 hipError_t launch_naive(const GemmArgs &p, hipStream_t stream);
