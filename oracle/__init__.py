@@ -6,7 +6,8 @@ TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
 CPU-baseline leg may import this package.  It shares no code with the HIP
 library under ``tiled_dense_gemm_05_amd`` and never imports it.
 
-The arithmetic lives in ``gemm_relu_oracle.c`` (plain C, compiled with gcc,
+The arithmetic lives in ``gemm_relu_oracle.c`` and ``attention_oracle.c``
+(plain C, compiled with gcc,
 no BLAS, no SIMD intrinsics, no fast-math); this module only builds it, loads it
 with ctypes and marshals numpy arrays.  What it computes, and the passages it
 follows, are stated at the top of the C file: the matmul_relu tile program in
@@ -28,6 +29,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gemm_relu_oracle.c")
+_SRC_ATTN = os.path.join(_HERE, "attention_oracle.c")
 _LIB = os.path.join(_HERE, "_build", "liboracle.so")
 
 _lib = None
@@ -40,7 +42,7 @@ def build(force: bool = True) -> str:
     os.makedirs(os.path.dirname(_LIB), exist_ok=True)
     tmp = _LIB + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11",
-           "-D_GNU_SOURCE", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm", "-lpthread"]
+           "-D_GNU_SOURCE", "-fPIC", "-shared", "-o", tmp, _SRC, _SRC_ATTN, "-lm", "-lpthread"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB)
     return _LIB
@@ -80,6 +82,8 @@ def _load():
     lib.oracle_s4_decode_array.restype = None
     lib.oracle_gemm_w4.argtypes = [ci, ci, vp, vp, vp, vp, vp] + [i64] * 8 + [vp, vp, ci]
     lib.oracle_gemm_w4.restype = ctypes.c_int
+    lib.oracle_attention_f16.argtypes = [vp] * 4 + [i64] * 5 + [ctypes.c_double, ci, vp, vp, ci]
+    lib.oracle_attention_f16.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -378,3 +382,32 @@ def gemm_w4(A, Wq, S, M: int, N: int, K: int, G: int, lda: int | None = None,
     if want_sums:
         return C, Sm, Sa
     return C
+
+
+def attention(Q, K, V, B: int, Sq: int, Sk: int, H: int, D: int, scale: float,
+              causal: bool = False, want_stats: bool = False, threads: int | None = None):
+    """softmax(scale * Q K^T) V per (batch, head), fp16 bits laid out
+    (batch, seq, heads, head_dim); with ``causal`` key j is visible to query i
+    when j <= i + (Sk - Sq).  Returns O (uint16, B*Sq*H*D) and, with
+    ``want_stats``, each query's row maximum and sum of exponentials, shaped
+    (B, H, Sq)."""
+    Q = _u16(Q).reshape(-1)
+    K = _u16(K).reshape(-1)
+    V = _u16(V).reshape(-1)
+    for name, t, n in (("Q", Q, B * Sq * H * D), ("K", K, B * Sk * H * D), ("V", V, B * Sk * H * D)):
+        if t.size < n:
+            raise ValueError(f"{name} holds {t.size} elements, needs {n}")
+    O = np.zeros(B * Sq * H * D, dtype=np.uint16)
+    mx = sm = None
+    if want_stats:
+        mx = np.zeros((B, H, Sq), dtype=np.float64)
+        sm = np.zeros((B, H, Sq), dtype=np.float64)
+    rc = _load().oracle_attention_f16(
+        _ptr(Q), _ptr(K), _ptr(V), _ptr(O), B, Sq, Sk, H, D, float(scale), int(causal),
+        _ptr(mx) if mx is not None else None, _ptr(sm) if sm is not None else None,
+        host_threads() if threads is None else threads)
+    if rc != 0:
+        raise ValueError("bad attention sizes")
+    if want_stats:
+        return O, mx, sm
+    return O

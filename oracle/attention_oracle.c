@@ -1,0 +1,169 @@
+/*
+ * CPU oracle for the fused attention forward (scaled dot-product attention).
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may include, link or
+ * call this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header or table with the HIP
+ * library.
+ *
+ * The pages name fused attention kernels (FlashAttention, MLA) among the tile
+ * programs they measure ("TileLang paper reading" page, section 5; the
+ * "80-line MLA article" page) but give no formula.  The reading taken is the
+ * standard definition, written out: for every batch b, head h and query i,
+ *
+ *   s_j   = scale * sum_d Q[b][i][h][d] * K[b][j][h][d]     (binary64, d ascending)
+ *   keys j visible to i: all j < Sk, or with `causal` only j <= i + (Sk - Sq)
+ *   p_j   = exp(s_j - max_visible s) / sum_visible exp(s - max s)
+ *   O[b][i][h][d] = enc16( sum_j p_j * V[b][j][h][d] )      (binary64, j ascending)
+ *
+ * Q, K, V, O are fp16 (bit patterns), laid out (batch, seq, heads, head_dim)
+ * contiguously.  A query with no visible key (causal, Sk < Sq) gets O = 0.
+ * exp is the C library's binary64 exp.  The result is exact up to binary64
+ * rounding; the GPU kernel (fp32 scores and sums, an online maximum,
+ * exp2-based exponentials, fp16 probabilities) is expected to agree within a
+ * tolerance derived from those steps.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <unistd.h>
+
+static double a_dec16(uint16_t h)
+{
+    int sign = h >> 15, e = (h >> 10) & 0x1f, m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);
+    else if (e < 31)
+        v = ldexp((double)(1024 + m), e - 25);
+    else
+        v = m ? NAN : INFINITY;
+    return sign ? -v : v;
+}
+
+static double a_rhe(double q)
+{
+    double f = floor(q), d = q - f;
+    if (d > 0.5)
+        return f + 1.0;
+    if (d < 0.5)
+        return f;
+    return fmod(f, 2.0) == 0.0 ? f : f + 1.0;
+}
+
+static uint16_t a_enc16(double x)
+{
+    if (isnan(x))
+        return 0x7e00;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (a >= 65520.0)
+        return sign | 0x7c00;
+    if (a < ldexp(1.0, -14))
+        return sign | (uint16_t)a_rhe(ldexp(a, 24));
+    int e;
+    frexp(a, &e);
+    double q = a_rhe(ldexp(a, 11 - e));
+    return sign | (uint16_t)(((uint32_t)(e + 14) << 10) + ((uint32_t)q - 1024u));
+}
+
+typedef struct {
+    const uint16_t *Q, *K, *V;
+    uint16_t *O;
+    double *rowmax, *rowsum;   /* optional, [b][h][i] */
+    int64_t B, Sq, Sk, H, D;
+    double scale;
+    int causal, nthreads, tid;
+} ajob_t;
+
+static void *attn_worker(void *p)
+{
+    ajob_t *j = (ajob_t *)p;
+    const int64_t D = j->D, Sk = j->Sk, H = j->H;
+    double *q = (double *)malloc(sizeof(double) * (size_t)D);
+    double *s = (double *)malloc(sizeof(double) * (size_t)(Sk > 0 ? Sk : 1));
+    double *o = (double *)malloc(sizeof(double) * (size_t)D);
+    const int64_t rows = j->B * H * j->Sq;
+    for (int64_t r = j->tid; r < rows; r += j->nthreads) {
+        const int64_t b = r / (H * j->Sq), h = (r / j->Sq) % H, i = r % j->Sq;
+        for (int64_t d = 0; d < D; ++d)
+            q[d] = a_dec16(j->Q[((b * j->Sq + i) * H + h) * D + d]);
+        int64_t visible = Sk;
+        if (j->causal) {
+            visible = i + (Sk - j->Sq) + 1;
+            if (visible < 0)
+                visible = 0;
+            if (visible > Sk)
+                visible = Sk;
+        }
+        double mx = -INFINITY;
+        for (int64_t k = 0; k < visible; ++k) {
+            const uint16_t *kr = j->K + ((b * Sk + k) * H + h) * D;
+            double acc = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                acc += q[d] * a_dec16(kr[d]);
+            s[k] = j->scale * acc;
+            if (s[k] > mx)
+                mx = s[k];
+        }
+        double sum = 0.0;
+        for (int64_t k = 0; k < visible; ++k) {
+            s[k] = exp(s[k] - mx);
+            sum += s[k];
+        }
+        for (int64_t d = 0; d < D; ++d)
+            o[d] = 0.0;
+        for (int64_t k = 0; k < visible; ++k) {
+            const uint16_t *vr = j->V + ((b * Sk + k) * H + h) * D;
+            const double pk = s[k] / sum;
+            for (int64_t d = 0; d < D; ++d)
+                o[d] += pk * a_dec16(vr[d]);
+        }
+        for (int64_t d = 0; d < D; ++d)
+            j->O[((b * j->Sq + i) * H + h) * D + d] = a_enc16(o[d]);
+        if (j->rowmax) {
+            j->rowmax[(b * H + h) * j->Sq + i] = mx;
+            j->rowsum[(b * H + h) * j->Sq + i] = sum;
+        }
+    }
+    free(q);
+    free(s);
+    free(o);
+    return NULL;
+}
+
+/* Returns 0, or -2 for a bad size. */
+int oracle_attention_f16(const uint16_t *Q, const uint16_t *K, const uint16_t *V, uint16_t *O,
+                         int64_t B, int64_t Sq, int64_t Sk, int64_t H, int64_t D, double scale,
+                         int causal, double *rowmax, double *rowsum, int nthreads)
+{
+    if (B < 0 || Sq < 0 || Sk < 0 || H < 0 || D <= 0)
+        return -2;
+    if (nthreads <= 0) {
+        long n = sysconf(_SC_NPROCESSORS_ONLN);
+        nthreads = n > 0 ? (int)n : 1;
+    }
+    if (nthreads > 256)
+        nthreads = 256;
+    const int64_t rows = B * H * Sq;
+    if (rows == 0)
+        return 0;
+    int nt = (int)(rows < nthreads ? rows : nthreads);
+    pthread_t th[256];
+    ajob_t jobs[256];
+    for (int t = 0; t < nt; ++t) {
+        ajob_t *j = &jobs[t];
+        j->Q = Q; j->K = K; j->V = V; j->O = O; j->rowmax = rowmax; j->rowsum = rowsum;
+        j->B = B; j->Sq = Sq; j->Sk = Sk; j->H = H; j->D = D; j->scale = scale;
+        j->causal = causal; j->nthreads = nt; j->tid = t;
+        if (nt == 1)
+            attn_worker(j);
+        else
+            pthread_create(&th[t], NULL, attn_worker, j);
+    }
+    if (nt > 1)
+        for (int t = 0; t < nt; ++t)
+            pthread_join(th[t], NULL);
+    return 0;
+}
