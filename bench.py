@@ -199,6 +199,39 @@ def run_w4(tg, torch, M: int, N: int, K: int, G: int, steps: int, warmup: int, d
     return ms, tg.tg_path_name(tg.tg_last_path()), nbuf, wbytes + 2 * (M * K + M * N)
 
 
+def run_attention(tg, torch, B: int, S: int, H: int, D: int, causal: bool, steps: int,
+                  warmup: int):
+    """Times the fused attention forward (tg_attention_fwd_f16) on (B, S, H, D)
+    queries, keys and values with normal(0,1) Q and K, uniform(-1,1) V."""
+    rng = np.random.default_rng(11)
+    dev = torch.device("cuda:0")
+    n = B * S * H * D
+    Q, K, V = (torch.from_numpy(wl.to_f16_bits(rng.normal(0, 1, n) if i < 2 else
+                                               rng.uniform(-1, 1, n)).view(np.int16)).to(dev)
+               for i in range(3))
+    O = torch.empty(n, dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+    scale = 1.0 / float(np.sqrt(D))
+
+    def call():
+        st = tg.tg_attention_fwd_f16(Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), B,
+                                     S, S, H, D, scale, int(causal), stream.cuda_stream)
+        if st != tg.TG_OK:
+            raise RuntimeError(tg.tg_status_string(st))
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        call()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
 def cpu_baseline(w: wl.Workload, target_s: float = 12.0):
     """The oracle, as it stands, on the host cores: rows 0..r-1 of the
     workload's C (all N columns, full K), r sized for about target_s seconds."""
@@ -409,6 +442,9 @@ def main():
                     help="element type (bf16: through tg_gemm_ex)")
     ap.add_argument("--layout", choices=["kn", "nk"], default="kn",
                     help="B stored (K,N) or (N,K) (nk: through tg_gemm_ex)")
+    ap.add_argument("--attention", choices=["full", "causal"], default=None,
+                    help="time the fused attention forward on 4 x 4096 x 32 heads x 128 "
+                         "(tg_attention_fwd_f16) and exit")
     ap.add_argument("--w4", action="store_true",
                     help="time the weight-only int4 GEMM on the decode shape "
                          "16 x 16384 x 8192, groups of 128 (tg_gemm_w4) and exit")
@@ -443,6 +479,27 @@ def main():
         knobs["b_layout"] = args.layout
     if args.calibrate_copy:
         calibration_copy(torch)
+    if args.attention:
+        B, S, H, D = 4, 4096, 32, 128
+        causal = args.attention == "causal"
+        ms = run_attention(tg, torch, B, S, H, D, causal, args.steps, args.warmup)
+        # two products of 2*S*S*D flop per (batch, head); half the pairs when causal
+        flops = 4.0 * B * H * S * S * D * (0.5 if causal else 1.0)
+        tflops = flops / (ms * 1e-3) / 1e12
+        log(f"attention {B}x{S}x{H}x{D} {args.attention}: {ms * 1e3:.1f} us/call, "
+            f"{tflops:.1f} TFLOP/s")
+        print(json.dumps({
+            "metric": "TFLOP/s fused attention forward", "value": tflops, "unit": "TFLOP/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+            "data": "synthetic",
+            "config": {"workload": f"attention_{B}x{S}x{H}x{D}_{args.attention}", "batch": B,
+                       "seq": S, "heads": H, "head_dim": D, "causal": causal,
+                       "path": tg.tg_path_name(tg.tg_last_path())},
+            "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_F16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tflops / PEAK_F16_TFLOPS,
+                         "traffic": None}}), flush=True)
+        return
     if args.w4:
         M, N, K, G = 16, 16384, 8192, 128
         ms, path, nbuf, nbytes = run_w4(tg, torch, M, N, K, G, args.steps, args.warmup,

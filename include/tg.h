@@ -160,6 +160,32 @@ int tg_gemm_w4(int dtype, int activation, const void *A, const void *Wq, const v
                void *C, const void *bias, int64_t M, int64_t N, int64_t K, int64_t group_size,
                int64_t lda, int64_t ldw, int64_t lds, int64_t ldc, hipStream_t stream);
 
+/*
+ * Fused attention forward (softmax attention), fp16:
+ *
+ *   O[b][i][h][:] = sum_j p_ij V[b][j][h][:],
+ *   p_ij = exp(s_ij - max_j s_ij) / sum_j exp(s_ij - max_j s_ij),
+ *   s_ij = scale * sum_d Q[b][i][h][d] K[b][j][h][d]
+ *
+ * over the keys j visible to query i: all j < seq_k, or with causal = 1 only
+ * j <= i + (seq_k - seq_q) (a query with no visible key gets O = 0).  The
+ * pages name fused attention kernels (FlashAttention, MLA decode) among the
+ * tile programs they measure ("TileLang paper reading" page, section 5; the
+ * "80-line MLA article" page) without their formulas: this is the standard
+ * definition, computed in one pass with a running maximum.
+ *   Q, O  (batch, seq_q, heads, head_dim) fp16, contiguous, DEVICE pointers
+ *   K, V  (batch, seq_k, heads, head_dim) fp16, contiguous, DEVICE pointers
+ *   head_dim 64 or 128; heads <= 65535 and heads * head_dim < 2^24;
+ *   all four pointers 16-byte aligned; scale finite (e.g. 1/sqrt(head_dim)).
+ * Scores and sums are fp32, probabilities enter the value product as fp16
+ * (the products with V are accumulated in fp32).  Errors, asynchrony and
+ * determinism as for the other entry points; batch, seq_q or heads = 0 is a
+ * no-op; seq_k = 0 writes zeros.
+ */
+int tg_attention_fwd_f16(const void *Q, const void *K, const void *V, void *O,
+                         int64_t batch, int64_t seq_q, int64_t seq_k, int64_t heads,
+                         int64_t head_dim, float scale, int causal, hipStream_t stream);
+
 /* A static, human-readable name for a tg_status value. */
 const char *tg_status_string(int status);
 
@@ -178,7 +204,8 @@ enum {
     TG_PATH_TILE256 = 4,    /* 256x256 tiles for large shapes, aligned operands */
     TG_PATH_SKINNY = 5,     /* M <= 64: column slices streaming B, K split over waves */
     TG_PATH_W4 = 6,         /* tg_gemm_w4's int4-weight kernel (reported, not forced) */
-    TG_PATH_COUNT = 7
+    TG_PATH_ATTENTION = 7,  /* tg_attention_fwd_f16's kernel (reported, not forced) */
+    TG_PATH_COUNT = 8
 };
 int tg_set_path(int path);
 

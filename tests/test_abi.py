@@ -153,6 +153,24 @@ def test_w4_validation(tg):
     assert tg.tg_path_name(tg.TG_PATH_W4) == "w4"
 
 
+def test_attention_validation(tg):
+    f = tg.tg_attention_fwd_f16
+
+    def call(Q=P, B=1, Sq=8, Sk=8, H=2, D=128, scale=0.1, causal=0):
+        return f(Q, P, P, P, B, Sq, Sk, H, D, scale, causal, 0)
+
+    assert call(D=96) == tg.TG_ERR_INVALID_ARG          # head_dim 64 or 128
+    assert call(Q=P + 2) == tg.TG_ERR_INVALID_ARG       # 16-byte alignment
+    assert call(causal=2) == tg.TG_ERR_INVALID_ARG
+    assert call(H=70000) == tg.TG_ERR_INVALID_ARG
+    assert call(H=1 << 17) == tg.TG_ERR_INVALID_ARG
+    assert call(Sq=-1) == tg.TG_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == tg.TG_ERR_INVALID_ARG
+    assert call(Q=0) == tg.TG_ERR_INVALID_ARG
+    assert call(B=0) == tg.TG_OK and call(Sq=0) == tg.TG_OK and call(H=0) == tg.TG_OK
+    assert tg.tg_path_name(tg.TG_PATH_ATTENTION) == "attention"
+
+
 def _gpu_visible():
     try:
         import torch
@@ -170,6 +188,7 @@ def test_valid_call_without_device_reports_no_device(tg):
     assert st == tg.TG_ERR_NO_DEVICE
     assert tg.tg_gemm_w4(0, 1, P, P, P, P, 0, 4, 8, 128, 64, 128, 64, 2, 8,
                          0) == tg.TG_ERR_NO_DEVICE
+    assert tg.tg_attention_fwd_f16(P, P, P, P, 1, 8, 8, 2, 64, 0.1, 1, 0) == tg.TG_ERR_NO_DEVICE
     for dtype in (tg.TG_DTYPE_F16, tg.TG_DTYPE_BF16):
         for layout in (tg.TG_B_KN, tg.TG_B_NK):
             st = tg.tg_gemm_ex(dtype, layout, tg.TG_ACT_NONE, P, P, P, 0, 4, 4, 4, 4, 4, 4, 0, 0,

@@ -1,0 +1,144 @@
+"""GPU parity of the fused attention forward (tg_attention_fwd_f16) against the
+CPU oracle, through the C ABI.
+
+Tolerance, from the kernel's arithmetic: scores and sums are fp32 (their
+error is far below the rest), each probability is rounded to fp16 before the
+value product (relative error <= 2^-11, so the output moves by at most
+2^-11 * max|V| from the probabilities and as much again from the normalizer
+built from the unrounded ones), and the output is rounded to fp16 once:
+|O_gpu - O_ref| <= 2^-9 * max|V| + ulp16(O_ref), with a 2x margin.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def tg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tiled_dense_gemm_05_amd as tg
+    return tg
+
+
+def dev(bits) -> "torch.Tensor":
+    x = np.asarray(bits, dtype=np.uint16).reshape(-1)
+    return torch.from_numpy(x.view(np.int16).copy()).to("cuda")
+
+
+def host(t) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def f16(x):
+    return np.asarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def v16(b):
+    return np.asarray(b, np.uint16).view(np.float16).astype(np.float64)
+
+
+def qkv(B, Sq, Sk, H, D, seed, spread=1.0):
+    rng = np.random.default_rng(40_000 + seed)
+    q = f16(rng.normal(0, spread, B * Sq * H * D))
+    k = f16(rng.normal(0, spread, B * Sk * H * D))
+    v = f16(rng.uniform(-1, 1, B * Sk * H * D))
+    return q, k, v
+
+
+def check(got, ref, v):
+    g, r = v16(got), v16(ref)
+    assert not np.any(np.isnan(g)), "NaN in the output"
+    vmax = np.abs(v16(v)).max() if v.size else 0.0
+    ulp = np.spacing(np.abs(r).astype(np.float16)).astype(np.float64)
+    err = np.abs(g - r)
+    bound = 2.0 ** -9 * vmax + ulp
+    bad = int((err > bound).sum())
+    assert bad == 0, f"{bad} outputs beyond the bound, max err {err.max():.3g}"
+
+
+def run(tg, q, k, v, B, Sq, Sk, H, D, scale, causal):
+    q_d, k_d, v_d = dev(q), dev(k) if k.size else dev(np.zeros(8)), dev(v) if v.size else dev(np.zeros(8))
+    o_d = dev(np.full(B * Sq * H * D + 64, 0x7E00, np.uint16))
+    st = tg.tg_attention_fwd_f16(q_d.data_ptr(), k_d.data_ptr(), v_d.data_ptr(), o_d.data_ptr(),
+                                 B, Sq, Sk, H, D, scale, int(causal),
+                                 torch.cuda.current_stream().cuda_stream)
+    assert st == tg.TG_OK, tg.tg_status_string(st)
+    torch.cuda.synchronize()
+    out = host(o_d)
+    assert np.all(out[B * Sq * H * D:] == 0x7E00), "wrote past O"
+    assert tg.tg_path_name(tg.tg_last_path()) == "attention"
+    return out[:B * Sq * H * D]
+
+
+CASES = [
+    (1, 128, 128, 1, 128, False), (2, 200, 333, 3, 64, False), (1, 256, 256, 2, 128, True),
+    (2, 77, 300, 2, 128, True), (1, 300, 77, 1, 64, True), (1, 1, 4096, 4, 128, False),
+    (3, 130, 1, 2, 64, False), (1, 64, 0, 1, 128, False), (1, 129, 129, 1, 64, True),
+    (2, 33, 65, 5, 128, False),
+]
+
+
+@pytest.mark.parametrize("B,Sq,Sk,H,D,causal", CASES)
+def test_attention_matches_oracle(tg, oracle_lib, B, Sq, Sk, H, D, causal):
+    q, k, v = qkv(B, Sq, Sk, H, D, Sq + Sk + D)
+    scale = 1.0 / np.sqrt(D)
+    ref = oracle_lib.attention(q, k, v, B, Sq, Sk, H, D, scale, causal)
+    say(f"attention B={B} Sq={Sq} Sk={Sk} H={H} D={D} causal={causal}")
+    got = run(tg, q, k, v, B, Sq, Sk, H, D, scale, causal)
+    check(got, ref, v)
+
+
+@pytest.mark.parametrize("spread,scale", [(3.0, 0.5), (0.01, 1.0), (1.0, 4.0)])
+def test_sharp_and_flat_softmax(tg, oracle_lib, spread, scale):
+    # peaked (large scores: exp2 underflow, one dominant key), flat (nearly
+    # uniform weights), and in between
+    B, Sq, Sk, H, D = 1, 192, 320, 2, 128
+    q, k, v = qkv(B, Sq, Sk, H, D, 7, spread=spread)
+    ref = oracle_lib.attention(q, k, v, B, Sq, Sk, H, D, scale, False)
+    say(f"attention spread={spread} scale={scale}")
+    check(run(tg, q, k, v, B, Sq, Sk, H, D, scale, False), ref, v)
+
+
+def test_deterministic(tg, oracle_lib):
+    B, Sq, Sk, H, D = 2, 300, 500, 2, 128
+    q, k, v = qkv(B, Sq, Sk, H, D, 9)
+    say("attention determinism")
+    a = run(tg, q, k, v, B, Sq, Sk, H, D, 0.1, True)
+    b = run(tg, q, k, v, B, Sq, Sk, H, D, 0.1, True)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_benchmark_shape_sampled(tg, oracle_lib, causal):
+    # the benchmark shape 4 x 4096 x 32 heads x 128: the oracle computes two
+    # (batch, head) slices at 64-query windows at the start and the end
+    B, S, H, D = 4, 4096, 32, 128
+    rng = np.random.default_rng(11)
+    q = f16(rng.normal(0, 1, B * S * H * D))
+    k = f16(rng.normal(0, 1, B * S * H * D))
+    v = f16(rng.uniform(-1, 1, B * S * H * D))
+    scale = 1.0 / np.sqrt(D)
+    say(f"attention benchmark shape causal={causal}")
+    out = run(tg, q, k, v, B, S, S, H, D, scale, causal).reshape(B, S, H, D)
+    Q, K, V = (t.reshape(B, S, H, D) for t in (q, k, v))
+    for b, h in ((0, 0), (3, 31)):
+        for s0 in (0, S - 64):
+            n = 64
+            sl_q = np.ascontiguousarray(Q[b, s0:s0 + n, h]).reshape(-1)
+            nk = s0 + n if causal else S                  # keys the window can see
+            sl_k = np.ascontiguousarray(K[b, :nk, h]).reshape(-1)
+            sl_v = np.ascontiguousarray(V[b, :nk, h]).reshape(-1)
+            ref = oracle_lib.attention(sl_q, sl_k, sl_v, 1, n, nk, 1, D, scale, causal)
+            check(np.ascontiguousarray(out[b, s0:s0 + n, h]).reshape(-1), ref, sl_v)

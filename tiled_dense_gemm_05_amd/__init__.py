@@ -29,7 +29,8 @@ TG_PATH_TILE128 = 3
 TG_PATH_TILE256 = 4
 TG_PATH_SKINNY = 5
 TG_PATH_W4 = 6
-TG_PATH_COUNT = 7
+TG_PATH_ATTENTION = 7
+TG_PATH_COUNT = 8
 
 EXPORTED_SYMBOLS = (
     "tg_gemm_relu_f16",
@@ -43,6 +44,7 @@ EXPORTED_SYMBOLS = (
     "tg_set_raster",
     "tg_gemm_ex",
     "tg_gemm_w4",
+    "tg_attention_fwd_f16",
 )
 
 TG_DTYPE_F16 = 0
@@ -75,6 +77,8 @@ _lib.tg_gemm_ex.argtypes = [ctypes.c_int] * 3 + [_vp] * 4 + [_i64] * 10 + [_vp]
 _lib.tg_gemm_ex.restype = ctypes.c_int
 _lib.tg_gemm_w4.argtypes = [ctypes.c_int] * 2 + [_vp] * 5 + [_i64] * 8 + [_vp]
 _lib.tg_gemm_w4.restype = ctypes.c_int
+_lib.tg_attention_fwd_f16.argtypes = [_vp] * 4 + [_i64] * 5 + [ctypes.c_float, ctypes.c_int, _vp]
+_lib.tg_attention_fwd_f16.restype = ctypes.c_int
 _lib.tg_status_string.argtypes = [ctypes.c_int]
 _lib.tg_status_string.restype = ctypes.c_char_p
 _lib.tg_set_path.argtypes = [ctypes.c_int]
@@ -122,6 +126,14 @@ def tg_gemm_w4(dtype: int, activation: int, A: int, Wq: int, scales: int, C: int
     """Raw weight-only int4 call (bias may be 0 for none), returns the tg_status code."""
     return _lib.tg_gemm_w4(dtype, activation, A, Wq, scales, C, bias or None, M, N, K,
                            group_size, lda, ldw, lds, ldc, stream)
+
+
+def tg_attention_fwd_f16(Q: int, K: int, V: int, O: int, batch: int, seq_q: int, seq_k: int,
+                         heads: int, head_dim: int, scale: float, causal: int,
+                         stream: int = 0) -> int:
+    """Raw attention-forward call, returns the tg_status code."""
+    return _lib.tg_attention_fwd_f16(Q, K, V, O, batch, seq_q, seq_k, heads, head_dim, scale,
+                                     causal, stream)
 
 
 def tg_status_string(status: int) -> str:

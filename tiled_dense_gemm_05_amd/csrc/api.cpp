@@ -166,7 +166,7 @@ int run(const void *A, const void *B, void *C, const void *bias, bool relu, bool
     const int mode = p.bf16 | (p.b_nk << 1);
 
     int path = g_forced_path.load(std::memory_order_relaxed);
-    if (path == TG_PATH_AUTO || path == TG_PATH_W4)
+    if (path == TG_PATH_AUTO || path == TG_PATH_W4 || path == TG_PATH_ATTENTION)
         path = choose_path(p);
     else if (path != TG_PATH_NAIVE && path != TG_PATH_GENERIC && !fast_layout(p))
         path = TG_PATH_GENERIC;
@@ -298,6 +298,46 @@ int tg_gemm_w4(int dtype, int activation, const void *A, const void *Wq, const v
     return TG_OK;
 }
 
+int tg_attention_fwd_f16(const void *Q, const void *K, const void *V, void *O, int64_t batch,
+                         int64_t seq_q, int64_t seq_k, int64_t heads, int64_t head_dim,
+                         float scale, int causal, hipStream_t stream)
+{
+    if (batch < 0 || seq_q < 0 || seq_k < 0 || heads < 0 || batch > kMaxDim ||
+        seq_q > kMaxDim || seq_k > kMaxDim || heads > 65535)
+        return TG_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128)
+        return TG_ERR_INVALID_ARG;
+    if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f || (causal != 0 && causal != 1))
+        return TG_ERR_INVALID_ARG;
+    if (heads * head_dim >= (1 << 24))
+        return TG_ERR_INVALID_ARG;
+    if (batch == 0 || seq_q == 0 || heads == 0)
+        return TG_OK;
+    if (Q == nullptr || O == nullptr || (seq_k > 0 && (K == nullptr || V == nullptr)))
+        return TG_ERR_INVALID_ARG;
+    if (!aligned16(Q) || !aligned16(O) || (seq_k > 0 && (!aligned16(K) || !aligned16(V))))
+        return TG_ERR_INVALID_ARG;
+    const __int128 rows_q = (__int128)batch * seq_q * heads * head_dim;
+    const __int128 rows_k = (__int128)batch * seq_k * heads * head_dim;
+    if (rows_q > kMaxExtent || rows_k > kMaxExtent)
+        return TG_ERR_INVALID_ARG;
+    int st = check_device();
+    if (st != TG_OK)
+        return st;
+    tg::AttnArgs p;
+    p.Q = static_cast<const uint16_t *>(Q);
+    p.K = static_cast<const uint16_t *>(K);
+    p.V = static_cast<const uint16_t *>(V);
+    p.O = static_cast<uint16_t *>(O);
+    p.B = batch; p.Sq = seq_q; p.Sk = seq_k; p.H = heads; p.D = head_dim;
+    p.scale = scale;
+    p.causal = causal;
+    if (tg::launch_attention(p, stream) != hipSuccess)
+        return TG_ERR_HIP;
+    g_last_path.store(TG_PATH_ATTENTION, std::memory_order_relaxed);
+    return TG_OK;
+}
+
 const char *tg_status_string(int status)
 {
     switch (status) {
@@ -353,6 +393,7 @@ const char *tg_path_name(int path)
     case TG_PATH_TILE256: return "tile256";
     case TG_PATH_SKINNY: return "skinny";
     case TG_PATH_W4: return "w4";
+    case TG_PATH_ATTENTION: return "attention";
     default: return "unknown";
     }
 }

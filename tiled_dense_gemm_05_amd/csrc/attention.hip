@@ -1,0 +1,334 @@
+// Fused attention forward on gfx950: O = softmax(scale * Q K^T) V per batch
+// and head, fp16 in and out, one pass over K and V (online softmax).
+//
+// The pages name fused attention (FlashAttention, MLA decode) among the tile
+// programs they measure ("TileLang paper reading" page, section 5; the
+// "80-line MLA article" page, sections 1-2) without giving the algorithm;
+// this kernel reuses the GEMM's tile machinery for the standard one-pass
+// form: per query block, walk the key/value tiles, keep a running maximum
+// and sum of exponentials per query, rescale the output accumulator when the
+// maximum grows, divide once at the end.
+//
+// Layout: Q (B, Sq, H, D), K and V (B, Sk, H, D), O (B, Sq, H, D), each
+// contiguous; D = 64 or 128.  Key j is visible to query i always, or with
+// `causal` when j <= i + (Sk - Sq).
+//
+// gfx950 design:
+//  * One workgroup of four waves per 128 queries of one (batch, head); wave w
+//    owns queries 32w .. 32w+31.  K/V tiles of 64 keys are staged in a
+//    2-stage LDS ring by buffer_load_dwordx4 ... lds (rows past Sk read as
+//    zeros and are masked out of the softmax).
+//  * Both products run on v_mfma_f32_32x32x16_f16 with the operand roles
+//    swapped as in the GEMM kernels: S^T = K Q^T and O^T = V^T P^T.  A lane
+//    then holds 32 scores (and, later, 4-column groups of the output) of ONE
+//    query, so the softmax statistics need one cross-lane exchange (the lane
+//    32 apart holds the query's other keys) and the probabilities, packed to
+//    fp16, are already the second operand of the P V product: the key order
+//    inside a 16-key step is permuted identically on both operands (the V^T
+//    fragments come from transpose reads that fetch exactly those keys).
+//  * Q fragments stay in registers for the whole walk; scores use exp2 with
+//    scale * log2(e) folded in.
+#include "tg_internal.h"
+
+namespace tg {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) f16x8 lds_f16x8;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kBQ = 128;   // queries per workgroup (4 waves x 32)
+constexpr int kBK = 64;    // keys per tile
+
+template <int D_>
+struct AttnCfg {
+    static constexpr int D = D_;
+    static constexpr int CD = D / 8;                 // 16-byte chunks per row
+    static constexpr int TILE = kBK * D;             // fp16 elements of a K (or V) tile
+    static constexpr int STAGE = 2 * TILE;           // K then V
+    static constexpr int LDS = 2 * STAGE * 2;        // two stages, bytes
+    static constexpr int RPB = 64 / CD;              // rows per 1 KiB block
+    static constexpr int LD = TILE / 512 / 4;        // 1 KiB blocks per wave per tile
+    static constexpr int DS = D / 16;                // 16-wide d steps
+    static constexpr int DB = D / 32;                // 32-wide d blocks of the output
+    static_assert(D == 64 || D == 128, "head dim");
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt");
+    constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(imm);
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void block_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((3 << 14) | (0 << 8) | (7 << 4) | 15);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ i32x4 make_rsrc(const void *base)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+    r.z = (int)kOutOfRange;
+    r.w = 0x00020000;
+    return r;
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %2\n\t"
+                 "s_nop 0\n\t"
+                 "buffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(lds_addr)
+                 : "m0");
+}
+#pragma clang diagnostic pop
+
+// K tile rows (keys) are read as 16-byte chunks by 32 lanes of consecutive
+// rows: XOR the chunk with the row.  V tile rows are read by transpose reads
+// of 4 consecutive rows: move those rows to different quarters of the bank
+// line (256-byte rows: XOR with the row's position in the 4; 128-byte rows,
+// two to a bank line: XOR with its second bit).  Both stay inside the row.
+template <int CD>
+__device__ __forceinline__ int swz_k(int row, int c) { return c ^ (row % CD); }
+template <int CD>
+__device__ __forceinline__ int swz_v(int row, int c)
+{
+    if constexpr (CD >= 16)
+        return c ^ ((row & 3) << 2);
+    else
+        return c ^ (((row >> 1) & 1) << 2);
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) attention_fwd_kernel(AttnArgs p)
+{
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[T::LDS / 2];
+    const lds_u16 *lds = (const lds_u16 *)smem;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t bh = blockIdx.y;
+    const int64_t b = bh / p.H, h = bh % p.H;
+    const int64_t Sq = p.Sq, Sk = p.Sk;
+    const int64_t q0 = (int64_t)blockIdx.x * kBQ;
+    const int64_t rs = p.H * T::D;                   // elements between sequence positions
+    const int64_t q = q0 + wave * 32 + (lane & 31);  // this lane's query
+    const int hi = lane >> 5;
+
+    // Keys this block needs: all, or with the causal mask up to the block's
+    // last query's horizon.
+    int64_t kend = Sk;
+    if (p.causal) {
+        const int64_t lim = q0 + kBQ + (Sk - Sq);
+        kend = lim < 0 ? 0 : (lim < Sk ? lim : Sk);
+    }
+    const int tiles = (int)((kend + kBK - 1) / kBK);
+
+    // Q^T fragments (second operand): lane holds Q[q][16 ds + 8 hi .. + 7].
+    f16x8 qf[T::DS];
+    {
+        const uint16_t *qrow = p.Q + ((b * Sq + (q < Sq ? q : 0)) * p.H + h) * T::D;
+#pragma unroll
+        for (int ds = 0; ds < T::DS; ++ds) {
+            qf[ds] = f16x8{};
+            if (q < Sq)
+                qf[ds] = *reinterpret_cast<const f16x8 *>(qrow + ds * 16 + 8 * hi);
+        }
+    }
+
+    // DMA plan: a K (or V) tile is 64 rows of D fp16; wave w moves 1 KiB
+    // blocks w, w + 4, ...: lane L -> row blk * RPB + L / CD, physical chunk
+    // L % CD, which holds the swizzled logical chunk.
+    uint32_t k_voff[T::LD], v_voff[T::LD];
+    int k_row[T::LD];
+#pragma unroll
+    for (int i = 0; i < T::LD; ++i) {
+        const int blk = wave + 4 * i;
+        const int row = blk * T::RPB + lane / T::CD;
+        const int pc = lane % T::CD;
+        k_row[i] = row;
+        k_voff[i] = (uint32_t)((row * rs + swz_k<T::CD>(row, pc) * 8) * 2);
+        v_voff[i] = (uint32_t)((row * rs + swz_v<T::CD>(row, pc) * 8) * 2);
+    }
+    const uint16_t *Kb = p.K + (b * Sk * p.H + h) * T::D;
+    const uint16_t *Vb = p.V + (b * Sk * p.H + h) * T::D;
+    auto issue = [&](int t) {
+        const int64_t k0 = (int64_t)t * kBK;
+        const i32x4 rk = make_rsrc(Kb + k0 * rs);
+        const i32x4 rv = make_rsrc(Vb + k0 * rs);
+        const uint32_t base = lds_base + (uint32_t)((t & 1) * T::STAGE * 2);
+#pragma unroll
+        for (int i = 0; i < T::LD; ++i) {
+            const bool ok = k0 + k_row[i] < kend;
+            dma16(rk, ok ? k_voff[i] : kOutOfRange, base + (uint32_t)((wave + 4 * i) * 1024));
+            dma16(rv, ok ? v_voff[i] : kOutOfRange,
+                  base + (uint32_t)(T::TILE * 2 + (wave + 4 * i) * 1024));
+        }
+    };
+
+    f32x16 acc_o[T::DB];
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db)
+        acc_o[db] = f32x16{};
+    // running maximum (in log2 units, finite so a fully masked tile leaves it
+    // unchanged) and this lane's share of the sum of exponentials
+    float m_run = -1.0e30f, l_run = 0.0f;
+    const float sl2 = p.scale * 1.44269504088896340736f;   // scale * log2(e)
+    const int64_t horizon = q + (Sk - Sq);                 // causal: last visible key
+
+    if (tiles > 0)
+        issue(0);
+    for (int t = 0; t < tiles; ++t) {
+        wait_vmcnt<0>();      // tile t has landed (this wave's part)
+        block_barrier();      // ... every wave's part; tile t-1's stage is free
+        if (t + 1 < tiles)
+            issue(t + 1);
+        const lds_u16 *Ks = lds + (t & 1) * T::STAGE;
+        const lds_u16 *Vs = Ks + T::TILE;
+        const int64_t k0 = (int64_t)t * kBK;
+
+        // S^T = K Q^T: two 32-key blocks; lane: query q, keys
+        // k0 + 32 kb + 8 (r / 4) + 4 hi + r % 4 for register r.
+        f32x16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = f32x16{};
+            const int row = kb * 32 + (lane & 31);
+#pragma unroll
+            for (int ds = 0; ds < T::DS; ++ds) {
+                const int c = ds * 2 + hi;
+                const f16x8 kf = *reinterpret_cast<const lds_f16x8 *>(
+                    Ks + row * T::D + swz_k<T::CD>(row, c) * 8);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ds], s[kb], 0, 0, 0);
+            }
+        }
+        // scale to log2 units, mask invisible keys, this tile's maximum
+        float mt = -1.0e30f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t key = k0 + kb * 32 + 8 * (r / 4) + 4 * hi + (r % 4);
+                const bool vis = key < kend && (!p.causal || key <= horizon);
+                const float v = vis ? s[kb][r] * sl2 : -__builtin_inff();
+                s[kb][r] = v;
+                mt = v > mt ? v : mt;
+            }
+        }
+        const float mo = __shfl_xor(mt, 32);
+        mt = mo > mt ? mo : mt;
+        const float m_new = mt > m_run ? mt : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db)
+            acc_o[db] *= alpha;
+        // probabilities (fp32 for the sum, fp16 for the product)
+        f16x8 pf[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float e = __builtin_amdgcn_exp2f(s[kk / 2][8 * (kk % 2) + j] - m_new);
+                l_run += e;
+                pf[kk][j] = (_Float16)e;
+            }
+        }
+        // O^T += V^T P^T: k-step kk covers keys k0 + 16 kk + {4 hi .. 4 hi + 3,
+        // 8 + 4 hi .. 8 + 4 hi + 3} in the order of pf[kk]; two transpose
+        // reads fetch V for those keys, column 32 db + lane % 32.
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                s16x4 vh[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int key = kk * 16 + 4 * hi + 8 * hh + ((lane & 15) >> 2);
+                    const int d = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+                    const lds_u16 *src = Vs + key * T::D + swz_v<T::CD>(key, d >> 3) * 8 + (d & 7);
+                    vh[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src);
+                }
+                const f16x8 vf = __builtin_bit_cast(
+                    f16x8, __builtin_shufflevector(vh[0], vh[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[kk], acc_o[db], 0, 0, 0);
+            }
+        }
+    }
+    wait_vmcnt<0>();
+
+    // Output: the query's sum of exponentials is split over lanes l and l^32.
+    const float l_all = l_run + __shfl_xor(l_run, 32);
+    const float inv = l_all > 0.0f ? 1.0f / l_all : 0.0f;
+    if (q < Sq) {
+        uint16_t *orow = p.O + ((b * Sq + q) * p.H + h) * T::D;
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = db * 32 + 8 * g + 4 * hi;
+                u32x2 w;
+                w.x = epi_pack2<false>(acc_o[db][4 * g + 0] * inv, acc_o[db][4 * g + 1] * inv, false);
+                w.y = epi_pack2<false>(acc_o[db][4 * g + 2] * inv, acc_o[db][4 * g + 3] * inv, false);
+                *reinterpret_cast<u32x2 *>(orow + d) = w;
+            }
+        }
+    }
+}
+
+template <int D>
+hipError_t launch_attn(const AttnArgs &p, hipStream_t stream)
+{
+    const int64_t gx = (p.Sq + kBQ - 1) / kBQ;
+    if (gx > 0x7fffffff)
+        return hipErrorInvalidValue;
+    // grid rows are (batch, head) pairs; batches go in launches of at most
+    // 65535 rows
+    const int64_t per = 65535 / p.H;
+    for (int64_t b0 = 0; b0 < p.B; b0 += per) {
+        AttnArgs q = p;
+        q.B = (p.B - b0) < per ? (p.B - b0) : per;
+        q.Q = p.Q + b0 * p.Sq * p.H * D;
+        q.K = p.K + b0 * p.Sk * p.H * D;
+        q.V = p.V + b0 * p.Sk * p.H * D;
+        q.O = p.O + b0 * p.Sq * p.H * D;
+        hipLaunchKernelGGL((attention_fwd_kernel<AttnCfg<D>>), dim3((unsigned)gx,
+                           (unsigned)(q.B * p.H)), dim3(256), 0, stream, q);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnArgs &p, hipStream_t stream)
+{
+    return p.D == 64 ? launch_attn<64>(p, stream) : launch_attn<128>(p, stream);
+}
+
+}  // namespace tg

@@ -122,6 +122,19 @@ hipError_t launch_w4(const W4Args &p, hipStream_t stream);
 hipError_t launch_w4_naive(const W4Args &p, hipStream_t stream);
 bool w4_layout_ok(const W4Args &p);
 
+// One attention forward: O = softmax(scale * Q K^T) V for every (batch, head)
+// of Q (B, Sq, H, D), K and V (B, Sk, H, D), O (B, Sq, H, D), contiguous;
+// D is 64 or 128; with `causal`, key j is visible to query i iff
+// j <= i + (Sk - Sq).  Needs H <= 65535 and H * D < 2^24.
+struct AttnArgs {
+    const uint16_t *Q, *K, *V;
+    uint16_t *O;
+    int64_t B, Sq, Sk, H, D;
+    float scale;
+    int causal;
+};
+hipError_t launch_attention(const AttnArgs &p, hipStream_t stream);
+
 // Every launcher enqueues on `stream` and returns hipGetLastError().  The
 // tile launchers take the raster setting of tile_coords.
 hipError_t launch_naive(const GemmArgs &p, hipStream_t stream);
