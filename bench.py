@@ -445,6 +445,8 @@ def main():
     ap.add_argument("--attention", choices=["full", "causal"], default=None,
                     help="time the fused attention forward on 4 x 4096 x 32 heads x 128 "
                          "(tg_attention_fwd_f16) and exit")
+    ap.add_argument("--attention-variant", type=int, default=-1,
+                    help="attention workgroup shape (tg_set_attention_variant)")
     ap.add_argument("--w4", action="store_true",
                     help="time the weight-only int4 GEMM on the decode shape "
                          "16 x 16384 x 8192, groups of 128 (tg_gemm_w4) and exit")
@@ -481,6 +483,8 @@ def main():
         calibration_copy(torch)
     if args.attention:
         B, S, H, D = 4, 4096, 32, 128
+        if args.attention_variant != -1:
+            tg.tg_set_attention_variant(args.attention_variant)
         causal = args.attention == "causal"
         ms = run_attention(tg, torch, B, S, H, D, causal, args.steps, args.warmup)
         # two products of 2*S*S*D flop per (batch, head); half the pairs when causal

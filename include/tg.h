@@ -247,6 +247,15 @@ int tg_set_skinny_variant(int variant);
  */
 int tg_set_raster(int group_m);
 
+/*
+ * Tuning knob for benchmarks: the attention forward's workgroup shape, 0 =
+ * four waves (128 queries per workgroup), 1 = eight waves (256 queries, K/V
+ * tiles shared by twice the queries); -1 restores the default (1).  Returns
+ * the previous setting, or -2 for an unknown value.  Results are identical
+ * within the attention tolerance for both.
+ */
+int tg_set_attention_variant(int variant);
+
 /* A static name for a path number ("auto", "naive", ...), or "unknown". */
 const char *tg_path_name(int path);
 

@@ -169,6 +169,9 @@ def test_attention_validation(tg):
     assert call(Q=0) == tg.TG_ERR_INVALID_ARG
     assert call(B=0) == tg.TG_OK and call(Sq=0) == tg.TG_OK and call(H=0) == tg.TG_OK
     assert tg.tg_path_name(tg.TG_PATH_ATTENTION) == "attention"
+    assert tg.tg_set_attention_variant(0) == 1
+    assert tg.tg_set_attention_variant(2) == -2
+    assert tg.tg_set_attention_variant(-1) == 0
 
 
 def _gpu_visible():

@@ -90,13 +90,18 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("variant", [0, 1])
 @pytest.mark.parametrize("B,Sq,Sk,H,D,causal", CASES)
-def test_attention_matches_oracle(tg, oracle_lib, B, Sq, Sk, H, D, causal):
+def test_attention_matches_oracle(tg, oracle_lib, variant, B, Sq, Sk, H, D, causal):
     q, k, v = qkv(B, Sq, Sk, H, D, Sq + Sk + D)
     scale = 1.0 / np.sqrt(D)
     ref = oracle_lib.attention(q, k, v, B, Sq, Sk, H, D, scale, causal)
-    say(f"attention B={B} Sq={Sq} Sk={Sk} H={H} D={D} causal={causal}")
-    got = run(tg, q, k, v, B, Sq, Sk, H, D, scale, causal)
+    say(f"attention B={B} Sq={Sq} Sk={Sk} H={H} D={D} causal={causal} variant={variant}")
+    assert tg.tg_set_attention_variant(variant) >= 0
+    try:
+        got = run(tg, q, k, v, B, Sq, Sk, H, D, scale, causal)
+    finally:
+        tg.tg_set_attention_variant(-1)
     check(got, ref, v)
 
 

@@ -45,6 +45,7 @@ EXPORTED_SYMBOLS = (
     "tg_gemm_ex",
     "tg_gemm_w4",
     "tg_attention_fwd_f16",
+    "tg_set_attention_variant",
 )
 
 TG_DTYPE_F16 = 0
@@ -79,6 +80,8 @@ _lib.tg_gemm_w4.argtypes = [ctypes.c_int] * 2 + [_vp] * 5 + [_i64] * 8 + [_vp]
 _lib.tg_gemm_w4.restype = ctypes.c_int
 _lib.tg_attention_fwd_f16.argtypes = [_vp] * 4 + [_i64] * 5 + [ctypes.c_float, ctypes.c_int, _vp]
 _lib.tg_attention_fwd_f16.restype = ctypes.c_int
+_lib.tg_set_attention_variant.argtypes = [ctypes.c_int]
+_lib.tg_set_attention_variant.restype = ctypes.c_int
 _lib.tg_status_string.argtypes = [ctypes.c_int]
 _lib.tg_status_string.restype = ctypes.c_char_p
 _lib.tg_set_path.argtypes = [ctypes.c_int]
@@ -158,6 +161,10 @@ def tg_set_tile_variant(variant: int) -> int:
 
 def tg_set_skinny_variant(variant: int) -> int:
     return _lib.tg_set_skinny_variant(variant)
+
+
+def tg_set_attention_variant(variant: int) -> int:
+    return _lib.tg_set_attention_variant(variant)
 
 
 def tg_set_raster(group_m: int) -> int:

@@ -27,6 +27,9 @@ std::atomic<int> g_skinny_variant{-1};
 // renumbering (0: plain row-major order)
 constexpr int kGroupMDefault = 8;
 std::atomic<int> g_group_m{kGroupMDefault};
+// attention kernel configuration (0: four waves per workgroup, 1: eight)
+constexpr int kAttnDefault = 1;
+std::atomic<int> g_attn_variant{kAttnDefault};
 
 // Per-device architecture check, done once per device: 0 unknown, 1 gfx950,
 // 2 something else.
@@ -332,6 +335,7 @@ int tg_attention_fwd_f16(const void *Q, const void *K, const void *V, void *O, i
     p.B = batch; p.Sq = seq_q; p.Sk = seq_k; p.H = heads; p.D = head_dim;
     p.scale = scale;
     p.causal = causal;
+    p.variant = g_attn_variant.load(std::memory_order_relaxed);
     if (tg::launch_attention(p, stream) != hipSuccess)
         return TG_ERR_HIP;
     g_last_path.store(TG_PATH_ATTENTION, std::memory_order_relaxed);
@@ -372,6 +376,15 @@ int tg_set_tile_variant(int variant)
           variant == kRegStaged128 || variant == kRegStaged256))
         return -2;
     return g_tile_variant.exchange(variant);
+}
+
+int tg_set_attention_variant(int variant)
+{
+    if (variant == -1)
+        variant = kAttnDefault;
+    if (variant < 0 || variant > 1)
+        return -2;
+    return g_attn_variant.exchange(variant);
 }
 
 int tg_set_raster(int group_m)

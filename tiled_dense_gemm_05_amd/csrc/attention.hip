@@ -14,8 +14,8 @@
 // `causal` when j <= i + (Sk - Sq).
 //
 // gfx950 design:
-//  * One workgroup of four waves per 128 queries of one (batch, head); wave w
-//    owns queries 32w .. 32w+31.  K/V tiles of 64 keys are staged in a
+//  * One workgroup of NW waves per 32*NW queries of one (batch, head); wave
+//    w owns queries 32w .. 32w+31.  K/V tiles of 64 keys are staged in a
 //    2-stage LDS ring by buffer_load_dwordx4 ... lds (rows past Sk read as
 //    zeros and are masked out of the softmax).
 //  * Both products run on v_mfma_f32_32x32x16_f16 with the operand roles
@@ -44,18 +44,20 @@ typedef __attribute__((address_space(3))) f16x8 lds_f16x8;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 constexpr uint32_t kOutOfRange = 0x80000000u;
-constexpr int kBQ = 128;   // queries per workgroup (4 waves x 32)
 constexpr int kBK = 64;    // keys per tile
 
-template <int D_>
+template <int D_, int NW_>
 struct AttnCfg {
     static constexpr int D = D_;
+    static constexpr int NW = NW_;                   // waves; 32 queries each
+    static constexpr int BQ = 32 * NW;               // queries per workgroup
     static constexpr int CD = D / 8;                 // 16-byte chunks per row
     static constexpr int TILE = kBK * D;             // fp16 elements of a K (or V) tile
     static constexpr int STAGE = 2 * TILE;           // K then V
     static constexpr int LDS = 2 * STAGE * 2;        // two stages, bytes
     static constexpr int RPB = 64 / CD;              // rows per 1 KiB block
-    static constexpr int LD = TILE / 512 / 4;        // 1 KiB blocks per wave per tile
+    static constexpr int LD = TILE / 512 / NW;       // 1 KiB blocks per wave per tile
+    static_assert((TILE / 512) % NW == 0, "blocks per wave");
     static constexpr int DS = D / 16;                // 16-wide d steps
     static constexpr int DB = D / 32;                // 32-wide d blocks of the output
     static_assert(D == 64 || D == 128, "head dim");
@@ -120,7 +122,7 @@ __device__ __forceinline__ int swz_v(int row, int c)
 }
 
 template <class T>
-__global__ void __launch_bounds__(256) attention_fwd_kernel(AttnArgs p)
+__global__ void __launch_bounds__(64 * T::NW) attention_fwd_kernel(AttnArgs p)
 {
     __shared__ __attribute__((aligned(1024))) uint16_t smem[T::LDS / 2];
     const lds_u16 *lds = (const lds_u16 *)smem;
@@ -132,7 +134,9 @@ __global__ void __launch_bounds__(256) attention_fwd_kernel(AttnArgs p)
     const int64_t bh = blockIdx.y;
     const int64_t b = bh / p.H, h = bh % p.H;
     const int64_t Sq = p.Sq, Sk = p.Sk;
-    const int64_t q0 = (int64_t)blockIdx.x * kBQ;
+    // with the causal mask later query blocks have more keys: start those first
+    const int64_t qb = p.causal ? (int64_t)gridDim.x - 1 - blockIdx.x : (int64_t)blockIdx.x;
+    const int64_t q0 = qb * T::BQ;
     const int64_t rs = p.H * T::D;                   // elements between sequence positions
     const int64_t q = q0 + wave * 32 + (lane & 31);  // this lane's query
     const int hi = lane >> 5;
@@ -141,7 +145,7 @@ __global__ void __launch_bounds__(256) attention_fwd_kernel(AttnArgs p)
     // last query's horizon.
     int64_t kend = Sk;
     if (p.causal) {
-        const int64_t lim = q0 + kBQ + (Sk - Sq);
+        const int64_t lim = q0 + T::BQ + (Sk - Sq);
         kend = lim < 0 ? 0 : (lim < Sk ? lim : Sk);
     }
     const int tiles = (int)((kend + kBK - 1) / kBK);
@@ -165,7 +169,7 @@ __global__ void __launch_bounds__(256) attention_fwd_kernel(AttnArgs p)
     int k_row[T::LD];
 #pragma unroll
     for (int i = 0; i < T::LD; ++i) {
-        const int blk = wave + 4 * i;
+        const int blk = wave + T::NW * i;
         const int row = blk * T::RPB + lane / T::CD;
         const int pc = lane % T::CD;
         k_row[i] = row;
@@ -182,9 +186,10 @@ __global__ void __launch_bounds__(256) attention_fwd_kernel(AttnArgs p)
 #pragma unroll
         for (int i = 0; i < T::LD; ++i) {
             const bool ok = k0 + k_row[i] < kend;
-            dma16(rk, ok ? k_voff[i] : kOutOfRange, base + (uint32_t)((wave + 4 * i) * 1024));
+            dma16(rk, ok ? k_voff[i] : kOutOfRange,
+                  base + (uint32_t)((wave + T::NW * i) * 1024));
             dma16(rv, ok ? v_voff[i] : kOutOfRange,
-                  base + (uint32_t)(T::TILE * 2 + (wave + 4 * i) * 1024));
+                  base + (uint32_t)(T::TILE * 2 + (wave + T::NW * i) * 1024));
         }
     };
 
@@ -299,10 +304,10 @@ __global__ void __launch_bounds__(256) attention_fwd_kernel(AttnArgs p)
     }
 }
 
-template <int D>
+template <int D, int NW>
 hipError_t launch_attn(const AttnArgs &p, hipStream_t stream)
 {
-    const int64_t gx = (p.Sq + kBQ - 1) / kBQ;
+    const int64_t gx = (p.Sq + 32 * NW - 1) / (32 * NW);
     if (gx > 0x7fffffff)
         return hipErrorInvalidValue;
     // grid rows are (batch, head) pairs; batches go in launches of at most
@@ -315,8 +320,8 @@ hipError_t launch_attn(const AttnArgs &p, hipStream_t stream)
         q.K = p.K + b0 * p.Sk * p.H * D;
         q.V = p.V + b0 * p.Sk * p.H * D;
         q.O = p.O + b0 * p.Sq * p.H * D;
-        hipLaunchKernelGGL((attention_fwd_kernel<AttnCfg<D>>), dim3((unsigned)gx,
-                           (unsigned)(q.B * p.H)), dim3(256), 0, stream, q);
+        hipLaunchKernelGGL((attention_fwd_kernel<AttnCfg<D, NW>>), dim3((unsigned)gx,
+                           (unsigned)(q.B * p.H)), dim3(64 * NW), 0, stream, q);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -328,7 +333,10 @@ hipError_t launch_attn(const AttnArgs &p, hipStream_t stream)
 
 hipError_t launch_attention(const AttnArgs &p, hipStream_t stream)
 {
-    return p.D == 64 ? launch_attn<64>(p, stream) : launch_attn<128>(p, stream);
+    const int nw = p.variant == 1 ? 8 : 4;
+    if (p.D == 64)
+        return nw == 8 ? launch_attn<64, 8>(p, stream) : launch_attn<64, 4>(p, stream);
+    return nw == 8 ? launch_attn<128, 8>(p, stream) : launch_attn<128, 4>(p, stream);
 }
 
 }  // namespace tg

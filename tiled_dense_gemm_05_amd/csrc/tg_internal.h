@@ -132,6 +132,7 @@ struct AttnArgs {
     int64_t B, Sq, Sk, H, D;
     float scale;
     int causal;
+    int variant;      // 0: four waves per workgroup, 1: eight
 };
 hipError_t launch_attention(const AttnArgs &p, hipStream_t stream);
 
