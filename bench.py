@@ -410,7 +410,29 @@ def summarize_ablation(out_md: str, root: str, title: str):
     print(f"wrote {out_md}")
 
 
+def summarize_stats(out_md: str, title: str, stats_dir: str, commands: list[str]):
+    """Writes a kernel-trace summary (top kernels by total time) for runs that
+    are not one of the dense workloads (the int4 and attention benches)."""
+    stats = _csv_rows(_find(stats_dir, "kernel_stats.csv"))
+    stats.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    with open(out_md, "w") as f:
+        f.write(f"# {title}\n\nCommands (from the repository root on the GPU box):\n\n")
+        for c in commands:
+            f.write(f"    {c}\n")
+        f.write("\nKernel trace (rocprofv3 --kernel-trace --stats), top kernels:\n\n")
+        f.write("| kernel | calls | average ns | min ns | max ns |\n|---|---|---|---|---|\n")
+        for r in stats[:4]:
+            name = r["Name"].replace("tg::(anonymous namespace)::", "")
+            f.write(f"| {name[:120]} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                    f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} |\n")
+    print(f"wrote {out_md}")
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-stats":
+        # bench.py --summarize-stats OUT_MD TITLE STATS_DIR "cmd1" ...
+        summarize_stats(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5:])
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-ablation":
         # bench.py --summarize-ablation OUT_MD ROOT_DIR TITLE
         summarize_ablation(sys.argv[2], sys.argv[3], sys.argv[4])
