@@ -147,3 +147,33 @@ def test_benchmark_shape_sampled(tg, oracle_lib, causal):
             sl_v = np.ascontiguousarray(V[b, :nk, h]).reshape(-1)
             ref = oracle_lib.attention(sl_q, sl_k, sl_v, 1, n, nk, 1, D, scale, causal)
             check(np.ascontiguousarray(out[b, s0:s0 + n, h]).reshape(-1), ref, sl_v)
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 1e-3])
+def test_scale_sign_and_zero(tg, oracle_lib, scale):
+    # a negative scale flips which key dominates; a zero scale averages the
+    # visible values
+    B, Sq, Sk, H, D = 1, 100, 260, 2, 64
+    q, k, v = qkv(B, Sq, Sk, H, D, 12, spread=2.0)
+    for causal in (False, True):
+        ref = oracle_lib.attention(q, k, v, B, Sq, Sk, H, D, scale, causal)
+        say(f"attention scale={scale} causal={causal}")
+        check(run(tg, q, k, v, B, Sq, Sk, H, D, scale, causal), ref, v)
+
+
+@pytest.mark.parametrize("direction", ["rising", "falling"])
+def test_running_maximum_moves_every_tile(tg, oracle_lib, direction):
+    # scores that climb by about 12 (log2 units) per 64-key tile force the
+    # output to be rescaled at every tile; falling scores never raise the
+    # maximum after the first tile
+    B, Sq, Sk, H, D = 1, 96, 640, 1, 64
+    rng = np.random.default_rng(13)
+    q = f16(1.0 + rng.uniform(-0.05, 0.05, Sq * D))
+    ramp = np.arange(Sk) if direction == "rising" else np.arange(Sk)[::-1]
+    kk = (0.13 * ramp / D)[:, None] + rng.uniform(-0.01, 0.01, (Sk, D))
+    k = f16(kk.reshape(-1))
+    v = f16(rng.uniform(-1, 1, Sk * D))
+    for causal in (False, True):
+        ref = oracle_lib.attention(q, k, v, B, Sq, Sk, H, D, 1.0, causal)
+        say(f"attention {direction} scores causal={causal}")
+        check(run(tg, q, k, v, B, Sq, Sk, H, D, 1.0, causal), ref, v)

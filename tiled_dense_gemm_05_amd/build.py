@@ -28,10 +28,17 @@ COMMON = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 
+# Per-source flags.  The attention kernel's scores never hold NaN (masked keys
+# are -inf): telling the compiler so lets fmaxf map to v_max3_f32 without
+# first quieting each matrix-core result.
+PER_FILE = {
+    "attention.hip": ["-fno-honor-nans"],
+}
+
 
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, *extra, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *PER_FILE.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

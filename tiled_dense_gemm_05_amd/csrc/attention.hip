@@ -121,8 +121,89 @@ __device__ __forceinline__ int swz_v(int row, int c)
         return c ^ (((row >> 1) & 1) << 2);
 }
 
+// Exponentials are taken relative to a running maximum that is raised only
+// when a tile's maximum exceeds it by more than this (log2 units): every
+// exponential stays <= 2^8, the output accumulator is rescaled rarely, and
+// the final division by the sum taken against the same maximum cancels it.
+constexpr float kGrowLog2 = 8.0f;
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// The two lanes 32 apart hold the same query: combine their values.
+__device__ __forceinline__ float max_pair(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Masks the raw scores of keys at or past `lim` (tile offsets, see below).
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int lim, int hi)
+{
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int ko = kb * 32 + 8 * (r / 4) + 4 * hi + (r % 4);
+            s[kb][r] = ko < lim ? s[kb][r] : -__builtin_inff();
+        }
+    }
+}
+
+// One tile's softmax step for this lane's query: raw scores s (32 keys,
+// register r of block kb is key 32 kb + 8 (r / 4) + 4 hi + r % 4 of the
+// tile; masked keys hold -inf, and sl2 > 0 turns them into zeros).  Raises
+// the running maximum if needed (rescaling the accumulator and the sum),
+// writes the fp16 probabilities in the operand order of the P V product and
+// adds them to the sum (the rounded values, so the weights applied to V are
+// exactly the ones the sum divides by).
+template <int DB>
+__device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], f16x8 (&pf)[4], f32x16 (&acc_o)[DB],
+                                             float &m_run, float &l_run, float sl2)
+{
+    float mt = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2)
+            mt = __builtin_fmaxf(mt, __builtin_fmaxf(s[kb][r], s[kb][r + 1]));
+    }
+    mt = max_pair(mt);
+    const float m_tile = __builtin_fmaxf(mt * sl2, -1.0e30f);
+    const bool grow = m_tile > m_run + kGrowLog2;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? m_tile : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            acc_o[db] *= alpha;
+    }
+    const float neg_m = -m_run;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            pf[kk][j] = (_Float16)__builtin_amdgcn_exp2f(
+                __builtin_fmaf(s[kk / 2][8 * (kk % 2) + j], sl2, neg_m));
+    }
+    float ls[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            ls[j & 1] = __builtin_amdgcn_fdot2(f16x2{pf[kk][2 * j], pf[kk][2 * j + 1]},
+                                               f16x2{(_Float16)1.0f, (_Float16)1.0f}, ls[j & 1], false);
+    }
+    l_run += ls[0] + ls[1];
+}
+
+// Two waves per SIMD: lets the scheduler keep LDS reads in flight ahead of
+// the matrix instructions that consume them instead of minimizing registers.
 template <class T>
-__global__ void __launch_bounds__(64 * T::NW) attention_fwd_kernel(AttnArgs p)
+__global__ void __launch_bounds__(64 * T::NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attention_fwd_kernel(AttnArgs p)
 {
     __shared__ __attribute__((aligned(1024))) uint16_t smem[T::LDS / 2];
     const lds_u16 *lds = (const lds_u16 *)smem;
@@ -159,6 +240,10 @@ __global__ void __launch_bounds__(64 * T::NW) attention_fwd_kernel(AttnArgs p)
             qf[ds] = f16x8{};
             if (q < Sq)
                 qf[ds] = *reinterpret_cast<const f16x8 *>(qrow + ds * 16 + 8 * hi);
+            // a negative scale is carried by Q (negation is exact), so the
+            // scores are scaled by |scale| and their maximum stays a maximum
+            if (p.scale < 0.0f)
+                qf[ds] = -qf[ds];
         }
     }
 
@@ -197,11 +282,15 @@ __global__ void __launch_bounds__(64 * T::NW) attention_fwd_kernel(AttnArgs p)
 #pragma unroll
     for (int db = 0; db < T::DB; ++db)
         acc_o[db] = f32x16{};
-    // running maximum (in log2 units, finite so a fully masked tile leaves it
-    // unchanged) and this lane's share of the sum of exponentials
+    // running maximum (log2 units, finite so a fully masked tile leaves it
+    // unchanged) and this lane's share of the sum of probabilities
     float m_run = -1.0e30f, l_run = 0.0f;
-    const float sl2 = p.scale * 1.44269504088896340736f;   // scale * log2(e)
-    const int64_t horizon = q + (Sk - Sq);                 // causal: last visible key
+    // |scale| * log2(e), kept positive so masked scores (-inf) map to zero
+    // (a zero scale becomes 1e-30: every exponential is then 1 to fp32 precision)
+    const float sl2 = __builtin_fmaxf(__builtin_fabsf(p.scale) * 1.44269504088896340736f, 1.0e-30f);
+    const int64_t shift = Sk - Sq;               // causal: query i sees keys j <= i + shift
+    const int64_t horizon = q + shift;
+    const int64_t wq0 = q0 + wave * 32;          // this wave's first query
 
     if (tiles > 0)
         issue(0);
@@ -210,9 +299,13 @@ __global__ void __launch_bounds__(64 * T::NW) attention_fwd_kernel(AttnArgs p)
         block_barrier();      // ... every wave's part; tile t-1's stage is free
         if (t + 1 < tiles)
             issue(t + 1);
+        const int64_t k0 = (int64_t)t * kBK;
+        // causal: none of this wave's queries sees the tile (it was loaded
+        // for the block's later waves)
+        if (p.causal && k0 > wq0 + 31 + shift)
+            continue;
         const lds_u16 *Ks = lds + (t & 1) * T::STAGE;
         const lds_u16 *Vs = Ks + T::TILE;
-        const int64_t k0 = (int64_t)t * kBK;
 
         // S^T = K Q^T: two 32-key blocks; lane: query q, keys
         // k0 + 32 kb + 8 (r / 4) + 4 hi + r % 4 for register r.
@@ -229,39 +322,17 @@ __global__ void __launch_bounds__(64 * T::NW) attention_fwd_kernel(AttnArgs p)
                 s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ds], s[kb], 0, 0, 0);
             }
         }
-        // scale to log2 units, mask invisible keys, this tile's maximum
-        float mt = -1.0e30f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t key = k0 + kb * 32 + 8 * (r / 4) + 4 * hi + (r % 4);
-                const bool vis = key < kend && (!p.causal || key <= horizon);
-                const float v = vis ? s[kb][r] * sl2 : -__builtin_inff();
-                s[kb][r] = v;
-                mt = v > mt ? v : mt;
-            }
+        // mask only where some key of the tile is hidden from some query of
+        // the wave
+        if (!(k0 + kBK <= kend && (!p.causal || k0 + kBK - 1 <= wq0 + shift))) {
+            int64_t lim = kend - k0;
+            if (p.causal && horizon + 1 - k0 < lim)
+                lim = horizon + 1 - k0;
+            lim = lim < 0 ? 0 : (lim > kBK ? kBK : lim);
+            mask_tile(s, (int)lim, hi);
         }
-        const float mo = __shfl_xor(mt, 32);
-        mt = mo > mt ? mo : mt;
-        const float m_new = mt > m_run ? mt : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < T::DB; ++db)
-            acc_o[db] *= alpha;
-        // probabilities (fp32 for the sum, fp16 for the product)
         f16x8 pf[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float e = __builtin_amdgcn_exp2f(s[kk / 2][8 * (kk % 2) + j] - m_new);
-                l_run += e;
-                pf[kk][j] = (_Float16)e;
-            }
-        }
+        softmax_tile<T::DB>(s, pf, acc_o, m_run, l_run, sl2);
         // O^T += V^T P^T: k-step kk covers keys k0 + 16 kk + {4 hi .. 4 hi + 3,
         // 8 + 4 hi .. 8 + 4 hi + 3} in the order of pf[kk]; two transpose
         // reads fetch V for those keys, column 32 db + lane % 32.
