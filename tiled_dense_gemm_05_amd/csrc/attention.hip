@@ -7,7 +7,7 @@
 // this kernel reuses the GEMM's tile machinery for the standard one-pass
 // form: per query block, walk the key/value tiles, keep a running maximum
 // and sum of exponentials per query, rescale the output accumulator when the
-// maximum grows, divide once at the end.
+// maximum grows (here: by more than 2^8), divide once at the end.
 //
 // Layout: Q (B, Sq, H, D), K and V (B, Sk, H, D), O (B, Sq, H, D), each
 // contiguous; D = 64 or 128.  Key j is visible to query i always, or with
@@ -27,7 +27,9 @@
 //    inside a 16-key step is permuted identically on both operands (the V^T
 //    fragments come from transpose reads that fetch exactly those keys).
 //  * Q fragments stay in registers for the whole walk; scores use exp2 with
-//    scale * log2(e) folded in.
+//    |scale| * log2(e) folded into one FMA per score (a negative scale is
+//    carried by Q), tiles that every query of a wave sees skip the mask,
+//    and the row sums add the fp16 probabilities in pairs (v_dot2).
 #include "tg_internal.h"
 
 namespace tg {
