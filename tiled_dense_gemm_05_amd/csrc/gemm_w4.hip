@@ -166,8 +166,9 @@ __device__ __forceinline__ int swz_w(int row, int c) { return c ^ ((row >> 1) & 
 // nibble in the low half and the high nibble (as 16 * (q + 8)) in the high
 // half under the exponent bits 0x64, giving the halves 1024 + (q + 8) and
 // 1024 + 16 (q + 8); one packed FMA (times 1 and 1/16, less 1032 and 72)
-// leaves both q exactly.  bf16: u converts exactly to fp32, less 8, then to
-// bf16.
+// leaves both q exactly.  bf16: a byte permute places each nibble of the
+// masked halves under the fp32 exponent of 2^23, one subtraction leaves q,
+// one conversion packs two bf16 (all exact).
 template <bool BF16>
 __device__ __forceinline__ f16x8 dequant8(uint32_t w)
 {
@@ -184,13 +185,19 @@ __device__ __forceinline__ f16x8 dequant8(uint32_t w)
                 f16x2{(_Float16)-1032.0f, (_Float16)-72.0f});
             out[i] = __builtin_bit_cast(uint32_t, h);
         } else {
-            const uint32_t y = u & 0x0f0f0f0fu;
-            const uint32_t z = (u >> 4) & 0x0f0f0f0fu;
-            const float lo = (float)((y >> (8 * i)) & 0xffu) - 8.0f;   // exact
-            const float hi = (float)((z >> (8 * i)) & 0xffu) - 8.0f;
-            const uint16_t bl = __builtin_bit_cast(uint16_t, (__bf16)lo);
-            const uint16_t bh = __builtin_bit_cast(uint16_t, (__bf16)hi);
-            out[i] = (uint32_t)bl | ((uint32_t)bh << 16);
+            typedef float f32x2 __attribute__((ext_vector_type(2)));
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            const uint32_t y = u & 0x0f0f0f0fu;             // even k: q + 8 per byte
+            const uint32_t z = (u >> 4) & 0x0f0f0f0fu;      // odd k
+            // byte i under the fp32 exponent of 2^23: 2^23 + q + 8, then
+            // less 2^23 + 8 (exact), and both converted in one instruction
+            // (exact: small integers)
+            const uint32_t sel = 0x070c0c00u | (uint32_t)i;
+            const float lo = __builtin_bit_cast(float, __builtin_amdgcn_perm(0x4b000000u, y, sel)) -
+                             8388616.0f;
+            const float hi = __builtin_bit_cast(float, __builtin_amdgcn_perm(0x4b000000u, z, sel)) -
+                             8388616.0f;
+            out[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
         }
     }
     return __builtin_bit_cast(f16x8, out);
@@ -217,52 +224,6 @@ __global__ void __launch_bounds__(T::NT) gemm_w4_kernel(W4Args p)
     const int64_t n0 = (int64_t)blockIdx.x * kRows;
     const int64_t m0 = (int64_t)blockIdx.y * (16 * T::MB);
     const int groups = (int)(K / p.G);
-
-    // Scales of rows n0 .. n0+63, all groups, into LDS as [group][row] (rows
-    // past N: 0).  Threads walk each row's scales in order (coalesced), eight
-    // at a time when a row's scales are 16-byte aligned, and every load of a
-    // thread is issued before its LDS writes.
-    if (p.scales_vec) {
-        const int chunks = groups / 8;             // 16-byte chunks per row
-        for (int e0 = 0; e0 < chunks * kRows; e0 += 4 * T::NT) {
-            u32x4 v[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int e = e0 + u * T::NT + tid;
-                const int r = e / chunks, c = e % chunks;
-                v[u] = u32x4{0, 0, 0, 0};
-                if (e < chunks * kRows && n0 + r < N)
-                    v[u] = *reinterpret_cast<const u32x4 *>(p.S + (n0 + r) * p.lds + c * 8);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int e = e0 + u * T::NT + tid;
-                const int r = e / chunks, c = e % chunks;
-                if (e < chunks * kRows) {
-#pragma unroll
-                    for (int t = 0; t < 8; ++t)
-                        scl[(c * 8 + t) * kRows + r] = (uint16_t)(v[u][t / 2] >> (16 * (t & 1)));
-                }
-            }
-        }
-    } else {
-        for (int e0 = 0; e0 < groups * kRows; e0 += 4 * T::NT) {
-            uint16_t v[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int e = e0 + u * T::NT + tid;
-                const int r = e / groups, g = e % groups;
-                v[u] = (e < groups * kRows && n0 + r < N) ? p.S[(n0 + r) * p.lds + g]
-                                                          : (uint16_t)0;
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int e = e0 + u * T::NT + tid;
-                if (e < groups * kRows)
-                    scl[(e % groups) * kRows + e / groups] = v[u];
-            }
-        }
-    }
 
     // Load plan: A block j (2 rows of 512 bytes): lane L -> row 2j + L / 32,
     // physical chunk L % 32; weight block j (8 rows of 128 bytes): lane L ->
@@ -359,6 +320,54 @@ __global__ void __launch_bounds__(T::NT) gemm_w4_kernel(W4Args p)
         issue_a(s);
         issue_w(s + T::DW - T::DA);
     }
+    // Scales of rows n0 .. n0+63, all groups, into LDS as [group][row] (rows
+    // past N: 0), loaded while the prologue's weight and A are in flight
+    // (the loop's first barrier publishes them).  Threads walk each row's
+    // scales in order (coalesced), eight at a time when a row's scales are
+    // 16-byte aligned, and every load of a thread is issued before its LDS
+    // writes.
+    if (p.scales_vec) {
+        const int chunks = groups / 8;             // 16-byte chunks per row
+        for (int e0 = 0; e0 < chunks * kRows; e0 += 4 * T::NT) {
+            u32x4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + u * T::NT + tid;
+                const int r = e / chunks, c = e % chunks;
+                v[u] = u32x4{0, 0, 0, 0};
+                if (e < chunks * kRows && n0 + r < N)
+                    v[u] = *reinterpret_cast<const u32x4 *>(p.S + (n0 + r) * p.lds + c * 8);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + u * T::NT + tid;
+                const int r = e / chunks, c = e % chunks;
+                if (e < chunks * kRows) {
+#pragma unroll
+                    for (int t = 0; t < 8; ++t)
+                        scl[(c * 8 + t) * kRows + r] = (uint16_t)(v[u][t / 2] >> (16 * (t & 1)));
+                }
+            }
+        }
+    } else {
+        for (int e0 = 0; e0 < groups * kRows; e0 += 4 * T::NT) {
+            uint16_t v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + u * T::NT + tid;
+                const int r = e / groups, g = e % groups;
+                v[u] = (e < groups * kRows && n0 + r < N) ? p.S[(n0 + r) * p.lds + g]
+                                                          : (uint16_t)0;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + u * T::NT + tid;
+                if (e < groups * kRows)
+                    scl[(e % groups) * kRows + e / groups] = v[u];
+            }
+        }
+    }
+
     for (int st = 0; st < gsteps; ++st) {
         // this wave's loads of step st have landed once at most WAIT later
         // loads are outstanding (A of step st is the newest of the two); the
