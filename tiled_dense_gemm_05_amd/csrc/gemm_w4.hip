@@ -169,8 +169,12 @@ __device__ __forceinline__ int swz_w(int row, int c) { return c ^ ((row >> 1) & 
 // leaves both q exactly.  bf16: a byte permute places each nibble of the
 // masked halves under the fp32 exponent of 2^23, one subtraction leaves q,
 // one conversion packs two bf16 (all exact).
+// `nib` holds 0x00f0000f in a register: with the mask in a VGPR the AND and
+// the OR with the exponent bits fuse into one v_and_or_b32 (a VOP3
+// instruction takes no literal here, and two literals would cost two
+// instructions).
 template <bool BF16>
-__device__ __forceinline__ f16x8 dequant8(uint32_t w)
+__device__ __forceinline__ f16x8 dequant8(uint32_t w, uint32_t nib)
 {
     const uint32_t u = w ^ 0x88888888u;
     u32x4 out;
@@ -179,7 +183,7 @@ __device__ __forceinline__ f16x8 dequant8(uint32_t w)
         if constexpr (!BF16) {
             typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
             const uint32_t sel = 0x0c000c00u | ((uint32_t)i << 16) | (uint32_t)i;
-            const uint32_t v = (__builtin_amdgcn_perm(u, u, sel) & 0x00f0000fu) | 0x64006400u;
+            const uint32_t v = (__builtin_amdgcn_perm(u, u, sel) & nib) | 0x64006400u;
             const f16x2 h = __builtin_elementwise_fma(
                 __builtin_bit_cast(f16x2, v), f16x2{(_Float16)1.0f, (_Float16)0.0625f},
                 f16x2{(_Float16)-1032.0f, (_Float16)-72.0f});
@@ -291,6 +295,8 @@ __global__ void __launch_bounds__(T::NT) gemm_w4_kernel(W4Args p)
 #pragma unroll
     for (int mb = 0; mb < T::MB; ++mb)
         acc[mb] = part[mb] = f32x4{};
+    uint32_t nib = 0x00f0000fu;                      // see dequant8
+    asm volatile("" : "+v"(nib));
     const int wrow = wave * 16 + (lane & 15);        // the lane's weight row (operand)
     const int orow = wave * 16 + 4 * (lane >> 4);    // the lane's first output column
     const int sub_per_group = p.G / 32;
@@ -401,7 +407,7 @@ __global__ void __launch_bounds__(T::NT) gemm_w4_kernel(W4Args p)
                     af[(ks + 1) & 1][mb] = *reinterpret_cast<const lds_f16x8 *>(
                         As + mb * 16 * 512 + a_off[ks + 1]);
             }
-            const f16x8 wf = dequant8<T::BF16>(wb[ks]);
+            const f16x8 wf = dequant8<T::BF16>(wb[ks], nib);
 #pragma unroll
             for (int mb = 0; mb < T::MB; ++mb) {
                 if constexpr (T::BF16)
