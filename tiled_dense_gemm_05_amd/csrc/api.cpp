@@ -21,7 +21,7 @@ constexpr int kTile128ShortK = 12;   // 128x128x32, 2 stages, 4 waves/SIMD: seve
 constexpr int kTile64 = 20;          // 64x64x64, 4 stages, two K groups: grids with few tiles
 constexpr int kRegStaged128 = 100;   // register-staged kernels, kept for comparison
 constexpr int kRegStaged256 = 101;
-constexpr int kSkinnyDefault = 4;   // 64-column slices, 4 waves, 6 stages, non-temporal B
+constexpr int kSkinnyDefault = 7;   // 64-column slices, 8 waves, 3 stages, non-temporal B
 std::atomic<int> g_skinny_variant{-1};
 // tile order of the tile kernels: panels of this many tile rows after the XCD
 // renumbering (0: plain row-major order)
