@@ -315,7 +315,8 @@ def summarize(workload: str, stats_dir: str, fetch_dir: str, write_dir: str, com
     g_write = sum(write[gemm_name]) / len(write[gemm_name]) * kib * f_write
     w = wl.WORKLOADS[workload]
     family = ("gemm_relu_dma_kernel" if "dma_kernel" in top["Name"] else
-              "gemm_relu_skinny_kernel" if "skinny_kernel" in top["Name"] else "kernel")
+              "gemm_relu_skinny_kernel" if "skinny_kernel" in top["Name"] else
+              "gemm_relu_tile_kernel" if "tile_kernel" in top["Name"] else "kernel")
     md = os.path.join(PROFILES, f"{family}-{workload}.md")
     with open(md, "w") as f:
         f.write(f"# {top['Name'].replace('tg::(anonymous namespace)::', '')} on {workload}\n\n")
