@@ -175,7 +175,7 @@ int tg_gemm_w4(int dtype, int activation, const void *A, const void *Wq, const v
  * definition, computed in one pass with a running maximum.
  *   Q, O  (batch, seq_q, heads, head_dim) fp16, contiguous, DEVICE pointers
  *   K, V  (batch, seq_k, heads, head_dim) fp16, contiguous, DEVICE pointers
- *   head_dim 64 or 128; heads <= 65535 and heads * head_dim < 2^24;
+ *   head_dim 64 or 128; heads * head_dim < 2^24 and batch * heads < 2^31;
  *   all four pointers 16-byte aligned; scale finite (e.g. 1/sqrt(head_dim)).
  * Scores and sums are fp32, probabilities enter the value product as fp16
  * (the products with V are accumulated in fp32).  Errors, asynchrony and

@@ -162,8 +162,8 @@ def test_attention_validation(tg):
     assert call(D=96) == tg.TG_ERR_INVALID_ARG          # head_dim 64 or 128
     assert call(Q=P + 2) == tg.TG_ERR_INVALID_ARG       # 16-byte alignment
     assert call(causal=2) == tg.TG_ERR_INVALID_ARG
-    assert call(H=70000) == tg.TG_ERR_INVALID_ARG
-    assert call(H=1 << 17) == tg.TG_ERR_INVALID_ARG
+    assert call(B=1 << 20, H=1 << 12, D=64) == tg.TG_ERR_INVALID_ARG   # batch * heads >= 2^31
+    assert call(H=1 << 17) == tg.TG_ERR_INVALID_ARG                    # heads * head_dim >= 2^24
     assert call(Sq=-1) == tg.TG_ERR_INVALID_ARG
     assert call(scale=float("nan")) == tg.TG_ERR_INVALID_ARG
     assert call(Q=0) == tg.TG_ERR_INVALID_ARG

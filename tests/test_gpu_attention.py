@@ -177,3 +177,14 @@ def test_running_maximum_moves_every_tile(tg, oracle_lib, direction):
         ref = oracle_lib.attention(q, k, v, B, Sq, Sk, H, D, 1.0, causal)
         say(f"attention {direction} scores causal={causal}")
         check(run(tg, q, k, v, B, Sq, Sk, H, D, 1.0, causal), ref, v)
+
+
+def test_more_heads_than_a_grid_row(tg, oracle_lib):
+    # 70000 (batch, head) pairs: more than 65535, the limit of a grid's y
+    # extent, so the pairs run along x
+    B, Sq, Sk, H, D = 1, 3, 5, 70000, 64
+    q, k, v = qkv(B, Sq, Sk, H, D, 14)
+    for causal in (False, True):
+        ref = oracle_lib.attention(q, k, v, B, Sq, Sk, H, D, 0.125, causal)
+        say(f"attention H={H} causal={causal}")
+        check(run(tg, q, k, v, B, Sq, Sk, H, D, 0.125, causal), ref, v)

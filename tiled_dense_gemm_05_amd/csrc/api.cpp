@@ -306,7 +306,9 @@ int tg_attention_fwd_f16(const void *Q, const void *K, const void *V, void *O, i
                          float scale, int causal, hipStream_t stream)
 {
     if (batch < 0 || seq_q < 0 || seq_k < 0 || heads < 0 || batch > kMaxDim ||
-        seq_q > kMaxDim || seq_k > kMaxDim || heads > 65535)
+        seq_q > kMaxDim || seq_k > kMaxDim || heads > kMaxDim)
+        return TG_ERR_INVALID_ARG;
+    if ((__int128)batch * heads > kMaxDim)      // (batch, head) pairs run along the grid's x
         return TG_ERR_INVALID_ARG;
     if (head_dim != 64 && head_dim != 128)
         return TG_ERR_INVALID_ARG;

@@ -214,11 +214,14 @@ attention_fwd_kernel(AttnArgs p)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t bh = blockIdx.y;
+    const int64_t bh = blockIdx.x;
     const int64_t b = bh / p.H, h = bh % p.H;
     const int64_t Sq = p.Sq, Sk = p.Sk;
-    // with the causal mask later query blocks have more keys: start those first
-    const int64_t qb = p.causal ? (int64_t)gridDim.x - 1 - blockIdx.x : (int64_t)blockIdx.x;
+    // Workgroups are dispatched x fastest: every (batch, head) of one query
+    // block before the next block.  With the causal mask later query blocks
+    // have more keys, so those go first, across all (batch, head) at once.
+    const int64_t qj = p.qb0 + (int64_t)blockIdx.y;
+    const int64_t qb = p.causal ? p.nqb - 1 - qj : qj;
     const int64_t q0 = qb * T::BQ;
     const int64_t rs = p.H * T::D;                   // elements between sequence positions
     const int64_t q = q0 + wave * 32 + (lane & 31);  // this lane's query
@@ -380,21 +383,19 @@ attention_fwd_kernel(AttnArgs p)
 template <int D, int NW>
 hipError_t launch_attn(const AttnArgs &p, hipStream_t stream)
 {
-    const int64_t gx = (p.Sq + 32 * NW - 1) / (32 * NW);
-    if (gx > 0x7fffffff)
+    // grid x: (batch, head) pairs; grid y: query blocks, in launches of at
+    // most 65535
+    const int64_t bh = p.B * p.H;
+    const int64_t nqb = (p.Sq + 32 * NW - 1) / (32 * NW);
+    if (bh > 0x7fffffff)
         return hipErrorInvalidValue;
-    // grid rows are (batch, head) pairs; batches go in launches of at most
-    // 65535 rows
-    const int64_t per = 65535 / p.H;
-    for (int64_t b0 = 0; b0 < p.B; b0 += per) {
+    for (int64_t y0 = 0; y0 < nqb; y0 += 65535) {
         AttnArgs q = p;
-        q.B = (p.B - b0) < per ? (p.B - b0) : per;
-        q.Q = p.Q + b0 * p.Sq * p.H * D;
-        q.K = p.K + b0 * p.Sk * p.H * D;
-        q.V = p.V + b0 * p.Sk * p.H * D;
-        q.O = p.O + b0 * p.Sq * p.H * D;
-        hipLaunchKernelGGL((attention_fwd_kernel<AttnCfg<D, NW>>), dim3((unsigned)gx,
-                           (unsigned)(q.B * p.H)), dim3(64 * NW), 0, stream, q);
+        q.nqb = nqb;
+        q.qb0 = y0;
+        const int64_t gy = (nqb - y0) < 65535 ? (nqb - y0) : 65535;
+        hipLaunchKernelGGL((attention_fwd_kernel<AttnCfg<D, NW>>), dim3((unsigned)bh, (unsigned)gy),
+                           dim3(64 * NW), 0, stream, q);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;

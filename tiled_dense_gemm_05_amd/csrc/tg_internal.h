@@ -133,6 +133,7 @@ struct AttnArgs {
     float scale;
     int causal;
     int variant;      // 0: four waves per workgroup, 1: eight
+    int64_t nqb, qb0; // query blocks in all, and the first one of this launch (set by the launcher)
 };
 hipError_t launch_attention(const AttnArgs &p, hipStream_t stream);
 
