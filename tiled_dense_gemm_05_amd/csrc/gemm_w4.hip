@@ -40,6 +40,8 @@
 // the scales of 64 rows fit in the LDS left over by the ring.
 #include "tg_internal.h"
 
+#include <utility>
+
 namespace tg {
 namespace {
 
@@ -63,10 +65,14 @@ constexpr int kLds = 160 * 1024;
 // The weight (from HBM) and A (small, L2-resident) have separate rings per K
 // group: SW weight stages (loads SW-1 steps ahead) and SA A stages (SA-1
 // steps ahead, SA <= SW), so the LDS goes to keeping more weight in flight.
-template <int MB_, int SW_, int SA_, bool BF16_, int KG_ = 1>
+template <int MB_, int SW_, int SA_, bool BF16_, int KG_ = 1, int GS_ = 0>
 struct W4Cfg {
     static constexpr int MB = MB_;                   // 16-row blocks of A
     static constexpr int SW = SW_, SA = SA_;         // ring stages per K group
+    // GS > 0: a scale group is GS 32-k substeps (G = 32 GS divides the 256-k
+    // step), fixed at compile time; 0: any G, tracked at run time
+    static constexpr int GS = GS_;
+    static constexpr int P = SW % SA == 0 ? SW : SW * SA;   // steps after which both rings repeat
     static constexpr int DW = SW - 1, DA = SA - 1;   // steps of look-ahead
     static constexpr bool BF16 = BF16_;
     static constexpr int KG = KG_;                   // K groups of four waves
@@ -93,8 +99,8 @@ struct W4Cfg {
 // rings fit, depths chosen so the rings plus the scales of K/G <= 64..128
 // groups fit the 160 KiB of LDS.  The single-group forms serve group sizes
 // that do not divide 256.
-template <int MB, bool BF16>
-using W4Two = W4Cfg<MB, MB == 1 ? 6 : MB == 2 ? 5 : 3, MB == 1 ? 3 : 2, BF16, 2>;
+template <int MB, bool BF16, int GS>
+using W4Two = W4Cfg<MB, MB == 1 ? 6 : MB == 2 ? 5 : 3, MB == 1 ? 3 : 2, BF16, 2, GS>;
 template <int MB, bool BF16>
 using W4One = W4Cfg<MB, MB <= 2 ? 8 : 6, MB == 1 ? 4 : 3, BF16, 1>;
 
@@ -207,6 +213,13 @@ __device__ __forceinline__ f16x8 dequant8(uint32_t w, uint32_t nib)
     return __builtin_bit_cast(f16x8, out);
 }
 
+// f(integral_constant<int, I>) for each I of the sequence, in order.
+template <class F, int... I>
+__device__ __forceinline__ void for_each_index(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
 template <class T>
 __global__ void __launch_bounds__(T::NT) gemm_w4_kernel(W4Args p)
 {
@@ -270,10 +283,21 @@ __global__ void __launch_bounds__(T::NT) gemm_w4_kernel(W4Args p)
         const int gs = st * T::KG + kg;
         return (int64_t)(gs < steps ? step_of(gs) : gs) * kKS;
     };
+    // When K is a multiple of the step, a step is either wholly inside K or
+    // wholly past it: the descriptor's record count (0 past the end) makes
+    // the range check, with no per-lane compare.
+    const bool kfull = K % kKS == 0;
     auto issue_a = [&](int st) {
         const int64_t k0 = k_of(st);
-        const i32x4 ra = make_rsrc(Ab + k0);
+        i32x4 ra = make_rsrc(Ab + k0);
         const uint32_t base = aring + (uint32_t)((st % T::SA) * T::A_BYTES);
+        if (kfull) {
+            ra.z = k0 < K ? (int)kOutOfRange : 0;
+#pragma unroll
+            for (int i = 0; i < T::A_LD; ++i)
+                dma16(ra, a_voff[i], base + (uint32_t)((wave + 4 * i) * 1024));
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < T::A_LD; ++i)
             dma16(ra, k0 + a_col[i] < K ? a_voff[i] : kOutOfRange,
@@ -281,8 +305,15 @@ __global__ void __launch_bounds__(T::NT) gemm_w4_kernel(W4Args p)
     };
     auto issue_w = [&](int st) {
         const int64_t k0 = k_of(st);
-        const i32x4 rw = make_rsrc(Wb + k0 / 2);
+        i32x4 rw = make_rsrc(Wb + k0 / 2);
         const uint32_t base = wring + (uint32_t)((st % T::SW) * T::W_BYTES);
+        if (kfull) {
+            rw.z = k0 < K ? (int)kOutOfRange : 0;
+#pragma unroll
+            for (int i = 0; i < T::W_LD; ++i)
+                dma16_nt(rw, w_voff[i], base + (uint32_t)((wave + 4 * i) * 1024));
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < T::W_LD; ++i)
             dma16_nt(rw, k0 + w_col[i] < K ? w_voff[i] : kOutOfRange,
@@ -374,6 +405,86 @@ __global__ void __launch_bounds__(T::NT) gemm_w4_kernel(W4Args p)
         }
     }
 
+    if constexpr (T::GS > 0) {
+        // Fixed group size: the loop is unrolled over the rings' period P so
+        // every stage offset is a constant (LDS reads are a per-lane base
+        // register plus an immediate), the first product of a group starts
+        // from a zero accumulator and the group ends are known.
+        uint32_t wb_off[kKS / 32], ab_off[kKS / 32];
+#pragma unroll
+        for (int ks = 0; ks < kKS / 32; ++ks) {
+            wb_off[ks] = (uint32_t)(kg * T::GROUP) + w_off[ks];
+            ab_off[ks] = (uint32_t)(kg * T::GROUP + T::W_RING) + a_off[ks];
+        }
+        const uint8_t *sm = smem;
+        constexpr int GPS = 8 / T::GS;                   // groups per step
+        auto body = [&](int st, auto u_c) {
+            constexpr int u = decltype(u_c)::value;
+            wait_vmcnt<T::WAIT>();
+            block_barrier();
+            issue_a(st + T::DA);
+            issue_w(st + T::DW);
+            constexpr uint32_t ws = (uint32_t)((u % T::SW) * T::W_BYTES);
+            constexpr uint32_t as = (uint32_t)((u % T::SA) * T::A_BYTES);
+            const int gs = st * T::KG + kg;
+            const int g0 = (gs < steps ? step_of(gs) : gs) * GPS;   // first group of the step
+            uint32_t wb[kKS / 32];
+#pragma unroll
+            for (int ks = 0; ks < kKS / 32; ++ks)
+                wb[ks] = *reinterpret_cast<const lds_u32 *>(
+                    (const lds_u8 *)sm + (wb_off[ks] + ws));
+            f16x8 af[2][T::MB];
+#pragma unroll
+            for (int mb = 0; mb < T::MB; ++mb)
+                af[0][mb] = *reinterpret_cast<const lds_f16x8 *>(
+                    (const lds_u8 *)sm + (ab_off[0] + as + mb * 16 * 512));
+#pragma unroll
+            for (int ks = 0; ks < kKS / 32; ++ks) {
+                if (ks + 1 < kKS / 32) {
+#pragma unroll
+                    for (int mb = 0; mb < T::MB; ++mb)
+                        af[(ks + 1) & 1][mb] = *reinterpret_cast<const lds_f16x8 *>(
+                            (const lds_u8 *)sm + (ab_off[ks + 1] + as + mb * 16 * 512));
+                }
+                const f16x8 wf = dequant8<T::BF16>(wb[ks], nib);
+                const bool first = ks % T::GS == 0;
+#pragma unroll
+                for (int mb = 0; mb < T::MB; ++mb) {
+                    const f32x4 c = first ? f32x4{} : part[mb];
+                    if constexpr (T::BF16)
+                        part[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, wf),
+                            __builtin_bit_cast(bf16x8, af[ks & 1][mb]), c, 0, 0, 0);
+                    else
+                        part[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf, af[ks & 1][mb], c, 0,
+                                                                          0, 0);
+                }
+                if (ks % T::GS == T::GS - 1) {
+                    const int g = g0 + ks / T::GS;
+                    if (g < groups) {
+                        const u32x2 sv =
+                            *reinterpret_cast<const lds_u32x2 *>(scl + g * kRows + orow);
+                        const float s0 = bits_to_float<T::BF16>((uint16_t)(sv.x & 0xffff));
+                        const float s1 = bits_to_float<T::BF16>((uint16_t)(sv.x >> 16));
+                        const float s2 = bits_to_float<T::BF16>((uint16_t)(sv.y & 0xffff));
+                        const float s3 = bits_to_float<T::BF16>((uint16_t)(sv.y >> 16));
+#pragma unroll
+                        for (int mb = 0; mb < T::MB; ++mb) {
+                            acc[mb][0] += s0 * part[mb][0];
+                            acc[mb][1] += s1 * part[mb][1];
+                            acc[mb][2] += s2 * part[mb][2];
+                            acc[mb][3] += s3 * part[mb][3];
+                        }
+                    }
+                }
+            }
+        };
+        for (int st0 = 0; st0 < gsteps; st0 += T::P)
+            for_each_index([&](auto u_c) {
+                if (st0 + decltype(u_c)::value < gsteps)
+                    body(st0 + decltype(u_c)::value, u_c);
+            }, std::make_integer_sequence<int, T::P>{});
+    } else
     for (int st = 0; st < gsteps; ++st) {
         // this wave's loads of step st have landed once at most WAIT later
         // loads are outstanding (A of step st is the newest of the two); the
@@ -493,6 +604,15 @@ hipError_t launch_w4(const W4Args &p, hipStream_t stream)
     return hipGetLastError();
 }
 
+// Two K groups with the group size fixed at compile time (G = 32 GS).
+template <int GS, bool BF16>
+hipError_t launch_two(int64_t mb, const W4Args &p, hipStream_t stream)
+{
+    if (mb <= 1) return launch_w4<W4Two<1, BF16, GS>>(p, stream);
+    if (mb <= 2) return launch_w4<W4Two<2, BF16, GS>>(p, stream);
+    return launch_w4<W4Two<3, BF16, GS>>(p, stream);
+}
+
 template <bool BF16>
 hipError_t launch_w4_mb(const W4Args &p, hipStream_t stream)
 {
@@ -501,13 +621,20 @@ hipError_t launch_w4_mb(const W4Args &p, hipStream_t stream)
     // every scale group inside one 256-k step.
     const int64_t mb = (p.M + 15) / 16;
     const bool two = kKS % p.G == 0;
-    if (mb <= 1)
-        return two ? launch_w4<W4Two<1, BF16>>(p, stream) : launch_w4<W4One<1, BF16>>(p, stream);
-    if (mb <= 2)
-        return two ? launch_w4<W4Two<2, BF16>>(p, stream) : launch_w4<W4One<2, BF16>>(p, stream);
-    if (mb <= 3)
-        return two ? launch_w4<W4Two<3, BF16>>(p, stream) : launch_w4<W4One<3, BF16>>(p, stream);
-    return launch_w4<W4One<4, BF16>>(p, stream);
+    if (!two) {
+        if (mb <= 1) return launch_w4<W4One<1, BF16>>(p, stream);
+        if (mb <= 2) return launch_w4<W4One<2, BF16>>(p, stream);
+        if (mb <= 3) return launch_w4<W4One<3, BF16>>(p, stream);
+        return launch_w4<W4One<4, BF16>>(p, stream);
+    }
+    if (mb > 3)
+        return launch_w4<W4One<4, BF16>>(p, stream);
+    switch (p.G) {
+    case 32: return launch_two<1, BF16>(mb, p, stream);
+    case 64: return launch_two<2, BF16>(mb, p, stream);
+    case 128: return launch_two<4, BF16>(mb, p, stream);
+    default: return launch_two<8, BF16>(mb, p, stream);
+    }
 }
 
 // The plain form: one thread per output, fp32 fused multiply-add over k
@@ -553,9 +680,9 @@ bool w4_layout_ok(const W4Args &p)
         return false;
     const int64_t mb = (p.M + 15) / 16;
     const bool two = kKS % p.G == 0;
-    const int64_t ring = mb <= 1 ? (two ? W4Two<1, false>::RING : W4One<1, false>::RING)
-                         : mb <= 2 ? (two ? W4Two<2, false>::RING : W4One<2, false>::RING)
-                         : mb <= 3 ? (two ? W4Two<3, false>::RING : W4One<3, false>::RING)
+    const int64_t ring = mb <= 1 ? (two ? W4Two<1, false, 4>::RING : W4One<1, false>::RING)
+                         : mb <= 2 ? (two ? W4Two<2, false, 4>::RING : W4One<2, false>::RING)
+                         : mb <= 3 ? (two ? W4Two<3, false, 4>::RING : W4One<3, false>::RING)
                                    : W4One<4, false>::RING;
     return ring + (p.K / p.G) * kRows * 2 <= kLds;
 }
