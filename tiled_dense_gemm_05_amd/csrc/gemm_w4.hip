@@ -25,14 +25,24 @@
 //    columns of one row).  A lane's weight fragment is one 4-byte LDS read:
 //    eight nibbles, turned into eight exact fp16 / bf16 integers -8..7 in
 //    registers (fp16: the bit pattern 0x6400 | (q + 8) is 1024 + q + 8, less
-//    1032; bf16: through fp32).
+//    1032; bf16: the fp32 pattern 0x4b000000 | (q + 8) is 2^23 + q + 8, less
+//    2^23 + 8, then packed).
 //  * Products of A with q are exact, and the sums of one group of k run in
 //    fp32 on the matrix cores; at the end of each group the lane multiplies
 //    its four partial sums by their rows' scales and adds them to the
 //    accumulator.  The scales of the workgroup's 64 rows are copied to LDS
-//    once, before the loop.
+//    once, while the first weight steps are in flight.
+//  * The kernel is bound by instruction issue on its two waves per SIMD, not
+//    by HBM.  When G divides the 256-k step (G = 32, 64, 128, 256: the
+//    common formats) the group structure is a template parameter and the
+//    step loop is unrolled over the rings' period, so LDS addresses are
+//    loop-invariant registers (no address arithmetic per read) and a
+//    group's first product starts from a zero accumulator; other G keep a
+//    run-time group counter.
 //  * Weight chunks past N, A rows past M and k past K read as zeros through
-//    the buffer descriptors' range check (a zero byte is two zero weights).
+//    the buffer descriptors' range check (a zero byte is two zero weights);
+//    when K is a multiple of 256 a step is wholly in or out of K and the
+//    check is the descriptor's record count alone.
 //  * Workgroups start their K walk at different steps (see `rot`).
 // Requirements (checked by the dispatcher): A 16-byte aligned, lda % 8 == 0;
 // Wq 16-byte aligned, ldw % 16 == 0; K % G == 0 with G a multiple of 32;
