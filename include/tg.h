@@ -202,7 +202,7 @@ enum {
     TG_PATH_GENERIC = 2,    /* 128x128 tiles, any alignment, masked loads */
     TG_PATH_TILE128 = 3,    /* 128x128x32 tiles, 256 threads, aligned operands */
     TG_PATH_TILE256 = 4,    /* 256x256 tiles for large shapes, aligned operands */
-    TG_PATH_SKINNY = 5,     /* M <= 64: column slices streaming B, K split over waves */
+    TG_PATH_SKINNY = 5,     /* M <= 64: column slices streaming B, K steps dealt to waves */
     TG_PATH_W4 = 6,         /* tg_gemm_w4's int4-weight kernel (reported, not forced) */
     TG_PATH_ATTENTION = 7,  /* tg_attention_fwd_f16's kernel (reported, not forced) */
     TG_PATH_COUNT = 8
