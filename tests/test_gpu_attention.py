@@ -188,3 +188,36 @@ def test_more_heads_than_a_grid_row(tg, oracle_lib):
         ref = oracle_lib.attention(q, k, v, B, Sq, Sk, H, D, 0.125, causal)
         say(f"attention H={H} causal={causal}")
         check(run(tg, q, k, v, B, Sq, Sk, H, D, 0.125, causal), ref, v)
+
+
+@pytest.mark.parametrize("variant", [0, 1])
+def test_more_query_blocks_than_a_grid_column(tg, variant):
+    # 65536 * 256 + 100 queries: more query blocks than 65535 (the grid's y
+    # extent), so the launcher splits them over several launches.  One key:
+    # without the mask every query's output is that key's value row; with it
+    # only the last query sees the key and every other output is 0.
+    B, Sq, Sk, H, D = 1, 65536 * 256 + 100, 1, 1, 64
+    Q = torch.zeros(B * Sq * H * D, dtype=torch.int16, device="cuda")
+    K = torch.zeros(B * Sk * H * D, dtype=torch.int16, device="cuda")
+    vrow = np.arange(D, dtype=np.float64) / 16.0 - 2.0
+    V = dev(f16(vrow))
+    stream = torch.cuda.current_stream().cuda_stream
+    assert tg.tg_set_attention_variant(variant) >= 0
+    try:
+        for causal in (0, 1):
+            say(f"attention Sq={Sq} causal={causal} variant={variant}")
+            O = torch.full((B * Sq * H * D,), 0x7E00, dtype=torch.int16, device="cuda")
+            st = tg.tg_attention_fwd_f16(Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(),
+                                         B, Sq, Sk, H, D, 0.125, causal, stream)
+            assert st == tg.TG_OK, tg.tg_status_string(st)
+            torch.cuda.synchronize()
+            O = O.view(Sq, D)
+            want = V.view(1, D)
+            if causal:
+                assert torch.equal(O[-1:], want)
+                assert int(torch.count_nonzero(O[:-1])) == 0
+            else:
+                assert bool((O == want).all())
+            del O
+    finally:
+        tg.tg_set_attention_variant(-1)
