@@ -163,6 +163,42 @@ def run_workload(tg, torch, w: wl.Workload, steps: int, warmup: int, epilogue=No
     return ms, path, nbuf
 
 
+def run_vendor(torch, w: wl.Workload, steps: int, warmup: int, dtype: str, layout: str):
+    """Times torch.matmul (hipBLASLt on ROCm) on the workload's operands, as
+    context for the library's own rate: the same product without the ReLU,
+    into a preallocated output.  Dense layouts only (the named workloads with
+    lda = K, ldb = N); a batch goes through torch.bmm with contiguous
+    operands."""
+    a, b = wl.generate_dense(w.M, w.N, w.K, w.dist, w.seed, batch=w.batch, dtype=dtype)
+    td = torch.bfloat16 if dtype == "bf16" else torch.float16
+    dev = torch.device("cuda:0")
+    A = torch.from_numpy(a.view(np.int16)).to(dev).view(td).reshape(w.batch, w.M, w.K)
+    B = torch.from_numpy(b.view(np.int16)).to(dev).view(td).reshape(w.batch, w.K, w.N)
+    if layout == "nk":
+        # an (N,K) weight: the product reads it through a transposed view
+        Bt = B.transpose(1, 2).contiguous()
+        B = Bt.transpose(1, 2)
+    C = torch.empty(w.batch, w.M, w.N, dtype=td, device=dev)
+    if w.batch == 1:
+        A2, B2, C2 = A[0], B[0], C[0]
+        call = lambda: torch.matmul(A2, B2, out=C2)
+    else:
+        B = B.contiguous()
+        call = lambda: torch.bmm(A, B, out=C)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        call()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
 def run_w4(tg, torch, M: int, N: int, K: int, G: int, steps: int, warmup: int, dtype: str):
     """Times the weight-only int4 GEMM (tg_gemm_w4) on an (N,K) int4 weight with
     group scales; several weight copies rotate so reruns come from HBM."""
@@ -473,6 +509,9 @@ def main():
     ap.add_argument("--w4", action="store_true",
                     help="time the weight-only int4 GEMM on the decode shape "
                          "16 x 16384 x 8192, groups of 128 (tg_gemm_w4) and exit")
+    ap.add_argument("--vendor", action="store_true",
+                    help="context only: time the vendor GEMM (torch.matmul, i.e. hipBLASLt) "
+                         "on the same operands, without the ReLU, and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -504,6 +543,21 @@ def main():
         knobs["b_layout"] = args.layout
     if args.calibrate_copy:
         calibration_copy(torch)
+    if args.vendor:
+        w = wl.WORKLOADS[args.workload]
+        ms = run_vendor(torch, w, args.steps, args.warmup, args.dtype, args.layout)
+        rate = w.flops / (ms * 1e-3) / 1e12
+        log(f"vendor {args.workload} {args.dtype} {args.layout}: {ms * 1e3:.1f} us/call, "
+            f"{rate:.1f} TFLOP/s")
+        print(json.dumps({
+            "metric": "TFLOP/s vendor fp16 GEMM (context, no ReLU)", "value": rate,
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
+            "config": {"workload": args.workload, "M": w.M, "N": w.N, "K": w.K,
+                       "batch": w.batch, "b_layout": args.layout,
+                       "library": "torch.matmul (hipBLASLt)"}}), flush=True)
+        return
     if args.attention:
         B, S, H, D = 4, 4096, 32, 128
         if args.attention_variant != -1:
