@@ -84,6 +84,9 @@ def _load():
     lib.oracle_gemm_w4.restype = ctypes.c_int
     lib.oracle_attention_f16.argtypes = [vp] * 4 + [i64] * 5 + [ctypes.c_double, ci, vp, vp, ci]
     lib.oracle_attention_f16.restype = ctypes.c_int
+    lib.oracle_attention_gqa_f16.argtypes = [vp] * 4 + [i64] * 6 + [ctypes.c_double, ci, vp, vp,
+                                                                    ci]
+    lib.oracle_attention_gqa_f16.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -385,16 +388,21 @@ def gemm_w4(A, Wq, S, M: int, N: int, K: int, G: int, lda: int | None = None,
 
 
 def attention(Q, K, V, B: int, Sq: int, Sk: int, H: int, D: int, scale: float,
-              causal: bool = False, want_stats: bool = False, threads: int | None = None):
-    """softmax(scale * Q K^T) V per (batch, head), fp16 bits laid out
-    (batch, seq, heads, head_dim); with ``causal`` key j is visible to query i
+              causal: bool = False, want_stats: bool = False, threads: int | None = None,
+              kv_heads: int | None = None):
+    """softmax(scale * Q K^T) V per (batch, head), fp16 bits; Q and O laid out
+    (batch, seq, heads, head_dim), K and V (batch, seq, kv_heads, head_dim)
+    with query head h reading key/value head h // (heads // kv_heads)
+    (kv_heads defaults to heads); with ``causal`` key j is visible to query i
     when j <= i + (Sk - Sq).  Returns O (uint16, B*Sq*H*D) and, with
     ``want_stats``, each query's row maximum and sum of exponentials, shaped
     (B, H, Sq)."""
+    Hkv = H if kv_heads is None else kv_heads
     Q = _u16(Q).reshape(-1)
     K = _u16(K).reshape(-1)
     V = _u16(V).reshape(-1)
-    for name, t, n in (("Q", Q, B * Sq * H * D), ("K", K, B * Sk * H * D), ("V", V, B * Sk * H * D)):
+    for name, t, n in (("Q", Q, B * Sq * H * D), ("K", K, B * Sk * Hkv * D),
+                       ("V", V, B * Sk * Hkv * D)):
         if t.size < n:
             raise ValueError(f"{name} holds {t.size} elements, needs {n}")
     O = np.zeros(B * Sq * H * D, dtype=np.uint16)
@@ -402,8 +410,8 @@ def attention(Q, K, V, B: int, Sq: int, Sk: int, H: int, D: int, scale: float,
     if want_stats:
         mx = np.zeros((B, H, Sq), dtype=np.float64)
         sm = np.zeros((B, H, Sq), dtype=np.float64)
-    rc = _load().oracle_attention_f16(
-        _ptr(Q), _ptr(K), _ptr(V), _ptr(O), B, Sq, Sk, H, D, float(scale), int(causal),
+    rc = _load().oracle_attention_gqa_f16(
+        _ptr(Q), _ptr(K), _ptr(V), _ptr(O), B, Sq, Sk, H, Hkv, D, float(scale), int(causal),
         _ptr(mx) if mx is not None else None, _ptr(sm) if sm is not None else None,
         host_threads() if threads is None else threads)
     if rc != 0:

@@ -10,14 +10,18 @@
  * programs they measure ("TileLang paper reading" page, section 5; the
  * "80-line MLA article" page) but give no formula.  The reading taken is the
  * standard definition, written out: for every batch b, head h and query i,
+ * with kv = h / (H / Hkv) the key/value head that query head h reads,
  *
- *   s_j   = scale * sum_d Q[b][i][h][d] * K[b][j][h][d]     (binary64, d ascending)
+ *   s_j   = scale * sum_d Q[b][i][h][d] * K[b][j][kv][d]    (binary64, d ascending)
  *   keys j visible to i: all j < Sk, or with `causal` only j <= i + (Sk - Sq)
  *   p_j   = exp(s_j - max_visible s) / sum_visible exp(s - max s)
- *   O[b][i][h][d] = enc16( sum_j p_j * V[b][j][h][d] )      (binary64, j ascending)
+ *   O[b][i][h][d] = enc16( sum_j p_j * V[b][j][kv][d] )     (binary64, j ascending)
  *
- * Q, K, V, O are fp16 (bit patterns), laid out (batch, seq, heads, head_dim)
- * contiguously.  A query with no visible key (causal, Sk < Sq) gets O = 0.
+ * Q, O are fp16 (bit patterns) laid out (batch, seq, heads, head_dim), K, V
+ * (batch, seq, kv_heads, head_dim), contiguously; kv_heads = heads is
+ * multi-head attention, fewer key/value heads each shared by a group of
+ * consecutive query heads is grouped-query attention (one: multi-query).  A
+ * query with no visible key (causal, Sk < Sq) gets O = 0.
  * exp is the C library's binary64 exp.  The result is exact up to binary64
  * rounding; the GPU kernel (fp32 scores and sums, an online maximum,
  * exp2-based exponentials, fp16 probabilities) is expected to agree within a
@@ -72,7 +76,7 @@ typedef struct {
     const uint16_t *Q, *K, *V;
     uint16_t *O;
     double *rowmax, *rowsum;   /* optional, [b][h][i] */
-    int64_t B, Sq, Sk, H, D;
+    int64_t B, Sq, Sk, H, Hkv, D;
     double scale;
     int causal, nthreads, tid;
 } ajob_t;
@@ -80,7 +84,7 @@ typedef struct {
 static void *attn_worker(void *p)
 {
     ajob_t *j = (ajob_t *)p;
-    const int64_t D = j->D, Sk = j->Sk, H = j->H;
+    const int64_t D = j->D, Sk = j->Sk, H = j->H, Hkv = j->Hkv, group = H / Hkv;
     double *q = (double *)malloc(sizeof(double) * (size_t)D);
     double *s = (double *)malloc(sizeof(double) * (size_t)(Sk > 0 ? Sk : 1));
     double *o = (double *)malloc(sizeof(double) * (size_t)D);
@@ -99,7 +103,7 @@ static void *attn_worker(void *p)
         }
         double mx = -INFINITY;
         for (int64_t k = 0; k < visible; ++k) {
-            const uint16_t *kr = j->K + ((b * Sk + k) * H + h) * D;
+            const uint16_t *kr = j->K + ((b * Sk + k) * Hkv + h / group) * D;
             double acc = 0.0;
             for (int64_t d = 0; d < D; ++d)
                 acc += q[d] * a_dec16(kr[d]);
@@ -115,7 +119,7 @@ static void *attn_worker(void *p)
         for (int64_t d = 0; d < D; ++d)
             o[d] = 0.0;
         for (int64_t k = 0; k < visible; ++k) {
-            const uint16_t *vr = j->V + ((b * Sk + k) * H + h) * D;
+            const uint16_t *vr = j->V + ((b * Sk + k) * Hkv + h / group) * D;
             const double pk = s[k] / sum;
             for (int64_t d = 0; d < D; ++d)
                 o[d] += pk * a_dec16(vr[d]);
@@ -133,12 +137,17 @@ static void *attn_worker(void *p)
     return NULL;
 }
 
-/* Returns 0, or -2 for a bad size. */
-int oracle_attention_f16(const uint16_t *Q, const uint16_t *K, const uint16_t *V, uint16_t *O,
-                         int64_t B, int64_t Sq, int64_t Sk, int64_t H, int64_t D, double scale,
-                         int causal, double *rowmax, double *rowsum, int nthreads)
+/* Returns 0, or -2 for a bad size (kv_heads must divide heads). */
+int oracle_attention_gqa_f16(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                             uint16_t *O, int64_t B, int64_t Sq, int64_t Sk, int64_t H,
+                             int64_t Hkv, int64_t D, double scale, int causal, double *rowmax,
+                             double *rowsum, int nthreads)
 {
     if (B < 0 || Sq < 0 || Sk < 0 || H < 0 || D <= 0)
+        return -2;
+    if (H == 0)
+        return 0;
+    if (Hkv <= 0 || H % Hkv != 0)
         return -2;
     if (nthreads <= 0) {
         long n = sysconf(_SC_NPROCESSORS_ONLN);
@@ -155,7 +164,7 @@ int oracle_attention_f16(const uint16_t *Q, const uint16_t *K, const uint16_t *V
     for (int t = 0; t < nt; ++t) {
         ajob_t *j = &jobs[t];
         j->Q = Q; j->K = K; j->V = V; j->O = O; j->rowmax = rowmax; j->rowsum = rowsum;
-        j->B = B; j->Sq = Sq; j->Sk = Sk; j->H = H; j->D = D; j->scale = scale;
+        j->B = B; j->Sq = Sq; j->Sk = Sk; j->H = H; j->Hkv = Hkv; j->D = D; j->scale = scale;
         j->causal = causal; j->nthreads = nt; j->tid = t;
         if (nt == 1)
             attn_worker(j);
@@ -166,4 +175,13 @@ int oracle_attention_f16(const uint16_t *Q, const uint16_t *K, const uint16_t *V
         for (int t = 0; t < nt; ++t)
             pthread_join(th[t], NULL);
     return 0;
+}
+
+/* Multi-head attention: as many key/value heads as query heads. */
+int oracle_attention_f16(const uint16_t *Q, const uint16_t *K, const uint16_t *V, uint16_t *O,
+                         int64_t B, int64_t Sq, int64_t Sk, int64_t H, int64_t D, double scale,
+                         int causal, double *rowmax, double *rowsum, int nthreads)
+{
+    return oracle_attention_gqa_f16(Q, K, V, O, B, Sq, Sk, H, H, D, scale, causal, rowmax, rowsum,
+                                    nthreads);
 }

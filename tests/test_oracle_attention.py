@@ -152,3 +152,49 @@ def test_row_statistics(oracle_lib):
         s = 0.5 * (K[:i + 1] @ Q[i])
         assert np.isclose(mx[0, 0, i], s.max(), rtol=0, atol=1e-12)
         assert np.isclose(sm[0, 0, i], np.exp(s - s.max()).sum(), rtol=1e-12)
+
+
+def numpy_attention_gqa(q, k, v, B, Sq, Sk, H, Hkv, D, scale, causal):
+    # independent reference: repeat each key/value head over its group of
+    # query heads, then plain multi-head attention in numpy
+    g = H // Hkv
+    K = v16(k).reshape(B, Sk, Hkv, D).repeat(g, axis=2)
+    V = v16(v).reshape(B, Sk, Hkv, D).repeat(g, axis=2)
+    return numpy_attention(q, f16(K.reshape(-1)), f16(V.reshape(-1)), B, Sq, Sk, H, D, scale,
+                           causal)
+
+
+@pytest.mark.parametrize("B,Sq,Sk,H,Hkv,D,causal", [
+    (1, 7, 9, 4, 2, 8, False), (2, 5, 11, 6, 3, 16, True), (1, 1, 33, 8, 1, 32, False),
+    (2, 12, 12, 4, 4, 16, True), (1, 3, 20, 6, 2, 64, True)])
+def test_grouped_query_heads_match_numpy(oracle_lib, B, Sq, Sk, H, Hkv, D, causal):
+    rng = np.random.default_rng(Sq * 31 + H)
+    q = f16(rng.uniform(-2, 2, B * Sq * H * D))
+    k = f16(rng.uniform(-2, 2, B * Sk * Hkv * D))
+    v = f16(rng.uniform(-1, 1, B * Sk * Hkv * D))
+    scale = 1.0 / np.sqrt(D)
+    got = oracle_lib.attention(q, k, v, B, Sq, Sk, H, D, scale, causal, kv_heads=Hkv)
+    ref16 = f16(numpy_attention_gqa(q, k, v, B, Sq, Sk, H, Hkv, D, scale, causal))
+    ulp = np.spacing(np.abs(ref16.view(np.float16))).astype(np.float64)
+    assert np.all(np.abs(v16(got) - v16(ref16)) <= ulp)
+    assert np.mean(got == ref16) > 0.99
+
+
+def test_query_heads_of_a_group_share_keys_and_values(oracle_lib):
+    # two query heads with identical queries in one group give identical
+    # outputs; the same queries in another group (other keys) differ
+    B, Sq, Sk, H, Hkv, D = 1, 4, 10, 4, 2, 16
+    rng = np.random.default_rng(21)
+    qh = f16(rng.uniform(-1, 1, Sq * D)).reshape(Sq, 1, D)
+    q = np.repeat(qh, H, axis=1).reshape(-1)
+    k = f16(rng.uniform(-1, 1, B * Sk * Hkv * D))
+    v = f16(rng.uniform(-1, 1, B * Sk * Hkv * D))
+    o = oracle_lib.attention(q, k, v, B, Sq, Sk, H, D, 0.5, kv_heads=Hkv).reshape(Sq, H, D)
+    assert np.array_equal(o[:, 0], o[:, 1]) and np.array_equal(o[:, 2], o[:, 3])
+    assert not np.array_equal(o[:, 0], o[:, 2])
+
+
+def test_grouped_query_bad_group_is_rejected(oracle_lib):
+    z = np.zeros(64, np.uint16)
+    with pytest.raises(ValueError):
+        oracle_lib.attention(z, z, z, 1, 1, 1, 3, 8, 1.0, kv_heads=2)
