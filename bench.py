@@ -235,23 +235,30 @@ def run_w4(tg, torch, M: int, N: int, K: int, G: int, steps: int, warmup: int, d
     return ms, tg.tg_path_name(tg.tg_last_path()), nbuf, wbytes + 2 * (M * K + M * N)
 
 
-def run_attention(tg, torch, B: int, S: int, H: int, D: int, causal: bool, steps: int,
-                  warmup: int):
-    """Times the fused attention forward (tg_attention_fwd_f16) on (B, S, H, D)
-    queries, keys and values with normal(0,1) Q and K, uniform(-1,1) V."""
+def run_attention(tg, torch, B: int, S: int, H: int, Hkv: int, D: int, causal: bool,
+                  steps: int, warmup: int):
+    """Times the fused attention forward on (B, S, H, D) queries and (B, S, Hkv, D)
+    keys and values (tg_attention_fwd_f16 when Hkv = H, else
+    tg_attention_fwd_f16_gqa), normal(0,1) Q and K, uniform(-1,1) V."""
     rng = np.random.default_rng(11)
     dev = torch.device("cuda:0")
     n = B * S * H * D
-    Q, K, V = (torch.from_numpy(wl.to_f16_bits(rng.normal(0, 1, n) if i < 2 else
-                                               rng.uniform(-1, 1, n)).view(np.int16)).to(dev)
-               for i in range(3))
+    nkv = B * S * Hkv * D
+    Q, K, V = (torch.from_numpy(wl.to_f16_bits(rng.normal(0, 1, m) if i < 2 else
+                                               rng.uniform(-1, 1, m)).view(np.int16)).to(dev)
+               for i, m in enumerate((n, nkv, nkv)))
     O = torch.empty(n, dtype=torch.int16, device=dev)
     stream = torch.cuda.current_stream()
     scale = 1.0 / float(np.sqrt(D))
 
     def call():
-        st = tg.tg_attention_fwd_f16(Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), B,
-                                     S, S, H, D, scale, int(causal), stream.cuda_stream)
+        if Hkv == H:
+            st = tg.tg_attention_fwd_f16(Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(),
+                                         B, S, S, H, D, scale, int(causal), stream.cuda_stream)
+        else:
+            st = tg.tg_attention_fwd_f16_gqa(Q.data_ptr(), K.data_ptr(), V.data_ptr(),
+                                             O.data_ptr(), B, S, S, H, Hkv, D, scale,
+                                             int(causal), stream.cuda_stream)
         if st != tg.TG_OK:
             raise RuntimeError(tg.tg_status_string(st))
 
@@ -504,6 +511,9 @@ def main():
     ap.add_argument("--attention", choices=["full", "causal"], default=None,
                     help="time the fused attention forward on 4 x 4096 x 32 heads x 128 "
                          "(tg_attention_fwd_f16) and exit")
+    ap.add_argument("--kv-heads", type=int, default=32,
+                    help="key/value heads of the attention bench (32: multi-head; a divisor "
+                         "of 32: grouped-query, tg_attention_fwd_f16_gqa)")
     ap.add_argument("--attention-variant", type=int, default=-1,
                     help="attention workgroup shape (tg_set_attention_variant)")
     ap.add_argument("--w4", action="store_true",
@@ -562,20 +572,23 @@ def main():
         B, S, H, D = 4, 4096, 32, 128
         if args.attention_variant != -1:
             tg.tg_set_attention_variant(args.attention_variant)
+        Hkv = args.kv_heads
+        if Hkv <= 0 or H % Hkv:
+            sys.exit(f"--kv-heads must divide {H}")
         causal = args.attention == "causal"
-        ms = run_attention(tg, torch, B, S, H, D, causal, args.steps, args.warmup)
+        ms = run_attention(tg, torch, B, S, H, Hkv, D, causal, args.steps, args.warmup)
         # two products of 2*S*S*D flop per (batch, head); half the pairs when causal
         flops = 4.0 * B * H * S * S * D * (0.5 if causal else 1.0)
         tflops = flops / (ms * 1e-3) / 1e12
-        log(f"attention {B}x{S}x{H}x{D} {args.attention}: {ms * 1e3:.1f} us/call, "
-            f"{tflops:.1f} TFLOP/s")
+        name = f"attention_{B}x{S}x{H}x{D}" + (f"_kv{Hkv}" if Hkv != H else "")
+        log(f"{name} {args.attention}: {ms * 1e3:.1f} us/call, {tflops:.1f} TFLOP/s")
         print(json.dumps({
             "metric": "TFLOP/s fused attention forward", "value": tflops, "unit": "TFLOP/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
             "data": "synthetic",
-            "config": {"workload": f"attention_{B}x{S}x{H}x{D}_{args.attention}", "batch": B,
-                       "seq": S, "heads": H, "head_dim": D, "causal": causal,
+            "config": {"workload": f"{name}_{args.attention}", "batch": B,
+                       "seq": S, "heads": H, "kv_heads": Hkv, "head_dim": D, "causal": causal,
                        "path": tg.tg_path_name(tg.tg_last_path())},
             "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_F16_TFLOPS,
                          "unit": "TFLOP/s", "frac": tflops / PEAK_F16_TFLOPS,

@@ -186,6 +186,22 @@ int tg_attention_fwd_f16(const void *Q, const void *K, const void *V, void *O,
                          int64_t batch, int64_t seq_q, int64_t seq_k, int64_t heads,
                          int64_t head_dim, float scale, int causal, hipStream_t stream);
 
+/*
+ * The same with grouped-query heads: K and V hold kv_heads heads, laid out
+ * (batch, seq_k, kv_heads, head_dim), and query head h reads key/value head
+ * h / (heads / kv_heads) (kv_heads = heads: tg_attention_fwd_f16; 1:
+ * multi-query attention).  The standard grouped-query form of the definition
+ * above (the pages' MLA decode shares one latent key/value across all query
+ * heads in the same way).  kv_heads must divide heads; batch * kv_heads and
+ * seq_q * (heads / kv_heads) must stay below 2^31.  The query heads of a
+ * group run in the same workgroups, so every K/V tile is read once per group
+ * of heads.  Otherwise as tg_attention_fwd_f16.
+ */
+int tg_attention_fwd_f16_gqa(const void *Q, const void *K, const void *V, void *O,
+                             int64_t batch, int64_t seq_q, int64_t seq_k, int64_t heads,
+                             int64_t kv_heads, int64_t head_dim, float scale, int causal,
+                             hipStream_t stream);
+
 /* A static, human-readable name for a tg_status value. */
 const char *tg_status_string(int status);
 
@@ -204,7 +220,7 @@ enum {
     TG_PATH_TILE256 = 4,    /* 256x256 tiles for large shapes, aligned operands */
     TG_PATH_SKINNY = 5,     /* M <= 64: column slices streaming B, K steps dealt to waves */
     TG_PATH_W4 = 6,         /* tg_gemm_w4's int4-weight kernel (reported, not forced) */
-    TG_PATH_ATTENTION = 7,  /* tg_attention_fwd_f16's kernel (reported, not forced) */
+    TG_PATH_ATTENTION = 7,  /* the attention entry points' kernel (reported, not forced) */
     TG_PATH_COUNT = 8
 };
 int tg_set_path(int path);

@@ -174,6 +174,28 @@ def test_attention_validation(tg):
     assert tg.tg_set_attention_variant(-1) == 0
 
 
+def test_grouped_query_attention_validation(tg):
+    f = tg.tg_attention_fwd_f16_gqa
+
+    def call(B=1, Sq=8, Sk=8, H=8, Hkv=2, D=64, causal=0, K=P):
+        return f(P, K, P, P, B, Sq, Sk, H, Hkv, D, 0.1, causal, 0)
+
+    assert call(Hkv=3) == tg.TG_ERR_INVALID_ARG          # kv_heads must divide heads
+    assert call(Hkv=16) == tg.TG_ERR_INVALID_ARG         # more key/value heads than heads
+    assert call(Hkv=0) == tg.TG_ERR_INVALID_ARG
+    assert call(Hkv=-2) == tg.TG_ERR_INVALID_ARG
+    # (batch, key/value head) pairs and the query rows of one key/value head
+    # (positions x heads per group) each stay below 2^31
+    assert call(B=1 << 20, H=1 << 12, Hkv=1 << 12) == tg.TG_ERR_INVALID_ARG
+    assert call(Sq=1 << 20, H=1 << 12, Hkv=1) == tg.TG_ERR_INVALID_ARG
+    assert call(Sq=1 << 21, H=1 << 11, Hkv=2) == tg.TG_ERR_INVALID_ARG   # 2^21 x 1024 rows
+    assert call(D=96) == tg.TG_ERR_INVALID_ARG
+    assert call(K=0) == tg.TG_ERR_INVALID_ARG                          # keys but no K
+    # empty problems succeed without touching the device, whatever kv_heads is
+    assert call(B=0) == tg.TG_OK and call(Sq=0) == tg.TG_OK
+    assert call(H=0, Hkv=0) == tg.TG_OK and call(H=0, Hkv=3) == tg.TG_OK
+
+
 def _gpu_visible():
     try:
         import torch
@@ -192,6 +214,8 @@ def test_valid_call_without_device_reports_no_device(tg):
     assert tg.tg_gemm_w4(0, 1, P, P, P, P, 0, 4, 8, 128, 64, 128, 64, 2, 8,
                          0) == tg.TG_ERR_NO_DEVICE
     assert tg.tg_attention_fwd_f16(P, P, P, P, 1, 8, 8, 2, 64, 0.1, 1, 0) == tg.TG_ERR_NO_DEVICE
+    assert tg.tg_attention_fwd_f16_gqa(P, P, P, P, 1, 8, 8, 8, 2, 64, 0.1, 1,
+                                       0) == tg.TG_ERR_NO_DEVICE
     for dtype in (tg.TG_DTYPE_F16, tg.TG_DTYPE_BF16):
         for layout in (tg.TG_B_KN, tg.TG_B_NK):
             st = tg.tg_gemm_ex(dtype, layout, tg.TG_ACT_NONE, P, P, P, 0, 4, 4, 4, 4, 4, 4, 0, 0,

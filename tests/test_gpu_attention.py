@@ -221,3 +221,95 @@ def test_more_query_blocks_than_a_grid_column(tg, variant):
             del O
     finally:
         tg.tg_set_attention_variant(-1)
+
+
+# Grouped-query heads: K and V hold Hkv heads, query head h reads key/value
+# head h / (H / Hkv).
+GQA_CASES = [
+    # B, Sq, Sk, H, Hkv, D, causal
+    (2, 100, 300, 8, 2, 128, False), (2, 100, 300, 8, 2, 128, True),
+    (1, 1, 4096, 32, 8, 128, False),        # one decode step, four heads a group
+    (1, 1, 2000, 16, 1, 64, True),          # multi-query decode step
+    (3, 37, 37, 6, 3, 64, True),            # two heads a group, odd lengths
+    (1, 200, 77, 4, 1, 64, True),           # fewer keys than queries: early rows see none
+    (1, 65, 129, 12, 4, 128, True),         # three heads a group: rows straddle blocks
+    (2, 5, 0, 4, 2, 128, False),            # no keys
+    (1, 33, 300, 128, 1, 64, False),        # 128 heads on one key/value head
+    (1, 70, 70, 5, 5, 128, True),           # one head a group: the multi-head layout
+]
+
+
+def qkv_gqa(B, Sq, Sk, H, Hkv, D, seed):
+    rng = np.random.default_rng(41_000 + seed)
+    q = f16(rng.normal(0, 1, B * Sq * H * D))
+    k = f16(rng.normal(0, 1, B * Sk * Hkv * D))
+    v = f16(rng.uniform(-1, 1, B * Sk * Hkv * D))
+    return q, k, v
+
+
+def run_gqa(tg, q, k, v, B, Sq, Sk, H, Hkv, D, scale, causal):
+    q_d = dev(q)
+    k_d = dev(k) if k.size else dev(np.zeros(8))
+    v_d = dev(v) if v.size else dev(np.zeros(8))
+    n = B * Sq * H * D
+    o_d = dev(np.full(n + 64, 0x7E00, np.uint16))
+    st = tg.tg_attention_fwd_f16_gqa(q_d.data_ptr(), k_d.data_ptr(), v_d.data_ptr(),
+                                     o_d.data_ptr(), B, Sq, Sk, H, Hkv, D, scale, int(causal),
+                                     torch.cuda.current_stream().cuda_stream)
+    assert st == tg.TG_OK, tg.tg_status_string(st)
+    torch.cuda.synchronize()
+    out = host(o_d)
+    assert np.all(out[n:] == 0x7E00), "wrote past O"
+    assert tg.tg_path_name(tg.tg_last_path()) == "attention"
+    return out[:n]
+
+
+@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("B,Sq,Sk,H,Hkv,D,causal", GQA_CASES)
+def test_grouped_query_matches_oracle(tg, oracle_lib, variant, B, Sq, Sk, H, Hkv, D, causal):
+    q, k, v = qkv_gqa(B, Sq, Sk, H, Hkv, D, Sq + Sk + H)
+    scale = 1.0 / np.sqrt(D)
+    ref = oracle_lib.attention(q, k, v, B, Sq, Sk, H, D, scale, causal, kv_heads=Hkv)
+    say(f"gqa B={B} Sq={Sq} Sk={Sk} H={H} Hkv={Hkv} D={D} causal={causal} variant={variant}")
+    assert tg.tg_set_attention_variant(variant) >= 0
+    try:
+        got = run_gqa(tg, q, k, v, B, Sq, Sk, H, Hkv, D, scale, causal)
+    finally:
+        tg.tg_set_attention_variant(-1)
+    check(got, ref, v)
+
+
+def test_grouped_query_with_one_head_a_group_is_the_multi_head_call(tg):
+    B, Sq, Sk, H, D = 2, 150, 260, 3, 128
+    q, k, v = qkv(B, Sq, Sk, H, D, 15)
+    say("gqa with kv_heads = heads against tg_attention_fwd_f16")
+    a = run(tg, q, k, v, B, Sq, Sk, H, D, 0.09, True)
+    b = run_gqa(tg, q, k, v, B, Sq, Sk, H, H, D, 0.09, True)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_query_benchmark_shape_sampled(tg, oracle_lib, causal):
+    # 4 x 4096 positions, 32 query heads on 8 key/value heads, head size 128:
+    # the oracle computes 64-position windows of a few heads at the start and
+    # the end of the sequence
+    B, S, H, Hkv, D = 4, 4096, 32, 8, 128
+    g = H // Hkv
+    rng = np.random.default_rng(16)
+    q = f16(rng.normal(0, 1, B * S * H * D))
+    k = f16(rng.normal(0, 1, B * S * Hkv * D))
+    v = f16(rng.uniform(-1, 1, B * S * Hkv * D))
+    scale = 1.0 / np.sqrt(D)
+    say(f"gqa benchmark shape causal={causal}")
+    out = run_gqa(tg, q, k, v, B, S, S, H, Hkv, D, scale, causal).reshape(B, S, H, D)
+    Q = q.reshape(B, S, H, D)
+    K, V = (t.reshape(B, S, Hkv, D) for t in (k, v))
+    for b, h in ((0, 0), (1, g - 1), (3, H - 1)):
+        for s0 in (0, S - 64):
+            n = 64
+            nk = s0 + n if causal else S
+            sl_q = np.ascontiguousarray(Q[b, s0:s0 + n, h]).reshape(-1)
+            sl_k = np.ascontiguousarray(K[b, :nk, h // g]).reshape(-1)
+            sl_v = np.ascontiguousarray(V[b, :nk, h // g]).reshape(-1)
+            ref = oracle_lib.attention(sl_q, sl_k, sl_v, 1, n, nk, 1, D, scale, causal)
+            check(np.ascontiguousarray(out[b, s0:s0 + n, h]).reshape(-1), ref, sl_v)

@@ -45,6 +45,7 @@ EXPORTED_SYMBOLS = (
     "tg_gemm_ex",
     "tg_gemm_w4",
     "tg_attention_fwd_f16",
+    "tg_attention_fwd_f16_gqa",
     "tg_set_attention_variant",
 )
 
@@ -80,6 +81,9 @@ _lib.tg_gemm_w4.argtypes = [ctypes.c_int] * 2 + [_vp] * 5 + [_i64] * 8 + [_vp]
 _lib.tg_gemm_w4.restype = ctypes.c_int
 _lib.tg_attention_fwd_f16.argtypes = [_vp] * 4 + [_i64] * 5 + [ctypes.c_float, ctypes.c_int, _vp]
 _lib.tg_attention_fwd_f16.restype = ctypes.c_int
+_lib.tg_attention_fwd_f16_gqa.argtypes = [_vp] * 4 + [_i64] * 6 + [ctypes.c_float, ctypes.c_int,
+                                                                 _vp]
+_lib.tg_attention_fwd_f16_gqa.restype = ctypes.c_int
 _lib.tg_set_attention_variant.argtypes = [ctypes.c_int]
 _lib.tg_set_attention_variant.restype = ctypes.c_int
 _lib.tg_status_string.argtypes = [ctypes.c_int]
@@ -137,6 +141,15 @@ def tg_attention_fwd_f16(Q: int, K: int, V: int, O: int, batch: int, seq_q: int,
     """Raw attention-forward call, returns the tg_status code."""
     return _lib.tg_attention_fwd_f16(Q, K, V, O, batch, seq_q, seq_k, heads, head_dim, scale,
                                      causal, stream)
+
+
+def tg_attention_fwd_f16_gqa(Q: int, K: int, V: int, O: int, batch: int, seq_q: int, seq_k: int,
+                             heads: int, kv_heads: int, head_dim: int, scale: float, causal: int,
+                             stream: int = 0) -> int:
+    """Raw grouped-query attention-forward call (K and V hold kv_heads heads), returns the
+    tg_status code."""
+    return _lib.tg_attention_fwd_f16_gqa(Q, K, V, O, batch, seq_q, seq_k, heads, kv_heads,
+                                         head_dim, scale, causal, stream)
 
 
 def tg_status_string(status: int) -> str:

@@ -301,14 +301,17 @@ int tg_gemm_w4(int dtype, int activation, const void *A, const void *Wq, const v
     return TG_OK;
 }
 
-int tg_attention_fwd_f16(const void *Q, const void *K, const void *V, void *O, int64_t batch,
-                         int64_t seq_q, int64_t seq_k, int64_t heads, int64_t head_dim,
-                         float scale, int causal, hipStream_t stream)
+int tg_attention_fwd_f16_gqa(const void *Q, const void *K, const void *V, void *O,
+                             int64_t batch, int64_t seq_q, int64_t seq_k, int64_t heads,
+                             int64_t kv_heads, int64_t head_dim, float scale, int causal,
+                             hipStream_t stream)
 {
-    if (batch < 0 || seq_q < 0 || seq_k < 0 || heads < 0 || batch > kMaxDim ||
+    if (batch < 0 || seq_q < 0 || seq_k < 0 || heads < 0 || kv_heads < 0 || batch > kMaxDim ||
         seq_q > kMaxDim || seq_k > kMaxDim || heads > kMaxDim)
         return TG_ERR_INVALID_ARG;
-    if ((__int128)batch * heads > kMaxDim)      // (batch, head) pairs run along the grid's x
+    if (heads > 0 && (kv_heads == 0 || heads % kv_heads != 0))
+        return TG_ERR_INVALID_ARG;
+    if ((__int128)batch * kv_heads > kMaxDim)   // (batch, key/value head) pairs run along grid x
         return TG_ERR_INVALID_ARG;
     if (head_dim != 64 && head_dim != 128)
         return TG_ERR_INVALID_ARG;
@@ -318,12 +321,14 @@ int tg_attention_fwd_f16(const void *Q, const void *K, const void *V, void *O, i
         return TG_ERR_INVALID_ARG;
     if (batch == 0 || seq_q == 0 || heads == 0)
         return TG_OK;
+    if ((__int128)seq_q * (heads / kv_heads) > kMaxDim)   // query rows of one key/value head
+        return TG_ERR_INVALID_ARG;
     if (Q == nullptr || O == nullptr || (seq_k > 0 && (K == nullptr || V == nullptr)))
         return TG_ERR_INVALID_ARG;
     if (!aligned16(Q) || !aligned16(O) || (seq_k > 0 && (!aligned16(K) || !aligned16(V))))
         return TG_ERR_INVALID_ARG;
     const __int128 rows_q = (__int128)batch * seq_q * heads * head_dim;
-    const __int128 rows_k = (__int128)batch * seq_k * heads * head_dim;
+    const __int128 rows_k = (__int128)batch * seq_k * kv_heads * head_dim;
     if (rows_q > kMaxExtent || rows_k > kMaxExtent)
         return TG_ERR_INVALID_ARG;
     int st = check_device();
@@ -334,7 +339,7 @@ int tg_attention_fwd_f16(const void *Q, const void *K, const void *V, void *O, i
     p.K = static_cast<const uint16_t *>(K);
     p.V = static_cast<const uint16_t *>(V);
     p.O = static_cast<uint16_t *>(O);
-    p.B = batch; p.Sq = seq_q; p.Sk = seq_k; p.H = heads; p.D = head_dim;
+    p.B = batch; p.Sq = seq_q; p.Sk = seq_k; p.H = heads; p.Hkv = kv_heads; p.D = head_dim;
     p.scale = scale;
     p.causal = causal;
     p.variant = g_attn_variant.load(std::memory_order_relaxed);
@@ -342,6 +347,14 @@ int tg_attention_fwd_f16(const void *Q, const void *K, const void *V, void *O, i
         return TG_ERR_HIP;
     g_last_path.store(TG_PATH_ATTENTION, std::memory_order_relaxed);
     return TG_OK;
+}
+
+int tg_attention_fwd_f16(const void *Q, const void *K, const void *V, void *O, int64_t batch,
+                         int64_t seq_q, int64_t seq_k, int64_t heads, int64_t head_dim,
+                         float scale, int causal, hipStream_t stream)
+{
+    return tg_attention_fwd_f16_gqa(Q, K, V, O, batch, seq_q, seq_k, heads, heads, head_dim,
+                                    scale, causal, stream);
 }
 
 const char *tg_status_string(int status)

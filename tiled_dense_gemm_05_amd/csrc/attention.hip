@@ -9,15 +9,20 @@
 // and sum of exponentials per query, rescale the output accumulator when the
 // maximum grows (here: by more than 2^8), divide once at the end.
 //
-// Layout: Q (B, Sq, H, D), K and V (B, Sk, H, D), O (B, Sq, H, D), each
-// contiguous; D = 64 or 128.  Key j is visible to query i always, or with
-// `causal` when j <= i + (Sk - Sq).
+// Layout: Q (B, Sq, H, D), K and V (B, Sk, Hkv, D), O (B, Sq, H, D), each
+// contiguous; D = 64 or 128; query head h reads key/value head h / (H / Hkv)
+// (Hkv = H: multi-head; fewer: grouped-query, one: multi-query).  Key j is
+// visible to query i always, or with `causal` when j <= i + (Sk - Sq).
 //
 // gfx950 design:
-//  * One workgroup of NW waves per 32*NW queries of one (batch, head); wave
-//    w owns queries 32w .. 32w+31.  K/V tiles of 64 keys are staged in a
-//    2-stage LDS ring by buffer_load_dwordx4 ... lds (rows past Sk read as
-//    zeros and are masked out of the softmax).
+//  * One workgroup of NW waves per 32*NW query rows of one (batch,
+//    key/value head); the rows are the (position, query head) pairs of the
+//    heads that share it, position-major, so a K/V tile serves every head of
+//    the group and positions still grow with the row (the causal logic sees
+//    row r at position r / g, g = H / Hkv).  Wave w owns rows 32w .. 32w+31.
+//    K/V tiles of 64 keys are staged in a 2-stage LDS ring by
+//    buffer_load_dwordx4 ... lds (rows past Sk read as zeros and are masked
+//    out of the softmax).
 //  * Both products run on v_mfma_f32_32x32x16_f16 with the operand roles
 //    swapped as in the GEMM kernels: S^T = K Q^T and O^T = V^T P^T.  A lane
 //    then holds 32 scores (and, later, 4-column groups of the output) of ONE
@@ -214,24 +219,32 @@ attention_fwd_kernel(AttnArgs p)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t bh = blockIdx.x;
-    const int64_t b = bh / p.H, h = bh % p.H;
+    const int64_t bh = blockIdx.x;                 // (batch, key/value head)
+    const int64_t b = bh / p.Hkv, kvh = bh % p.Hkv;
     const int64_t Sq = p.Sq, Sk = p.Sk;
+    const int64_t g = p.H / p.Hkv;                   // query heads per key/value head
+    const int64_t rows = Sq * g;
     // Workgroups are dispatched x fastest: every (batch, head) of one query
     // block before the next block.  With the causal mask later query blocks
     // have more keys, so those go first, across all (batch, head) at once.
     const int64_t qj = p.qb0 + (int64_t)blockIdx.y;
     const int64_t qb = p.causal ? p.nqb - 1 - qj : qj;
-    const int64_t q0 = qb * T::BQ;
-    const int64_t rs = p.H * T::D;                   // elements between sequence positions
-    const int64_t q = q0 + wave * 32 + (lane & 31);  // this lane's query
+    const int64_t q0 = qb * T::BQ;                 // first row of the block
+    const int64_t rs = p.Hkv * T::D;                 // K/V elements between positions
+    const int64_t r = q0 + wave * 32 + (lane & 31);  // this lane's row
+    const bool live = r < rows;
+    const int64_t q = r / g;                         // its query position
+    const int64_t h = kvh * g + r % g;               // and query head
     const int hi = lane >> 5;
+    const int64_t shift = Sk - Sq;                   // causal: query i sees keys j <= i + shift
+    const int64_t wq0 = (q0 + wave * 32) / g;        // position of the wave's first row
+    const int64_t wq1 = (q0 + wave * 32 + 31) / g;   // ... and of its last
 
     // Keys this block needs: all, or with the causal mask up to the block's
-    // last query's horizon.
+    // last position's horizon.
     int64_t kend = Sk;
     if (p.causal) {
-        const int64_t lim = q0 + T::BQ + (Sk - Sq);
+        const int64_t lim = (q0 + T::BQ - 1) / g + shift + 1;
         kend = lim < 0 ? 0 : (lim < Sk ? lim : Sk);
     }
     const int tiles = (int)((kend + kBK - 1) / kBK);
@@ -239,11 +252,11 @@ attention_fwd_kernel(AttnArgs p)
     // Q^T fragments (second operand): lane holds Q[q][16 ds + 8 hi .. + 7].
     f16x8 qf[T::DS];
     {
-        const uint16_t *qrow = p.Q + ((b * Sq + (q < Sq ? q : 0)) * p.H + h) * T::D;
+        const uint16_t *qrow = p.Q + ((b * Sq + (live ? q : 0)) * p.H + (live ? h : 0)) * T::D;
 #pragma unroll
         for (int ds = 0; ds < T::DS; ++ds) {
             qf[ds] = f16x8{};
-            if (q < Sq)
+            if (live)
                 qf[ds] = *reinterpret_cast<const f16x8 *>(qrow + ds * 16 + 8 * hi);
             // a negative scale is carried by Q (negation is exact), so the
             // scores are scaled by |scale| and their maximum stays a maximum
@@ -266,8 +279,8 @@ attention_fwd_kernel(AttnArgs p)
         k_voff[i] = (uint32_t)((row * rs + swz_k<T::CD>(row, pc) * 8) * 2);
         v_voff[i] = (uint32_t)((row * rs + swz_v<T::CD>(row, pc) * 8) * 2);
     }
-    const uint16_t *Kb = p.K + (b * Sk * p.H + h) * T::D;
-    const uint16_t *Vb = p.V + (b * Sk * p.H + h) * T::D;
+    const uint16_t *Kb = p.K + (b * Sk * p.Hkv + kvh) * T::D;
+    const uint16_t *Vb = p.V + (b * Sk * p.Hkv + kvh) * T::D;
     auto issue = [&](int t) {
         const int64_t k0 = (int64_t)t * kBK;
         const i32x4 rk = make_rsrc(Kb + k0 * rs);
@@ -293,9 +306,7 @@ attention_fwd_kernel(AttnArgs p)
     // |scale| * log2(e), kept positive so masked scores (-inf) map to zero
     // (a zero scale becomes 1e-30: every exponential is then 1 to fp32 precision)
     const float sl2 = __builtin_fmaxf(__builtin_fabsf(p.scale) * 1.44269504088896340736f, 1.0e-30f);
-    const int64_t shift = Sk - Sq;               // causal: query i sees keys j <= i + shift
     const int64_t horizon = q + shift;
-    const int64_t wq0 = q0 + wave * 32;          // this wave's first query
 
     if (tiles > 0)
         issue(0);
@@ -307,7 +318,7 @@ attention_fwd_kernel(AttnArgs p)
         const int64_t k0 = (int64_t)t * kBK;
         // causal: none of this wave's queries sees the tile (it was loaded
         // for the block's later waves)
-        if (p.causal && k0 > wq0 + 31 + shift)
+        if (p.causal && k0 > wq1 + shift)
             continue;
         const lds_u16 *Ks = lds + (t & 1) * T::STAGE;
         const lds_u16 *Vs = Ks + T::TILE;
@@ -364,7 +375,7 @@ attention_fwd_kernel(AttnArgs p)
     // Output: the query's sum of exponentials is split over lanes l and l^32.
     const float l_all = l_run + __shfl_xor(l_run, 32);
     const float inv = l_all > 0.0f ? 1.0f / l_all : 0.0f;
-    if (q < Sq) {
+    if (live) {
         uint16_t *orow = p.O + ((b * Sq + q) * p.H + h) * T::D;
 #pragma unroll
         for (int db = 0; db < T::DB; ++db) {
@@ -383,10 +394,10 @@ attention_fwd_kernel(AttnArgs p)
 template <int D, int NW>
 hipError_t launch_attn(const AttnArgs &p, hipStream_t stream)
 {
-    // grid x: (batch, head) pairs; grid y: query blocks, in launches of at
-    // most 65535
-    const int64_t bh = p.B * p.H;
-    const int64_t nqb = (p.Sq + 32 * NW - 1) / (32 * NW);
+    // grid x: (batch, key/value head) pairs; grid y: blocks of query rows,
+    // in launches of at most 65535
+    const int64_t bh = p.B * p.Hkv;
+    const int64_t nqb = (p.Sq * (p.H / p.Hkv) + 32 * NW - 1) / (32 * NW);
     if (bh > 0x7fffffff)
         return hipErrorInvalidValue;
     for (int64_t y0 = 0; y0 < nqb; y0 += 65535) {

@@ -129,7 +129,7 @@ bool w4_layout_ok(const W4Args &p);
 struct AttnArgs {
     const uint16_t *Q, *K, *V;
     uint16_t *O;
-    int64_t B, Sq, Sk, H, D;
+    int64_t B, Sq, Sk, H, Hkv, D;     // Hkv divides H
     float scale;
     int causal;
     int variant;      // 0: four waves per workgroup, 1: eight
