@@ -7,6 +7,7 @@ CPU-baseline leg may import this package.  It shares no code with the HIP
 library under ``tiled_dense_gemm_05_amd`` and never imports it.
 
 The arithmetic lives in ``gemm_relu_oracle.c`` and ``attention_oracle.c``
+(attention, grouped-query attention and the latent-attention decode)
 (plain C, compiled with gcc,
 no BLAS, no SIMD intrinsics, no fast-math); this module only builds it, loads it
 with ctypes and marshals numpy arrays.  What it computes, and the passages it
@@ -87,6 +88,8 @@ def _load():
     lib.oracle_attention_gqa_f16.argtypes = [vp] * 4 + [i64] * 6 + [ctypes.c_double, ci, vp, vp,
                                                                     ci]
     lib.oracle_attention_gqa_f16.restype = ctypes.c_int
+    lib.oracle_mla_decode_f16.argtypes = [vp] * 4 + [i64] * 5 + [ctypes.c_double, vp, vp, ci]
+    lib.oracle_mla_decode_f16.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -416,6 +419,40 @@ def attention(Q, K, V, B: int, Sq: int, Sk: int, H: int, D: int, scale: float,
         host_threads() if threads is None else threads)
     if rc != 0:
         raise ValueError("bad attention sizes")
+    if want_stats:
+        return O, mx, sm
+    return O
+
+
+def mla_decode(Q, KV, B: int, H: int, Sk: int, scale: float, seqlens=None, Dl: int = 512,
+               Dr: int = 64, want_stats: bool = False, threads: int | None = None):
+    """Latent-attention decode, fp16 bits: Q (B, H, Dl + Dr), the cache KV
+    (B, Sk, Dl + Dr) whose first Dl values per token are both key and value,
+    O (B, H, Dl) = softmax over the first seqlens[b] tokens (all Sk when
+    seqlens is None) of scale * q . c_j, applied to the latent parts c_j[:Dl].
+    Returns O (uint16, B*H*Dl) and, with ``want_stats``, each (b, h)'s score
+    maximum and sum of exponentials, shaped (B, H)."""
+    Dq = Dl + Dr
+    Q = _u16(Q).reshape(-1)
+    KV = _u16(KV).reshape(-1)
+    if Q.size < B * H * Dq or KV.size < B * Sk * Dq:
+        raise ValueError("Q or KV too small")
+    sl = None
+    if seqlens is not None:
+        sl = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32).reshape(-1))
+        if sl.size < B:
+            raise ValueError("seqlens needs one entry per sequence")
+    O = np.zeros(B * H * Dl, dtype=np.uint16)
+    mx = sm = None
+    if want_stats:
+        mx = np.zeros((B, H), dtype=np.float64)
+        sm = np.zeros((B, H), dtype=np.float64)
+    rc = _load().oracle_mla_decode_f16(
+        _ptr(Q), _ptr(KV), _ptr(O), _ptr(sl) if sl is not None else None, B, H, Sk, Dl, Dr,
+        float(scale), _ptr(mx) if mx is not None else None,
+        _ptr(sm) if sm is not None else None, host_threads() if threads is None else threads)
+    if rc != 0:
+        raise ValueError("bad latent-attention sizes")
     if want_stats:
         return O, mx, sm
     return O

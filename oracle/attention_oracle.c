@@ -185,3 +185,119 @@ int oracle_attention_f16(const uint16_t *Q, const uint16_t *K, const uint16_t *V
     return oracle_attention_gqa_f16(Q, K, V, O, B, Sq, Sk, H, H, D, scale, causal, rowmax, rowsum,
                                     nthreads);
 }
+
+/*
+ * Latent-attention decode (the MLA decode the pages measure: the "TileLang
+ * paper reading" page, section 5, and the "80-line MLA article" page, which
+ * give its head size of 512 + 64 but no formula).  The reading taken is the
+ * absorbed DeepSeek form, written out: every cached token j of sequence b
+ * holds one row c_j of Dl + Dr fp16 values, the first Dl a latent vector
+ * shared by all heads as key and as value, the last Dr a rotary key part;
+ * each query head h holds q of Dl + Dr values (latent part, then rotary
+ * part), and with n = seqlens[b] (all Sk when seqlens is NULL)
+ *
+ *   s_j = scale * sum_{d < Dl+Dr} q[d] * c_j[d]      (binary64, d ascending)
+ *   p_j = exp(s_j - max_{j<n} s) / sum_{j<n} exp(s - max s)
+ *   O[b][h][d] = enc16( sum_{j<n} p_j * c_j[d] )     (d < Dl; binary64, j ascending)
+ *
+ * Q is (batch, heads, Dl + Dr), the cache KV (batch, Sk, Dl + Dr) and O
+ * (batch, heads, Dl), contiguously; n = 0 gives O = 0.  rowmax / rowsum,
+ * when given, receive max s and the sum of exp(s - max s) per (b, h).
+ * Returns 0, or -2 for a bad size or a seqlens entry outside [0, Sk].
+ */
+typedef struct {
+    const uint16_t *Q, *KV;
+    uint16_t *O;
+    const int32_t *seqlens;
+    double *rowmax, *rowsum;
+    int64_t B, H, Sk, Dl, Dr;
+    double scale;
+    int nthreads, tid;
+} mjob_t;
+
+static void *mla_worker(void *p)
+{
+    mjob_t *j = (mjob_t *)p;
+    const int64_t Dq = j->Dl + j->Dr, Sk = j->Sk;
+    double *q = (double *)malloc(sizeof(double) * (size_t)Dq);
+    double *s = (double *)malloc(sizeof(double) * (size_t)(Sk > 0 ? Sk : 1));
+    double *o = (double *)malloc(sizeof(double) * (size_t)(j->Dl > 0 ? j->Dl : 1));
+    for (int64_t r = j->tid; r < j->B * j->H; r += j->nthreads) {
+        const int64_t b = r / j->H, h = r % j->H;
+        const int64_t n = j->seqlens ? j->seqlens[b] : Sk;
+        for (int64_t d = 0; d < Dq; ++d)
+            q[d] = a_dec16(j->Q[(b * j->H + h) * Dq + d]);
+        double mx = -INFINITY;
+        for (int64_t k = 0; k < n; ++k) {
+            const uint16_t *c = j->KV + (b * Sk + k) * Dq;
+            double acc = 0.0;
+            for (int64_t d = 0; d < Dq; ++d)
+                acc += q[d] * a_dec16(c[d]);
+            s[k] = j->scale * acc;
+            if (s[k] > mx)
+                mx = s[k];
+        }
+        double sum = 0.0;
+        for (int64_t k = 0; k < n; ++k) {
+            s[k] = exp(s[k] - mx);
+            sum += s[k];
+        }
+        for (int64_t d = 0; d < j->Dl; ++d)
+            o[d] = 0.0;
+        for (int64_t k = 0; k < n; ++k) {
+            const uint16_t *c = j->KV + (b * Sk + k) * Dq;
+            const double pk = s[k] / sum;
+            for (int64_t d = 0; d < j->Dl; ++d)
+                o[d] += pk * a_dec16(c[d]);
+        }
+        for (int64_t d = 0; d < j->Dl; ++d)
+            j->O[(b * j->H + h) * j->Dl + d] = a_enc16(o[d]);
+        if (j->rowmax) {
+            j->rowmax[b * j->H + h] = mx;
+            j->rowsum[b * j->H + h] = sum;
+        }
+    }
+    free(q);
+    free(s);
+    free(o);
+    return NULL;
+}
+
+int oracle_mla_decode_f16(const uint16_t *Q, const uint16_t *KV, uint16_t *O,
+                          const int32_t *seqlens, int64_t B, int64_t H, int64_t Sk, int64_t Dl,
+                          int64_t Dr, double scale, double *rowmax, double *rowsum, int nthreads)
+{
+    if (B < 0 || H < 0 || Sk < 0 || Dl < 0 || Dr < 0 || Dl + Dr <= 0)
+        return -2;
+    if (seqlens)
+        for (int64_t b = 0; b < B; ++b)
+            if (seqlens[b] < 0 || seqlens[b] > Sk)
+                return -2;
+    if (nthreads <= 0) {
+        long n = sysconf(_SC_NPROCESSORS_ONLN);
+        nthreads = n > 0 ? (int)n : 1;
+    }
+    if (nthreads > 256)
+        nthreads = 256;
+    const int64_t rows = B * H;
+    if (rows == 0)
+        return 0;
+    int nt = (int)(rows < nthreads ? rows : nthreads);
+    pthread_t th[256];
+    mjob_t jobs[256];
+    for (int t = 0; t < nt; ++t) {
+        mjob_t *j = &jobs[t];
+        j->Q = Q; j->KV = KV; j->O = O; j->seqlens = seqlens;
+        j->rowmax = rowmax; j->rowsum = rowsum;
+        j->B = B; j->H = H; j->Sk = Sk; j->Dl = Dl; j->Dr = Dr; j->scale = scale;
+        j->nthreads = nt; j->tid = t;
+        if (nt == 1)
+            mla_worker(j);
+        else
+            pthread_create(&th[t], NULL, mla_worker, j);
+    }
+    if (nt > 1)
+        for (int t = 0; t < nt; ++t)
+            pthread_join(th[t], NULL);
+    return 0;
+}
