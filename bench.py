@@ -275,6 +275,41 @@ def run_attention(tg, torch, B: int, S: int, H: int, Hkv: int, D: int, causal: b
     return t0.elapsed_time(t1) / steps
 
 
+def run_mla(tg, torch, steps: int, warmup: int):
+    """Times the latent-attention decode (tg_mla_decode_f16) on the 64 x 8192-token,
+    128-head workload; returns (ms per call, path, workspace bytes)."""
+    w = wl.MLA_WORKLOAD
+    B, H, Sk = w["B"], w["H"], w["Sk"]
+    q, kv = wl.generate_mla(B, H, Sk, w["seed"])
+    dev = torch.device("cuda:0")
+    Q = torch.from_numpy(q.view(np.int16)).to(dev)
+    KV = torch.from_numpy(kv.view(np.int16)).to(dev)
+    del q, kv
+    O = torch.empty(B * H * 512, dtype=torch.int16, device=dev)
+    need = tg.tg_mla_decode_workspace_bytes(B, H, Sk)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    scale = 1.0 / float(np.sqrt(192.0))
+
+    def call():
+        st = tg.tg_mla_decode_f16(Q.data_ptr(), KV.data_ptr(), O.data_ptr(), 0, B, H, Sk,
+                                  scale, ws.data_ptr(), need, stream.cuda_stream)
+        if st != tg.TG_OK:
+            raise RuntimeError(tg.tg_status_string(st))
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        call()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps, tg.tg_path_name(tg.tg_last_path()), need
+
+
 def cpu_baseline(w: wl.Workload, target_s: float = 12.0):
     """The oracle, as it stands, on the host cores: rows 0..r-1 of the
     workload's C (all N columns, full K), r sized for about target_s seconds."""
@@ -516,6 +551,11 @@ def main():
                          "of 32: grouped-query, tg_attention_fwd_f16_gqa)")
     ap.add_argument("--attention-variant", type=int, default=-1,
                     help="attention workgroup shape (tg_set_attention_variant)")
+    ap.add_argument("--mla", action="store_true",
+                    help="time the latent-attention decode on 64 sequences x 8192 cached "
+                         "tokens x 128 heads, rows of 512 + 64 (tg_mla_decode_f16) and exit")
+    ap.add_argument("--mla-splits", type=int, default=-1,
+                    help="key ranges per sequence of the decode bench (tg_set_mla_splits)")
     ap.add_argument("--w4", action="store_true",
                     help="time the weight-only int4 GEMM on the decode shape "
                          "16 x 16384 x 8192, groups of 128 (tg_gemm_w4) and exit")
@@ -593,6 +633,30 @@ def main():
             "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_F16_TFLOPS,
                          "unit": "TFLOP/s", "frac": tflops / PEAK_F16_TFLOPS,
                          "traffic": None}}), flush=True)
+        return
+    if args.mla:
+        if args.mla_splits != -1:
+            tg.tg_set_mla_splits(args.mla_splits)
+        w = wl.MLA_WORKLOAD
+        B, H, Sk = w["B"], w["H"], w["Sk"]
+        ms, path, need = run_mla(tg, torch, args.steps, args.warmup)
+        # score product over 576 values and value product over 512, per (sequence, head, token)
+        flops = 2.0 * B * H * Sk * (576 + 512)
+        nbytes = 2.0 * (B * Sk * 576 + B * H * 576 + B * H * 512)
+        tflops = flops / (ms * 1e-3) / 1e12
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        log(f"{w['name']}: {ms * 1e3:.1f} us/call, {tflops:.1f} TFLOP/s, {gbs:.0f} GB/s, "
+            f"workspace {need} bytes")
+        print(json.dumps({
+            "metric": "GB/s latent-attention decode", "value": gbs, "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+            "data": "synthetic",
+            "config": {"workload": w["name"], "batch": B, "heads": H, "seq_k": Sk,
+                       "row": "512+64", "tflops": tflops, "path": path,
+                       "splits": args.mla_splits, "workspace_bytes": need},
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "traffic": None}}), flush=True)
         return
     if args.w4:
         M, N, K, G = 16, 16384, 8192, 128

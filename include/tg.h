@@ -202,6 +202,55 @@ int tg_attention_fwd_f16_gqa(const void *Q, const void *K, const void *V, void *
                              int64_t kv_heads, int64_t head_dim, float scale, int causal,
                              hipStream_t stream);
 
+/*
+ * Latent-attention decode (MLA), fp16: one query per sequence, every query
+ * head reading one shared cached row per token of 512 + 64 values (the head
+ * size the pages give for the MLA decode they measure: "TileLang paper
+ * reading" page, section 5; "80-line MLA article" page, sections 1-2).  The
+ * pages give no formula; this is the absorbed form, written out:
+ *
+ *   s_j = scale * sum_{d < 576} Q[b][h][d] KV[b][j][d]        (j < n_b)
+ *   O[b][h][d] = sum_j softmax(s)_j KV[b][j][d]              (d < 512)
+ *
+ * i.e. the first 512 values of a cached row are key and value, the last 64
+ * a rotary key part, and n_b = seqlens[b] (every seq_k tokens when seqlens
+ * is NULL; entries are clamped to [0, seq_k] on the device); n_b = 0 gives
+ * O = 0.
+ *   Q   (batch, heads, 576) fp16, contiguous, DEVICE pointer, 16-byte aligned
+ *   KV  (batch, seq_k, 576) fp16, contiguous, DEVICE pointer, 16-byte aligned
+ *   O   (batch, heads, 512) fp16, contiguous, DEVICE pointer, 16-byte aligned
+ *   seqlens  NULL or batch int32 values, DEVICE pointer
+ *   workspace  NULL or a DEVICE buffer of workspace_bytes (16-byte aligned),
+ *     owned by the caller, used as scratch by this call only (it must not be
+ *     shared by calls that may overlap).  With fewer sequences than the chip
+ *     has compute units the keys of each sequence are split into ranges whose
+ *     fp32 partial results live there; tg_mla_decode_workspace_bytes gives
+ *     the size the call would use.  A smaller (or no) workspace is accepted
+ *     and only lowers the number of ranges (results stay within the same
+ *     accuracy; the same workspace size gives the same bits).
+ * Scores and sums are fp32, probabilities enter the value product as fp16.
+ * scale must be finite (the absorbed form uses 1/sqrt(192)).  batch or
+ * heads = 0 is a no-op.  Errors, asynchrony and determinism as for the other
+ * entry points.
+ */
+int tg_mla_decode_f16(const void *Q, const void *KV, void *O, const int32_t *seqlens,
+                      int64_t batch, int64_t heads, int64_t seq_k, float scale,
+                      void *workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Workspace bytes tg_mla_decode_f16 uses for these sizes (0: none needed),
+ * or -1 for sizes it rejects.  Host-only: no HIP call.
+ */
+int64_t tg_mla_decode_workspace_bytes(int64_t batch, int64_t heads, int64_t seq_k);
+
+/*
+ * Test knob: the number of key ranges per sequence tg_mla_decode_f16 uses
+ * (0 or -1: chosen from the sizes, the default; still capped by the number
+ * of 32-key tiles and the workspace).  Returns the previous setting (0 for
+ * the default), or -2 for a value below -1.
+ */
+int tg_set_mla_splits(int splits);
+
 /* A static, human-readable name for a tg_status value. */
 const char *tg_status_string(int status);
 
@@ -221,7 +270,8 @@ enum {
     TG_PATH_SKINNY = 5,     /* M <= 64: column slices streaming B, K steps dealt to waves */
     TG_PATH_W4 = 6,         /* tg_gemm_w4's int4-weight kernel (reported, not forced) */
     TG_PATH_ATTENTION = 7,  /* the attention entry points' kernel (reported, not forced) */
-    TG_PATH_COUNT = 8
+    TG_PATH_MLA = 8,        /* tg_mla_decode_f16's kernels (reported, not forced) */
+    TG_PATH_COUNT = 9
 };
 int tg_set_path(int path);
 

@@ -30,7 +30,8 @@ TG_PATH_TILE256 = 4
 TG_PATH_SKINNY = 5
 TG_PATH_W4 = 6
 TG_PATH_ATTENTION = 7
-TG_PATH_COUNT = 8
+TG_PATH_MLA = 8
+TG_PATH_COUNT = 9
 
 EXPORTED_SYMBOLS = (
     "tg_gemm_relu_f16",
@@ -47,6 +48,9 @@ EXPORTED_SYMBOLS = (
     "tg_attention_fwd_f16",
     "tg_attention_fwd_f16_gqa",
     "tg_set_attention_variant",
+    "tg_mla_decode_f16",
+    "tg_mla_decode_workspace_bytes",
+    "tg_set_mla_splits",
 )
 
 TG_DTYPE_F16 = 0
@@ -86,6 +90,12 @@ _lib.tg_attention_fwd_f16_gqa.argtypes = [_vp] * 4 + [_i64] * 6 + [ctypes.c_floa
 _lib.tg_attention_fwd_f16_gqa.restype = ctypes.c_int
 _lib.tg_set_attention_variant.argtypes = [ctypes.c_int]
 _lib.tg_set_attention_variant.restype = ctypes.c_int
+_lib.tg_mla_decode_f16.argtypes = [_vp] * 4 + [_i64] * 3 + [ctypes.c_float, _vp, _i64, _vp]
+_lib.tg_mla_decode_f16.restype = ctypes.c_int
+_lib.tg_mla_decode_workspace_bytes.argtypes = [_i64] * 3
+_lib.tg_mla_decode_workspace_bytes.restype = ctypes.c_int64
+_lib.tg_set_mla_splits.argtypes = [ctypes.c_int]
+_lib.tg_set_mla_splits.restype = ctypes.c_int
 _lib.tg_status_string.argtypes = [ctypes.c_int]
 _lib.tg_status_string.restype = ctypes.c_char_p
 _lib.tg_set_path.argtypes = [ctypes.c_int]
@@ -150,6 +160,23 @@ def tg_attention_fwd_f16_gqa(Q: int, K: int, V: int, O: int, batch: int, seq_q: 
     tg_status code."""
     return _lib.tg_attention_fwd_f16_gqa(Q, K, V, O, batch, seq_q, seq_k, heads, kv_heads,
                                          head_dim, scale, causal, stream)
+
+
+def tg_mla_decode_f16(Q: int, KV: int, O: int, seqlens: int, batch: int, heads: int,
+                      seq_k: int, scale: float, workspace: int, workspace_bytes: int,
+                      stream: int = 0) -> int:
+    """Raw latent-attention decode call (seqlens and workspace may be 0 for none), returns the
+    tg_status code."""
+    return _lib.tg_mla_decode_f16(Q, KV, O, seqlens or None, batch, heads, seq_k, scale,
+                                  workspace or None, workspace_bytes, stream)
+
+
+def tg_mla_decode_workspace_bytes(batch: int, heads: int, seq_k: int) -> int:
+    return _lib.tg_mla_decode_workspace_bytes(batch, heads, seq_k)
+
+
+def tg_set_mla_splits(splits: int) -> int:
+    return _lib.tg_set_mla_splits(splits)
 
 
 def tg_status_string(status: int) -> str:
@@ -308,3 +335,40 @@ def linear(x, weight, bias=None, activation="none", out=None, stream=None):
     (M, K), weight (N, K) (the (N,K) B layout), bias N elements."""
     return gemm_ex(x, weight, bias=bias, activation=activation, b_layout="nk", out=out,
                    stream=stream)
+
+
+MLA_DL, MLA_DR = 512, 64
+
+
+def mla_decode(q, kv, scale, seqlens=None, out=None, workspace=None, stream=None):
+    """Latent-attention decode through tg_mla_decode_f16: q (B, H, 576) and the
+    cache kv (B, Sk, 576) fp16 device tensors, contiguous; returns O (B, H, 512).
+    seqlens: optional int32 device tensor of B visible lengths.  The workspace
+    (a uint8 device tensor) is allocated here when not given."""
+    import torch
+    if q.dtype != torch.float16 or kv.dtype != torch.float16:
+        raise TypeError("q and kv must be float16")
+    if q.dim() != 3 or kv.dim() != 3 or q.shape[2] != MLA_DL + MLA_DR or \
+            kv.shape[2] != MLA_DL + MLA_DR or kv.shape[0] != q.shape[0]:
+        raise ValueError("q must be (B, H, 576) and kv (B, Sk, 576)")
+    if not q.is_contiguous() or not kv.is_contiguous():
+        raise ValueError("q and kv must be contiguous")
+    B, H, Sk = q.shape[0], q.shape[1], kv.shape[1]
+    sl = 0
+    if seqlens is not None:
+        if seqlens.dtype != torch.int32 or seqlens.numel() != B or not seqlens.is_contiguous():
+            raise ValueError("seqlens must be a contiguous int32 tensor of B entries")
+        sl = seqlens.data_ptr()
+    if out is None:
+        out = torch.empty((B, H, MLA_DL), dtype=torch.float16, device=q.device)
+    if tuple(out.shape) != (B, H, MLA_DL) or out.dtype != torch.float16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous (B, H, 512) float16 tensor")
+    need = tg_mla_decode_workspace_bytes(B, H, Sk)
+    if need < 0:
+        raise ValueError("sizes out of range")
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws, wsb = (workspace.data_ptr(), workspace.numel()) if workspace is not None else (0, 0)
+    _check(tg_mla_decode_f16(q.data_ptr(), kv.data_ptr(), out.data_ptr(), sl, B, H, Sk,
+                             float(scale), ws, wsb, _stream_handle(stream)))
+    return out

@@ -145,10 +145,11 @@ __device__ __forceinline__ float max_pair(float x)
 }
 
 // Masks the raw scores of keys at or past `lim` (tile offsets, see below).
-__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int lim, int hi)
+template <int KB = 2>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[KB], int lim, int hi)
 {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int ko = kb * 32 + 8 * (r / 4) + 4 * hi + (r % 4);
@@ -157,20 +158,21 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int lim, int hi)
     }
 }
 
-// One tile's softmax step for this lane's query: raw scores s (32 keys,
-// register r of block kb is key 32 kb + 8 (r / 4) + 4 hi + r % 4 of the
-// tile; masked keys hold -inf, and sl2 > 0 turns them into zeros).  Raises
+// One tile's softmax step for this lane's query: raw scores s (16 KB of the
+// tile's 32 KB keys: register r of block kb is key 32 kb + 8 (r / 4) +
+// 4 hi + r % 4; masked keys hold -inf, and sl2 > 0 turns them into zeros).  Raises
 // the running maximum if needed (rescaling the accumulator and the sum),
 // writes the fp16 probabilities in the operand order of the P V product and
 // adds them to the sum (the rounded values, so the weights applied to V are
 // exactly the ones the sum divides by).
-template <int DB>
-__device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], f16x8 (&pf)[4], f32x16 (&acc_o)[DB],
-                                             float &m_run, float &l_run, float sl2)
+template <int DB, int KB = 2>
+__device__ __forceinline__ void softmax_tile(f32x16 (&s)[KB], f16x8 (&pf)[2 * KB],
+                                             f32x16 (&acc_o)[DB], float &m_run, float &l_run,
+                                             float sl2)
 {
     float mt = -__builtin_inff();
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; r += 2)
             mt = __builtin_fmaxf(mt, __builtin_fmaxf(s[kb][r], s[kb][r + 1]));
@@ -189,7 +191,7 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], f16x8 (&pf)[4], f32
     }
     const float neg_m = -m_run;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < 2 * KB; ++kk) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             pf[kk][j] = (_Float16)__builtin_amdgcn_exp2f(
@@ -197,7 +199,7 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], f16x8 (&pf)[4], f32
     }
     float ls[2] = {0.0f, 0.0f};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < 2 * KB; ++kk) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             ls[j & 1] = __builtin_amdgcn_fdot2(f16x2{pf[kk][2 * j], pf[kk][2 * j + 1]},
@@ -414,6 +416,280 @@ hipError_t launch_attn(const AttnArgs &p, hipStream_t stream)
     return hipSuccess;
 }
 
+// ---------------------------------------------------------------------------
+// Latent-attention decode (the MLA decode the pages measure: "TileLang paper
+// reading" page, section 5; "80-line MLA article" page, sections 1-2, which
+// give its 512 + 64 head size).  One query per sequence; every cached token
+// holds one row of 576 fp16 values, all of them the key and the first 512 the
+// value, shared by every query head.
+//
+// gfx950 design:
+//  * A workgroup of four waves, one per SIMD, serves 64 query heads of one
+//    sequence over one range of its keys.  Waves 2g and 2g + 1 share heads
+//    32g .. 32g + 31 (one per lane pair) and split the head dimension: wave
+//    half e holds Q^T for values 288e .. 288e + 287 and accumulates output
+//    values 256e .. 256e + 255.  A wave thus keeps 18 Q^T fragments and a
+//    32 x 256 fp32 accumulator in registers (the whole 576 / 512 would not
+//    fit one wave's registers) while each LDS fragment read still feeds 32
+//    heads.
+//  * Tiles of 32 cached rows (36 KiB) are staged in a 3-stage LDS ring by
+//    buffer_load_dwordx4 ... lds; the buffer's record count ends at the
+//    range's last visible row, so later rows read as zeros (and are masked
+//    out of the softmax).
+//  * Scores S^T = K Q^T as in the attention forward above, each wave over
+//    its half of the values; the two halves are swapped through LDS and
+//    added (addition commutes, so both waves hold the same bits), both run
+//    the same softmax, and each adds its half of O^T += V^T P^T.  The same
+//    LDS rows are read as K (16-byte reads) and as V (transpose reads of the
+//    first 512 values), so one chunk swizzle serves both: chunk c of row r
+//    sits at c ^ x(r), x a bijection of r mod 8 (eight consecutive rows,
+//    read by the K fragments, land on eight different chunks of a 128-byte
+//    line) that puts four consecutive rows (read together by the transpose
+//    reads) in alternate halves of the line.
+//  * When the sequences are too few to fill the chip the keys are split
+//    into ranges (flash-decoding); each range writes its unnormalised fp32
+//    output with its running maximum and sum, and a combine kernel rescales
+//    and adds the ranges in a fixed order, so results are deterministic.
+//    The head blocks of one range are numbered 8 apart so that they run on
+//    one XCD and share its L2.
+namespace mla {
+constexpr int D = kMlaDl + kMlaDr;   // 576 values per cached row
+constexpr int NW = 4;                // waves: two head groups x two halves
+constexpr int BK = 32;               // cached rows per tile
+constexpr int TILE = BK * D;         // fp16 elements per tile
+constexpr int STAGES = 3;
+constexpr int BLOCKS = TILE * 2 / 1024;  // 1 KiB DMA blocks per tile
+constexpr int LD = BLOCKS / NW;      // ... per wave
+constexpr int DS = D / 16 / 2;       // 16-wide score steps per half
+constexpr int DB = kMlaDl / 32 / 2;  // 32-wide output blocks per half
+constexpr int XCH = NW * 16 * 64;    // floats of the score exchange
+static_assert(BLOCKS % NW == 0, "blocks per wave");
+static_assert(32 * NW / 2 == kMlaHeadsPerBlock, "heads per workgroup");
+}  // namespace mla
+
+__device__ __forceinline__ int mla_swz(int row, int c)
+{
+    return c ^ (((row & 1) << 2) | ((row >> 1) & 3));
+}
+
+__global__ void __launch_bounds__(64 * mla::NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+mla_decode_kernel(MlaArgs p)
+{
+    using namespace mla;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * TILE];
+    __shared__ __attribute__((aligned(16))) float xch[XCH];
+    const lds_u16 *lds = (const lds_u16 *)smem;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hg = wave >> 1, e = wave & 1;
+    const int hi = lane >> 5;
+    // grid x: 8 consecutive (sequence, key range) units, then the same 8
+    // for the next head block, ...
+    const int64_t nhb = (p.H + kMlaHeadsPerBlock - 1) / kMlaHeadsPerBlock;
+    const int64_t gid = blockIdx.x;
+    const int64_t unit = gid / (8 * nhb) * 8 + gid % 8;
+    const int64_t hb = gid / 8 % nhb;
+    if (unit >= p.B * p.splits)
+        return;
+    const int64_t b = unit / p.splits, sp = unit % p.splits;
+    const int64_t h = hb * kMlaHeadsPerBlock + hg * 32 + (lane & 31);
+    const bool live = h < p.H;
+
+    int64_t n = p.Sk;
+    if (p.seqlens) {
+        const int64_t v = p.seqlens[b];
+        n = v < 0 ? 0 : (v > p.Sk ? p.Sk : v);
+    }
+    const int64_t kbeg = sp * p.keys_per_split;
+    int64_t kend = kbeg + p.keys_per_split;
+    kend = kend < n ? kend : n;
+    const int tiles = kend > kbeg ? (int)((kend - kbeg + BK - 1) / BK) : 0;
+
+    // Q^T fragments (second operand): lane holds Q[b][h][288 e + 16 ds + 8 hi .. + 7]
+    f16x8 qf[DS];
+    {
+        const uint16_t *qrow = p.Q + (b * p.H + (live ? h : 0)) * D + e * (D / 2);
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+            qf[ds] = f16x8{};
+            if (live)
+                qf[ds] = *reinterpret_cast<const f16x8 *>(qrow + ds * 16 + 8 * hi);
+            if (p.scale < 0.0f)    // a negative scale is carried by Q
+                qf[ds] = -qf[ds];
+        }
+    }
+
+    // DMA plan: slot s (16 bytes) of a tile is row s / 72, physical chunk
+    // s % 72, which receives the row's logical chunk mla_swz(row, chunk);
+    // wave w moves 1 KiB blocks w, w + 4, ...
+    uint32_t voff[LD];
+#pragma unroll
+    for (int i = 0; i < LD; ++i) {
+        const int slot = (wave + NW * i) * 64 + lane;
+        const int row = slot / (D / 8);
+        const int pc = slot % (D / 8);
+        voff[i] = (uint32_t)((row * D + mla_swz(row, pc) * 8) * 2);
+    }
+    const uint16_t *kvb = p.KV + b * p.Sk * D;
+    auto issue = [&](int t) {
+        const int64_t k0 = kbeg + (int64_t)t * BK;
+        const int64_t rows = kend - k0 < BK ? kend - k0 : BK;
+        i32x4 rsrc = make_rsrc(kvb + k0 * D);
+        rsrc.z = __builtin_amdgcn_readfirstlane((int)(rows * D * 2));
+        const uint32_t base = lds_base + (uint32_t)((t % STAGES) * TILE * 2);
+#pragma unroll
+        for (int i = 0; i < LD; ++i)
+            dma16(rsrc, voff[i], base + (uint32_t)((wave + NW * i) * 1024));
+    };
+
+    f32x16 acc_o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+        acc_o[db] = f32x16{};
+    float m_run = -1.0e30f, l_run = 0.0f;
+    const float sl2 = __builtin_fmaxf(__builtin_fabsf(p.scale) * 1.44269504088896340736f, 1.0e-30f);
+    // score exchange: this wave's partial at mine, its partner's at theirs;
+    // float4 j of a lane at (4 * slot + j) * 64 + lane
+    float4 *mine = reinterpret_cast<float4 *>(xch) + wave * 4 * 64 + lane;
+    const float4 *theirs = reinterpret_cast<const float4 *>(xch) + (wave ^ 1) * 4 * 64 + lane;
+
+    for (int t = 0; t < STAGES - 1 && t < tiles; ++t)
+        issue(t);
+    for (int t = 0; t < tiles; ++t) {
+        // tile t has landed (this wave's part): later tiles may stay in flight
+        if (t + 1 < tiles)
+            wait_vmcnt<LD * (STAGES - 2)>();
+        else
+            wait_vmcnt<0>();
+        block_barrier();      // ... every wave's part; tile t-1's stage is free
+        if (t + STAGES - 1 < tiles)
+            issue(t + STAGES - 1);
+        const int64_t k0 = kbeg + (int64_t)t * BK;
+        const lds_u16 *Ks = lds + (t % STAGES) * TILE;
+
+        // this half's scores: lane holds head h's partial sums for keys
+        // k0 + 8 (r / 4) + 4 hi + r % 4
+        f32x16 s[1];
+        s[0] = f32x16{};
+        {
+            const int row = lane & 31;
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds) {
+                const int c = (e * DS + ds) * 2 + hi;
+                const f16x8 kf = *reinterpret_cast<const lds_f16x8 *>(Ks + row * D + mla_swz(row, c) * 8);
+                s[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ds], s[0], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            mine[j * 64] = float4{s[0][4 * j], s[0][4 * j + 1], s[0][4 * j + 2], s[0][4 * j + 3]};
+        block_barrier();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float4 o = theirs[j * 64];
+            s[0][4 * j + 0] += o.x;
+            s[0][4 * j + 1] += o.y;
+            s[0][4 * j + 2] += o.z;
+            s[0][4 * j + 3] += o.w;
+        }
+        if (k0 + BK > kend)
+            mask_tile<1>(s, (int)(kend - k0), hi);
+        f16x8 pf[2];
+        softmax_tile<DB, 1>(s, pf, acc_o, m_run, l_run, sl2);
+        // this half of O^T += V^T P^T (values 256 e .. 256 e + 255)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                s16x4 vh[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int key = kk * 16 + 4 * hi + 8 * hh + ((lane & 15) >> 2);
+                    const int d = e * (kMlaDl / 2) + db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+                    const lds_u16 *src = Ks + key * D + mla_swz(key, d >> 3) * 8 + (d & 7);
+                    vh[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src);
+                }
+                const f16x8 vf = __builtin_bit_cast(
+                    f16x8, __builtin_shufflevector(vh[0], vh[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[kk], acc_o[db], 0, 0, 0);
+            }
+        }
+    }
+    wait_vmcnt<0>();
+
+    // this head's sum of exponentials is split over lanes l and l ^ 32
+    const float l_all = l_run + __shfl_xor(l_run, 32);
+    if (!live)
+        return;
+    const int d0 = e * (kMlaDl / 2);
+    if (p.splits == 1) {
+        const float inv = l_all > 0.0f ? 1.0f / l_all : 0.0f;
+        uint16_t *orow = p.O + (b * p.H + h) * kMlaDl + d0;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = db * 32 + 8 * g + 4 * hi;
+                u32x2 w;
+                w.x = epi_pack2<false>(acc_o[db][4 * g + 0] * inv, acc_o[db][4 * g + 1] * inv, false);
+                w.y = epi_pack2<false>(acc_o[db][4 * g + 2] * inv, acc_o[db][4 * g + 3] * inv, false);
+                *reinterpret_cast<u32x2 *>(orow + d) = w;
+            }
+        }
+        return;
+    }
+    const int64_t slot = (b * p.H + h) * p.splits + sp;
+    float *po = p.part + slot * kMlaDl + d0;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int d = db * 32 + 8 * g + 4 * hi;
+            *reinterpret_cast<float4 *>(po + d) =
+                float4{acc_o[db][4 * g + 0], acc_o[db][4 * g + 1], acc_o[db][4 * g + 2],
+                       acc_o[db][4 * g + 3]};
+        }
+    }
+    if (hi == 0 && e == 0) {
+        float2 *ml = reinterpret_cast<float2 *>(p.part + p.B * p.H * p.splits * kMlaDl);
+        ml[slot] = float2{m_run, l_all};
+    }
+}
+
+// Combines the key ranges of one (sequence, head): O = sum_s 2^(m_s - M) O_s
+// / sum_s 2^(m_s - M) l_s with M the largest range maximum, ranges added in
+// order; thread t owns output values 4t .. 4t + 3.
+__global__ void __launch_bounds__(kMlaDl / 4) mla_combine_kernel(MlaArgs p)
+{
+    const int64_t bh = blockIdx.x;
+    const int d = threadIdx.x * 4;
+    const int S = p.splits;
+    const float2 *ml = reinterpret_cast<const float2 *>(p.part + p.B * p.H * S * kMlaDl) + bh * S;
+    float M = -1.0e30f;
+    for (int s = 0; s < S; ++s)
+        M = __builtin_fmaxf(M, ml[s].x);
+    float L = 0.0f;
+    float4 acc = float4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < S; ++s) {
+        const float2 v = ml[s];
+        const float w = __builtin_amdgcn_exp2f(v.x - M);
+        L += w * v.y;
+        const float4 o = *reinterpret_cast<const float4 *>(p.part + (bh * S + s) * kMlaDl + d);
+        acc.x += w * o.x;
+        acc.y += w * o.y;
+        acc.z += w * o.z;
+        acc.w += w * o.w;
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    u32x2 out;
+    out.x = epi_pack2<false>(acc.x * inv, acc.y * inv, false);
+    out.y = epi_pack2<false>(acc.z * inv, acc.w * inv, false);
+    *reinterpret_cast<u32x2 *>(p.O + bh * kMlaDl + d) = out;
+}
+
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs &p, hipStream_t stream)
@@ -422,6 +698,25 @@ hipError_t launch_attention(const AttnArgs &p, hipStream_t stream)
     if (p.D == 64)
         return nw == 8 ? launch_attn<64, 8>(p, stream) : launch_attn<64, 4>(p, stream);
     return nw == 8 ? launch_attn<128, 8>(p, stream) : launch_attn<128, 4>(p, stream);
+}
+
+}  // namespace tg
+
+namespace tg {
+
+hipError_t launch_mla_decode(const MlaArgs &p, hipStream_t stream)
+{
+    // the host has checked that the grid fits 2^31 workgroups
+    const int64_t nhb = (p.H + kMlaHeadsPerBlock - 1) / kMlaHeadsPerBlock;
+    const int64_t units = (p.B * p.splits + 7) / 8 * 8;
+    hipLaunchKernelGGL(mla_decode_kernel, dim3((unsigned)(units * nhb)), dim3(64 * mla::NW), 0,
+                       stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splits == 1)
+        return e;
+    hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(p.B * p.H)), dim3(kMlaDl / 4), 0,
+                       stream, p);
+    return hipGetLastError();
 }
 
 }  // namespace tg

@@ -219,3 +219,24 @@ def generate_w4(N: int, K: int, G: int, seed: int, dtype: str = "f16"):
     wq = (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
     s = rng.uniform(0.5, 1.5, (N, K // G)) / (8.0 * np.sqrt(K))
     return wq.reshape(-1), to_bits(s.reshape(-1), dtype)
+
+
+# Latent-attention decode workload: 64 sequences of 8192 cached tokens, 128
+# query heads, rows of 512 + 64 values (the pages plot batch 64 and 128 at fp16
+# for this kernel; 8192 tokens is the cache length used here).
+MLA_WORKLOAD = {"name": "mla_decode_64x128x8192", "B": 64, "H": 128, "Sk": 8192, "seed": 6}
+MLA_ROW = 576
+
+
+def generate_mla(B: int, H: int, Sk: int, seed: int):
+    """Q (B, H, 576) and the cache KV (B, Sk, 576) as fp16 bits, each value
+    normal(0, 1) drawn in binary32 from one default_rng(60_000 + seed), Q first,
+    rounded to nearest even.  Returns (Q, KV) flattened."""
+    rng = np.random.default_rng(60_000 + seed)
+    q = rng.standard_normal(B * H * MLA_ROW, dtype=np.float32).astype(np.float16)
+    kv = np.empty(B * Sk * MLA_ROW, dtype=np.float16)
+    step = 1 << 24
+    for i in range(0, kv.size, step):
+        n = min(step, kv.size - i)
+        kv[i:i + n] = rng.standard_normal(n, dtype=np.float32).astype(np.float16)
+    return q.view(np.uint16), kv.view(np.uint16)
