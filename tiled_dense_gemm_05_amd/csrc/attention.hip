@@ -165,7 +165,23 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[KB], int lim, int hi)
 // writes the fp16 probabilities in the operand order of the P V product and
 // adds them to the sum (the rounded values, so the weights applied to V are
 // exactly the ones the sum divides by).
-template <int DB, int KB = 2>
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// x *= a for an accumulator held in an AGPR, in place: keeps the rare
+// rescale from making the compiler move a whole accumulator into VGPRs and
+// back on every tile.  The caller has waited out the matrix-core write of x.
+__device__ __forceinline__ void scale_agpr(float &x, float a)
+{
+    float tmp;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\t"
+                 "v_mul_f32_e32 %1, %2, %1\n\t"
+                 "v_accvgpr_write_b32 %0, %1"
+                 : "+a"(x), "=&v"(tmp)
+                 : "v"(a));
+}
+#pragma clang diagnostic pop
+
+template <int DB, int KB = 2, bool AGPR_RESCALE = false>
 __device__ __forceinline__ void softmax_tile(f32x16 (&s)[KB], f16x8 (&pf)[2 * KB],
                                              f32x16 (&acc_o)[DB], float &m_run, float &l_run,
                                              float sl2)
@@ -185,9 +201,25 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[KB], f16x8 (&pf)[2 * KB
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
+        if constexpr (AGPR_RESCALE) {
+            // the last matrix-core writes of acc_o are a tile back; wait out
+            // the longest result latency anyway before reading them
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-            acc_o[db] *= alpha;
+            for (int db = 0; db < DB; ++db) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float x = acc_o[db][r];
+                    scale_agpr(x, alpha);
+                    acc_o[db][r] = x;
+                }
+            }
+            asm volatile("s_nop 4" ::: "memory");
+        } else {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                acc_o[db] *= alpha;
+        }
     }
     const float neg_m = -m_run;
 #pragma unroll
@@ -432,7 +464,7 @@ hipError_t launch_attn(const AttnArgs &p, hipStream_t stream)
 //    32 x 256 fp32 accumulator in registers (the whole 576 / 512 would not
 //    fit one wave's registers) while each LDS fragment read still feeds 32
 //    heads.
-//  * Tiles of 32 cached rows (36 KiB) are staged in a 3-stage LDS ring by
+//  * Tiles of 32 cached rows (36 KiB) are staged in a 4-stage LDS ring by
 //    buffer_load_dwordx4 ... lds; the buffer's record count ends at the
 //    range's last visible row, so later rows read as zeros (and are masked
 //    out of the softmax).
@@ -441,11 +473,12 @@ hipError_t launch_attn(const AttnArgs &p, hipStream_t stream)
 //    added (addition commutes, so both waves hold the same bits), both run
 //    the same softmax, and each adds its half of O^T += V^T P^T.  The same
 //    LDS rows are read as K (16-byte reads) and as V (transpose reads of the
-//    first 512 values), so one chunk swizzle serves both: chunk c of row r
-//    sits at c ^ x(r), x a bijection of r mod 8 (eight consecutive rows,
-//    read by the K fragments, land on eight different chunks of a 128-byte
-//    line) that puts four consecutive rows (read together by the transpose
-//    reads) in alternate halves of the line.
+//    first 512 values), so one chunk swizzle serves both.  Rows are 1152
+//    bytes, so in the 256-byte bank line (64 banks) consecutive rows start
+//    alternately at 0 and 128; chunk c of row r sits at c ^ x(r) with
+//    x(r) = 2 ((r / 2) mod 4) + (r / 8) mod 2, which with that alternation
+//    puts the 16 rows a K fragment read serves at once on 16 different
+//    16-byte slots, and the 4 rows x 2 chunks of a transpose read on 8.
 //  * When the sequences are too few to fill the chip the keys are split
 //    into ranges (flash-decoding); each range writes its unnormalised fp32
 //    output with its running maximum and sum, and a combine kernel rescales
@@ -457,7 +490,7 @@ constexpr int D = kMlaDl + kMlaDr;   // 576 values per cached row
 constexpr int NW = 4;                // waves: two head groups x two halves
 constexpr int BK = 32;               // cached rows per tile
 constexpr int TILE = BK * D;         // fp16 elements per tile
-constexpr int STAGES = 3;
+constexpr int STAGES = 4;
 constexpr int BLOCKS = TILE * 2 / 1024;  // 1 KiB DMA blocks per tile
 constexpr int LD = BLOCKS / NW;      // ... per wave
 constexpr int DS = D / 16 / 2;       // 16-wide score steps per half
@@ -469,7 +502,7 @@ static_assert(32 * NW / 2 == kMlaHeadsPerBlock, "heads per workgroup");
 
 __device__ __forceinline__ int mla_swz(int row, int c)
 {
-    return c ^ (((row & 1) << 2) | ((row >> 1) & 3));
+    return c ^ (2 * ((row >> 1) & 3) + ((row >> 3) & 1));
 }
 
 __global__ void __launch_bounds__(64 * mla::NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -552,71 +585,166 @@ mla_decode_kernel(MlaArgs p)
     float m_run = -1.0e30f, l_run = 0.0f;
     const float sl2 = __builtin_fmaxf(__builtin_fabsf(p.scale) * 1.44269504088896340736f, 1.0e-30f);
     // score exchange: this wave's partial at mine, its partner's at theirs;
-    // float4 j of a lane at (4 * slot + j) * 64 + lane
+    // float4 j of a lane at (4 * wave + j) * 64 + lane
     float4 *mine = reinterpret_cast<float4 *>(xch) + wave * 4 * 64 + lane;
     const float4 *theirs = reinterpret_cast<const float4 *>(xch) + (wave ^ 1) * 4 * 64 + lane;
 
-    for (int t = 0; t < STAGES - 1 && t < tiles; ++t)
-        issue(t);
-    for (int t = 0; t < tiles; ++t) {
-        // tile t has landed (this wave's part): later tiles may stay in flight
-        if (t + 1 < tiles)
-            wait_vmcnt<LD * (STAGES - 2)>();
-        else
-            wait_vmcnt<0>();
-        block_barrier();      // ... every wave's part; tile t-1's stage is free
-        if (t + STAGES - 1 < tiles)
-            issue(t + STAGES - 1);
-        const int64_t k0 = kbeg + (int64_t)t * BK;
-        const lds_u16 *Ks = lds + (t % STAGES) * TILE;
-
-        // this half's scores: lane holds head h's partial sums for keys
-        // k0 + 8 (r / 4) + 4 hi + r % 4
-        f32x16 s[1];
-        s[0] = f32x16{};
-        {
-            const int row = lane & 31;
-#pragma unroll
-            for (int ds = 0; ds < DS; ++ds) {
-                const int c = (e * DS + ds) * 2 + hi;
-                const f16x8 kf = *reinterpret_cast<const lds_f16x8 *>(Ks + row * D + mla_swz(row, c) * 8);
-                s[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ds], s[0], 0, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            mine[j * 64] = float4{s[0][4 * j], s[0][4 * j + 1], s[0][4 * j + 2], s[0][4 * j + 3]};
-        block_barrier();
+    // this half's score partials for tile t: lane holds head h's sums for
+    // keys k0 + 8 (r / 4) + 4 hi + r % 4
+    // LDS addresses as per-lane bases plus compile-time offsets: a K fragment
+    // of step ds sits at kbase[ds % 4] + 64 (ds / 4) elements (adding 8 to a
+    // chunk index leaves the XOR-ed low bits alone), a V fragment at
+    // vbase[hh][db % 2] + 64 (db / 2) + 576 * 16 kk (its row mod 16 depends
+    // on hh, not on kk)
+    int kbase[4], vbase[2][2];   // fp16 elements from the stage start
+    {
+        const int row = lane & 31;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float4 o = theirs[j * 64];
-            s[0][4 * j + 0] += o.x;
-            s[0][4 * j + 1] += o.y;
-            s[0][4 * j + 2] += o.z;
-            s[0][4 * j + 3] += o.w;
+            const int c = e * 2 * DS + 2 * j + hi;
+            kbase[j] = row * D + mla_swz(row, c) * 8;
         }
-        if (k0 + BK > kend)
-            mask_tile<1>(s, (int)(kend - k0), hi);
-        f16x8 pf[2];
-        softmax_tile<DB, 1>(s, pf, acc_o, m_run, l_run, sl2);
-        // this half of O^T += V^T P^T (values 256 e .. 256 e + 255)
+        const int dl = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+        for (int hh = 0; hh < 2; ++hh) {
+            const int key = 8 * hh + 4 * hi + ((lane & 15) >> 2);
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                s16x4 vh[2];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int key = kk * 16 + 4 * hi + 8 * hh + ((lane & 15) >> 2);
-                    const int d = e * (kMlaDl / 2) + db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-                    const lds_u16 *src = Ks + key * D + mla_swz(key, d >> 3) * 8 + (d & 7);
-                    vh[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src);
-                }
-                const f16x8 vf = __builtin_bit_cast(
-                    f16x8, __builtin_shufflevector(vh[0], vh[1], 0, 1, 2, 3, 4, 5, 6, 7));
-                acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[kk], acc_o[db], 0, 0, 0);
+            for (int par = 0; par < 2; ++par) {
+                const int d = e * (kMlaDl / 2) + par * 32 + dl;
+                vbase[hh][par] = key * D + mla_swz(key, d >> 3) * 8 + (d & 7);
             }
         }
+    }
+    auto scores = [&](int t) {
+        // the stage offset kept opaque, so the addresses stay base + constant
+        const lds_u16 *Ks = lds + __builtin_amdgcn_readfirstlane((t % STAGES) * TILE);
+        const lds_u16 *kb[4] = {Ks + kbase[0], Ks + kbase[1], Ks + kbase[2], Ks + kbase[3]};
+        // K fragments read KA steps ahead of the products that use them: one
+        // wave per SIMD has nothing else to hide the LDS latency behind
+        constexpr int KA = 6;
+        f16x8 kf[DS];
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int ds = 0; ds < KA; ++ds)
+            kf[ds] = *reinterpret_cast<const lds_f16x8 *>(kb[ds & 3] + (ds >> 2) * 64);
+        // the scheduler may move vector and scalar ALU work across these
+        // fences, not LDS reads or matrix instructions
+        __builtin_amdgcn_sched_barrier(0x6);
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+            if (ds + KA < DS)
+                kf[ds + KA] = *reinterpret_cast<const lds_f16x8 *>(kb[(ds + KA) & 3] + ((ds + KA) >> 2) * 64);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ds], qf[ds], acc, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0x6);
+        }
+        return acc;
+    };
+    auto publish = [&](const f32x16 &acc) {
+        float4 *dst = mine;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            dst[j * 64] = float4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
+    };
+    // the partner's partial for tile t, added (addition commutes: both
+    // waves of the pair hold the same bits), masked past the range
+    auto complete = [&](int t, f32x16 &acc, bool last) {
+        const float4 *src = theirs;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float4 o = src[j * 64];
+            acc[4 * j + 0] += o.x;
+            acc[4 * j + 1] += o.y;
+            acc[4 * j + 2] += o.z;
+            acc[4 * j + 3] += o.w;
+        }
+        const int64_t k0 = kbeg + (int64_t)t * BK;
+        if (last && k0 + BK > kend) {    // only the range's last tile can be partial
+            f32x16 sm[1] = {acc};
+            mask_tile<1>(sm, (int)(kend - k0), hi);
+            acc = sm[0];
+        }
+    };
+    // this half of O^T += V^T P^T (values 256 e .. 256 e + 255) for tile t
+    auto values = [&](int t, const f16x8 (&pf)[2]) {
+        const lds_u16 *Vs = lds + __builtin_amdgcn_readfirstlane((t % STAGES) * TILE);
+        const lds_u16 *vb[2][2] = {{Vs + vbase[0][0], Vs + vbase[0][1]},
+                                   {Vs + vbase[1][0], Vs + vbase[1][1]}};
+        // V^T fragments read VA products ahead (products in (db, kk) order)
+        constexpr int NP = DB * 2, VA = 3;
+        f16x8 vf[NP];
+        auto load_v = [&](int i) {
+            const int db = i / 2, kk = i % 2;
+            s16x4 vh[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                vh[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4 *)(vb[hh][db & 1] + (db >> 1) * 64 + 16 * kk * D));
+            vf[i] = __builtin_bit_cast(
+                f16x8, __builtin_shufflevector(vh[0], vh[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+#pragma unroll
+        for (int i = 0; i < VA; ++i)
+            load_v(i);
+        __builtin_amdgcn_sched_barrier(0x6);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            if (i + VA < NP)
+                load_v(i + VA);
+            acc_o[i / 2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[i], pf[i % 2], acc_o[i / 2], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0x6);
+        }
+    };
+
+    // Software pipeline over a 4-stage ring: iteration t computes tile t's
+    // score partials on the matrix cores while the vector units finish tile
+    // t-1's softmax, then tile t-1's value product.  A barrier in the middle
+    // (every wave is past its read of the exchange and of tile t-1's stage)
+    // lets tile t's partials be published and tile t+3 be loaded into that
+    // stage; the barrier at the end publishes the partials and makes tile t+1
+    // visible, which has had two iterations to arrive.
+    auto wait_tiles_beyond = [&](int n) {   // all but the n newest tiles landed
+        if (n >= 2)
+            wait_vmcnt<2 * LD>();
+        else if (n == 1)
+            wait_vmcnt<LD>();
+        else
+            wait_vmcnt<0>();
+    };
+    if (tiles > 0) {
+        for (int t = 0; t < STAGES - 1 && t < tiles; ++t)
+            issue(t);
+        wait_tiles_beyond(tiles - 1 < 2 ? tiles - 1 : 2);
+        block_barrier();                      // tile 0 visible
+        f32x16 prev = scores(0);
+        publish(prev);
+        if (tiles > 1)
+            wait_tiles_beyond(tiles - 2 < 1 ? tiles - 2 : 1);
+        block_barrier();                      // partials 0 published, tile 1 visible
+        if (tiles > 3)
+            issue(3);
+        for (int t = 1; t < tiles; ++t) {
+            complete(t - 1, prev, false);
+            f16x8 pf[2];
+            f32x16 sm[1] = {prev};
+            softmax_tile<DB, 1, true>(sm, pf, acc_o, m_run, l_run, sl2);
+            const f32x16 cur = scores(t);
+            values(t - 1, pf);
+            block_barrier();                  // exchange read, tile t-1's stage free
+            publish(cur);
+            if (t + 3 < tiles)
+                issue(t + 3);
+            prev = cur;
+            if (t + 1 < tiles) {
+                const int ahead = (t + 3 < tiles ? t + 3 : tiles - 1) - (t + 1);
+                wait_tiles_beyond(ahead);     // tile t+1 landed
+            }
+            block_barrier();                  // partials t published, tile t+1 visible
+        }
+        complete(tiles - 1, prev, true);
+        f16x8 pf[2];
+        f32x16 sm[1] = {prev};
+        softmax_tile<DB, 1, true>(sm, pf, acc_o, m_run, l_run, sl2);
+        values(tiles - 1, pf);
     }
     wait_vmcnt<0>();
 
