@@ -43,6 +43,7 @@ def tg():
 def _default_splits(tg):
     yield
     tg.tg_set_mla_splits(-1)
+    tg.tg_set_mla_variant(-1)
 
 
 def dev(bits) -> "torch.Tensor":
@@ -109,21 +110,24 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("variant", [0, 1])
 @pytest.mark.parametrize("splits", [-1, 1, 2, 5])
 @pytest.mark.parametrize("B,H,Sk", CASES)
-def test_mla_matches_oracle(tg, oracle_lib, splits, B, H, Sk):
+def test_mla_matches_oracle(tg, oracle_lib, variant, splits, B, H, Sk):
     q, kv = inputs(B, H, Sk, B * 7 + H + Sk)
     ref = oracle_lib.mla_decode(q, kv, B, H, Sk, SCALE)
-    say(f"mla B={B} H={H} Sk={Sk} splits={splits}")
+    say(f"mla B={B} H={H} Sk={Sk} splits={splits} variant={variant}")
     tg.tg_set_mla_splits(splits)
+    assert tg.tg_set_mla_variant(variant) >= 0
     need = tg.tg_mla_decode_workspace_bytes(B, H, Sk)
     per = B * H * (DL + 2) * 4
     ws = max(need, per * max(splits, 1))
     check(run(tg, q, kv, B, H, Sk, SCALE, ws_bytes=ws), ref, kv, B, Sk)
 
 
+@pytest.mark.parametrize("variant", [0, 1])
 @pytest.mark.parametrize("splits", [1, 3])
-def test_ragged_lengths_and_junk_past_them(tg, oracle_lib, splits):
+def test_ragged_lengths_and_junk_past_them(tg, oracle_lib, splits, variant):
     # lengths 0, 1, a tile edge, mid-tile and full; rows past a length hold NaN
     B, H, Sk = 6, 80, 300
     lens = [0, 1, 32, 33, 299, 300]
@@ -132,8 +136,9 @@ def test_ragged_lengths_and_junk_past_them(tg, oracle_lib, splits):
     junk = kv.reshape(B, Sk, DQ).copy()
     for b, n in enumerate(lens):
         junk[b, n:] = 0x7E00
-    say(f"mla ragged splits={splits}")
+    say(f"mla ragged splits={splits} variant={variant}")
     tg.tg_set_mla_splits(splits)
+    tg.tg_set_mla_variant(variant)
     got = run(tg, q, junk.reshape(-1), B, H, Sk, SCALE, lens=lens,
               ws_bytes=B * H * (DL + 2) * 4 * splits)
     check(got, ref, kv, B, Sk, lens)
@@ -149,13 +154,15 @@ def test_lengths_outside_the_cache_are_clamped(tg, oracle_lib):
     check(run(tg, q, kv, B, H, Sk, SCALE, lens=[-5, 100, 1 << 30]), ref, kv, B, Sk)
 
 
+@pytest.mark.parametrize("variant", [0, 1])
 @pytest.mark.parametrize("spread,scale", [(3.0, 0.5), (0.01, 1.0), (1.0, -SCALE), (1.0, 0.0)])
-def test_sharp_flat_negative_and_zero_scale(tg, oracle_lib, spread, scale):
+def test_sharp_flat_negative_and_zero_scale(tg, oracle_lib, spread, scale, variant):
     B, H, Sk = 2, 64, 700
     q, kv = inputs(B, H, Sk, 5, spread=spread)
     ref = oracle_lib.mla_decode(q, kv, B, H, Sk, scale)
-    say(f"mla spread={spread} scale={scale}")
+    say(f"mla spread={spread} scale={scale} variant={variant}")
     tg.tg_set_mla_splits(3)
+    tg.tg_set_mla_variant(variant)
     check(run(tg, q, kv, B, H, Sk, scale, ws_bytes=B * H * (DL + 2) * 4 * 3), ref, kv, B, Sk)
 
 
@@ -170,10 +177,12 @@ def test_small_workspace_lowers_the_split_count(tg, oracle_lib):
         check(o, ref, kv, B, Sk)
 
 
-def test_deterministic(tg):
+@pytest.mark.parametrize("variant", [0, 1])
+def test_deterministic(tg, variant):
     B, H, Sk = 4, 128, 2000
     q, kv = inputs(B, H, Sk, 8)
-    say("mla determinism")
+    say(f"mla determinism variant={variant}")
+    tg.tg_set_mla_variant(variant)
     a = run(tg, q, kv, B, H, Sk, SCALE)
     b = run(tg, q, kv, B, H, Sk, SCALE)
     assert np.array_equal(a, b)
@@ -210,14 +219,16 @@ def test_torch_helper(tg, oracle_lib):
           [333, 100])
 
 
-def test_benchmark_shape_sampled(tg, oracle_lib):
+@pytest.mark.parametrize("variant", [0, 1])
+def test_benchmark_shape_sampled(tg, oracle_lib, variant):
     # the benchmark workload (64 sequences x 8192 tokens, 128 heads) in the
     # launch configuration the benchmark times; the oracle computes three
     # whole sequences
     w = workloads.MLA_WORKLOAD
     B, H, Sk = w["B"], w["H"], w["Sk"]
     q, kv = workloads.generate_mla(B, H, Sk, w["seed"])
-    say("mla benchmark shape")
+    say(f"mla benchmark shape variant={variant}")
+    tg.tg_set_mla_variant(variant)
     got = run(tg, q, kv, B, H, Sk, SCALE).reshape(B, H, DL)
     o = v16(got)
     assert np.all(np.isfinite(o))

@@ -35,7 +35,7 @@
 //    |scale| * log2(e) folded into one FMA per score (a negative scale is
 //    carried by Q), tiles that every query of a wave sees skip the mask,
 //    and the row sums add the fp16 probabilities in pairs (v_dot2).
-#include "tg_internal.h"
+#include "tg_mla.h"
 
 namespace tg {
 namespace {
@@ -487,17 +487,24 @@ hipError_t launch_attn(const AttnArgs &p, hipStream_t stream)
 //    one XCD and share its L2.
 namespace mla {
 constexpr int D = kMlaDl + kMlaDr;   // 576 values per cached row
-constexpr int NW = 4;                // waves: two head groups x two halves
 constexpr int BK = 32;               // cached rows per tile
 constexpr int TILE = BK * D;         // fp16 elements per tile
-constexpr int STAGES = 4;
 constexpr int BLOCKS = TILE * 2 / 1024;  // 1 KiB DMA blocks per tile
-constexpr int LD = BLOCKS / NW;      // ... per wave
-constexpr int DS = D / 16 / 2;       // 16-wide score steps per half
-constexpr int DB = kMlaDl / 32 / 2;  // 32-wide output blocks per half
-constexpr int XCH = NW * 16 * 64;    // floats of the score exchange
-static_assert(BLOCKS % NW == 0, "blocks per wave");
-static_assert(32 * NW / 2 == kMlaHeadsPerBlock, "heads per workgroup");
+
+// NQ parts of the head dimension per 32-head group, two groups per workgroup
+template <int NQ_>
+struct Cfg {
+    static constexpr int NQ = NQ_;
+    static constexpr int NW = 2 * NQ;                    // waves
+    static constexpr int WPE = NW / 4;                   // waves per SIMD
+    static constexpr int STAGES = NQ == 2 ? 4 : 3;       // ring depth (LDS: 160 / 140 KiB)
+    static constexpr int LD = (BLOCKS + NW - 1) / NW;    // DMA blocks per wave per tile
+    static constexpr int DS = D / 16 / NQ;               // 16-wide score steps per part
+    static constexpr int DB = kMlaDl / 32 / NQ;          // 32-wide output blocks per part
+    static constexpr int XCH = NW * 16 * 64;             // floats of the score exchange
+    static_assert(D % (16 * NQ) == 0 && kMlaDl % (32 * NQ) == 0, "parts");
+    static_assert(32 * 2 == kMlaHeadsPerBlock, "heads per workgroup");
+};
 }  // namespace mla
 
 __device__ __forceinline__ int mla_swz(int row, int c)
@@ -505,19 +512,22 @@ __device__ __forceinline__ int mla_swz(int row, int c)
     return c ^ (2 * ((row >> 1) & 3) + ((row >> 3) & 1));
 }
 
-__global__ void __launch_bounds__(64 * mla::NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <class T>
+__global__ void __launch_bounds__(64 * T::NW) __attribute__((amdgpu_waves_per_eu(T::WPE, T::WPE)))
 mla_decode_kernel(MlaArgs p)
 {
     using namespace mla;
+    constexpr int NQ = T::NQ, NW = T::NW, STAGES = T::STAGES, LD = T::LD, DS = T::DS,
+                  DB = T::DB;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * TILE];
-    __shared__ __attribute__((aligned(16))) float xch[XCH];
+    __shared__ __attribute__((aligned(16))) float xch[T::XCH];
     const lds_u16 *lds = (const lds_u16 *)smem;
     const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hg = wave >> 1, e = wave & 1;
+    const int hg = wave / NQ, e = wave % NQ;   // head group, part of the head dimension
     const int hi = lane >> 5;
     // grid x: 8 consecutive (sequence, key range) units, then the same 8
     // for the next head block, ...
@@ -541,10 +551,10 @@ mla_decode_kernel(MlaArgs p)
     kend = kend < n ? kend : n;
     const int tiles = kend > kbeg ? (int)((kend - kbeg + BK - 1) / BK) : 0;
 
-    // Q^T fragments (second operand): lane holds Q[b][h][288 e + 16 ds + 8 hi .. + 7]
+    // Q^T fragments (second operand): lane holds Q[b][h][(D / NQ) e + 16 ds + 8 hi .. + 7]
     f16x8 qf[DS];
     {
-        const uint16_t *qrow = p.Q + (b * p.H + (live ? h : 0)) * D + e * (D / 2);
+        const uint16_t *qrow = p.Q + (b * p.H + (live ? h : 0)) * D + e * (D / NQ);
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
             qf[ds] = f16x8{};
@@ -557,11 +567,13 @@ mla_decode_kernel(MlaArgs p)
 
     // DMA plan: slot s (16 bytes) of a tile is row s / 72, physical chunk
     // s % 72, which receives the row's logical chunk mla_swz(row, chunk);
-    // wave w moves 1 KiB blocks w, w + 4, ...
+    // wave w moves 1 KiB blocks w, w + NW, ... (past the last block it
+    // moves the last block again: the same bytes to the same place)
     uint32_t voff[LD];
 #pragma unroll
     for (int i = 0; i < LD; ++i) {
-        const int slot = (wave + NW * i) * 64 + lane;
+        const int blk = wave + NW * i < BLOCKS ? wave + NW * i : BLOCKS - 1;
+        const int slot = blk * 64 + lane;
         const int row = slot / (D / 8);
         const int pc = slot % (D / 8);
         voff[i] = (uint32_t)((row * D + mla_swz(row, pc) * 8) * 2);
@@ -574,8 +586,10 @@ mla_decode_kernel(MlaArgs p)
         rsrc.z = __builtin_amdgcn_readfirstlane((int)(rows * D * 2));
         const uint32_t base = lds_base + (uint32_t)((t % STAGES) * TILE * 2);
 #pragma unroll
-        for (int i = 0; i < LD; ++i)
-            dma16(rsrc, voff[i], base + (uint32_t)((wave + NW * i) * 1024));
+        for (int i = 0; i < LD; ++i) {
+            const int blk = wave + NW * i < BLOCKS ? wave + NW * i : BLOCKS - 1;
+            dma16(rsrc, voff[i], base + (uint32_t)(blk * 1024));
+        }
     };
 
     f32x16 acc_o[DB];
@@ -584,13 +598,10 @@ mla_decode_kernel(MlaArgs p)
         acc_o[db] = f32x16{};
     float m_run = -1.0e30f, l_run = 0.0f;
     const float sl2 = __builtin_fmaxf(__builtin_fabsf(p.scale) * 1.44269504088896340736f, 1.0e-30f);
-    // score exchange: this wave's partial at mine, its partner's at theirs;
-    // float4 j of a lane at (4 * wave + j) * 64 + lane
+    // score exchange: float4 j of a lane of wave w at (4 w + j) * 64 + lane
     float4 *mine = reinterpret_cast<float4 *>(xch) + wave * 4 * 64 + lane;
-    const float4 *theirs = reinterpret_cast<const float4 *>(xch) + (wave ^ 1) * 4 * 64 + lane;
+    const float4 *group = reinterpret_cast<const float4 *>(xch) + hg * NQ * 4 * 64 + lane;
 
-    // this half's score partials for tile t: lane holds head h's sums for
-    // keys k0 + 8 (r / 4) + 4 hi + r % 4
     // LDS addresses as per-lane bases plus compile-time offsets: a K fragment
     // of step ds sits at kbase[ds % 4] + 64 (ds / 4) elements (adding 8 to a
     // chunk index leaves the XOR-ed low bits alone), a V fragment at
@@ -610,18 +621,19 @@ mla_decode_kernel(MlaArgs p)
             const int key = 8 * hh + 4 * hi + ((lane & 15) >> 2);
 #pragma unroll
             for (int par = 0; par < 2; ++par) {
-                const int d = e * (kMlaDl / 2) + par * 32 + dl;
+                const int d = e * (kMlaDl / NQ) + par * 32 + dl;
                 vbase[hh][par] = key * D + mla_swz(key, d >> 3) * 8 + (d & 7);
             }
         }
     }
+    // this part's score partials for tile t: lane holds head h's sums for
+    // keys k0 + 8 (r / 4) + 4 hi + r % 4
     auto scores = [&](int t) {
         // the stage offset kept opaque, so the addresses stay base + constant
         const lds_u16 *Ks = lds + __builtin_amdgcn_readfirstlane((t % STAGES) * TILE);
         const lds_u16 *kb[4] = {Ks + kbase[0], Ks + kbase[1], Ks + kbase[2], Ks + kbase[3]};
-        // K fragments read KA steps ahead of the products that use them: one
-        // wave per SIMD has nothing else to hide the LDS latency behind
-        constexpr int KA = 6;
+        // K fragments read KA steps ahead of the products that use them
+        constexpr int KA = DS < 6 ? DS : 6;
         f16x8 kf[DS];
         f32x16 acc = f32x16{};
 #pragma unroll
@@ -640,22 +652,35 @@ mla_decode_kernel(MlaArgs p)
         return acc;
     };
     auto publish = [&](const f32x16 &acc) {
-        float4 *dst = mine;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            dst[j * 64] = float4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
+            mine[j * 64] = float4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
     };
-    // the partner's partial for tile t, added (addition commutes: both
-    // waves of the pair hold the same bits), masked past the range
+    // the group's partials for tile t added in a fixed tree over the parts
+    // (this wave's own from its registers): every wave of the group holds
+    // the same bits; masked past the range
     auto complete = [&](int t, f32x16 &acc, bool last) {
-        const float4 *src = theirs;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float4 o = src[j * 64];
-            acc[4 * j + 0] += o.x;
-            acc[4 * j + 1] += o.y;
-            acc[4 * j + 2] += o.z;
-            acc[4 * j + 3] += o.w;
+            float4 part[NQ];
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                part[q] = q == e ? float4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]}
+                                 : group[(q * 4 + j) * 64];
+#pragma unroll
+            for (int w = 1; w < NQ; w *= 2) {
+#pragma unroll
+                for (int q = 0; q + w < NQ; q += 2 * w) {
+                    part[q].x += part[q + w].x;
+                    part[q].y += part[q + w].y;
+                    part[q].z += part[q + w].z;
+                    part[q].w += part[q + w].w;
+                }
+            }
+            acc[4 * j + 0] = part[0].x;
+            acc[4 * j + 1] = part[0].y;
+            acc[4 * j + 2] = part[0].z;
+            acc[4 * j + 3] = part[0].w;
         }
         const int64_t k0 = kbeg + (int64_t)t * BK;
         if (last && k0 + BK > kend) {    // only the range's last tile can be partial
@@ -664,7 +689,7 @@ mla_decode_kernel(MlaArgs p)
             acc = sm[0];
         }
     };
-    // this half of O^T += V^T P^T (values 256 e .. 256 e + 255) for tile t
+    // this part of O^T += V^T P^T (values (512 / NQ) e ..) for tile t
     auto values = [&](int t, const f16x8 (&pf)[2]) {
         const lds_u16 *Vs = lds + __builtin_amdgcn_readfirstlane((t % STAGES) * TILE);
         const lds_u16 *vb[2][2] = {{Vs + vbase[0][0], Vs + vbase[0][1]},
@@ -695,13 +720,13 @@ mla_decode_kernel(MlaArgs p)
         }
     };
 
-    // Software pipeline over a 4-stage ring: iteration t computes tile t's
-    // score partials on the matrix cores while the vector units finish tile
-    // t-1's softmax, then tile t-1's value product.  A barrier in the middle
-    // (every wave is past its read of the exchange and of tile t-1's stage)
-    // lets tile t's partials be published and tile t+3 be loaded into that
-    // stage; the barrier at the end publishes the partials and makes tile t+1
-    // visible, which has had two iterations to arrive.
+    // Software pipeline: iteration t computes tile t's score partials on the
+    // matrix cores while the vector units finish tile t-1's softmax, then
+    // tile t-1's value product.  A barrier in the middle (every wave is past
+    // its read of the exchange and of tile t-1's stage) lets tile t's
+    // partials be published and tile t + STAGES - 1 be loaded into that
+    // stage; the barrier at the end publishes the partials and makes tile
+    // t+1 visible.
     auto wait_tiles_beyond = [&](int n) {   // all but the n newest tiles landed
         if (n >= 2)
             wait_vmcnt<2 * LD>();
@@ -710,18 +735,19 @@ mla_decode_kernel(MlaArgs p)
         else
             wait_vmcnt<0>();
     };
+    constexpr int AHEAD = STAGES - 1;        // tiles in flight beyond the one computed
     if (tiles > 0) {
-        for (int t = 0; t < STAGES - 1 && t < tiles; ++t)
+        for (int t = 0; t < AHEAD && t < tiles; ++t)
             issue(t);
-        wait_tiles_beyond(tiles - 1 < 2 ? tiles - 1 : 2);
+        wait_tiles_beyond(tiles - 1 < AHEAD - 1 ? tiles - 1 : AHEAD - 1);
         block_barrier();                      // tile 0 visible
         f32x16 prev = scores(0);
         publish(prev);
         if (tiles > 1)
-            wait_tiles_beyond(tiles - 2 < 1 ? tiles - 2 : 1);
+            wait_tiles_beyond(tiles - 2 < AHEAD - 2 ? tiles - 2 : AHEAD - 2);
         block_barrier();                      // partials 0 published, tile 1 visible
-        if (tiles > 3)
-            issue(3);
+        if (tiles > AHEAD)
+            issue(AHEAD);
         for (int t = 1; t < tiles; ++t) {
             complete(t - 1, prev, false);
             f16x8 pf[2];
@@ -731,12 +757,12 @@ mla_decode_kernel(MlaArgs p)
             values(t - 1, pf);
             block_barrier();                  // exchange read, tile t-1's stage free
             publish(cur);
-            if (t + 3 < tiles)
-                issue(t + 3);
+            if (t + AHEAD < tiles)
+                issue(t + AHEAD);
             prev = cur;
             if (t + 1 < tiles) {
-                const int ahead = (t + 3 < tiles ? t + 3 : tiles - 1) - (t + 1);
-                wait_tiles_beyond(ahead);     // tile t+1 landed
+                const int last = t + AHEAD < tiles ? t + AHEAD : tiles - 1;
+                wait_tiles_beyond(last - (t + 1));   // tile t+1 landed
             }
             block_barrier();                  // partials t published, tile t+1 visible
         }
@@ -752,7 +778,7 @@ mla_decode_kernel(MlaArgs p)
     const float l_all = l_run + __shfl_xor(l_run, 32);
     if (!live)
         return;
-    const int d0 = e * (kMlaDl / 2);
+    const int d0 = e * (kMlaDl / NQ);
     if (p.splits == 1) {
         const float inv = l_all > 0.0f ? 1.0f / l_all : 0.0f;
         uint16_t *orow = p.O + (b * p.H + h) * kMlaDl + d0;
@@ -837,8 +863,12 @@ hipError_t launch_mla_decode(const MlaArgs &p, hipStream_t stream)
     // the host has checked that the grid fits 2^31 workgroups
     const int64_t nhb = (p.H + kMlaHeadsPerBlock - 1) / kMlaHeadsPerBlock;
     const int64_t units = (p.B * p.splits + 7) / 8 * 8;
-    hipLaunchKernelGGL(mla_decode_kernel, dim3((unsigned)(units * nhb)), dim3(64 * mla::NW), 0,
-                       stream, p);
+    if (p.variant == 1)
+        hipLaunchKernelGGL(mla_decode_kernel<mla::Cfg<4>>, dim3((unsigned)(units * nhb)),
+                           dim3(64 * mla::Cfg<4>::NW), 0, stream, p);
+    else
+        hipLaunchKernelGGL(mla_decode_kernel<mla::Cfg<2>>, dim3((unsigned)(units * nhb)),
+                           dim3(64 * mla::Cfg<2>::NW), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1)
         return e;

@@ -137,26 +137,11 @@ struct AttnArgs {
 };
 hipError_t launch_attention(const AttnArgs &p, hipStream_t stream);
 
-// One latent-attention decode: for every sequence b and query head h,
-// O[b][h][:512] = softmax_j(scale * Q[b][h][:] . KV[b][j][:]) KV[b][j][:512]
-// over the first n_b cached rows (n_b = seqlens[b] clamped to [0, Sk], or Sk
-// without seqlens).  Q (B, H, 576), KV (B, Sk, 576), O (B, H, 512) fp16,
-// contiguous.  With splits > 1 the keys of a sequence are cut into `splits`
-// ranges of keys_per_split (a multiple of 64) and each range writes an
-// unnormalised fp32 partial to `part` (B * H * splits * 512 floats, then
-// B * H * splits (maximum, sum) pairs), which a second kernel combines.
-struct MlaArgs {
-    const uint16_t *Q, *KV;
-    uint16_t *O;
-    const int32_t *seqlens;
-    float *part;
-    int64_t B, H, Sk;
-    float scale;
-    int splits;
-    int64_t keys_per_split;
-};
-constexpr int kMlaDl = 512, kMlaDr = 64, kMlaHeadsPerBlock = 64;
-hipError_t launch_mla_decode(const MlaArgs &p, hipStream_t stream);
+// Host helpers of the entry points (defined in api.cpp): the per-device
+// architecture check (TG_OK or an error status) and the record of the last
+// path used.
+int host_check_device();
+void host_set_last_path(int path);
 
 // Every launcher enqueues on `stream` and returns hipGetLastError().  The
 // tile launchers take the raster setting of tile_coords.

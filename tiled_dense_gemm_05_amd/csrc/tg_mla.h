@@ -1,0 +1,31 @@
+// Internal interface of the latent-attention decode: entry point
+// (mla_api.cpp) to kernels (attention.hip).
+#pragma once
+
+#include "tg_internal.h"
+
+namespace tg {
+
+// One latent-attention decode: for every sequence b and query head h,
+// O[b][h][:512] = softmax_j(scale * Q[b][h][:] . KV[b][j][:]) KV[b][j][:512]
+// over the first n_b cached rows (n_b = seqlens[b] clamped to [0, Sk], or Sk
+// without seqlens).  Q (B, H, 576), KV (B, Sk, 576), O (B, H, 512) fp16,
+// contiguous.  With splits > 1 the keys of a sequence are cut into `splits`
+// ranges of keys_per_split (a multiple of 64) and each range writes an
+// unnormalised fp32 partial to `part` (B * H * splits * 512 floats, then
+// B * H * splits (maximum, sum) pairs), which a second kernel combines.
+struct MlaArgs {
+    const uint16_t *Q, *KV;
+    uint16_t *O;
+    const int32_t *seqlens;
+    float *part;
+    int64_t B, H, Sk;
+    float scale;
+    int splits;
+    int64_t keys_per_split;
+    int variant;   // 0: two parts of the head dimension, four waves; 1: four parts, eight waves
+};
+constexpr int kMlaDl = 512, kMlaDr = 64, kMlaHeadsPerBlock = 64;
+hipError_t launch_mla_decode(const MlaArgs &p, hipStream_t stream);
+
+}  // namespace tg
