@@ -556,8 +556,6 @@ def main():
                          "tokens x 128 heads, rows of 512 + 64 (tg_mla_decode_f16) and exit")
     ap.add_argument("--mla-splits", type=int, default=-1,
                     help="key ranges per sequence of the decode bench (tg_set_mla_splits)")
-    ap.add_argument("--mla-variant", type=int, default=-1,
-                    help="decode workgroup shape (tg_set_mla_variant), -1 = default")
     ap.add_argument("--w4", action="store_true",
                     help="time the weight-only int4 GEMM on the decode shape "
                          "16 x 16384 x 8192, groups of 128 (tg_gemm_w4) and exit")
@@ -639,8 +637,6 @@ def main():
     if args.mla:
         if args.mla_splits != -1:
             tg.tg_set_mla_splits(args.mla_splits)
-        if args.mla_variant != -1 and tg.tg_set_mla_variant(args.mla_variant) < -1:
-            sys.exit(f"invalid --mla-variant {args.mla_variant}")
         w = wl.MLA_WORKLOAD
         B, H, Sk = w["B"], w["H"], w["Sk"]
         ms, path, need = run_mla(tg, torch, args.steps, args.warmup)
@@ -658,8 +654,7 @@ def main():
             "data": "synthetic",
             "config": {"workload": w["name"], "batch": B, "heads": H, "seq_k": Sk,
                        "row": "512+64", "tflops": tflops, "path": path,
-                       "splits": args.mla_splits, "variant": args.mla_variant,
-                       "workspace_bytes": need},
+                       "splits": args.mla_splits, "workspace_bytes": need},
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM_GBS, "traffic": None}}), flush=True)
         return

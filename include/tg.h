@@ -251,15 +251,6 @@ int64_t tg_mla_decode_workspace_bytes(int64_t batch, int64_t heads, int64_t seq_
  */
 int tg_set_mla_splits(int splits);
 
-/*
- * Tuning knob for benchmarks: the decode kernel's workgroup shape (0: each
- * 32-head group split over 2 waves along the head dimension, one wave per
- * SIMD; 1: over 4 waves, two per SIMD; -1: the default).  Every variant
- * computes the same result within the accuracy of tg_mla_decode_f16.
- * Returns the previous setting, or -2 for an unknown variant (unchanged).
- */
-int tg_set_mla_variant(int variant);
-
 /* A static, human-readable name for a tg_status value. */
 const char *tg_status_string(int status);
 

@@ -196,6 +196,44 @@ def test_grouped_query_attention_validation(tg):
     assert call(H=0, Hkv=0) == tg.TG_OK and call(H=0, Hkv=3) == tg.TG_OK
 
 
+def test_mla_decode_validation(tg):
+    f = tg.tg_mla_decode_f16
+
+    def call(Q=P, KV=P, O=P, sl=0, B=2, H=16, Sk=100, scale=0.1, ws=0, wsb=0):
+        return f(Q, KV, O, sl, B, H, Sk, scale, ws, wsb, 0)
+
+    bad = tg.TG_ERR_INVALID_ARG
+    assert call(Q=0) == bad and call(O=0) == bad and call(KV=0) == bad
+    assert call(KV=0, Sk=0) != bad                       # no cached rows: no KV needed
+    assert call(Q=P + 2) == bad and call(O=P + 8) == bad and call(KV=P + 4) == bad
+    assert call(sl=P + 2) == bad                          # int32 lengths, 4-byte aligned
+    assert call(ws=P + 4, wsb=1 << 20) == bad             # workspace 16-byte aligned
+    assert call(wsb=-1) == bad
+    assert call(B=-1) == bad and call(H=-1) == bad and call(Sk=-1) == bad
+    assert call(scale=float("nan")) == bad and call(scale=float("inf")) == bad
+    assert call(B=1 << 31) == bad                          # beyond int32 sequence counts
+    assert call(B=0) == tg.TG_OK and call(H=0) == tg.TG_OK
+    assert tg.tg_path_name(tg.TG_PATH_MLA) == "mla"
+
+
+def test_mla_workspace_sizes(tg):
+    ws = tg.tg_mla_decode_workspace_bytes
+    per = lambda B, H: B * H * (512 + 2) * 4   # one key range: fp32 outputs, maximum and sum
+    # 64 sequences of 128 heads: 128 workgroups of 64 heads, two ranges fill 256 CUs
+    assert ws(64, 128, 8192) == 2 * per(64, 128)
+    # one sequence: as many ranges as give each CU a workgroup, at least 8 tiles of 32 each
+    assert ws(1, 64, 4096) == 16 * per(1, 64)
+    assert ws(1, 128, 1 << 20) == 128 * per(1, 128)
+    assert ws(1, 16, 100) == 0                           # too short to split
+    assert ws(512, 128, 8192) == 0                       # enough sequences to fill the chip
+    assert ws(0, 16, 100) == 0 and ws(4, 0, 100) == 0 and ws(4, 16, 0) == 0
+    assert ws(-1, 16, 100) == -1 and ws(1 << 31, 1, 1) == -1
+    assert tg.tg_set_mla_splits(3) == 0
+    assert ws(1, 64, 4096) == 3 * per(1, 64)             # forced ranges
+    assert tg.tg_set_mla_splits(-1) == 3
+    assert tg.tg_set_mla_splits(-2) == -2
+
+
 def _gpu_visible():
     try:
         import torch
@@ -213,6 +251,7 @@ def test_valid_call_without_device_reports_no_device(tg):
     assert st == tg.TG_ERR_NO_DEVICE
     assert tg.tg_gemm_w4(0, 1, P, P, P, P, 0, 4, 8, 128, 64, 128, 64, 2, 8,
                          0) == tg.TG_ERR_NO_DEVICE
+    assert tg.tg_mla_decode_f16(P, P, P, 0, 2, 16, 100, 0.1, 0, 0, 0) == tg.TG_ERR_NO_DEVICE
     assert tg.tg_attention_fwd_f16(P, P, P, P, 1, 8, 8, 2, 64, 0.1, 1, 0) == tg.TG_ERR_NO_DEVICE
     assert tg.tg_attention_fwd_f16_gqa(P, P, P, P, 1, 8, 8, 8, 2, 64, 0.1, 1,
                                        0) == tg.TG_ERR_NO_DEVICE

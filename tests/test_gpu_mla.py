@@ -43,7 +43,6 @@ def tg():
 def _default_splits(tg):
     yield
     tg.tg_set_mla_splits(-1)
-    tg.tg_set_mla_variant(-1)
 
 
 def dev(bits) -> "torch.Tensor":
@@ -110,24 +109,21 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("variant", [0, 1])
 @pytest.mark.parametrize("splits", [-1, 1, 2, 5])
 @pytest.mark.parametrize("B,H,Sk", CASES)
-def test_mla_matches_oracle(tg, oracle_lib, variant, splits, B, H, Sk):
+def test_mla_matches_oracle(tg, oracle_lib, splits, B, H, Sk):
     q, kv = inputs(B, H, Sk, B * 7 + H + Sk)
     ref = oracle_lib.mla_decode(q, kv, B, H, Sk, SCALE)
-    say(f"mla B={B} H={H} Sk={Sk} splits={splits} variant={variant}")
+    say(f"mla B={B} H={H} Sk={Sk} splits={splits}")
     tg.tg_set_mla_splits(splits)
-    assert tg.tg_set_mla_variant(variant) >= 0
     need = tg.tg_mla_decode_workspace_bytes(B, H, Sk)
     per = B * H * (DL + 2) * 4
     ws = max(need, per * max(splits, 1))
     check(run(tg, q, kv, B, H, Sk, SCALE, ws_bytes=ws), ref, kv, B, Sk)
 
 
-@pytest.mark.parametrize("variant", [0, 1])
 @pytest.mark.parametrize("splits", [1, 3])
-def test_ragged_lengths_and_junk_past_them(tg, oracle_lib, splits, variant):
+def test_ragged_lengths_and_junk_past_them(tg, oracle_lib, splits):
     # lengths 0, 1, a tile edge, mid-tile and full; rows past a length hold NaN
     B, H, Sk = 6, 80, 300
     lens = [0, 1, 32, 33, 299, 300]
@@ -136,9 +132,8 @@ def test_ragged_lengths_and_junk_past_them(tg, oracle_lib, splits, variant):
     junk = kv.reshape(B, Sk, DQ).copy()
     for b, n in enumerate(lens):
         junk[b, n:] = 0x7E00
-    say(f"mla ragged splits={splits} variant={variant}")
+    say(f"mla ragged splits={splits}")
     tg.tg_set_mla_splits(splits)
-    tg.tg_set_mla_variant(variant)
     got = run(tg, q, junk.reshape(-1), B, H, Sk, SCALE, lens=lens,
               ws_bytes=B * H * (DL + 2) * 4 * splits)
     check(got, ref, kv, B, Sk, lens)
@@ -154,15 +149,13 @@ def test_lengths_outside_the_cache_are_clamped(tg, oracle_lib):
     check(run(tg, q, kv, B, H, Sk, SCALE, lens=[-5, 100, 1 << 30]), ref, kv, B, Sk)
 
 
-@pytest.mark.parametrize("variant", [0, 1])
 @pytest.mark.parametrize("spread,scale", [(3.0, 0.5), (0.01, 1.0), (1.0, -SCALE), (1.0, 0.0)])
-def test_sharp_flat_negative_and_zero_scale(tg, oracle_lib, spread, scale, variant):
+def test_sharp_flat_negative_and_zero_scale(tg, oracle_lib, spread, scale):
     B, H, Sk = 2, 64, 700
     q, kv = inputs(B, H, Sk, 5, spread=spread)
     ref = oracle_lib.mla_decode(q, kv, B, H, Sk, scale)
-    say(f"mla spread={spread} scale={scale} variant={variant}")
+    say(f"mla spread={spread} scale={scale}")
     tg.tg_set_mla_splits(3)
-    tg.tg_set_mla_variant(variant)
     check(run(tg, q, kv, B, H, Sk, scale, ws_bytes=B * H * (DL + 2) * 4 * 3), ref, kv, B, Sk)
 
 
@@ -177,12 +170,10 @@ def test_small_workspace_lowers_the_split_count(tg, oracle_lib):
         check(o, ref, kv, B, Sk)
 
 
-@pytest.mark.parametrize("variant", [0, 1])
-def test_deterministic(tg, variant):
+def test_deterministic(tg):
     B, H, Sk = 4, 128, 2000
     q, kv = inputs(B, H, Sk, 8)
-    say(f"mla determinism variant={variant}")
-    tg.tg_set_mla_variant(variant)
+    say("mla determinism")
     a = run(tg, q, kv, B, H, Sk, SCALE)
     b = run(tg, q, kv, B, H, Sk, SCALE)
     assert np.array_equal(a, b)
@@ -219,16 +210,14 @@ def test_torch_helper(tg, oracle_lib):
           [333, 100])
 
 
-@pytest.mark.parametrize("variant", [0, 1])
-def test_benchmark_shape_sampled(tg, oracle_lib, variant):
+def test_benchmark_shape_sampled(tg, oracle_lib):
     # the benchmark workload (64 sequences x 8192 tokens, 128 heads) in the
     # launch configuration the benchmark times; the oracle computes three
     # whole sequences
     w = workloads.MLA_WORKLOAD
     B, H, Sk = w["B"], w["H"], w["Sk"]
     q, kv = workloads.generate_mla(B, H, Sk, w["seed"])
-    say(f"mla benchmark shape variant={variant}")
-    tg.tg_set_mla_variant(variant)
+    say("mla benchmark shape")
     got = run(tg, q, kv, B, H, Sk, SCALE).reshape(B, H, DL)
     o = v16(got)
     assert np.all(np.isfinite(o))

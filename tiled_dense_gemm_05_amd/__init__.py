@@ -51,7 +51,6 @@ EXPORTED_SYMBOLS = (
     "tg_mla_decode_f16",
     "tg_mla_decode_workspace_bytes",
     "tg_set_mla_splits",
-    "tg_set_mla_variant",
 )
 
 TG_DTYPE_F16 = 0
@@ -97,8 +96,6 @@ _lib.tg_mla_decode_workspace_bytes.argtypes = [_i64] * 3
 _lib.tg_mla_decode_workspace_bytes.restype = ctypes.c_int64
 _lib.tg_set_mla_splits.argtypes = [ctypes.c_int]
 _lib.tg_set_mla_splits.restype = ctypes.c_int
-_lib.tg_set_mla_variant.argtypes = [ctypes.c_int]
-_lib.tg_set_mla_variant.restype = ctypes.c_int
 _lib.tg_status_string.argtypes = [ctypes.c_int]
 _lib.tg_status_string.restype = ctypes.c_char_p
 _lib.tg_set_path.argtypes = [ctypes.c_int]
@@ -180,10 +177,6 @@ def tg_mla_decode_workspace_bytes(batch: int, heads: int, seq_k: int) -> int:
 
 def tg_set_mla_splits(splits: int) -> int:
     return _lib.tg_set_mla_splits(splits)
-
-
-def tg_set_mla_variant(variant: int) -> int:
-    return _lib.tg_set_mla_variant(variant)
 
 
 def tg_status_string(status: int) -> str:

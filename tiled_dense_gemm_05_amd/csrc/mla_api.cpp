@@ -14,9 +14,6 @@ constexpr int64_t kMaxDim = 0x7fffffff;
 constexpr __int128 kMaxExtent = (__int128)1 << 62;
 // forced number of key ranges (0: chosen from the sizes)
 std::atomic<int> g_mla_splits{0};
-// kernel configuration (see tg_set_mla_variant)
-constexpr int kMlaVariantDefault = 0;
-std::atomic<int> g_mla_variant{kMlaVariantDefault};
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -114,7 +111,6 @@ int tg_mla_decode_f16(const void *Q, const void *KV, void *O, const int32_t *seq
     p.part = static_cast<float *>(workspace);
     p.B = batch; p.H = heads; p.Sk = seq_k;
     p.scale = scale;
-    p.variant = g_mla_variant.load(std::memory_order_relaxed);
     const int64_t s = mla_splits(batch, heads, seq_k, workspace_bytes);
     const int64_t tiles = (seq_k + kMlaTile - 1) / kMlaTile;
     const int64_t per = (tiles + s - 1) / s;                 // tiles per range
@@ -130,15 +126,6 @@ int tg_mla_decode_f16(const void *Q, const void *KV, void *O, const int32_t *seq
         return TG_ERR_HIP;
     tg::host_set_last_path(TG_PATH_MLA);
     return TG_OK;
-}
-
-int tg_set_mla_variant(int variant)
-{
-    if (variant == -1)
-        variant = kMlaVariantDefault;
-    if (variant < 0 || variant > 1)
-        return -2;
-    return g_mla_variant.exchange(variant);
 }
 
 int tg_set_mla_splits(int splits)

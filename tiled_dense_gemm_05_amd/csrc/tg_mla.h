@@ -23,7 +23,6 @@ struct MlaArgs {
     float scale;
     int splits;
     int64_t keys_per_split;
-    int variant;   // 0: two parts of the head dimension, four waves; 1: four parts, eight waves
 };
 constexpr int kMlaDl = 512, kMlaDr = 64, kMlaHeadsPerBlock = 64;
 hipError_t launch_mla_decode(const MlaArgs &p, hipStream_t stream);
