@@ -240,6 +240,43 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[KB], f16x8 (&pf)[2 * KB
     l_run += ls[0] + ls[1];
 }
 
+// The softmax step of softmax_tile for one 32-key block without the
+// accumulator rescale: raises the running maximum when the block exceeds it
+// by more than 2^8 (`grow`, with `alpha` the factor the caller must apply to
+// its output accumulator), rescales the sum and writes the fp16
+// probabilities.  Free of branches, so it can share a basic block (and the
+// scheduler's interleaving) with independent matrix work.
+__device__ __forceinline__ void softmax_block(const f32x16 &s, f16x8 (&pf)[2], float &m_run,
+                                              float &l_run, float sl2, float &alpha, bool &grow)
+{
+    float mt = -__builtin_inff();
+#pragma unroll
+    for (int r = 0; r < 16; r += 2)
+        mt = __builtin_fmaxf(mt, __builtin_fmaxf(s[r], s[r + 1]));
+    mt = max_pair(mt);
+    const float m_tile = __builtin_fmaxf(mt * sl2, -1.0e30f);
+    grow = m_tile > m_run + kGrowLog2;
+    const float m_new = grow ? m_tile : m_run;
+    alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    const float neg_m = -m_run;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            pf[kk][j] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * kk + j], sl2, neg_m));
+    }
+    float ls[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            ls[j & 1] = __builtin_amdgcn_fdot2(f16x2{pf[kk][2 * j], pf[kk][2 * j + 1]},
+                                               f16x2{(_Float16)1.0f, (_Float16)1.0f}, ls[j & 1], false);
+    }
+    l_run = l_run * alpha + (ls[0] + ls[1]);
+}
+
 // Two waves per SIMD: lets the scheduler keep LDS reads in flight ahead of
 // the matrix instructions that consume them instead of minimizing registers.
 template <class T>
@@ -659,31 +696,21 @@ mla_decode_kernel(MlaArgs p)
         for (int j = 0; j < 4; ++j)
             mine[j * 64] = float4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
     };
-    // the group's partials for tile t added in a fixed tree over the parts
-    // (this wave's own from its registers): every wave of the group holds
-    // the same bits; masked past the range
+    // the partner's partial for tile t added (addition commutes: both waves
+    // of the pair hold the same bits)
+    static_assert(NQ == 2, "the exchange adds one partner's partial");
+    const float4 *theirs = group + (e ^ 1) * 4 * 64;
     auto complete = [&](int t, f32x16 &acc, bool last) {
+        float4 o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            o[j] = theirs[j * 64];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            float4 part[NQ];
-#pragma unroll
-            for (int q = 0; q < NQ; ++q)
-                part[q] = q == e ? float4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]}
-                                 : group[(q * 4 + j) * 64];
-#pragma unroll
-            for (int w = 1; w < NQ; w *= 2) {
-#pragma unroll
-                for (int q = 0; q + w < NQ; q += 2 * w) {
-                    part[q].x += part[q + w].x;
-                    part[q].y += part[q + w].y;
-                    part[q].z += part[q + w].z;
-                    part[q].w += part[q + w].w;
-                }
-            }
-            acc[4 * j + 0] = part[0].x;
-            acc[4 * j + 1] = part[0].y;
-            acc[4 * j + 2] = part[0].z;
-            acc[4 * j + 3] = part[0].w;
+            acc[4 * j + 0] += o[j].x;
+            acc[4 * j + 1] += o[j].y;
+            acc[4 * j + 2] += o[j].z;
+            acc[4 * j + 3] += o[j].w;
         }
         const int64_t k0 = kbeg + (int64_t)t * BK;
         if (last && k0 + BK > kend) {    // only the range's last tile can be partial
@@ -723,6 +750,24 @@ mla_decode_kernel(MlaArgs p)
         }
     };
 
+    // acc_o *= alpha in place in the accumulation registers (rare: the
+    // running maximum of some head grew by more than 2^8)
+    auto rescale = [&](float alpha) {
+        // the last matrix-core writes of acc_o are a tile back; wait out the
+        // longest result latency anyway before reading them
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float x = acc_o[db][r];
+                scale_agpr(x, alpha);
+                acc_o[db][r] = x;
+            }
+        }
+        asm volatile("s_nop 4" ::: "memory");
+    };
+
     // Software pipeline: iteration t computes tile t's score partials on the
     // matrix cores while the vector units finish tile t-1's softmax, then
     // tile t-1's value product.  A barrier in the middle (every wave is past
@@ -752,11 +797,19 @@ mla_decode_kernel(MlaArgs p)
         if (tiles > AHEAD)
             issue(AHEAD);
         for (int t = 1; t < tiles; ++t) {
+            // the partner's partials are read first and tile t's products
+            // issued next; tile t-1's softmax fills the gaps between them
             complete(t - 1, prev, false);
-            f16x8 pf[2];
-            f32x16 sm[1] = {prev};
-            softmax_tile<DB, 1, true>(sm, pf, acc_o, m_run, l_run, sl2);
             const f32x16 cur = scores(t);
+            f16x8 pf[2];
+            float alpha;
+            bool grow;
+            softmax_block(prev, pf, m_run, l_run, sl2, alpha, grow);
+            // the probabilities are needed here, before the rare rescale
+            // branch, so they are computed beside tile t's products
+            asm volatile("" ::"v"(pf[0]), "v"(pf[1]));
+            if (__builtin_amdgcn_ballot_w64(grow))
+                rescale(alpha);
             values(t - 1, pf);
             block_barrier();                  // exchange read, tile t-1's stage free
             publish(cur);
@@ -771,8 +824,11 @@ mla_decode_kernel(MlaArgs p)
         }
         complete(tiles - 1, prev, true);
         f16x8 pf[2];
-        f32x16 sm[1] = {prev};
-        softmax_tile<DB, 1, true>(sm, pf, acc_o, m_run, l_run, sl2);
+        float alpha;
+        bool grow;
+        softmax_block(prev, pf, m_run, l_run, sl2, alpha, grow);
+        if (__builtin_amdgcn_ballot_w64(grow))
+            rescale(alpha);
         values(tiles - 1, pf);
     }
     wait_vmcnt<0>();
