@@ -210,6 +210,16 @@ def test_torch_helper(tg, oracle_lib):
           [333, 100])
 
 
+@pytest.mark.parametrize("B,H,Sk", [(1, 128, 65536), (3, 256, 1000), (300, 8, 40)])
+def test_long_wide_and_many(tg, oracle_lib, B, H, Sk):
+    # one long sequence (the most key ranges: 256 of 256 keys), four head
+    # blocks, and more sequences than the chip has compute units
+    q, kv = inputs(B, H, Sk, B + H)
+    ref = oracle_lib.mla_decode(q, kv, B, H, Sk, SCALE)
+    say(f"mla long/wide B={B} H={H} Sk={Sk}")
+    check(run(tg, q, kv, B, H, Sk, SCALE), ref, kv, B, Sk)
+
+
 def test_benchmark_shape_sampled(tg, oracle_lib):
     # the benchmark workload (64 sequences x 8192 tokens, 128 heads) in the
     # launch configuration the benchmark times; the oracle computes three
