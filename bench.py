@@ -310,7 +310,7 @@ def run_mla(tg, torch, steps: int, warmup: int):
     return t0.elapsed_time(t1) / steps, tg.tg_path_name(tg.tg_last_path()), need
 
 
-def cpu_baseline(w: wl.Workload, target_s: float = 12.0):
+def cpu_baseline(w: wl.Workload, target_s: float = 16.0):
     """The oracle, as it stands, on the host cores: rows 0..r-1 of the
     workload's C (all N columns, full K), r sized for about target_s seconds."""
     import oracle
@@ -327,7 +327,7 @@ def cpu_baseline(w: wl.Workload, target_s: float = 12.0):
     r2, dt2 = max(threads, 16), 0.0
     for _ in range(4):
         dt2 = timed(r2)
-        if dt2 >= 0.6 * target_s or r2 >= w.M:
+        if dt2 >= 0.7 * target_s or r2 >= w.M:   # a sample of 11-30 s
             break
         r2 = int(min(w.M, r2 * target_s / max(dt2, 1e-3)))
         r2 = max(threads, (r2 // threads) * threads)
