@@ -310,6 +310,41 @@ def run_mla(tg, torch, steps: int, warmup: int):
     return t0.elapsed_time(t1) / steps, tg.tg_path_name(tg.tg_last_path()), need
 
 
+def run_splitk(tg, torch, splits: int, steps: int, warmup: int):
+    """Times the split-K form of the skinny GEMM+ReLU (tg_gemm_relu_f16_splitk) on the
+    16 x 16384 x 8192 workload, input copies rotated as for the single-pass path;
+    returns (ms per call, copies, workspace bytes)."""
+    w = wl.WORKLOADS["skinny_16x16384x8192"]
+    a, b = wl.generate(w)
+    dev = torch.device("cuda:0")
+    nbuf = max(2, int(np.ceil(600e6 / w.compulsory_bytes)))
+    A = [torch.from_numpy(a.view(np.int16)).to(dev) for _ in range(nbuf)]
+    B = [torch.from_numpy(b.view(np.int16)).to(dev) for _ in range(nbuf)]
+    C = [torch.empty(w.M * w.N, dtype=torch.int16, device=dev) for _ in range(nbuf)]
+    need = tg.tg_gemm_splitk_workspace_bytes(w.M, w.N, splits)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call(j):
+        st = tg.tg_gemm_relu_f16_splitk(A[j].data_ptr(), B[j].data_ptr(), C[j].data_ptr(), w.M,
+                                        w.N, w.K, w.K, w.N, w.N, splits, ws.data_ptr(), need,
+                                        stream.cuda_stream)
+        if st != tg.TG_OK:
+            raise RuntimeError(tg.tg_status_string(st))
+
+    for i in range(warmup):
+        call(i % nbuf)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        call(i % nbuf)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps, nbuf, need
+
+
 def cpu_baseline(w: wl.Workload, target_s: float = 16.0):
     """The oracle, as it stands, on the host cores: rows 0..r-1 of the
     workload's C (all N columns, full K), r sized for about target_s seconds."""
@@ -556,6 +591,9 @@ def main():
                          "tokens x 128 heads, rows of 512 + 64 (tg_mla_decode_f16) and exit")
     ap.add_argument("--mla-splits", type=int, default=-1,
                     help="key ranges per sequence of the decode bench (tg_set_mla_splits)")
+    ap.add_argument("--skinny-splitk", type=int, default=0, metavar="S",
+                    help="ablation: time the split-K form (S chunks of K, fp32 partials in a "
+                         "workspace, tg_gemm_relu_f16_splitk) on the skinny workload and exit")
     ap.add_argument("--w4", action="store_true",
                     help="time the weight-only int4 GEMM on the decode shape "
                          "16 x 16384 x 8192, groups of 128 (tg_gemm_w4) and exit")
@@ -633,6 +671,22 @@ def main():
             "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_F16_TFLOPS,
                          "unit": "TFLOP/s", "frac": tflops / PEAK_F16_TFLOPS,
                          "traffic": None}}), flush=True)
+        return
+    if args.skinny_splitk:
+        w = wl.WORKLOADS["skinny_16x16384x8192"]
+        S = args.skinny_splitk
+        ms, nbuf, need = run_splitk(tg, torch, S, args.steps, args.warmup)
+        gbs = w.compulsory_bytes / (ms * 1e-3) / 1e9
+        log(f"skinny split-K S={S}: {ms * 1e3:.1f} us/call, {gbs:.0f} GB/s, workspace {need} bytes")
+        print(json.dumps({
+            "metric": "GB/s fp16 GEMM+ReLU at M=16, split-K form (ablation)", "value": gbs,
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f16", "data": "synthetic",
+            "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "splits": S,
+                       "input_copies": nbuf, "workspace_bytes": need},
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "traffic": None}}), flush=True)
         return
     if args.mla:
         if args.mla_splits != -1:

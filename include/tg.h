@@ -203,6 +203,28 @@ int tg_attention_fwd_f16_gqa(const void *Q, const void *K, const void *V, void *
                              hipStream_t stream);
 
 /*
+ * The skinny GEMM+ReLU split along K (the split-K form of the decode-shaped
+ * path, kept as an alternative to tg_gemm_relu_f16's single-pass skinny
+ * kernel for comparison): C = ReLU(A B) exactly as tg_gemm_relu_f16, computed
+ * as `splits` chunks of K (whole 32-k steps) whose fp32 partial sums are
+ * written to the caller's workspace and then added in chunk order, before
+ * the ReLU, by a second kernel (deterministic).  The same ReLU-after-the-
+ * full-sum rule as the tile program: K accumulates serially.
+ *   M <= 64; A, B, C, workspace DEVICE pointers, 16-byte aligned; N, K,
+ *   lda, ldb, ldc multiples of 8; 1 <= splits <= 65535 and, for K > 0,
+ *   splits <= ceil(K / 32); workspace_bytes >= splits * M * N * 4
+ *   (tg_gemm_splitk_workspace_bytes).  The workspace is scratch for this
+ *   call only (calls that may overlap need their own).  M = 0 or N = 0 is a
+ *   no-op; K = 0 writes zeros.  Errors and asynchrony as tg_gemm_relu_f16.
+ */
+int tg_gemm_relu_f16_splitk(const void *A, const void *B, void *C, int64_t M, int64_t N,
+                            int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int64_t splits,
+                            void *workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes tg_gemm_relu_f16_splitk needs, or -1 for sizes it rejects. */
+int64_t tg_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits);
+
+/*
  * Latent-attention decode (MLA), fp16: one query per sequence, every query
  * head reading one shared cached row per token of 512 + 64 values (the head
  * size the pages give for the MLA decode they measure: "TileLang paper

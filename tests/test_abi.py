@@ -234,6 +234,29 @@ def test_mla_workspace_sizes(tg):
     assert tg.tg_set_mla_splits(-2) == -2
 
 
+def test_splitk_validation(tg):
+    f = tg.tg_gemm_relu_f16_splitk
+
+    def call(A=P, B=P, C=P, M=16, N=64, K=256, lda=256, ldb=64, ldc=64, S=2, ws=P, wsb=1 << 20):
+        return f(A, B, C, M, N, K, lda, ldb, ldc, S, ws, wsb, 0)
+
+    bad = tg.TG_ERR_INVALID_ARG
+    assert call(M=65) == bad                       # skinny shapes only
+    assert call(N=60, ldb=64, ldc=64) == bad       # N multiple of 8
+    assert call(K=250, lda=256) == bad             # K multiple of 8
+    assert call(lda=260) == bad and call(ldb=68) == bad and call(ldc=66) == bad
+    assert call(lda=128) == bad                    # lda < K
+    assert call(S=0) == bad and call(S=65536) == bad
+    assert call(S=9) == bad                        # more chunks than 32-k steps (256 / 32 = 8)
+    assert call(wsb=16 * 64 * 4 * 2 - 1) == bad    # workspace too small
+    assert call(ws=0) == bad and call(ws=P + 8) == bad
+    assert call(A=P + 2) == bad and call(C=0) == bad
+    assert call(M=0) == tg.TG_OK and call(N=0, ldb=8, ldc=8) == tg.TG_OK
+    assert tg.tg_gemm_splitk_workspace_bytes(16, 16384, 4) == 4 * 16 * 16384 * 4
+    assert tg.tg_gemm_splitk_workspace_bytes(65, 16, 1) == -1
+    assert tg.tg_gemm_splitk_workspace_bytes(16, 16, 0) == -1
+
+
 def _gpu_visible():
     try:
         import torch

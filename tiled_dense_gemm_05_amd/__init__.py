@@ -51,6 +51,8 @@ EXPORTED_SYMBOLS = (
     "tg_mla_decode_f16",
     "tg_mla_decode_workspace_bytes",
     "tg_set_mla_splits",
+    "tg_gemm_relu_f16_splitk",
+    "tg_gemm_splitk_workspace_bytes",
 )
 
 TG_DTYPE_F16 = 0
@@ -96,6 +98,10 @@ _lib.tg_mla_decode_workspace_bytes.argtypes = [_i64] * 3
 _lib.tg_mla_decode_workspace_bytes.restype = ctypes.c_int64
 _lib.tg_set_mla_splits.argtypes = [ctypes.c_int]
 _lib.tg_set_mla_splits.restype = ctypes.c_int
+_lib.tg_gemm_relu_f16_splitk.argtypes = [_vp] * 3 + [_i64] * 7 + [_vp, _i64, _vp]
+_lib.tg_gemm_relu_f16_splitk.restype = ctypes.c_int
+_lib.tg_gemm_splitk_workspace_bytes.argtypes = [_i64] * 3
+_lib.tg_gemm_splitk_workspace_bytes.restype = ctypes.c_int64
 _lib.tg_status_string.argtypes = [ctypes.c_int]
 _lib.tg_status_string.restype = ctypes.c_char_p
 _lib.tg_set_path.argtypes = [ctypes.c_int]
@@ -177,6 +183,18 @@ def tg_mla_decode_workspace_bytes(batch: int, heads: int, seq_k: int) -> int:
 
 def tg_set_mla_splits(splits: int) -> int:
     return _lib.tg_set_mla_splits(splits)
+
+
+def tg_gemm_relu_f16_splitk(A: int, B: int, C: int, M: int, N: int, K: int, lda: int, ldb: int,
+                            ldc: int, splits: int, workspace: int, workspace_bytes: int,
+                            stream: int = 0) -> int:
+    """Raw split-K skinny call, returns the tg_status code."""
+    return _lib.tg_gemm_relu_f16_splitk(A, B, C, M, N, K, lda, ldb, ldc, splits,
+                                        workspace or None, workspace_bytes, stream)
+
+
+def tg_gemm_splitk_workspace_bytes(M: int, N: int, splits: int) -> int:
+    return _lib.tg_gemm_splitk_workspace_bytes(M, N, splits)
 
 
 def tg_status_string(status: int) -> str:

@@ -36,7 +36,7 @@
 //    (64-byte rows of 32 k) and read with one 16-byte read per fragment.
 // Requirements (checked by the dispatcher): 16-byte aligned A, B, C; lda,
 // ldb, ldc, N, K multiples of 8; M <= 16 * MB.
-#include "tg_internal.h"
+#include "tg_splitk.h"
 
 namespace tg {
 namespace {
@@ -59,6 +59,9 @@ struct Skinny {
     static constexpr bool NTB = NTB_;            // stream B with non-temporal loads
     static constexpr bool BF16 = (MODE_ & 1) != 0;
     static constexpr bool BT = (MODE_ & 2) != 0;  // B stored (N,K)
+    // fp32 partial sums of one K chunk per grid.y entry (split-K): see
+    // launch_skinny_partial
+    static constexpr bool PARTIAL = (MODE_ & 4) != 0;
     static constexpr int MB = MB_;               // 16-row blocks of A / C
     static constexpr int NB = NB_;               // columns of C per workgroup
     static constexpr int NW = NW_;               // waves (K split)
@@ -175,7 +178,13 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_skinny_kernel(GemmArgs p, int
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t bidx = blockIdx.y;
-    const int64_t M = p.M, N = p.N, K = p.K;
+    // split-K: grid.y entry bidx covers k in [bidx * sA, bidx * sA + sA) of K
+    int64_t K = p.K;
+    if constexpr (T::PARTIAL) {
+        const int64_t left = p.K - bidx * p.sA;
+        K = left < 0 ? 0 : (left < p.sA ? left : p.sA);
+    }
+    const int64_t M = p.M, N = p.N;
     const int64_t n0 = (int64_t)blockIdx.x * T::NB;
     const uint16_t *Ab = p.A + bidx * p.sA;
     const uint16_t *Bb = p.B + bidx * p.sB + (T::BT ? n0 * p.ldb : n0);
@@ -318,6 +327,13 @@ __global__ void __launch_bounds__(T::NT) gemm_relu_skinny_kernel(GemmArgs p, int
         const int mb = q / T::NF, f = q % T::NF;
         const int64_t m = mb * 16 + (lane & 15);
         const int64_t n = n0 + f * 16 + 4 * (lane >> 4);
+        if constexpr (T::PARTIAL) {
+            // the chunk's fp32 sums, (M, N) row-major at C + bidx * sC floats
+            if (m < M && n < N)
+                *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.C) + bidx * p.sC +
+                                           m * N + n) = s;
+            continue;
+        }
         if (m < M && n < N) {
             float bv[4];
             load_bias4<T::BF16>(p.bias, n, N, bv);
@@ -353,7 +369,63 @@ hipError_t launch(const GemmArgs &p, hipStream_t stream)
     return hipSuccess;
 }
 
+// Split-K reduction: C[m][n] = fp16_rne(ReLU(sum_s part[s][m][n])), the
+// chunks added in order; thread owns 4 consecutive columns of one row.
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *part, uint16_t *C,
+                                                             int64_t M, int64_t N, int64_t ldc,
+                                                             int64_t splits)
+{
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t per_row = N / 4;
+    if (q >= M * per_row)
+        return;
+    const int64_t m = q / per_row, n = (q % per_row) * 4;
+    f32x4 s = *reinterpret_cast<const f32x4 *>(part + m * N + n);
+    for (int64_t c = 1; c < splits; ++c)
+        s += *reinterpret_cast<const f32x4 *>(part + c * M * N + m * N + n);
+    u32x2 w;
+    w.x = epi_pack2<false>(s[0], s[1], true);
+    w.y = epi_pack2<false>(s[2], s[3], true);
+    *reinterpret_cast<u32x2 *>(C + m * ldc + n) = w;
+}
+
 }  // namespace
+
+hipError_t launch_skinny_splitk(const GemmArgs &p, int64_t splits, float *part,
+                                hipStream_t stream)
+{
+    // chunks of whole 32-k steps; each grid.y entry writes its (M, N) fp32 sums
+    const int64_t steps = (p.K + 31) / 32;
+    const int64_t kc = (steps + splits - 1) / splits * 32;
+    GemmArgs q = p;
+    q.C = reinterpret_cast<uint16_t *>(part);
+    q.sA = kc;
+    q.sB = kc * p.ldb;
+    q.sC = p.M * p.N;
+    q.batch = splits;
+    q.bias = nullptr;
+    q.relu = 0;
+    q.bf16 = 0;
+    q.b_nk = 0;
+    q.K = p.K;
+    using T = Skinny<1, 64, 8, 3, true, 4>;
+    using T4 = Skinny<4, 64, 8, 2, true, 4>;
+    const int64_t slices = (p.N + 63) / 64;
+    const int64_t per_wave = (kc / 32 + 7) / 8;
+    if (p.M <= 16)
+        hipLaunchKernelGGL((gemm_relu_skinny_kernel<T>), dim3((unsigned)slices, (unsigned)splits),
+                           dim3(T::NT), 0, stream, q, (int)per_wave);
+    else
+        hipLaunchKernelGGL((gemm_relu_skinny_kernel<T4>), dim3((unsigned)slices, (unsigned)splits),
+                           dim3(T4::NT), 0, stream, q, (int)per_wave);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int64_t threads = p.M * (p.N / 4);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       stream, part, p.C, p.M, p.N, p.ldc, splits);
+    return hipGetLastError();
+}
 
 bool skinny_layout_ok(const GemmArgs &p)
 {
