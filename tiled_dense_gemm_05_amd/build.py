@@ -2,7 +2,7 @@
 
 Every source under ``csrc/`` is compiled with hipcc into ``_build/`` and
 linked into ``tiled_dense_gemm_05_amd/libtg.so`` next to this file.  Run
-``python tiled_dense_gemm_05_amd/build.py`` (or ``__graft_entry__.build()``);
+``python tiled_dense_gemm_05_amd/build.py`` (the repository root's entry module calls it too);
 it is a plain script so that it never imports the package it builds.
 """
 
