@@ -67,3 +67,21 @@ def test_json_line_contract():
     assert rf["traffic"] is None or rf["traffic"] > 0
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0 and cb["sample"]
+
+
+@pytest.mark.gpu
+def test_capi_bench_runs_through_the_c_abi():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    exe = os.path.join(ROOT, "tiled_dense_gemm_05_amd", "tg_capi_bench")
+    if not os.path.exists(exe):
+        pytest.fail("tg_capi_bench is not built")
+    print("[case] tg_capi_bench 512 512 512 5 2", flush=True)
+    r = subprocess.run([exe, "512", "512", "512", "5", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    assert d["M"] == 512 and d["iters"] == 5 and d["copies"] == 2
+    assert d["us_per_call"] > 0 and d["path"] == "tile128"
+    assert d["tflops"] == pytest.approx(2 * 512 ** 3 / (d["us_per_call"] * 1e-6) / 1e12, rel=1e-2)

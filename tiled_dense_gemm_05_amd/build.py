@@ -64,7 +64,24 @@ def build_library(extra: list[str] | None = None) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_capi_bench()
     return LIB
+
+
+BENCH_SRC = os.path.join(HERE, "capi_bench.cpp")
+BENCH_BIN = os.path.join(HERE, "tg_capi_bench")
+
+
+def build_capi_bench() -> str:
+    """The C++ timing program that calls the library through its C ABI only."""
+    tmp = BENCH_BIN + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "-O2", "-std=c++17", "-I", os.path.join(ROOT, "include"), BENCH_SRC,
+           "-o", tmp, "-L", HERE, "-ltg", "-Wl,-rpath,$ORIGIN"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"building the C ABI benchmark failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, BENCH_BIN)
+    return BENCH_BIN
 
 
 if __name__ == "__main__":
