@@ -34,6 +34,10 @@
  *    multiples of 8 take the fastest kernels.
  *  - Results are deterministic: the same inputs, shape and device give the
  *    same bits on every call (no floating-point atomics).
+ *  - Calls only enqueue kernels on `stream` (no allocation, copy, memset or
+ *    synchronisation; besides the launches they read the current device, its
+ *    architecture once per device, and the launch status), so they can be
+ *    captured into a HIP graph and replayed.
  */
 #ifndef TG_H
 #define TG_H
