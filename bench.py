@@ -98,10 +98,12 @@ def calibration_copy(torch):
 
 
 def run_workload(tg, torch, w: wl.Workload, steps: int, warmup: int, epilogue=None,
-                 dtype: str = "f16", layout: str = "kn"):
+                 dtype: str = "f16", layout: str = "kn", graph: bool = False):
     """Times `steps` calls after `warmup`.  epilogue = (activation, with_bias)
     routes the calls through tg_gemm_ex, as do a bf16 element type and an
-    (N,K) B; otherwise the GEMM+ReLU entry points are timed."""
+    (N,K) B; otherwise the GEMM+ReLU entry points are timed.  With `graph`
+    the `steps` calls are captured into one HIP graph and one replay is timed
+    (no host launch cost between the kernels)."""
     a, b = wl.generate_dense(w.M, w.N, w.K, w.dist, w.seed, batch=w.batch, dtype=dtype)
     ex = epilogue is not None or dtype != "f16" or layout != "kn"
     if epilogue is None:
@@ -131,7 +133,7 @@ def run_workload(tg, torch, w: wl.Workload, steps: int, warmup: int, epilogue=No
     dt = tg.TG_DTYPE_BF16 if dtype == "bf16" else tg.TG_DTYPE_F16
     lay = tg.TG_B_NK if layout == "nk" else tg.TG_B_KN
 
-    def call(i):
+    def call(i, sh=sh):
         j = i % nbuf
         if ex:
             st = tg.tg_gemm_ex(dt, lay, epilogue[0], A[j].data_ptr(), B[j].data_ptr(),
@@ -153,10 +155,22 @@ def run_workload(tg, torch, w: wl.Workload, steps: int, warmup: int, epilogue=No
     # events recorded on the stream the kernels are launched on
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(steps):
-        call(i)
-    t1.record(stream)
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream().cuda_stream
+            for i in range(steps):
+                call(i, cs)
+        g.replay()
+        torch.cuda.synchronize()
+        t0.record(stream)
+        g.replay()
+        t1.record(stream)
+    else:
+        t0.record(stream)
+        for i in range(steps):
+            call(i)
+        t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
     path = tg.tg_path_name(tg.tg_last_path())
@@ -594,6 +608,8 @@ def main():
     ap.add_argument("--skinny-splitk", type=int, default=0, metavar="S",
                     help="ablation: time the split-K form (S chunks of K, fp32 partials in a "
                          "workspace, tg_gemm_relu_f16_splitk) on the skinny workload and exit")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the timed calls into one HIP graph and time its replay")
     ap.add_argument("--w4", action="store_true",
                     help="time the weight-only int4 GEMM on the decode shape "
                          "16 x 16384 x 8192, groups of 128 (tg_gemm_w4) and exit")
@@ -629,6 +645,8 @@ def main():
         knobs["epilogue"] = ("bias+" if args.bias else "") + args.act
     if args.layout != "kn":
         knobs["b_layout"] = args.layout
+    if args.graph:
+        knobs["graph"] = True
     if args.calibrate_copy:
         calibration_copy(torch)
     if args.vendor:
@@ -731,7 +749,7 @@ def main():
     w = wl.WORKLOADS[args.workload]
     log(f"workload {w.name}: M={w.M} N={w.N} K={w.K} batch={w.batch}")
     ms, path, nbuf = run_workload(tg, torch, w, args.steps, args.warmup, epilogue, args.dtype,
-                                  args.layout)
+                                  args.layout, graph=args.graph)
     tflops = w.flops / (ms * 1e-3) / 1e12
     gbs = w.compulsory_bytes / (ms * 1e-3) / 1e9
     compute_bound = w.flops / w.compulsory_bytes > PEAK_F16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
@@ -771,7 +789,7 @@ def main():
     if not args.no_secondary and w.name != "skinny_16x16384x8192":
         s = wl.WORKLOADS["skinny_16x16384x8192"]
         sms, spath, snbuf = run_workload(tg, torch, s, max(args.steps, 20), args.warmup,
-                                         epilogue, args.dtype, args.layout)
+                                         epilogue, args.dtype, args.layout, graph=args.graph)
         sgbs = s.compulsory_bytes / (sms * 1e-3) / 1e9
         log(f"{s.name}: {sms * 1e3:.1f} us/call, {sgbs:.0f} GB/s, path={spath}")
         out["secondary"] = {
