@@ -87,6 +87,180 @@ def measured_traffic(workload: str):
     return e[1] + e[2]
 
 
+TRIALS = 10            # timed trials per workload (median and min reported)
+TRIAL_MS = 20.0        # each trial at least this long
+
+
+class ClockSampler:
+    """Samples the GPU's shader (gfx) clock in a background thread while a
+    timed region runs, through the ROCm SMI library (amdsmi), on the device
+    whose PCI bus id matches cuda:0.  Any failure leaves `samples` empty
+    (the line then carries null)."""
+
+    def __init__(self, torch):
+        self.samples = []
+        self.source = None
+        self._h = None
+        self._stop = None
+        self._thread = None
+        try:
+            import amdsmi
+            self._amdsmi = amdsmi
+            amdsmi.amdsmi_init()
+            props = torch.cuda.get_device_properties(0)
+            want = (int(props.pci_domain_id), int(props.pci_bus_id), int(props.pci_device_id))
+            for h in amdsmi.amdsmi_get_processor_handles():
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)          # "dddd:bb:dd.f"
+                dom, bus, rest = bdf.split(":")
+                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                    self._h = h
+                    break
+            if self._h is not None and self._read() is None:
+                self._h = None
+        except Exception as e:   # no SMI access on this machine: report no clock
+            log(f"clock sampling unavailable: {type(e).__name__}: {e}")
+            self._h = None
+
+    def _read(self):
+        a = self._amdsmi
+        try:
+            m = a.amdsmi_get_gpu_metrics_info(self._h)
+            xs = m.get("current_gfxclks")
+            if isinstance(xs, (list, tuple)):
+                xs = [x for x in xs if isinstance(x, (int, float)) and 0 < x < 10000]
+                if xs:
+                    self.source = "gpu_metrics current_gfxclks (mean over XCDs)"
+                    return float(sum(xs)) / len(xs)
+            for key in ("current_gfxclk", "average_gfxclk_frequency"):
+                x = m.get(key)
+                if isinstance(x, (int, float)) and 0 < x < 10000:
+                    self.source = f"gpu_metrics {key}"
+                    return float(x)
+        except Exception:
+            pass
+        try:
+            c = a.amdsmi_get_clock_info(self._h, a.AmdSmiClkType.GFX)
+            self.source = "clock_info GFX"
+            return float(c["clk"])
+        except Exception:
+            return None
+
+    def __enter__(self):
+        import threading
+        if self._h is None:
+            return self
+        self._stop = threading.Event()
+
+        def loop():
+            while not self._stop.is_set():
+                v = self._read()
+                if v is not None:
+                    self.samples.append(v)
+                self._stop.wait(0.002)
+
+        self._thread = threading.Thread(target=loop, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def reset(self):
+        self.samples = []
+
+    def summary(self):
+        if not self.samples:
+            return None
+        x = sorted(self.samples)
+        return {"median": x[len(x) // 2], "min": x[0], "max": x[-1], "samples": len(x),
+                "source": self.source}
+
+
+def time_calls(torch, call, steps: int, warmup: int, clock: ClockSampler | None = None,
+               trials: int = TRIALS, graph_call=None):
+    """The timing protocol of every workload line.
+
+    1. `warmup` untimed calls.
+    2. `trials` trials of n back-to-back calls each, n chosen so a trial lasts
+       at least TRIAL_MS; one pair of HIP events per trial on the launch
+       stream; the shader clock is sampled meanwhile.  Median and min of the
+       per-call time over the trials are reported.
+    3. The contract window: exactly `steps` calls (or one replay of
+       `graph_call`, a graph of `steps` calls), synchronized on both sides
+       and bracketed by events on the launch stream; ms_per_step comes from
+       it.  It runs last, when the card has been busy for the trials, so it
+       measures the sustained (power-limited) rate.
+    call(i) enqueues call i on torch's current stream."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    out = {"trials": trials}
+    if trials > 0:
+        # a short probe sizes the trials
+        t0, t1 = ev(), ev()
+        t0.record(stream)
+        for i in range(3):
+            call(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        per = max(t0.elapsed_time(t1) / 3, 1e-4)
+        n = max(1, int(np.ceil(TRIAL_MS / per)))
+        per_call = []
+        with (clock if clock is not None else _Null()):
+            for t in range(trials):
+                a, b = ev(), ev()
+                a.record(stream)
+                for i in range(n):
+                    call(i)
+                b.record(stream)
+                b.synchronize()
+                per_call.append(a.elapsed_time(b) / n)
+        x = sorted(per_call)
+        out.update({"calls_per_trial": n, "trial_ms_min": x[0] * n,
+                    "median_ms_per_call": x[len(x) // 2], "min_ms_per_call": x[0],
+                    "max_ms_per_call": x[-1]})
+    torch.cuda.synchronize()
+    t0, t1 = ev(), ev()
+    t0.record(stream)
+    if graph_call is not None:
+        graph_call()
+    else:
+        for i in range(steps):
+            call(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    out["ms_per_step"] = t0.elapsed_time(t1) / steps
+    return out
+
+
+class _Null:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        return False
+
+
+def timing_fields(timing: dict, clock: ClockSampler | None, work: float, scale: float):
+    """The `timing` and `sclk_mhz` objects of a JSON line: work per call
+    (flop or bytes) / per-call time, in the line's unit (work / s / scale)."""
+    t = {"protocol": (f"{timing['trials']} trials of calls_per_trial back-to-back calls "
+                      f"(each trial >= {TRIAL_MS:.0f} ms, one pair of HIP events on the launch "
+                      f"stream), then the contract window of exactly `steps` calls that "
+                      f"ms_per_step comes from")}
+    t.update({k: v for k, v in timing.items() if k != "ms_per_step"})
+    if "median_ms_per_call" in timing:
+        t["rate_at_median"] = work / (timing["median_ms_per_call"] * 1e-3) / scale
+        t["rate_at_min"] = work / (timing["min_ms_per_call"] * 1e-3) / scale
+    sclk = clock.summary() if clock is not None else None
+    return t, sclk
+
+
 def calibration_copy(torch):
     """A plain 1 GiB device-to-device copy, twice, for counter calibration."""
     src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device="cuda")
@@ -98,12 +272,15 @@ def calibration_copy(torch):
 
 
 def run_workload(tg, torch, w: wl.Workload, steps: int, warmup: int, epilogue=None,
-                 dtype: str = "f16", layout: str = "kn", graph: bool = False):
+                 dtype: str = "f16", layout: str = "kn", graph: bool = False,
+                 clock: ClockSampler | None = None, trials: int = TRIALS):
     """Times `steps` calls after `warmup`.  epilogue = (activation, with_bias)
     routes the calls through tg_gemm_ex, as do a bf16 element type and an
     (N,K) B; otherwise the GEMM+ReLU entry points are timed.  With `graph`
-    the `steps` calls are captured into one HIP graph and one replay is timed
-    (no host launch cost between the kernels)."""
+    the `steps` calls of the contract window are captured into one HIP graph
+    and one replay is timed (no host launch cost between the kernels); the
+    trials always launch directly.  Returns (timing dict of time_calls, path,
+    input copies)."""
     a, b = wl.generate_dense(w.M, w.N, w.K, w.dist, w.seed, batch=w.batch, dtype=dtype)
     ex = epilogue is not None or dtype != "f16" or layout != "kn"
     if epilogue is None:
@@ -149,13 +326,11 @@ def run_workload(tg, torch, w: wl.Workload, steps: int, warmup: int, epilogue=No
         if st != tg.TG_OK:
             raise RuntimeError(tg.tg_status_string(st))
 
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
-    # events recorded on the stream the kernels are launched on
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    graph_call = None
     if graph:
+        for i in range(warmup):
+            call(i)
+        torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             cs = torch.cuda.current_stream().cuda_stream
@@ -163,21 +338,14 @@ def run_workload(tg, torch, w: wl.Workload, steps: int, warmup: int, epilogue=No
                 call(i, cs)
         g.replay()
         torch.cuda.synchronize()
-        t0.record(stream)
-        g.replay()
-        t1.record(stream)
-    else:
-        t0.record(stream)
-        for i in range(steps):
-            call(i)
-        t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+        graph_call = g.replay
+    timing = time_calls(torch, call, steps, warmup, clock, trials, graph_call)
     path = tg.tg_path_name(tg.tg_last_path())
-    return ms, path, nbuf
+    return timing, path, nbuf
 
 
-def run_vendor(torch, w: wl.Workload, steps: int, warmup: int, dtype: str, layout: str):
+def run_vendor(torch, w: wl.Workload, steps: int, warmup: int, dtype: str, layout: str,
+               trials: int = TRIALS):
     """Times torch.matmul (hipBLASLt on ROCm) on the workload's operands, as
     context for the library's own rate: the same product without the ReLU,
     into a preallocated output.  Dense layouts only (the named workloads with
@@ -199,21 +367,11 @@ def run_vendor(torch, w: wl.Workload, steps: int, warmup: int, dtype: str, layou
     else:
         B = B.contiguous()
         call = lambda: torch.bmm(A, B, out=C)
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(steps):
-        call()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps
+    return time_calls(torch, lambda i: call(), steps, warmup, trials=trials)
 
 
-def run_w4(tg, torch, M: int, N: int, K: int, G: int, steps: int, warmup: int, dtype: str):
+def run_w4(tg, torch, M: int, N: int, K: int, G: int, steps: int, warmup: int, dtype: str,
+           trials: int = TRIALS):
     """Times the weight-only int4 GEMM (tg_gemm_w4) on an (N,K) int4 weight with
     group scales; several weight copies rotate so reruns come from HBM."""
     a, _ = wl.generate_dense(M, 8, K, "uniform_invsqrtk", 3, dtype=dtype)
@@ -235,22 +393,12 @@ def run_w4(tg, torch, M: int, N: int, K: int, G: int, steps: int, warmup: int, d
         if st != tg.TG_OK:
             raise RuntimeError(tg.tg_status_string(st))
 
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(steps):
-        call(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
-    return ms, tg.tg_path_name(tg.tg_last_path()), nbuf, wbytes + 2 * (M * K + M * N)
+    timing = time_calls(torch, call, steps, warmup, trials=trials)
+    return timing, tg.tg_path_name(tg.tg_last_path()), nbuf, wbytes + 2 * (M * K + M * N)
 
 
 def run_attention(tg, torch, B: int, S: int, H: int, Hkv: int, D: int, causal: bool,
-                  steps: int, warmup: int):
+                  steps: int, warmup: int, trials: int = TRIALS):
     """Times the fused attention forward on (B, S, H, D) queries and (B, S, Hkv, D)
     keys and values (tg_attention_fwd_f16 when Hkv = H, else
     tg_attention_fwd_f16_gqa), normal(0,1) Q and K, uniform(-1,1) V."""
@@ -276,20 +424,10 @@ def run_attention(tg, torch, B: int, S: int, H: int, Hkv: int, D: int, causal: b
         if st != tg.TG_OK:
             raise RuntimeError(tg.tg_status_string(st))
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(steps):
-        call()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps
+    return time_calls(torch, lambda i: call(), steps, warmup, trials=trials)
 
 
-def run_mla(tg, torch, steps: int, warmup: int):
+def run_mla(tg, torch, steps: int, warmup: int, trials: int = TRIALS):
     """Times the latent-attention decode (tg_mla_decode_f16) on the 64 x 8192-token,
     128-head workload; returns (ms per call, path, workspace bytes)."""
     w = wl.MLA_WORKLOAD
@@ -311,20 +449,11 @@ def run_mla(tg, torch, steps: int, warmup: int):
         if st != tg.TG_OK:
             raise RuntimeError(tg.tg_status_string(st))
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(steps):
-        call()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps, tg.tg_path_name(tg.tg_last_path()), need
+    timing = time_calls(torch, lambda i: call(), steps, warmup, trials=trials)
+    return timing, tg.tg_path_name(tg.tg_last_path()), need
 
 
-def run_splitk(tg, torch, splits: int, steps: int, warmup: int):
+def run_splitk(tg, torch, splits: int, steps: int, warmup: int, trials: int = TRIALS):
     """Times the split-K form of the skinny GEMM+ReLU (tg_gemm_relu_f16_splitk) on the
     16 x 16384 x 8192 workload, input copies rotated as for the single-pass path;
     returns (ms per call, copies, workspace bytes)."""
@@ -346,17 +475,8 @@ def run_splitk(tg, torch, splits: int, steps: int, warmup: int):
         if st != tg.TG_OK:
             raise RuntimeError(tg.tg_status_string(st))
 
-    for i in range(warmup):
-        call(i % nbuf)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(steps):
-        call(i % nbuf)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps, nbuf, need
+    timing = time_calls(torch, lambda i: call(i % nbuf), steps, warmup, trials=trials)
+    return timing, nbuf, need
 
 
 def cpu_baseline(w: wl.Workload, target_s: float = 16.0):
@@ -538,6 +658,125 @@ def summarize_ablation(out_md: str, root: str, title: str):
     print(f"wrote {out_md}")
 
 
+PMC_SET = ("SQ_CYCLES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT "
+           "SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE TCC_HIT_sum TCC_MISS_sum")
+
+
+def summarize_run(workload: str, root: str, commands: list[str]):
+    """Writes profiles/<kernel family>-<workload>.md for the default kernel of a
+    dense workload from one directory of runs:
+      root/bench.json  the JSON line of a bench run made under
+                       `rocprofv3 --kernel-trace --stats -d root/trace`
+                       (the trace and the line come from the same invocation),
+      root/pmc         one --pmc run of PMC_SET,
+      root/fetch       one --pmc FETCH_SIZE run with --calibrate-copy,
+      root/write       one --pmc WRITE_SIZE run with --calibrate-copy,
+    and records the calibrated HBM bytes per launch in profiles/traffic.txt.
+    The summary recomputes the roofline fraction from the trace's average
+    kernel duration next to the bench line's own."""
+    import collections
+    with open(os.path.join(root, "bench.json")) as f:
+        b = json.loads([ln for ln in f.read().splitlines() if ln.startswith("{")][-1])
+    w = wl.WORKLOADS[workload]
+    stats = _csv_rows(_find(os.path.join(root, "trace"), "kernel_stats.csv"))
+    stats.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    top = stats[0]
+    name = top["Name"]
+    short = name.replace("tg::(anonymous namespace)::", "")
+    pmc = [v for v in _dispatch_counters(os.path.join(root, "pmc")).values()
+           if v["name"] == name]
+    n = len(pmc)
+    avg = lambda key: sum(v[key] for v in pmc) / n
+    # SQ_CYCLES and GRBM_GUI_ACTIVE are summed over the 32 shader engines
+    clock = sum(v["SQ_CYCLES"] / 32 / v["us"] / 1e3 for v in pmc) / n
+    gui = sum(v["GRBM_GUI_ACTIVE"] / 32 / v["us"] / 1e3 for v in pmc) / n
+    mfma = sum(v["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * v["SQ_CYCLES"] / 32) for v in pmc) / n
+    lds_conf = avg("SQ_LDS_BANK_CONFLICT") / max(avg("SQ_LDS_IDX_ACTIVE"), 1.0)
+    l2_hit = avg("TCC_HIT_sum") / max(avg("TCC_HIT_sum") + avg("TCC_MISS_sum"), 1.0)
+    pmc_us = avg("us")
+
+    def per_launch(sub, counter):
+        d = _dispatch_counters(os.path.join(root, sub))
+        copy = [v[counter] for v in d.values() if "copy" in v["name"].lower()]
+        gem = [v[counter] for v in d.values() if v["name"] == name]
+        factor = COPY_BYTES / (sum(copy) / len(copy) * 1024.0)
+        return sum(gem) / len(gem) * 1024.0 * factor, factor, sum(copy) / len(copy) * 1024.0
+
+    g_fetch, f_fetch, c_fetch = per_launch("fetch", "FETCH_SIZE")
+    g_write, f_write, c_write = per_launch("write", "WRITE_SIZE")
+    reads = 2 * (w.M * w.K + w.K * w.N) * w.batch
+    writes = 2 * w.M * w.N * w.batch
+    trace_ns = float(top["AverageNs"])
+    compute = b["roofline"]["bound"] == "mfma"
+    work = w.flops if compute else w.compulsory_bytes
+    scale = 1e12 if compute else 1e9
+    peak = PEAK_F16_TFLOPS if compute else PEAK_HBM_GBS
+    unit = "TFLOP/s" if compute else "GB/s"
+    rate_trace = work / (trace_ns * 1e-9) / scale
+    family = ("gemm_relu_dma_kernel" if "dma_kernel" in name else
+              "gemm_relu_skinny_kernel" if "skinny_kernel" in name else
+              "gemm_relu_tile_kernel" if "tile_kernel" in name else "kernel")
+    md = os.path.join(PROFILES, f"{family}-{workload}.md")
+    t = b.get("timing", {})
+    with open(md, "w") as f:
+        f.write(f"# {short} on {workload}\n\n")
+        f.write("Commands (from the repository root on the GPU box, R = that root):\n\n")
+        for c in commands:
+            f.write(f"    {c}\n")
+        f.write(f"\n## Bench line of the traced run\n\n")
+        f.write(f"* contract window: {b['steps']} calls after {b['warmup']} warm-ups, "
+                f"{b['ms_per_step'] * 1e3:.1f} us per call, {b['value']:.1f} {b['unit']}, "
+                f"frac {b['roofline']['frac']:.3f} of {b['roofline']['peak']} {unit}\n")
+        if "median_ms_per_call" in t:
+            f.write(f"* trials before it: {t['trials']} x {t['calls_per_trial']} calls, per call "
+                    f"median {t['median_ms_per_call'] * 1e3:.1f} us, min "
+                    f"{t['min_ms_per_call'] * 1e3:.1f} us, max {t['max_ms_per_call'] * 1e3:.1f} us "
+                    f"({t['rate_at_median']:.1f} / {t['rate_at_min']:.1f} {unit} at median / min)\n")
+        sc = b.get("sclk_mhz")
+        if sc:
+            f.write(f"* shader clock sampled during the trials ({sc['source']}): median "
+                    f"{sc['median']:.0f} MHz, range {sc['min']:.0f}-{sc['max']:.0f} MHz, "
+                    f"{sc['samples']} samples\n")
+        f.write("\n## Kernel trace of the same invocation (rocprofv3 --kernel-trace --stats)\n\n")
+        f.write("| kernel | calls | average ns | min ns | max ns |\n|---|---|---|---|---|\n")
+        for r in stats[:4]:
+            nm = r["Name"].replace("tg::(anonymous namespace)::", "")
+            f.write(f"| {nm[:140]} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                    f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} |\n")
+        f.write(f"\nAlgorithmic work per launch: {w.flops:.4e} flop, "
+                f"{w.compulsory_bytes:.4e} compulsory HBM bytes.  From the trace's average "
+                f"({trace_ns / 1e3:.1f} us over every call of the run: warm-ups, trials and the "
+                f"window): {rate_trace:.1f} {unit} = {rate_trace / peak:.3f} of {peak} {unit}; "
+                f"trace average / ms_per_step = {trace_ns / 1e6 / b['ms_per_step']:.3f}.\n")
+        f.write(f"\n## Counters (rocprofv3 --pmc, one set per run), {n} dispatches\n\n")
+        f.write(f"* shader clock {clock:.2f} GHz (SQ_CYCLES per shader engine / kernel time; "
+                f"GRBM_GUI_ACTIVE gives {gui:.2f} GHz), kernel time under the counters "
+                f"{pmc_us:.1f} us\n")
+        f.write(f"* matrix cores busy {mfma:.1%} of the SIMD cycles "
+                f"(SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x SQ_CYCLES per engine)); "
+                f"at that clock the busy fraction corresponds to "
+                f"{mfma * clock / 2.4 * PEAK_F16_TFLOPS:.0f} TFLOP/s of issued matrix work\n")
+        f.write(f"* LDS bank-conflict cycles per LDS-active cycle {lds_conf:.4f} "
+                f"(SQ_LDS_BANK_CONFLICT {avg('SQ_LDS_BANK_CONFLICT'):.4e}, "
+                f"SQ_LDS_IDX_ACTIVE {avg('SQ_LDS_IDX_ACTIVE'):.4e})\n")
+        f.write(f"* L2 hit rate {l2_hit:.1%} (TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum))\n")
+        f.write(f"* calibration copy of {COPY_BYTES} bytes: FETCH_SIZE {c_fetch:.4e} B, "
+                f"WRITE_SIZE {c_write:.4e} B -> factors {f_fetch:.3f} (fetch), "
+                f"{f_write:.3f} (write)\n")
+        f.write(f"* HBM read {g_fetch:.4e} B per launch ({g_fetch / reads:.2f} x the "
+                f"{reads:.4e} B of A and B), HBM write {g_write:.4e} B ({g_write / writes:.2f} "
+                f"x the {writes:.4e} B of C)\n")
+        f.write(f"* kernel source hash {kernel_source_hash(workload)} "
+                f"({', '.join(KERNEL_SOURCES.get(workload, DEFAULT_SOURCES))})\n")
+    lines = {k: v for k, v in read_traffic_file().items()}
+    lines[workload] = (kernel_source_hash(workload), g_fetch, g_write)
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("# workload source_hash hbm_read_bytes hbm_write_bytes (per launch, calibrated)\n")
+        for k, (h, r_, w_) in sorted(lines.items()):
+            f.write(f"{k} {h} {r_:.6e} {w_:.6e}\n")
+    print(f"wrote {md} and {TRAFFIC_FILE}")
+
+
 def summarize_stats(out_md: str, title: str, stats_dir: str, commands: list[str]):
     """Writes a kernel-trace summary (top kernels by total time) for runs that
     are not one of the dense workloads (the int4 and attention benches)."""
@@ -557,6 +796,10 @@ def summarize_stats(out_md: str, title: str, stats_dir: str, commands: list[str]
 
 
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-run":
+        # bench.py --summarize-run WORKLOAD ROOT_DIR "cmd1" ...
+        summarize_run(sys.argv[2], sys.argv[3], sys.argv[4:])
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-stats":
         # bench.py --summarize-stats OUT_MD TITLE STATS_DIR "cmd1" ...
         summarize_stats(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5:])
@@ -608,6 +851,9 @@ def main():
     ap.add_argument("--skinny-splitk", type=int, default=0, metavar="S",
                     help="ablation: time the split-K form (S chunks of K, fp32 partials in a "
                          "workspace, tg_gemm_relu_f16_splitk) on the skinny workload and exit")
+    ap.add_argument("--trials", type=int, default=TRIALS,
+                    help=f"timed trials of >= {TRIAL_MS:.0f} ms before the contract window "
+                         "(median and min reported; 0 skips them)")
     ap.add_argument("--graph", action="store_true",
                     help="capture the timed calls into one HIP graph and time its replay")
     ap.add_argument("--w4", action="store_true",
@@ -651,7 +897,9 @@ def main():
         calibration_copy(torch)
     if args.vendor:
         w = wl.WORKLOADS[args.workload]
-        ms = run_vendor(torch, w, args.steps, args.warmup, args.dtype, args.layout)
+        timing = run_vendor(torch, w, args.steps, args.warmup, args.dtype, args.layout,
+                            args.trials)
+        ms = timing["ms_per_step"]
         rate = w.flops / (ms * 1e-3) / 1e12
         log(f"vendor {args.workload} {args.dtype} {args.layout}: {ms * 1e3:.1f} us/call, "
             f"{rate:.1f} TFLOP/s")
@@ -662,7 +910,8 @@ def main():
             "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
             "config": {"workload": args.workload, "M": w.M, "N": w.N, "K": w.K,
                        "batch": w.batch, "b_layout": args.layout,
-                       "library": "torch.matmul (hipBLASLt)"}}), flush=True)
+                       "library": "torch.matmul (hipBLASLt)"},
+            "timing": timing_fields(timing, None, w.flops, 1e12)[0]}), flush=True)
         return
     if args.attention:
         B, S, H, D = 4, 4096, 32, 128
@@ -672,7 +921,9 @@ def main():
         if Hkv <= 0 or H % Hkv:
             sys.exit(f"--kv-heads must divide {H}")
         causal = args.attention == "causal"
-        ms = run_attention(tg, torch, B, S, H, Hkv, D, causal, args.steps, args.warmup)
+        timing = run_attention(tg, torch, B, S, H, Hkv, D, causal, args.steps, args.warmup,
+                               args.trials)
+        ms = timing["ms_per_step"]
         # two products of 2*S*S*D flop per (batch, head); half the pairs when causal
         flops = 4.0 * B * H * S * S * D * (0.5 if causal else 1.0)
         tflops = flops / (ms * 1e-3) / 1e12
@@ -688,12 +939,14 @@ def main():
                        "path": tg.tg_path_name(tg.tg_last_path())},
             "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_F16_TFLOPS,
                          "unit": "TFLOP/s", "frac": tflops / PEAK_F16_TFLOPS,
-                         "traffic": None}}), flush=True)
+                         "traffic": None},
+            "timing": timing_fields(timing, None, flops, 1e12)[0]}), flush=True)
         return
     if args.skinny_splitk:
         w = wl.WORKLOADS["skinny_16x16384x8192"]
         S = args.skinny_splitk
-        ms, nbuf, need = run_splitk(tg, torch, S, args.steps, args.warmup)
+        timing, nbuf, need = run_splitk(tg, torch, S, args.steps, args.warmup, args.trials)
+        ms = timing["ms_per_step"]
         gbs = w.compulsory_bytes / (ms * 1e-3) / 1e9
         log(f"skinny split-K S={S}: {ms * 1e3:.1f} us/call, {gbs:.0f} GB/s, workspace {need} bytes")
         print(json.dumps({
@@ -704,14 +957,16 @@ def main():
             "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "splits": S,
                        "input_copies": nbuf, "workspace_bytes": need},
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": gbs / PEAK_HBM_GBS, "traffic": None}}), flush=True)
+                         "frac": gbs / PEAK_HBM_GBS, "traffic": None},
+            "timing": timing_fields(timing, None, w.compulsory_bytes, 1e9)[0]}), flush=True)
         return
     if args.mla:
         if args.mla_splits != -1:
             tg.tg_set_mla_splits(args.mla_splits)
         w = wl.MLA_WORKLOAD
         B, H, Sk = w["B"], w["H"], w["Sk"]
-        ms, path, need = run_mla(tg, torch, args.steps, args.warmup)
+        timing, path, need = run_mla(tg, torch, args.steps, args.warmup, args.trials)
+        ms = timing["ms_per_step"]
         # score product over 576 values and value product over 512, per (sequence, head, token)
         flops = 2.0 * B * H * Sk * (576 + 512)
         nbytes = 2.0 * (B * Sk * 576 + B * H * 576 + B * H * 512)
@@ -728,12 +983,14 @@ def main():
                        "row": "512+64", "tflops": tflops, "path": path,
                        "splits": args.mla_splits, "workspace_bytes": need},
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": gbs / PEAK_HBM_GBS, "traffic": None}}), flush=True)
+                         "frac": gbs / PEAK_HBM_GBS, "traffic": None},
+            "timing": timing_fields(timing, None, nbytes, 1e9)[0]}), flush=True)
         return
     if args.w4:
         M, N, K, G = 16, 16384, 8192, 128
-        ms, path, nbuf, nbytes = run_w4(tg, torch, M, N, K, G, args.steps, args.warmup,
-                                        args.dtype)
+        timing, path, nbuf, nbytes = run_w4(tg, torch, M, N, K, G, args.steps, args.warmup,
+                                            args.dtype, args.trials)
+        ms = timing["ms_per_step"]
         gbs = nbytes / (ms * 1e-3) / 1e9
         log(f"w4 {M}x{N}x{K} g{G}: {ms * 1e3:.1f} us/call, {gbs:.0f} GB/s, path={path}")
         print(json.dumps({
@@ -744,12 +1001,16 @@ def main():
             "config": {"workload": f"w4_{M}x{N}x{K}_g{G}", "M": M, "N": N, "K": K,
                        "group_size": G, "path": path, "weight_copies": nbuf},
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": gbs / PEAK_HBM_GBS, "traffic": None}}), flush=True)
+                         "frac": gbs / PEAK_HBM_GBS, "traffic": None},
+            "timing": timing_fields(timing, None, nbytes, 1e9)[0]}), flush=True)
         return
     w = wl.WORKLOADS[args.workload]
     log(f"workload {w.name}: M={w.M} N={w.N} K={w.K} batch={w.batch}")
-    ms, path, nbuf = run_workload(tg, torch, w, args.steps, args.warmup, epilogue, args.dtype,
-                                  args.layout, graph=args.graph)
+    clock = ClockSampler(torch) if args.trials > 0 else None
+    timing, path, nbuf = run_workload(tg, torch, w, args.steps, args.warmup, epilogue,
+                                      args.dtype, args.layout, graph=args.graph, clock=clock,
+                                      trials=args.trials)
+    ms = timing["ms_per_step"]
     tflops = w.flops / (ms * 1e-3) / 1e12
     gbs = w.compulsory_bytes / (ms * 1e-3) / 1e9
     compute_bound = w.flops / w.compulsory_bytes > PEAK_F16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
@@ -759,10 +1020,16 @@ def main():
         value, unit = tflops, "TFLOP/s"
         roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                 "frac": tflops / PEAK_F16_TFLOPS}
+        tfields, sclk = timing_fields(timing, clock, w.flops, 1e12)
     else:
         value, unit = gbs, "GB/s"
         roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": gbs / PEAK_HBM_GBS}
+        tfields, sclk = timing_fields(timing, clock, w.compulsory_bytes, 1e9)
+    if "median_ms_per_call" in timing:
+        log(f"{w.name}: trials median {timing['median_ms_per_call'] * 1e3:.1f} us, min "
+            f"{timing['min_ms_per_call'] * 1e3:.1f} us ({timing['calls_per_trial']} calls each); "
+            f"sclk {sclk}")
     if args.dtype != "f16":
         knobs["element"] = args.dtype
     roof["traffic"] = None if knobs else measured_traffic(w.name)
@@ -784,20 +1051,29 @@ def main():
                    "inputs": f"{w.dist}, seed {w.seed}", "accumulate": "fp32", "path": path,
                    "input_copies": nbuf, **knobs},
         "roofline": roof,
+        "timing": tfields,
+        "sclk_mhz": sclk,
     }
 
     if not args.no_secondary and w.name != "skinny_16x16384x8192":
         s = wl.WORKLOADS["skinny_16x16384x8192"]
-        sms, spath, snbuf = run_workload(tg, torch, s, max(args.steps, 20), args.warmup,
-                                         epilogue, args.dtype, args.layout, graph=args.graph)
+        if clock is not None:
+            clock.reset()
+        stiming, spath, snbuf = run_workload(tg, torch, s, max(args.steps, 20), args.warmup,
+                                             epilogue, args.dtype, args.layout,
+                                             graph=args.graph, clock=clock, trials=args.trials)
+        sms = stiming["ms_per_step"]
         sgbs = s.compulsory_bytes / (sms * 1e-3) / 1e9
         log(f"{s.name}: {sms * 1e3:.1f} us/call, {sgbs:.0f} GB/s, path={spath}")
+        stf, ssclk = timing_fields(stiming, clock, s.compulsory_bytes, 1e9)
         out["secondary"] = {
             "workload": s.name, "value": sgbs, "unit": "GB/s", "ms_per_step": sms, "path": spath,
-            "input_copies": snbuf,
+            "steps": max(args.steps, 20), "input_copies": snbuf,
             "roofline": {"bound": "hbm", "achieved": sgbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": sgbs / PEAK_HBM_GBS,
                          "traffic": None if knobs else measured_traffic(s.name)},
+            "timing": stf,
+            "sclk_mhz": ssclk,
         }
 
     if not args.no_cpu_baseline:

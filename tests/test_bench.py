@@ -67,6 +67,13 @@ def test_json_line_contract():
     assert rf["traffic"] is None or rf["traffic"] > 0
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0 and cb["sample"]
+    # the trials protocol: >= 10 trials of >= 20 ms, median <= max, min <= median
+    t = d["timing"]
+    assert t["trials"] >= 10 and t["trial_ms_min"] >= 20.0 * 0.9
+    assert t["min_ms_per_call"] <= t["median_ms_per_call"] <= t["max_ms_per_call"]
+    assert t["rate_at_min"] >= t["rate_at_median"] > 0
+    sc = d["sclk_mhz"]
+    assert sc is None or (100 < sc["min"] <= sc["median"] <= sc["max"] < 5000)
 
 
 @pytest.mark.gpu

@@ -295,7 +295,7 @@ def test_strided_batched_broadcast_operand(tg, oracle_lib):
     assert rep.ok, str(rep)
 
 
-# --------------------------------------------------- full-size workloads (sampled)
+# ------------------------------------------- full-size workloads (every output)
 
 
 def _workload_case(tg, oracle_lib, name, n_samples=None):
@@ -332,9 +332,9 @@ def _workload_case(tg, oracle_lib, name, n_samples=None):
 @pytest.mark.parametrize("name,n", [
     ("small_512", None),
     ("mid_2048", None),
-    ("large_8192", 20000),
+    ("large_8192", None),
     ("skinny_16x16384x8192", None),
-    ("ragged_3001x5003x1000", 40000),
+    ("ragged_3001x5003x1000", None),
     ("batched_1024x128x128x64", None),
 ])
 def test_workloads_full_size(tg, oracle_lib, name, n):
