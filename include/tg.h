@@ -229,6 +229,27 @@ int tg_gemm_relu_f16_splitk(const void *A, const void *B, void *C, int64_t M, in
 int64_t tg_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * tg_gemm_relu_f16_splitk with its fp32 partial sums in a scratch array the
+ * library keeps on each device (TG_SPLITK_NOALLOC_SCRATCH_BYTES = 16 MiB,
+ * held from the first call on that device until the process ends) instead
+ * of a caller workspace.  Same arguments, results (bit for bit), errors and
+ * asynchrony as tg_gemm_relu_f16_splitk without the workspace; in addition
+ * splits * M * N * 4 > TG_SPLITK_NOALLOC_SCRATCH_BYTES returns
+ * TG_ERR_INVALID_ARG before any GPU work.  The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine).  Every call on a device
+ * shares that device's array: calls that may overlap on one device (other
+ * streams, other host threads) race on it and must be serialized by the
+ * caller.  Every partial sum is written before it is read, so the previous
+ * call's contents need no clearing.
+ */
+#define TG_SPLITK_NOALLOC_SCRATCH_BYTES (16ll << 20)
+int tg_gemm_relu_f16_splitk_noalloc(const void *A, const void *B, void *C, int64_t M, int64_t N,
+                                    int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                                    int64_t splits, hipStream_t stream);
+
+/*
  * Latent-attention decode (MLA), fp16: one query per sequence, every query
  * head reading one shared cached row per token of 512 + 64 values (the head
  * size the pages give for the MLA decode they measure: "TileLang paper

@@ -53,6 +53,7 @@ EXPORTED_SYMBOLS = (
     "tg_set_mla_splits",
     "tg_gemm_relu_f16_splitk",
     "tg_gemm_splitk_workspace_bytes",
+    "tg_gemm_relu_f16_splitk_noalloc",
 )
 
 TG_DTYPE_F16 = 0
@@ -102,6 +103,10 @@ _lib.tg_gemm_relu_f16_splitk.argtypes = [_vp] * 3 + [_i64] * 7 + [_vp, _i64, _vp
 _lib.tg_gemm_relu_f16_splitk.restype = ctypes.c_int
 _lib.tg_gemm_splitk_workspace_bytes.argtypes = [_i64] * 3
 _lib.tg_gemm_splitk_workspace_bytes.restype = ctypes.c_int64
+_lib.tg_gemm_relu_f16_splitk_noalloc.argtypes = [_vp] * 3 + [_i64] * 7 + [_vp]
+_lib.tg_gemm_relu_f16_splitk_noalloc.restype = ctypes.c_int
+
+TG_SPLITK_NOALLOC_SCRATCH_BYTES = 16 << 20
 _lib.tg_status_string.argtypes = [ctypes.c_int]
 _lib.tg_status_string.restype = ctypes.c_char_p
 _lib.tg_set_path.argtypes = [ctypes.c_int]
@@ -195,6 +200,14 @@ def tg_gemm_relu_f16_splitk(A: int, B: int, C: int, M: int, N: int, K: int, lda:
 
 def tg_gemm_splitk_workspace_bytes(M: int, N: int, splits: int) -> int:
     return _lib.tg_gemm_splitk_workspace_bytes(M, N, splits)
+
+
+def tg_gemm_relu_f16_splitk_noalloc(A: int, B: int, C: int, M: int, N: int, K: int, lda: int,
+                                    ldb: int, ldc: int, splits: int, stream: int = 0) -> int:
+    """Raw allocation-free split-K call (library-owned scratch), returns the
+    tg_status code."""
+    return _lib.tg_gemm_relu_f16_splitk_noalloc(A, B, C, M, N, K, lda, ldb, ldc, splits,
+                                                stream)
 
 
 def tg_status_string(status: int) -> str:

@@ -14,4 +14,10 @@ namespace tg {
 hipError_t launch_skinny_splitk(const GemmArgs &p, int64_t splits, float *part,
                                 hipStream_t stream);
 
+// Argument checks shared by the split-K entry points (everything but the
+// workspace): TG_OK with p filled in for the launch, or an error status.
+// M == 0 or N == 0 returns TG_OK with p untouched (a no-op call).
+int splitk_check(const void *A, const void *B, const void *C, int64_t M, int64_t N, int64_t K,
+                 int64_t lda, int64_t ldb, int64_t ldc, int64_t splits, GemmArgs &p);
+
 }  // namespace tg
