@@ -37,6 +37,7 @@
 //    (ds_read_b64_tr_b16), the swizzles, the XCD-aware tile order and the
 //    epilogue are shared with the register-staged kernel.
 #include "tg_internal.h"
+#include "tg_lds_dma.h"
 
 namespace tg {
 namespace {
@@ -53,7 +54,11 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) f16x8 lds_f16x8;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
-constexpr uint32_t kOutOfRange = 0x80000000u;   // == the descriptors' record count
+using dma::block_barrier;
+using dma::dma16;
+using dma::kOutOfRange;   // == the descriptors' record count
+using dma::make_rsrc;
+using dma::wait_vmcnt;
 
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int OCC_ = 1, int KG_ = 1,
           bool SWZ_ = true>
@@ -135,55 +140,6 @@ __device__ __forceinline__ int swz_b(int k, int c)
     else
         return c;
 }
-
-// s_waitcnt vmcnt(N), other counters untouched, fenced against compiler
-// reordering of memory operations.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N <= 63, "vmcnt");
-    constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(imm);
-    asm volatile("" ::: "memory");
-}
-
-// Workgroup barrier once this wave's LDS reads have completed (the lgkmcnt
-// wait is a builtin so the compiler's own wait tracking sees it).
-__device__ __forceinline__ void block_barrier()
-{
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt((3 << 14) | (0 << 8) | (7 << 4) | 15);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// Raw buffer descriptor over `base`: record count 2^31 (offsets at or past it
-// read as zero), 32-bit data format as the gfx9 family requires.
-__device__ __forceinline__ i32x4 make_rsrc(const void *base)
-{
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    i32x4 r;
-    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
-    r.z = (int)kOutOfRange;
-    r.w = 0x00020000;
-    return r;
-}
-
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-// 16 bytes per lane from rsrc + voff into the 1 KiB LDS block at lds_addr.
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_addr)
-{
-    asm volatile("s_mov_b32 m0, %2\n\t"
-                 "s_nop 0\n\t"
-                 "buffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :
-                 : "v"(voff), "s"(rsrc), "s"(lds_addr)
-                 : "m0");
-}
-#pragma clang diagnostic pop
 
 // Scheduling hint: alternate one MFMA with one LDS read, then the rest.
 template <int MFMAS, int READS>

@@ -36,6 +36,7 @@
 //    (64-byte rows of 32 k) and read with one 16-byte read per fragment.
 // Requirements (checked by the dispatcher): 16-byte aligned A, B, C; lda,
 // ldb, ldc, N, K multiples of 8; M <= 16 * MB.
+#include "tg_lds_dma.h"
 #include "tg_splitk.h"
 
 namespace tg {
@@ -52,7 +53,12 @@ typedef __attribute__((address_space(3))) f16x8 lds_f16x8;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
-constexpr uint32_t kOutOfRange = 0x80000000u;
+using dma::dma16;
+using dma::dma16_nt;
+using dma::kOutOfRange;
+using dma::make_rsrc;
+using dma::wait_lgkm0;
+using dma::wait_vmcnt;
 
 template <int MB_, int NB_, int NW_, int S_, bool NTB_ = false, int MODE_ = 0>
 struct Skinny {
@@ -113,59 +119,6 @@ __device__ __forceinline__ int swz_b(int k, int c)
     else
         return c ^ (((k >> 3) & 1) << 1);
 }
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N <= 63, "vmcnt");
-    constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(imm);
-    asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ void wait_lgkm0()
-{
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt((3 << 14) | (0 << 8) | (7 << 4) | 15);
-    asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ i32x4 make_rsrc(const void *base)
-{
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    i32x4 r;
-    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
-    r.z = (int)kOutOfRange;
-    r.w = 0x00020000;
-    return r;
-}
-
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_addr)
-{
-    asm volatile("s_mov_b32 m0, %2\n\t"
-                 "s_nop 0\n\t"
-                 "buffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :
-                 : "v"(voff), "s"(rsrc), "s"(lds_addr)
-                 : "m0");
-}
-
-// The same with the non-temporal hint: data streamed once is not kept in the
-// caches.
-__device__ __forceinline__ void dma16_nt(i32x4 rsrc, uint32_t voff, uint32_t lds_addr)
-{
-    asm volatile("s_mov_b32 m0, %2\n\t"
-                 "s_nop 0\n\t"
-                 "buffer_load_dwordx4 %0, %1, 0 offen nt lds"
-                 :
-                 : "v"(voff), "s"(rsrc), "s"(lds_addr)
-                 : "m0");
-}
-#pragma clang diagnostic pop
 
 template <class T>
 __global__ void __launch_bounds__(T::NT) gemm_relu_skinny_kernel(GemmArgs p, int steps_per_wave)
