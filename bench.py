@@ -49,10 +49,10 @@ def log(*a):
 # The sources that decide the kernel a workload's launch runs: the dispatcher,
 # the shared internal header and the kernel's own file.
 KERNEL_SOURCES = {
-    "skinny_16x16384x8192": ("api.cpp", "tg_internal.h", "gemm_skinny.hip"),
+    "skinny_16x16384x8192": ("api.cpp", "tg_internal.h", "tg_lds_dma.h", "gemm_skinny.hip"),
     "ragged_3001x5003x1000": ("api.cpp", "tg_internal.h", "gemm_tile.hip"),
 }
-DEFAULT_SOURCES = ("api.cpp", "tg_internal.h", "gemm_dma.hip")
+DEFAULT_SOURCES = ("api.cpp", "tg_internal.h", "tg_lds_dma.h", "gemm_dma.hip")
 
 
 def kernel_source_hash(workload: str) -> str:
@@ -92,80 +92,55 @@ TRIAL_MS = 20.0        # each trial at least this long
 
 
 class ClockSampler:
-    """Samples the GPU's shader (gfx) clock in a background thread while a
-    timed region runs, through the ROCm SMI library (amdsmi), on the device
-    whose PCI bus id matches cuda:0.  Any failure leaves `samples` empty
-    (the line then carries null)."""
+    """Measures the shader clock while a timed region runs: a one-wave spin
+    kernel (torch.cuda._sleep, which spins until clock64() has advanced by n
+    shader-clock cycles) runs on a second stream of default priority, next
+    to the workload, bracketed by HIP events on that stream; n / elapsed time
+    is the clock it saw.  The spinning wave needs no LDS and a few
+    registers, so it shares a compute unit with the workload's workgroups
+    instead of displacing one.  `idle` is the same measurement with nothing
+    else running (the boost clock)."""
 
-    def __init__(self, torch):
+    SOURCE = ("torch.cuda._sleep(n) on a second stream during the trials: n shader-clock "
+              "cycles / elapsed time between HIP events")
+
+    def __init__(self, torch, cycles: int = 30_000_000, spins: int = 6):
+        self.torch = torch
+        self.cycles = cycles
+        self.spins = spins
+        self.stream = torch.cuda.Stream()
         self.samples = []
-        self.source = None
-        self._h = None
-        self._stop = None
-        self._thread = None
-        try:
-            import amdsmi
-            self._amdsmi = amdsmi
-            amdsmi.amdsmi_init()
-            props = torch.cuda.get_device_properties(0)
-            want = (int(props.pci_domain_id), int(props.pci_bus_id), int(props.pci_device_id))
-            for h in amdsmi.amdsmi_get_processor_handles():
-                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)          # "dddd:bb:dd.f"
-                dom, bus, rest = bdf.split(":")
-                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
-                    self._h = h
-                    break
-            if self._h is not None and self._read() is None:
-                self._h = None
-        except Exception as e:   # no SMI access on this machine: report no clock
-            log(f"clock sampling unavailable: {type(e).__name__}: {e}")
-            self._h = None
+        self.idle = self._measure(1)[0]
+        self._pending = []
 
-    def _read(self):
-        a = self._amdsmi
-        try:
-            m = a.amdsmi_get_gpu_metrics_info(self._h)
-            xs = m.get("current_gfxclks")
-            if isinstance(xs, (list, tuple)):
-                xs = [x for x in xs if isinstance(x, (int, float)) and 0 < x < 10000]
-                if xs:
-                    self.source = "gpu_metrics current_gfxclks (mean over XCDs)"
-                    return float(sum(xs)) / len(xs)
-            for key in ("current_gfxclk", "average_gfxclk_frequency"):
-                x = m.get(key)
-                if isinstance(x, (int, float)) and 0 < x < 10000:
-                    self.source = f"gpu_metrics {key}"
-                    return float(x)
-        except Exception:
-            pass
-        try:
-            c = a.amdsmi_get_clock_info(self._h, a.AmdSmiClkType.GFX)
-            self.source = "clock_info GFX"
-            return float(c["clk"])
-        except Exception:
-            return None
+    def _enqueue(self, n):
+        t = self.torch
+        evs = []
+        with t.cuda.stream(self.stream):
+            for _ in range(n):
+                a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+                a.record(self.stream)
+                t.cuda._sleep(self.cycles)
+                b.record(self.stream)
+                evs.append((a, b))
+        return evs
+
+    def _collect(self, evs):
+        self.stream.synchronize()
+        return [self.cycles / (a.elapsed_time(b) * 1e3) for a, b in evs]   # MHz
+
+    def _measure(self, n):
+        return self._collect(self._enqueue(n))
 
     def __enter__(self):
-        import threading
-        if self._h is None:
-            return self
-        self._stop = threading.Event()
-
-        def loop():
-            while not self._stop.is_set():
-                v = self._read()
-                if v is not None:
-                    self.samples.append(v)
-                self._stop.wait(0.002)
-
-        self._thread = threading.Thread(target=loop, daemon=True)
-        self._thread.start()
+        # the current stream's work so far must not be overlapped by the spins
+        self.stream.wait_stream(self.torch.cuda.current_stream())
+        self._pending = self._enqueue(self.spins)
         return self
 
     def __exit__(self, *exc):
-        if self._thread is not None:
-            self._stop.set()
-            self._thread.join()
+        self.samples.extend(self._collect(self._pending))
+        self._pending = []
         return False
 
     def reset(self):
@@ -176,7 +151,7 @@ class ClockSampler:
             return None
         x = sorted(self.samples)
         return {"median": x[len(x) // 2], "min": x[0], "max": x[-1], "samples": len(x),
-                "source": self.source}
+                "idle": self.idle, "source": self.SOURCE}
 
 
 def time_calls(torch, call, steps: int, warmup: int, clock: ClockSampler | None = None,
@@ -209,7 +184,7 @@ def time_calls(torch, call, steps: int, warmup: int, clock: ClockSampler | None 
         t1.record(stream)
         torch.cuda.synchronize()
         per = max(t0.elapsed_time(t1) / 3, 1e-4)
-        n = max(1, int(np.ceil(TRIAL_MS / per)))
+        n = max(1, int(np.ceil(1.25 * TRIAL_MS / per)))
         per_call = []
         with (clock if clock is not None else _Null()):
             for t in range(trials):
@@ -658,7 +633,7 @@ def summarize_ablation(out_md: str, root: str, title: str):
     print(f"wrote {out_md}")
 
 
-PMC_SET = ("SQ_CYCLES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT "
+PMC_SET = ("SQ_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT "
            "SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE TCC_HIT_sum TCC_MISS_sum")
 
 
@@ -687,9 +662,10 @@ def summarize_run(workload: str, root: str, commands: list[str]):
            if v["name"] == name]
     n = len(pmc)
     avg = lambda key: sum(v[key] for v in pmc) / n
-    # SQ_CYCLES and GRBM_GUI_ACTIVE are summed over the 32 shader engines
+    # SQ_CYCLES is summed over the 32 shader engines, GRBM_GUI_ACTIVE over the
+    # 8 XCDs
     clock = sum(v["SQ_CYCLES"] / 32 / v["us"] / 1e3 for v in pmc) / n
-    gui = sum(v["GRBM_GUI_ACTIVE"] / 32 / v["us"] / 1e3 for v in pmc) / n
+    gui = sum(v["GRBM_GUI_ACTIVE"] / 8 / v["us"] / 1e3 for v in pmc) / n
     mfma = sum(v["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * v["SQ_CYCLES"] / 32) for v in pmc) / n
     lds_conf = avg("SQ_LDS_BANK_CONFLICT") / max(avg("SQ_LDS_IDX_ACTIVE"), 1.0)
     l2_hit = avg("TCC_HIT_sum") / max(avg("TCC_HIT_sum") + avg("TCC_MISS_sum"), 1.0)
@@ -750,7 +726,7 @@ def summarize_run(workload: str, root: str, commands: list[str]):
                 f"trace average / ms_per_step = {trace_ns / 1e6 / b['ms_per_step']:.3f}.\n")
         f.write(f"\n## Counters (rocprofv3 --pmc, one set per run), {n} dispatches\n\n")
         f.write(f"* shader clock {clock:.2f} GHz (SQ_CYCLES per shader engine / kernel time; "
-                f"GRBM_GUI_ACTIVE gives {gui:.2f} GHz), kernel time under the counters "
+                f"GRBM_GUI_ACTIVE per XCD gives {gui:.2f} GHz), kernel time under the counters "
                 f"{pmc_us:.1f} us\n")
         f.write(f"* matrix cores busy {mfma:.1%} of the SIMD cycles "
                 f"(SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x SQ_CYCLES per engine)); "

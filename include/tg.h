@@ -318,7 +318,9 @@ enum {
     TG_PATH_W4 = 6,         /* tg_gemm_w4's int4-weight kernel (reported, not forced) */
     TG_PATH_ATTENTION = 7,  /* the attention entry points' kernel (reported, not forced) */
     TG_PATH_MLA = 8,        /* tg_mla_decode_f16's kernels (reported, not forced) */
-    TG_PATH_COUNT = 9
+    TG_PATH_RAGGED = 9,     /* aligned A, any-alignment (K,N) B and C: A direct to LDS, B via
+                               registers, C stored through a parity-shifted LDS tile */
+    TG_PATH_COUNT = 10
 };
 int tg_set_path(int path);
 

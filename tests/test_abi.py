@@ -45,6 +45,8 @@ def test_status_strings(tg):
 
 def test_path_control(tg):
     assert tg.tg_path_name(tg.TG_PATH_TILE128) == "tile128"
+    assert tg.tg_path_name(tg.TG_PATH_RAGGED) == "ragged"
+    assert tg.TG_PATH_COUNT == tg.TG_PATH_RAGGED + 1
     assert tg.tg_path_name(77) == "unknown"
     prev = tg.tg_set_path(tg.TG_PATH_NAIVE)
     assert prev == tg.TG_PATH_AUTO
@@ -88,6 +90,28 @@ def test_null_pointers(tg):
     assert tg.tg_gemm_relu_f16(0, P, P, 4, 4, 4, 4, 4, 4, 0) == tg.TG_ERR_INVALID_ARG
     assert tg.tg_gemm_relu_f16(P, 0, P, 4, 4, 4, 4, 4, 4, 0) == tg.TG_ERR_INVALID_ARG
     assert tg.tg_gemm_relu_f16(P, P, 0, 4, 4, 4, 4, 4, 4, 0) == tg.TG_ERR_INVALID_ARG
+
+
+def test_odd_pointers_are_rejected(tg):
+    # elements are 2 bytes: an odd address is refused before any HIP call
+    bad = tg.TG_ERR_INVALID_ARG
+    assert tg.tg_gemm_relu_f16(P + 1, P, P, 4, 4, 4, 4, 4, 4, 0) == bad
+    assert tg.tg_gemm_relu_f16(P, P + 3, P, 4, 4, 4, 4, 4, 4, 0) == bad
+    assert tg.tg_gemm_relu_f16(P, P, P + 5, 4, 4, 4, 4, 4, 4, 0) == bad
+    assert tg.tg_gemm_ex(0, 0, 1, P, P, P, P + 1, 4, 4, 4, 4, 4, 4, 0, 0, 0, 1, 0) == bad
+
+
+def test_noalloc_splitk_refuses_beyond_its_scratch(tg):
+    f = tg.tg_gemm_relu_f16_splitk_noalloc
+    bad = tg.TG_ERR_INVALID_ARG
+    # 17 chunks of 16 x 16384 fp32 partials exceed the 16 MiB array: refused
+    # before the device is even looked at
+    assert f(P, P, P, 16, 16384, 4096, 4096, 16384, 16384, 17, 0) == bad
+    # the split-K argument rules apply as for the workspace form
+    assert f(P, P, P, 65, 64, 256, 256, 64, 64, 2, 0) == bad
+    assert f(P, P, P, 16, 64, 256, 256, 64, 64, 9, 0) == bad
+    assert f(P + 2, P, P, 16, 64, 256, 256, 64, 64, 2, 0) == bad
+    assert f(0, 0, 0, 0, 16, 64, 64, 16, 16, 1, 0) == tg.TG_OK
 
 
 def test_empty_calls_are_noops(tg):
@@ -268,6 +292,10 @@ def _gpu_visible():
 @pytest.mark.skipif(_gpu_visible(), reason="checks the no-device error on a host without a GPU")
 def test_valid_call_without_device_reports_no_device(tg):
     st = tg.tg_gemm_relu_f16(P, P, P, 4, 4, 4, 4, 4, 4, 0)
+    assert st == tg.TG_ERR_NO_DEVICE
+    # the largest request the allocation-free split-K form takes reaches the
+    # device check (exactly the 16 MiB of its scratch array)
+    st = tg.tg_gemm_relu_f16_splitk_noalloc(P, P, P, 16, 16384, 4096, 4096, 16384, 16384, 16, 0)
     assert st == tg.TG_ERR_NO_DEVICE
     # K = 0 with null operands is valid and also reaches the device check
     st = tg.tg_gemm_relu_f16(0, 0, P, 4, 4, 0, 1, 4, 4, 0)

@@ -125,7 +125,9 @@ def test_bias_and_activation_on_every_path(tg, oracle_lib, dtype, layout, path, 
     if path in ("naive", "generic"):
         assert used == path
     elif not aligned:
-        assert used == "generic"
+        # automatic dispatch sends an aligned A with a (K,N) B to the ragged kernel
+        ragged = path == "auto" and layout == "kn" and K % 8 == 0 and M > 64
+        assert used == ("ragged" if ragged else "generic")
     elif path == "skinny" and M > 64:
         assert used == "tile128"
     elif path != "auto":

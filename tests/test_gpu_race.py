@@ -34,6 +34,7 @@ DTYPES = {"f16": 0, "bf16": 1}
 LAYOUTS = {"kn": 0, "nk": 1}
 
 # one K group (any tile / stages / swizzle / waves), the register-staged kernels
+# (and, below, the any-layout and ragged-layout kernels)
 KG1 = [c for c in range(30) if c not in (14, 15, 16, 20)] + [100, 101]
 # two K groups: K tiles of 64 (configs 14, 20) or of 32 (15, 16) dealt alternately
 KG2_GROUPS = [[14, 20], [15, 16]]
@@ -114,6 +115,9 @@ def test_one_k_group_configs_bitwise_identical(tg, oracle_lib, M, N, K):
         assert used == "tile256"
     outs["generic"], used = run(tg, a_d, b_d, M, N, K, "f16", "kn", tg.TG_PATH_GENERIC, -1)
     assert used == "generic"
+    for v in (0, 1):
+        outs[f"ragged{v}"], used = run(tg, a_d, b_d, M, N, K, "f16", "kn", tg.TG_PATH_RAGGED, v)
+        assert used == "ragged"
     check_against_oracle(oracle_lib, outs[8], a, b, M, N, K, "f16", "kn")
     assert_same(outs, 8)
 

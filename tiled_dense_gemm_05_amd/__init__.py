@@ -31,7 +31,8 @@ TG_PATH_SKINNY = 5
 TG_PATH_W4 = 6
 TG_PATH_ATTENTION = 7
 TG_PATH_MLA = 8
-TG_PATH_COUNT = 9
+TG_PATH_RAGGED = 9
+TG_PATH_COUNT = 10
 
 EXPORTED_SYMBOLS = (
     "tg_gemm_relu_f16",

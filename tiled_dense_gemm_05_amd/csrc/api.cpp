@@ -92,6 +92,10 @@ int validate(const void *A, const void *B, const void *C, int64_t M, int64_t N, 
         return TG_ERR_INVALID_ARG;
     if (K > 0 && (A == nullptr || B == nullptr))
         return TG_ERR_INVALID_ARG;
+    // elements are 2 bytes: an odd address is not an element
+    if (((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B) |
+          reinterpret_cast<uintptr_t>(C)) & 1) != 0)
+        return TG_ERR_INVALID_ARG;
     const __int128 b_ext = b_nk ? extent(N, K, ldb, sB, batch) : extent(K, N, ldb, sB, batch);
     if (extent(M, K, lda, sA, batch) > kMaxExtent || b_ext > kMaxExtent ||
         extent(M, N, ldc, sC, batch) > kMaxExtent)
@@ -119,25 +123,44 @@ bool fast_layout(const tg::GemmArgs &p)
     return p.K > 0 && tg::dma_layout_ok(p);
 }
 
+// Whether the ragged kernel can serve a call: A as for the 16-byte-chunk
+// kernels, B stored (K,N); B, C and the bias at any 2-byte alignment.
+bool ragged_layout(const tg::GemmArgs &p)
+{
+    if (p.b_nk || p.K <= 0 || !aligned16(p.A) || ((p.lda | p.K) & 7))
+        return false;
+    if (p.batch > 1 && (p.sA & 7))
+        return false;
+    return tg::dma_layout_ok(p);
+}
+
+// Rounds of one workgroup per compute unit for square tiles of side `t`.
+int64_t tile_rounds(const tg::GemmArgs &p, int64_t t)
+{
+    const int64_t tiles = ((p.M + t - 1) / t) * ((p.N + t - 1) / t) * p.batch;
+    return (tiles + 255) / 256;
+}
+
+// Both tile kernels (aligned and ragged) run one workgroup per CU, so a
+// launch takes ceil(tiles / 256) rounds.  A round of 256x256 tiles does four
+// times the work of a round of 128x128 tiles and takes about 2.6 times as
+// long (measured from 2048^2 to 8192^2, K >= 1000); pick the cheaper one.
+bool prefer_256(const tg::GemmArgs &p)
+{
+    return (double)tile_rounds(p, 256) * 2.6 < (double)tile_rounds(p, 128);
+}
+
 int choose_path(const tg::GemmArgs &p)
 {
     if (!fast_layout(p))
-        return TG_PATH_GENERIC;
+        return (ragged_layout(p) && p.M > 64) ? TG_PATH_RAGGED : TG_PATH_GENERIC;
     if (p.M <= 64 && tg::skinny_layout_ok(p))
         return TG_PATH_SKINNY;
-    // Both tile kernels run one workgroup per CU, so a launch takes
-    // ceil(tiles / 256) rounds.  A round of 256x256 tiles does four times the
-    // work of a round of 128x128 tiles and takes about 2.6 times as long
-    // (measured from 2048^2 to 8192^2, K >= 1000); pick the cheaper estimate.
     // Short K (the batched shapes) stays on the 128x128 kernel, which then
     // runs several workgroups per CU.
     if (p.K <= 64)
         return TG_PATH_TILE128;
-    const int64_t tiles256 = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
-    const int64_t tiles128 = ((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch;
-    const double rounds256 = (double)((tiles256 + 255) / 256) * 2.6;
-    const double rounds128 = (double)((tiles128 + 255) / 256);
-    return rounds256 < rounds128 ? TG_PATH_TILE256 : TG_PATH_TILE128;
+    return prefer_256(p) ? TG_PATH_TILE256 : TG_PATH_TILE128;
 }
 
 int run(const void *A, const void *B, void *C, const void *bias, bool relu, bool bf16, bool b_nk,
@@ -147,6 +170,8 @@ int run(const void *A, const void *B, void *C, const void *bias, bool relu, bool
     int st = validate(A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC, batch, b_nk);
     if (st != TG_OK)
         return st;
+    if ((reinterpret_cast<uintptr_t>(bias) & 1) != 0)
+        return TG_ERR_INVALID_ARG;
     if (M == 0 || N == 0 || batch == 0)
         return TG_OK;
     st = check_device();
@@ -173,7 +198,10 @@ int run(const void *A, const void *B, void *C, const void *bias, bool relu, bool
     if (path == TG_PATH_AUTO || path == TG_PATH_W4 || path == TG_PATH_ATTENTION ||
         path == TG_PATH_MLA)
         path = choose_path(p);
-    else if (path != TG_PATH_NAIVE && path != TG_PATH_GENERIC && !fast_layout(p))
+    else if (path == TG_PATH_RAGGED && !ragged_layout(p))
+        path = TG_PATH_GENERIC;
+    else if (path != TG_PATH_NAIVE && path != TG_PATH_GENERIC && path != TG_PATH_RAGGED &&
+             !fast_layout(p))
         path = TG_PATH_GENERIC;
     else if (path == TG_PATH_SKINNY && !tg::skinny_layout_ok(p))
         path = TG_PATH_TILE128;
@@ -201,6 +229,14 @@ int run(const void *A, const void *B, void *C, const void *bias, bool relu, bool
             e = tg::launch_tile256(p, stream, gm);
         else
             e = tg::launch_dma_config(v, p, stream, gm);
+        break;
+    }
+    case TG_PATH_RAGGED: {
+        // tg_set_tile_variant 0 / 1 forces the 256x256 / 128x128 configuration
+        int v = g_tile_variant.load(std::memory_order_relaxed);
+        if (v != 0 && v != 1)
+            v = prefer_256(p) ? 0 : 1;
+        e = tg::launch_ragged_config(v, p, stream, g_group_m.load(std::memory_order_relaxed));
         break;
     }
     case TG_PATH_SKINNY: {
@@ -431,6 +467,7 @@ const char *tg_path_name(int path)
     case TG_PATH_W4: return "w4";
     case TG_PATH_ATTENTION: return "attention";
     case TG_PATH_MLA: return "mla";
+    case TG_PATH_RAGGED: return "ragged";
     default: return "unknown";
     }
 }

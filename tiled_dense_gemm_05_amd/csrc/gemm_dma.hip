@@ -542,6 +542,318 @@ hipError_t launch_dma(const GemmArgs &p, hipStream_t stream, int groupM)
     return hipSuccess;
 }
 
+// ---------------------------------------------------------------------------
+// Ragged layouts: an aligned A (16-byte aligned rows, K a multiple of 8) with a
+// (K,N) B and a C whose rows may start at any 2-byte boundary (odd or
+// unaligned ldb / ldc, N not a multiple of 8, B or C pointers at 2 mod 16).
+//
+//  * A is staged exactly as in gemm_relu_dma_kernel (direct to LDS, two
+//    stages, loads two K tiles ahead).
+//  * B goes through registers.  Each 16-byte chunk of a B row is read as the
+//    4-byte aligned window that holds it: one 16-byte load at the dword
+//    boundary at or below the chunk and, when the chunk starts at 2 mod 4, one
+//    4-byte load for the element that spills past that window; a funnel shift
+//    by 0 or 16 bits puts the eight elements in place, and one 16-byte LDS
+//    write stores them at the chunk's swizzled slot, where the transpose reads
+//    of the aligned kernel find them.  A chunk cut by the N edge reads only the
+//    dwords that hold one of its elements and zeroes the rest, so no access
+//    leaves the 4-byte words of the operand.  The loads of tile kt+2 are
+//    issued at the end of tile kt and written to LDS at the end of tile kt+1,
+//    so they have a whole tile of matrix work to land.
+//  * The epilogue stages the C tile in LDS with each row shifted by the parity
+//    of its first element's address (row stride BN + 8), so that every
+//    interior 16-byte chunk of a row lines up with a 4-byte aligned address
+//    and goes out as one 16-byte store; the chunks at the row's two ends are
+//    stored element by element.
+// Every configuration computes each output with the same sequence of 16-wide
+// k steps as the aligned kernel, so both give the same bits.
+
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+template <class T>
+struct RaggedPlan {
+    static constexpr int NCH = T::B_ELEMS / 8 / T::NT;   // B chunks per thread per tile
+    static constexpr int RSTEP = T::NT / T::CB;          // tile rows between them
+    static_assert(NCH * RSTEP == T::BK && T::NT % T::CB == 0, "B chunk plan");
+    static constexpr int CLD = T::BN + 8;                // staged C row (elements)
+    static constexpr int CCH = CLD / 8;                  // 16-byte chunks per staged row
+    static constexpr int CST = T::BM * CLD * 2;          // staged C tile (bytes)
+    static constexpr int RING = T::STAGES * T::STAGE * 2;
+    static constexpr int LDS = RING > CST ? RING : CST;
+    static_assert(LDS <= 160 * 1024, "LDS size");
+};
+
+// The raw dwords of one thread's B chunks for one K tile.
+template <class T>
+struct BRegs {
+    u32x4 w[RaggedPlan<T>::NCH];   // the 16-byte window (or its first four dwords)
+    uint32_t x[RaggedPlan<T>::NCH];   // the dword after it
+    uint32_t sh[RaggedPlan<T>::NCH];  // funnel shift: 0 or 16 bits
+};
+
+// Issues the loads of this thread's B chunks of the K tile starting at row
+// k0: tile row row0 + j * RSTEP, columns n0 + col .. + 7 (nv of them valid).
+template <class T>
+__device__ __forceinline__ void ragged_b_load(BRegs<T> &br, const uint16_t *Bb, int64_t k0,
+                                              int64_t K, int64_t ldb, int64_t n0, int row0,
+                                              int col, int64_t nv)
+{
+    constexpr int NCH = RaggedPlan<T>::NCH, RSTEP = RaggedPlan<T>::RSTEP;
+    // descriptor at the dword boundary at or below (k0, n0); d = 1 when that
+    // element sits at 2 mod 4
+    const uintptr_t a = reinterpret_cast<uintptr_t>(Bb + k0 * ldb + n0);
+    const int d = (int)((a >> 1) & 1);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void *>(a & ~(uintptr_t)3), (short)0, (int)kOutOfRange, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const int r = row0 + j * RSTEP;
+        const bool row_ok = k0 + r < K;
+        const int e = d + r * (int)ldb + col;   // element index from the descriptor base
+        const int odd = e & 1;
+        const int e0 = e - odd;                 // first element of the dword window
+        br.sh[j] = odd ? 16u : 0u;
+        if (row_ok && nv >= 8) {
+            br.w[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, 2 * e0, 0, 0);
+            br.x[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, odd ? 2 * (e0 + 8) : (int)kOutOfRange,
+                                                          0, 0);
+        } else {
+            // cut by the N edge (or past it / past K): only the dwords that
+            // hold an element of the chunk, the others read as zero
+            const int last = e + (int)(nv < 8 ? nv : 8) - 1;   // last valid element
+            const bool any = row_ok && nv > 0;
+            uint32_t q[5];
+#pragma unroll
+            for (int t = 0; t < 5; ++t)
+                q[t] = __builtin_amdgcn_raw_buffer_load_b32(
+                    rs, (any && e0 + 2 * t <= last) ? 2 * (e0 + 2 * t) : (int)kOutOfRange, 0, 0);
+            br.w[j] = u32x4{q[0], q[1], q[2], q[3]};
+            br.x[j] = q[4];
+        }
+    }
+}
+
+// Funnel-shifts the landed windows into chunks, zeroes columns past N and
+// writes them to the B tile of the LDS stage at stage_b.
+template <class T>
+__device__ __forceinline__ void ragged_b_store(const BRegs<T> &br, lds_u16 *stage_b, int row0,
+                                               int c, int64_t nv)
+{
+    constexpr int NCH = RaggedPlan<T>::NCH, RSTEP = RaggedPlan<T>::RSTEP;
+    // dword q keeps both elements when 2q + 1 < nv, the low one when 2q < nv
+    uint32_t m[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        m[q] = (2 * q + 1 < nv) ? 0xffffffffu : (2 * q < nv) ? 0x0000ffffu : 0u;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const int r = row0 + j * RSTEP;
+        const u32x4 w = br.w[j];
+        const uint32_t s = br.sh[j];
+        u32x4 v;
+        v.x = __builtin_amdgcn_alignbit(w.y, w.x, s) & m[0];
+        v.y = __builtin_amdgcn_alignbit(w.z, w.y, s) & m[1];
+        v.z = __builtin_amdgcn_alignbit(w.w, w.z, s) & m[2];
+        v.w = __builtin_amdgcn_alignbit(br.x[j], w.w, s) & m[3];
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4 *>(
+            stage_b + r * T::BN + swz_b<T::CB, T::SWZ>(r, c) * 8) = v;
+    }
+}
+
+template <class T, int I = 0>
+__device__ __forceinline__ void issue_a_tile(const LoadPlan<T> &lp, const i32x4 &ra, bool a_kok,
+                                             uint32_t stage_addr, int wave)
+{
+    if constexpr (I < T::A_LD) {
+        issue_one<T, I>(lp, ra, ra, a_kok, 0, stage_addr, wave);
+        issue_a_tile<T, I + 1>(lp, ra, a_kok, stage_addr, wave);
+    }
+}
+
+template <class T>
+__global__ void __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(T::OCC)))
+gemm_relu_ragged_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
+{
+    static_assert(T::STAGES == 2 && T::KG == 1 && !T::BT, "ragged kernel: 2 stages, (K,N) B");
+    using RP = RaggedPlan<T>;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[RP::LDS / 2];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const lds_u16 *lds = (const lds_u16 *)smem;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+    const int wm = wave / T::WN, wn = wave % T::WN;
+    int tm, tn;
+    tile_coords(blockIdx.x, tilesM, tilesN, groupM, tm, tn);
+    const int64_t bidx = blockIdx.y;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int64_t m0 = (int64_t)tm * T::BM, n0 = (int64_t)tn * T::BN;
+    const uint16_t *Ab = p.A + bidx * p.sA + m0 * p.lda;
+    const uint16_t *Bb = p.B + bidx * p.sB;
+    uint16_t *C = p.C + bidx * p.sC;
+
+    // A load plan, as in the aligned kernel
+    LoadPlan<T> lp;
+    {
+        const int r0 = wave * T::A_RPB + lane / T::CA;
+        const int c = swz_a<T::CA, T::SWZ>(r0, lane % T::CA);
+        lp.a_kcol = c * 8;
+#pragma unroll
+        for (int i = 0; i < T::A_LD; ++i) {
+            const int row = r0 + i * T::NW * T::A_RPB;
+            lp.a_voff[i] = (m0 + row < M) ? (uint32_t)((row * p.lda + c * 8) * 2) : kOutOfRange;
+        }
+    }
+    auto rsrc_a = [&](int t) { return make_rsrc(Ab + (int64_t)t * T::BK); };
+    auto a_kok = [&](int t) { return (int64_t)t * T::BK + lp.a_kcol < K; };
+    // B chunk plan: chunk column c, tile rows row0, row0 + RSTEP, ...
+    const int bc = tid % T::CB;
+    const int brow0 = tid / T::CB;
+    const int64_t bnv = N - (n0 + bc * 8);
+    BRegs<T> br;
+    auto b_load = [&](int t) {
+        ragged_b_load<T>(br, Bb, (int64_t)t * T::BK, K, p.ldb, n0, brow0, bc * 8, bnv);
+    };
+    auto b_store = [&](int t) {
+        ragged_b_store<T>(br, (lds_u16 *)smem + (t & 1) * T::STAGE + T::A_ELEMS, brow0, bc, bnv);
+    };
+
+    f32x16 acc[T::FM][T::FN];
+#pragma unroll
+    for (int fm = 0; fm < T::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < T::FN; ++fn)
+            acc[fm][fn] = f32x16{};
+
+    const int KT = (int)((K + T::BK - 1) / T::BK);
+    f16x8 af[2][T::FM], bf[2][T::FN];
+    // prologue: tile 0 in stage 0, tile 1's A loads and B registers in flight
+    b_load(0);
+    issue_a_tile<T>(lp, rsrc_a(0), a_kok(0), lds_base, wave);
+    wait_vmcnt<0>();
+    b_store(0);
+    b_load(1);
+    issue_a_tile<T>(lp, rsrc_a(1), a_kok(1), lds_base + (uint32_t)(T::STAGE * 2), wave);
+    block_barrier();
+    {
+        s16x4 bh[T::FN][2];
+        read_all<T>(lds, lds + T::A_ELEMS, 0, wm, wn, lane, af[0], bh);
+        join_b<T>(bh, bf[0]);
+    }
+
+    for (int kt = 0; kt < KT; ++kt) {
+        const int stage = kt & 1;
+        const lds_u16 *As = lds + stage * T::STAGE;
+        const lds_u16 *Bs = As + T::A_ELEMS;
+        inner_steps<T>(acc, af, bf, lp, i32x4{}, i32x4{}, false, 0, 0u, wave, As, Bs, wm, wn,
+                       lane);
+        constexpr int cur = (T::KSTEPS - 1) & 1, nxt = T::KSTEPS & 1;
+        // tile kt+1: its A loads and B registers (issued at the end of tile
+        // kt-1) have landed; its B chunks go to the other stage, free since
+        // that barrier
+        wait_vmcnt<0>();
+        b_store(kt + 1);
+        block_barrier();
+        {
+            // last k step of tile kt, with tile kt+2's A loads into the stage
+            // just released and the first fragment reads of tile kt+1
+            const lds_u16 *An = lds + (stage ^ 1) * T::STAGE;
+            const uint32_t laddr = lds_base + (uint32_t)(stage * T::STAGE * 2);
+            s16x4 bh[T::FN][2];
+            step<T, 0, T::A_LD>(acc, af[cur], bf[cur], lp, rsrc_a(kt + 2), i32x4{}, a_kok(kt + 2), 0,
+                                laddr, wave, An, An + T::A_ELEMS, 0, wm, wn, lane, af[nxt], bh);
+            join_b<T>(bh, bf[nxt]);
+        }
+        b_load(kt + 2);
+    }
+    // loads issued past the end of K must land before the LDS is reused
+    wait_vmcnt<0>();
+
+    // Epilogue: bias, ReLU, rounding; the tile staged with row r shifted by
+    // the parity of its first element's address.
+    block_barrier();
+    lds_u16 *cst = (lds_u16 *)smem;
+    const int cpar = (int)((reinterpret_cast<uintptr_t>(C) >> 1) & 1);
+    const bool relu = p.relu != 0;
+#pragma unroll
+    for (int fn = 0; fn < T::FN; ++fn) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int col = wn * T::TN + fn * 32 + 8 * g + 4 * (lane >> 5);
+            float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (p.bias != nullptr) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    if (n0 + col + t < N)
+                        bv[t] = bits_to_float<T::BF16>(p.bias[n0 + col + t]);
+            }
+#pragma unroll
+            for (int fm = 0; fm < T::FM; ++fm) {
+                const int row = wm * T::TM + fm * 32 + (lane & 31);
+                const int odd = (cpar + (int)(((m0 + row) * p.ldc + n0) & 1)) & 1;
+                const f32x16 &v = acc[fm][fn];
+                const uint32_t lo = epi_pack2<T::BF16>(v[4 * g + 0] + bv[0], v[4 * g + 1] + bv[1], relu);
+                const uint32_t hi = epi_pack2<T::BF16>(v[4 * g + 2] + bv[2], v[4 * g + 3] + bv[3], relu);
+                lds_u16 *dst = cst + row * RP::CLD + col;
+                if (!odd) {
+                    *reinterpret_cast<__attribute__((address_space(3))) u32x2 *>(dst) = u32x2{lo, hi};
+                } else {
+                    dst[1] = (uint16_t)(lo & 0xffff);
+                    *reinterpret_cast<__attribute__((address_space(3))) uint32_t *>(dst + 2) =
+                        (lo >> 16) | (hi << 16);
+                    dst[4] = (uint16_t)(hi >> 16);
+                }
+            }
+        }
+    }
+    block_barrier();
+    const int64_t nrow = (N - n0) < T::BN ? (N - n0) : T::BN;
+    for (int q = tid; q < T::BM * RP::CCH; q += T::NT) {
+        const int row = q / RP::CCH, ch = q % RP::CCH;
+        const int64_t gm = m0 + row;
+        if (gm >= M)
+            continue;
+        uint16_t *g = C + gm * p.ldc + n0;
+        const int odd = (cpar + (int)((gm * p.ldc + n0) & 1)) & 1;
+        const int j0 = 8 * ch - odd;   // row element held by the chunk's first slot
+        const lds_u16 *src = cst + row * RP::CLD + 8 * ch;
+        if (j0 >= 0 && j0 + 8 <= nrow) {
+            *reinterpret_cast<u32x4_a4 *>(g + j0) =
+                *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(src);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (j0 + i >= 0 && j0 + i < nrow)
+                    g[j0 + i] = src[i];
+        }
+    }
+}
+
+template <class T>
+hipError_t launch_ragged(const GemmArgs &p, hipStream_t stream, int groupM)
+{
+    const int64_t tilesM = (p.M + T::BM - 1) / T::BM;
+    const int64_t tilesN = (p.N + T::BN - 1) / T::BN;
+    const int64_t tiles = tilesM * tilesN;
+    if (tiles > 0x7fffffff)
+        return hipErrorInvalidValue;
+    GemmArgs q = p;
+    for (int64_t b0 = 0; b0 < p.batch; b0 += 65535) {
+        const int64_t nb = (p.batch - b0) < 65535 ? (p.batch - b0) : 65535;
+        q.A = p.A + b0 * p.sA;
+        q.B = p.B + b0 * p.sB;
+        q.C = p.C + b0 * p.sC;
+        q.batch = nb;
+        hipLaunchKernelGGL((gemm_relu_ragged_kernel<T>), dim3((unsigned)tiles, (unsigned)nb),
+                           dim3(T::NT), 0, stream, q, (int)tilesM, (int)tilesN, groupM);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_all_configs(int cfg, const GemmArgs &p, hipStream_t stream, int groupM)
 {
     switch (cfg) {
@@ -618,6 +930,22 @@ bool dma_config_has_mode(int cfg, int mode)
 {
     return mode == 0 ? (cfg >= 0 && cfg < kDmaConfigs)
                      : (cfg == 8 || cfg == 29 || cfg == 12 || cfg == 20);
+}
+
+hipError_t launch_ragged_config(int cfg, const GemmArgs &p, hipStream_t stream, int groupM)
+{
+    if (p.b_nk)
+        return hipErrorInvalidValue;
+    const bool bf = p.bf16 != 0;
+    switch (cfg) {
+    case 0:   // 256 x 256 x 64, 8 waves of 128 x 64 (the large-shape geometry)
+        return bf ? launch_ragged<Mode<Cfg<256, 256, 64, 2, 4, 2>, 1>>(p, stream, groupM)
+                  : launch_ragged<Mode<Cfg<256, 256, 64, 2, 4, 2>, 0>>(p, stream, groupM);
+    case 1:   // 128 x 128 x 64, 8 waves of 32 x 64
+        return bf ? launch_ragged<Mode<Cfg<128, 128, 64, 4, 2, 2>, 1>>(p, stream, groupM)
+                  : launch_ragged<Mode<Cfg<128, 128, 64, 4, 2, 2>, 0>>(p, stream, groupM);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_dma_config(int cfg, const GemmArgs &p, hipStream_t stream, int groupM)

@@ -156,6 +156,11 @@ hipError_t launch_tile256(const GemmArgs &p, hipStream_t stream, int groupM);
 // B (mode bits 1 and 2) exist for the default configurations only.
 constexpr int kDmaConfigs = 30;
 hipError_t launch_dma_config(int cfg, const GemmArgs &p, hipStream_t stream, int groupM);
+// Ragged layouts (see gemm_dma.hip): A as for the direct-to-LDS kernels
+// (16-byte aligned rows, K a multiple of 8), B stored (K,N) with any 2-byte
+// alignment and leading dimension, C likewise, N any.  cfg 0: 256x256x64
+// tiles, cfg 1: 128x128x64.
+hipError_t launch_ragged_config(int cfg, const GemmArgs &p, hipStream_t stream, int groupM);
 bool dma_config_has_mode(int cfg, int mode);
 // Skinny-M kernels (M <= 64, aligned layouts); `cfg` selects slice width,
 // waves and stages; see gemm_skinny.hip.
