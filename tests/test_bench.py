@@ -33,9 +33,10 @@ def test_traffic_only_while_sources_unchanged(tmp_path, monkeypatch):
 
 
 def test_source_hash_follows_the_workloads_kernel():
-    # the skinny and ragged workloads hash their own kernel files
+    # the skinny workload hashes its own kernel file; the ragged kernel lives
+    # in the same file as the aligned tile kernels
     assert bench.kernel_source_hash("skinny_16x16384x8192") != bench.kernel_source_hash("large_8192")
-    assert bench.kernel_source_hash("ragged_3001x5003x1000") != bench.kernel_source_hash("large_8192")
+    assert bench.kernel_source_hash("ragged_3001x5003x1000") == bench.kernel_source_hash("large_8192")
     assert bench.kernel_source_hash("mid_2048") == bench.kernel_source_hash("large_8192")
 
 

@@ -558,8 +558,9 @@ hipError_t launch_dma(const GemmArgs &p, hipStream_t stream, int groupM)
 //    of the aligned kernel find them.  A chunk cut by the N edge reads only the
 //    dwords that hold one of its elements and zeroes the rest, so no access
 //    leaves the 4-byte words of the operand.  The loads of tile kt+2 are
-//    issued at the end of tile kt and written to LDS at the end of tile kt+1,
-//    so they have a whole tile of matrix work to land.
+//    issued after the second k step of tile kt and written to LDS at the same
+//    point of tile kt+1, so they have a whole tile of matrix work to land and
+//    the LDS writes stay clear of the barrier that ends the tile.
 //  * The epilogue stages the C tile in LDS with each row shifted by the parity
 //    of its first element's address (row stride BN + 8), so that every
 //    interior 16-byte chunk of a row lines up with a 4-byte aligned address
@@ -674,7 +675,8 @@ template <class T>
 __global__ void __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(T::OCC)))
 gemm_relu_ragged_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
 {
-    static_assert(T::STAGES == 2 && T::KG == 1 && !T::BT, "ragged kernel: 2 stages, (K,N) B");
+    static_assert(T::STAGES == 2 && T::KG == 1 && !T::BT && T::KSTEPS == 4,
+                  "ragged kernel: 2 stages, 64-wide K tiles, (K,N) B");
     using RP = RaggedPlan<T>;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[RP::LDS / 2];
 
@@ -746,14 +748,33 @@ gemm_relu_ragged_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
         const int stage = kt & 1;
         const lds_u16 *As = lds + stage * T::STAGE;
         const lds_u16 *Bs = As + T::A_ELEMS;
-        inner_steps<T>(acc, af, bf, lp, i32x4{}, i32x4{}, false, 0, 0u, wave, As, Bs, wm, wn,
-                       lane);
-        constexpr int cur = (T::KSTEPS - 1) & 1, nxt = T::KSTEPS & 1;
-        // tile kt+1: its A loads and B registers (issued at the end of tile
-        // kt-1) have landed; its B chunks go to the other stage, free since
-        // that barrier
+        // k steps 0 and 1
+        {
+            s16x4 bh[T::FN][2];
+            step<T, 0, 0>(acc, af[0], bf[0], lp, i32x4{}, i32x4{}, false, 0, 0u, wave, As, Bs, 1,
+                          wm, wn, lane, af[1], bh);
+            join_b<T>(bh, bf[1]);
+        }
+        {
+            s16x4 bh[T::FN][2];
+            step<T, 0, 0>(acc, af[1], bf[1], lp, i32x4{}, i32x4{}, false, 0, 0u, wave, As, Bs, 2,
+                          wm, wn, lane, af[0], bh);
+            join_b<T>(bh, bf[0]);
+        }
+        // Tile kt+1's B registers (issued at this point of tile kt-1) have
+        // landed: write them to the other stage, free since the barrier that
+        // ended tile kt-1, and reload the registers with tile kt+2.  The
+        // scheduling barriers keep the funnel shifts that consume the loads
+        // here; hoisted to the top of the tile, they would make the wave wait
+        // for the loads two k steps after issuing them.
         wait_vmcnt<0>();
+        __builtin_amdgcn_sched_barrier(0);
         b_store(kt + 1);
+        b_load(kt + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        inner_steps<T, 2>(acc, af, bf, lp, i32x4{}, i32x4{}, false, 0, 0u, wave, As, Bs, wm, wn,
+                          lane);
+        constexpr int cur = (T::KSTEPS - 1) & 1, nxt = T::KSTEPS & 1;
         block_barrier();
         {
             // last k step of tile kt, with tile kt+2's A loads into the stage
@@ -765,7 +786,6 @@ gemm_relu_ragged_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
                                 laddr, wave, An, An + T::A_ELEMS, 0, wm, wn, lane, af[nxt], bh);
             join_b<T>(bh, bf[nxt]);
         }
-        b_load(kt + 2);
     }
     // loads issued past the end of K must land before the LDS is reused
     wait_vmcnt<0>();
