@@ -65,6 +65,7 @@ def build_library(extra: list[str] | None = None) -> str:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
     build_capi_bench()
+    build_ceilings()
     return LIB
 
 
@@ -82,6 +83,23 @@ def build_capi_bench() -> str:
         raise RuntimeError(f"building the C ABI benchmark failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, BENCH_BIN)
     return BENCH_BIN
+
+
+CEIL_SRC = os.path.join(HERE, "ceilings.hip")
+CEIL_BIN = os.path.join(HERE, "tg_ceilings")
+
+
+def build_ceilings() -> str:
+    """The program that measures the part's practical ceilings (matrix-core
+    rate and clock on the workload's data, LDS read rates)."""
+    tmp = CEIL_BIN + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", CEIL_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"building the ceilings program failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, CEIL_BIN)
+    return CEIL_BIN
 
 
 if __name__ == "__main__":

@@ -1,0 +1,210 @@
+// Measured ceilings of the part the GEMM kernels run on, as one JSON line per
+// figure: what the matrix cores sustain on their own, and how fast LDS
+// delivers the two fragment read forms the tile kernels use.  These are the
+// practical bounds the kernels' roofline fractions are read against (the
+// spec peak assumes the 2.4 GHz clock, which the matrix cores do not hold
+// under load).
+//
+//   mfma_f16_32x32x16  Every wave runs a loop of independent
+//                      v_mfma_f32_32x32x16_f16 on register operands drawn
+//                      from normal(0, 1/sqrt(8192)) (the 8192^3 workload's
+//                      distribution: the matrix cores' power, and so the
+//                      clock, depends on the data), 8 waves per CU, no memory
+//                      traffic in the loop.  Reports TFLOP/s and the shader
+//                      clock it ran at (clock64 / wall clock inside the kernel).
+//   lds_read_b128      ds_read_b128 (A fragments and (N,K) B fragments):
+//                      bytes per shader clock per CU, 8 waves per CU,
+//                      conflict-free addresses.
+//   lds_read_tr_b64    ds_read_b64_tr_b16 (transpose reads of a row-major
+//                      (K,N) B tile) in the tile kernels' XOR-swizzled layout.
+//
+// Usage: tg_ceilings [seconds_per_figure]   (default 0.2)
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <random>
+#include <vector>
+
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+constexpr int kOperands = 65536;   // f16x8 operand vectors drawn on the host
+constexpr int kChains = 8;         // independent accumulators per wave (128 registers)
+
+#define CHECK(x)                                                                         \
+    do {                                                                                 \
+        hipError_t e_ = (x);                                                             \
+        if (e_ != hipSuccess) {                                                          \
+            std::fprintf(stderr, "%s failed: %s\n", #x, hipGetErrorString(e_));         \
+            std::exit(1);                                                                \
+        }                                                                                \
+    } while (0)
+
+// clock64 and the 100 MHz wall clock at the first and last instruction of
+// wave 0 of each workgroup, for the clock the loop ran at.
+__global__ void __launch_bounds__(512) mfma_loop(const f16x8 *in, float *out, long long *clk,
+                                                 int iters)
+{
+    const int t = blockIdx.x * 512 + threadIdx.x;
+    f16x8 a[4], b[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        a[i] = in[(t * 6 + i) % kOperands];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        b[i] = in[(t * 6 + 4 + i) % kOperands];
+    f32x16 acc[kChains];
+#pragma unroll
+    for (int i = 0; i < kChains; ++i)
+        acc[i] = f32x16{};
+    const long long c0 = clock64(), w0 = wall_clock64();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < kChains; ++i)
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i & 3], b[i >> 2], acc[i], 0, 0, 0);
+        // rotate the operands so consecutive products see different values
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            a[i] = __builtin_shufflevector(a[i], a[i], 1, 2, 3, 4, 5, 6, 7, 0);
+    }
+    const long long c1 = clock64(), w1 = wall_clock64();
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kChains; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            s += acc[i][j];
+    out[t] = s;
+    if (threadIdx.x == 0) {
+        clk[2 * blockIdx.x] = c1 - c0;
+        clk[2 * blockIdx.x + 1] = w1 - w0;
+    }
+}
+
+// LDS reads: KIND 0 ds_read_b128, KIND 1 ds_read_b64_tr_b16 in the tile
+// kernels' B layout (512-byte rows, 16-byte chunk c of row k stored at chunk
+// c ^ ((k & 3) << 2)).  Every address stays inside the 64 KiB array.
+template <int KIND>
+__global__ void __launch_bounds__(512) lds_loop(uint32_t *out, long long *clk, int iters)
+{
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[32768];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < 32768; i += 512)
+        smem[i] = (uint16_t)i;
+    __syncthreads();
+    const lds_u8 *base = (const lds_u8 *)smem;
+    u32x4 acc = {0, 0, 0, 0};
+    const long long c0 = clock64();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            if constexpr (KIND == 0) {
+                const int off = ((wave * 8 + r) * 1024 + lane * 16 + it * 64) & 65535 & ~15;
+                acc += *(const lds_u32x4 *)(base + off);
+            } else {
+                const int k = 8 * (lane >> 5) + ((lane & 15) >> 2) + 16 * ((wave * 8 + r + it) & 3);
+                const int n = 16 * ((lane >> 4) & 1) + 4 * (lane & 3) + 32 * ((wave + it) & 7);
+                const int off = (k * 512 + (((n >> 3) ^ ((k & 3) << 2)) * 16) + (n & 7) * 2) & 65535;
+                const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + off));
+                acc.x += (uint32_t)(uint16_t)v.x;
+                acc.y += (uint32_t)(uint16_t)v.w;
+            }
+        }
+    }
+    const long long c1 = clock64();
+    out[blockIdx.x * 512 + tid] = acc.x + acc.y + acc.z + acc.w;
+    if (tid == 0)
+        clk[blockIdx.x] = c1 - c0;
+}
+
+}  // namespace
+
+int main(int argc, char **argv)
+{
+    const double target_s = argc > 1 ? std::atof(argv[1]) : 0.2;
+    int dev = 0, cus = 0, wall_khz = 0;
+    CHECK(hipGetDevice(&dev));
+    CHECK(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    CHECK(hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, dev));
+
+    std::vector<_Float16> h((size_t)kOperands * 8);
+    std::mt19937 gen(2);
+    std::normal_distribution<double> nd(0.0, 1.0 / std::sqrt(8192.0));
+    for (auto &x : h)
+        x = (_Float16)nd(gen);
+    f16x8 *d_in;
+    float *d_out;
+    long long *d_clk;
+    const int blocks = cus;   // one 8-wave workgroup per CU
+    CHECK(hipMalloc(&d_in, h.size() * sizeof(_Float16)));
+    CHECK(hipMemcpy(d_in, h.data(), h.size() * sizeof(_Float16), hipMemcpyHostToDevice));
+    CHECK(hipMalloc(&d_out, (size_t)blocks * 512 * sizeof(float)));
+    CHECK(hipMalloc(&d_clk, (size_t)blocks * 2 * sizeof(long long)));
+    hipEvent_t e0, e1;
+    CHECK(hipEventCreate(&e0));
+    CHECK(hipEventCreate(&e1));
+    std::vector<long long> clk((size_t)blocks * 2);
+
+    // matrix cores: size the loop for about target_s seconds from a short run
+    {
+        int iters = 2000;
+        for (int pass = 0; pass < 2; ++pass) {
+            CHECK(hipEventRecord(e0, 0));
+            hipLaunchKernelGGL(mfma_loop, dim3(blocks), dim3(512), 0, 0, d_in, d_out, d_clk, iters);
+            CHECK(hipGetLastError());
+            CHECK(hipEventRecord(e1, 0));
+            CHECK(hipEventSynchronize(e1));
+            float ms = 0;
+            CHECK(hipEventElapsedTime(&ms, e0, e1));
+            if (pass == 0) {
+                iters = (int)std::fmin(2.0e8, std::fmax(2000.0, iters * target_s * 1e3 / ms));
+                continue;
+            }
+            CHECK(hipMemcpy(clk.data(), d_clk, clk.size() * sizeof(long long), hipMemcpyDeviceToHost));
+            double c = 0, w = 0;
+            for (int i = 0; i < blocks; ++i) {
+                c += (double)clk[2 * i];
+                w += (double)clk[2 * i + 1];
+            }
+            const double mhz = c / (w / (wall_khz * 1e3)) / 1e6;
+            const double flop = (double)blocks * 8 /* waves */ * iters * kChains * 2.0 * 32 * 32 * 16;
+            std::printf("{\"figure\": \"mfma_f16_32x32x16\", \"tflops\": %.1f, \"sclk_mhz\": %.0f, "
+                        "\"ms\": %.3f, \"waves_per_cu\": 8, \"operands\": \"normal(0, 1/sqrt(8192))\"}\n",
+                        flop / (ms * 1e-3) / 1e12, mhz, ms);
+        }
+    }
+    // LDS read forms
+    for (int kind = 0; kind < 2; ++kind) {
+        const int iters = 20000;
+        for (int pass = 0; pass < 2; ++pass) {
+            if (kind == 0)
+                hipLaunchKernelGGL(lds_loop<0>, dim3(blocks), dim3(512), 0, 0, (uint32_t *)d_out, d_clk, iters);
+            else
+                hipLaunchKernelGGL(lds_loop<1>, dim3(blocks), dim3(512), 0, 0, (uint32_t *)d_out, d_clk, iters);
+            CHECK(hipGetLastError());
+            CHECK(hipDeviceSynchronize());
+        }
+        CHECK(hipMemcpy(clk.data(), d_clk, (size_t)blocks * sizeof(long long), hipMemcpyDeviceToHost));
+        double cyc = 0;
+        for (int i = 0; i < blocks; ++i)
+            cyc += (double)clk[i];
+        cyc /= blocks;
+        const double bytes = 8.0 * 64 * iters * 8 * (kind == 0 ? 16 : 8);   // per CU
+        std::printf("{\"figure\": \"%s\", \"bytes_per_clock_per_cu\": %.1f, \"waves_per_cu\": 8}\n",
+                    kind == 0 ? "lds_read_b128" : "lds_read_tr_b64", bytes / cyc);
+    }
+    CHECK(hipFree(d_in));
+    CHECK(hipFree(d_out));
+    CHECK(hipFree(d_clk));
+    return 0;
+}
