@@ -35,7 +35,7 @@ LAYOUTS = {"kn": 0, "nk": 1}
 
 # one K group (any tile / stages / swizzle / waves), the register-staged kernels
 # (and, below, the any-layout and ragged-layout kernels)
-KG1 = [c for c in range(30) if c not in (14, 15, 16, 20)] + [100, 101]
+KG1 = [c for c in range(32) if c not in (14, 15, 16, 20)] + [100, 101]
 # two K groups: K tiles of 64 (configs 14, 20) or of 32 (15, 16) dealt alternately
 KG2_GROUPS = [[14, 20], [15, 16]]
 # configurations that exist for bf16 elements and an (N,K) B

@@ -918,6 +918,10 @@ hipError_t launch_all_configs(int cfg, const GemmArgs &p, hipStream_t stream, in
     // eight-wave 128x128 tiles
     case 28: return launch_dma<Mode<Cfg<128, 128, 64, 2, 4, 4>, 0>>(p, stream, groupM);
     case 29: return launch_dma<Mode<Cfg<128, 128, 64, 4, 2, 4>, 0>>(p, stream, groupM);
+    // two workgroups per CU (64 KiB of LDS each): the two waves sharing a SIMD
+    // belong to different workgroups and meet different barriers
+    case 30: return launch_dma<Mode<Cfg<256, 128, 32, 2, 2, 2, 2>, 0>>(p, stream, groupM);
+    case 31: return launch_dma<Mode<Cfg<128, 256, 32, 2, 2, 2, 2>, 0>>(p, stream, groupM);
     default: return hipErrorInvalidValue;
     }
 }
