@@ -733,7 +733,10 @@ def summarize_run(workload: str, root: str, commands: list[str]):
         f.write(f"\n## Counters (rocprofv3 --pmc, one set per run), {n} dispatches\n\n")
         f.write(f"* shader clock {clock:.2f} GHz (SQ_CYCLES per shader engine / kernel time; "
                 f"GRBM_GUI_ACTIVE per XCD gives {gui:.2f} GHz), kernel time under the counters "
-                f"{pmc_us:.1f} us\n")
+                f"{pmc_us:.1f} us"
+                + ("; for a launch this short the counters' window is longer than the kernel, "
+                   "so this clock reads high and the busy fraction below is relative to it"
+                   if pmc_us < 100 else "") + "\n")
         f.write(f"* matrix cores busy {mfma:.1%} of the SIMD cycles "
                 f"(SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x SQ_CYCLES per engine)); "
                 f"at that clock the busy fraction corresponds to "

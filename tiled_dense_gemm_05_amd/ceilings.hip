@@ -17,6 +17,9 @@
 //                      conflict-free addresses.
 //   lds_read_tr_b64    ds_read_b64_tr_b16 (transpose reads of a row-major
 //                      (K,N) B tile) in the tile kernels' XOR-swizzled layout.
+//   hbm_read           A plain streaming read: 16 bytes per lane, grid-stride
+//                      over 256 MiB, three buffers taken in turn so that no
+//                      pass is served from the 256 MB last-level cache.
 //
 // Usage: tg_ceilings [seconds_per_figure]   (default 0.2)
 #include <hip/hip_runtime.h>
@@ -127,6 +130,19 @@ __global__ void __launch_bounds__(512) lds_loop(uint32_t *out, long long *clk, i
         clk[blockIdx.x] = c1 - c0;
 }
 
+// Reads n16 16-byte vectors, each lane striding by the grid; one sum per
+// workgroup keeps the loads alive.
+__global__ void __launch_bounds__(512) hbm_read(const u32x4 *p, int64_t n16, uint32_t *out)
+{
+    u32x4 acc = {0, 0, 0, 0};
+    const int64_t stride = (int64_t)gridDim.x * 512;
+    for (int64_t i = (int64_t)blockIdx.x * 512 + threadIdx.x; i < n16; i += stride)
+        acc ^= __builtin_nontemporal_load(p + i);
+    const uint32_t v = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    if (v == 0x9e3779b9u)   // practically never: keeps the reads without a store per lane
+        out[blockIdx.x] = v;
+}
+
 }  // namespace
 
 int main(int argc, char **argv)
@@ -202,6 +218,33 @@ int main(int argc, char **argv)
         const double bytes = 8.0 * 64 * iters * 8 * (kind == 0 ? 16 : 8);   // per CU
         std::printf("{\"figure\": \"%s\", \"bytes_per_clock_per_cu\": %.1f, \"waves_per_cu\": 8}\n",
                     kind == 0 ? "lds_read_b128" : "lds_read_tr_b64", bytes / cyc);
+    }
+    // HBM streaming read
+    {
+        const int64_t bytes = 256ll << 20, n16 = bytes / 16;
+        u32x4 *buf[3];
+        for (auto &b : buf) {
+            CHECK(hipMalloc(&b, bytes));
+            CHECK(hipMemset(b, 1, bytes));
+        }
+        const int grid = cus * 4;
+        for (int i = 0; i < 6; ++i)
+            hipLaunchKernelGGL(hbm_read, dim3(grid), dim3(512), 0, 0, buf[i % 3], n16, (uint32_t *)d_out);
+        CHECK(hipGetLastError());
+        CHECK(hipDeviceSynchronize());
+        const int reps = 30;
+        CHECK(hipEventRecord(e0, 0));
+        for (int i = 0; i < reps; ++i)
+            hipLaunchKernelGGL(hbm_read, dim3(grid), dim3(512), 0, 0, buf[i % 3], n16, (uint32_t *)d_out);
+        CHECK(hipGetLastError());
+        CHECK(hipEventRecord(e1, 0));
+        CHECK(hipEventSynchronize(e1));
+        float ms = 0;
+        CHECK(hipEventElapsedTime(&ms, e0, e1));
+        std::printf("{\"figure\": \"hbm_read\", \"gbs\": %.0f, \"us_per_256MiB\": %.1f}\n",
+                    (double)bytes * reps / (ms * 1e-3) / 1e9, ms * 1e3 / reps);
+        for (auto &b : buf)
+            CHECK(hipFree(b));
     }
     CHECK(hipFree(d_in));
     CHECK(hipFree(d_out));
