@@ -243,11 +243,12 @@ def test_mla_decode_validation(tg):
 def test_mla_workspace_sizes(tg):
     ws = tg.tg_mla_decode_workspace_bytes
     per = lambda B, H: B * H * (512 + 2) * 4   # one key range: fp32 outputs, maximum and sum
-    # 64 sequences of 128 heads: 128 workgroups of 64 heads, two ranges fill 256 CUs
-    assert ws(64, 128, 8192) == 2 * per(64, 128)
+    # 64 sequences of 128 heads: 64 workgroups of 128 heads, four ranges fill 256 CUs
+    assert ws(64, 128, 8192) == 4 * per(64, 128)
     # one sequence: as many ranges as give each CU a workgroup, at least 8 tiles of 32 each
     assert ws(1, 64, 4096) == 16 * per(1, 64)
-    assert ws(1, 128, 1 << 20) == 128 * per(1, 128)
+    assert ws(1, 128, 1 << 20) == 256 * per(1, 128)
+    assert ws(1, 256, 1 << 20) == 128 * per(1, 256)      # two head blocks
     assert ws(1, 16, 100) == 0                           # too short to split
     assert ws(512, 128, 8192) == 0                       # enough sequences to fill the chip
     assert ws(0, 16, 100) == 0 and ws(4, 0, 100) == 0 and ws(4, 16, 0) == 0

@@ -493,58 +493,62 @@ hipError_t launch_attn(const AttnArgs &p, hipStream_t stream)
 // value, shared by every query head.
 //
 // gfx950 design:
-//  * A workgroup of four waves, one per SIMD, serves 64 query heads of one
-//    sequence over one range of its keys.  Waves 2g and 2g + 1 share heads
-//    32g .. 32g + 31 (one per lane pair) and split the head dimension: wave
-//    half e holds Q^T for values 288e .. 288e + 287 and accumulates output
-//    values 256e .. 256e + 255.  A wave thus keeps 18 Q^T fragments and a
-//    32 x 256 fp32 accumulator in registers (the whole 576 / 512 would not
-//    fit one wave's registers) while each LDS fragment read still feeds 32
-//    heads.
+//  * A workgroup of four waves, one per SIMD, serves 128 query heads of one
+//    sequence over one range of its keys.  Wave w owns heads 32w .. 32w + 31
+//    (one per lane pair) outright: its Q^T (36 fragments, 144 registers)
+//    stays in registers and its 32 x 512 fp32 output in the 256 accumulation
+//    registers.  The waves share nothing but the staged rows, so a tile costs
+//    one barrier (to reuse its stage) and no exchange of partial scores, and
+//    each cached row is staged once per 128 heads.
+//  * What bounds the product on this part is the LDS read rate: every
+//    16-byte K read, and every pair of 8-byte transpose reads of V, feeds one
+//    32 x 32 x 16 product, and the LDS returns about one such read per 4
+//    clocks per CU whatever its width.  A tile takes 36 + 64 reads per wave
+//    (plus its 36 1 KiB stage writes) against 68 products of 32 clocks on
+//    each SIMD: about 80 % of the LDS's time, the rest of it hidden behind
+//    the matrix cores.
 //  * Tiles of 32 cached rows (36 KiB) are staged in a 4-stage LDS ring by
 //    buffer_load_dwordx4 ... lds; the buffer's record count ends at the
 //    range's last visible row, so later rows read as zeros (and are masked
-//    out of the softmax).
-//  * Scores S^T = K Q^T as in the attention forward above, each wave over
-//    its half of the values; the two halves are swapped through LDS and
-//    added (addition commutes, so both waves hold the same bits), both run
-//    the same softmax, and each adds its half of O^T += V^T P^T.  The same
-//    LDS rows are read as K (16-byte reads) and as V (transpose reads of the
-//    first 512 values), so one chunk swizzle serves both.  Rows are 1152
-//    bytes, so in the 256-byte bank line (64 banks) consecutive rows start
-//    alternately at 0 and 128; chunk c of row r sits at c ^ x(r) with
-//    x(r) = 2 ((r / 2) mod 4) + (r / 8) mod 2, which with that alternation
-//    puts the 16 rows a K fragment read serves at once on 16 different
-//    16-byte slots, and the 4 rows x 2 chunks of a transpose read on 8.
+//    out of the softmax).  Each wave moves 9 of a tile's 36 1-KiB blocks,
+//    one beside each of the first 9 score products two tiles earlier.
+//  * Scores S^T = K Q^T and O^T += V^T P^T as in the attention forward
+//    above.  The same LDS rows are read as K (16-byte reads) and as V
+//    (transpose reads of the first 512 values), so one chunk swizzle serves
+//    both.  Rows are 1152 bytes, so in the 256-byte bank line (64 banks)
+//    consecutive rows start alternately at 0 and 128; chunk c of row r sits
+//    at c ^ x(r) with x(r) = 2 ((r / 2) mod 4) + (r / 8) mod 2, which with
+//    that alternation puts the 16 rows a K fragment read serves at once on
+//    16 different 16-byte slots, and the 4 rows x 2 chunks of a transpose
+//    read on 8.
+//  * Software pipeline, per tile t: tile t's 36 score products run on the
+//    matrix cores while the vector units take tile t-1's softmax, one small
+//    step beside each product (the order is pinned with scheduling
+//    barriers); then tile t-1's 32 value products.  The barrier that frees
+//    tile t-1's stage (and shows tile t+1) sits before the last three value
+//    products, whose operands are already in registers, so the next tile's
+//    first K reads run under them.
 //  * When the sequences are too few to fill the chip the keys are split
 //    into ranges (flash-decoding); each range writes its unnormalised fp32
 //    output with its running maximum and sum, and a combine kernel rescales
 //    and adds the ranges in a fixed order, so results are deterministic.
-//    The head blocks of one range are numbered 8 apart so that they run on
-//    one XCD and share its L2.
 namespace mla {
-constexpr int D = kMlaDl + kMlaDr;   // 576 values per cached row
-constexpr int BK = 32;               // cached rows per tile
-constexpr int TILE = BK * D;         // fp16 elements per tile
-constexpr int BLOCKS = TILE * 2 / 1024;  // 1 KiB DMA blocks per tile
-
-// NQ parts of the head dimension per 32-head group, two groups per workgroup
-// (NQ = 2: one wave per SIMD.  Four parts at two waves per SIMD, with a
-// 3-stage ring to fit the larger exchange, measured slower: 361 against
-// 284 us on 64 sequences x 8192 tokens x 128 heads.)
-template <int NQ_>
-struct Cfg {
-    static constexpr int NQ = NQ_;
-    static constexpr int NW = 2 * NQ;                    // waves
-    static constexpr int WPE = NW / 4;                   // waves per SIMD
-    static constexpr int STAGES = NQ == 2 ? 4 : 3;       // ring depth (LDS: 160 / 140 KiB)
-    static constexpr int LD = (BLOCKS + NW - 1) / NW;    // DMA blocks per wave per tile
-    static constexpr int DS = D / 16 / NQ;               // 16-wide score steps per part
-    static constexpr int DB = kMlaDl / 32 / NQ;          // 32-wide output blocks per part
-    static constexpr int XCH = NW * 16 * 64;             // floats of the score exchange
-    static_assert(D % (16 * NQ) == 0 && kMlaDl % (32 * NQ) == 0, "parts");
-    static_assert(32 * 2 == kMlaHeadsPerBlock, "heads per workgroup");
-};
+constexpr int D = kMlaDl + kMlaDr;          // 576 values per cached row
+constexpr int BK = 32;                      // cached rows per tile
+constexpr int TILE = BK * D;                // fp16 elements per tile
+constexpr int BLOCKS = TILE * 2 / 1024;     // 1 KiB DMA blocks per tile (36)
+constexpr int NW = kMlaHeadsPerBlock / 32;  // waves, 32 heads each (4)
+constexpr int STAGES = 4;                   // ring depth (144 KiB of LDS)
+constexpr int LD = BLOCKS / NW;             // DMA blocks per wave per tile (9)
+constexpr int DS = D / 16;                  // 16-wide score steps (36)
+constexpr int DN = kMlaDl / 16;             // of them over the first 512 values (32)
+constexpr int QL = (DS - DN) * 512;         // fp16 elements of a wave's Q^T fragments kept in LDS
+constexpr int DB = kMlaDl / 32;             // 32-wide output blocks (16)
+constexpr int NV = 2 * DB;                  // value products per tile (32)
+constexpr int KA = 3;                       // K fragments read ahead of their product
+constexpr int VA = 3;                       // V fragments read ahead of their product
+static_assert(BLOCKS % NW == 0 && NW == 4, "four waves share a tile's blocks");
+static_assert(LD <= DS && VA <= DS && VA < NV, "pipeline steps");
 }  // namespace mla
 
 __device__ __forceinline__ int mla_swz(int row, int c)
@@ -552,23 +556,25 @@ __device__ __forceinline__ int mla_swz(int row, int c)
     return c ^ (2 * ((row >> 1) & 3) + ((row >> 3) & 1));
 }
 
-template <class T>
-__global__ void __launch_bounds__(64 * T::NW) __attribute__((amdgpu_waves_per_eu(T::WPE, T::WPE)))
+__device__ __forceinline__ float fmax3(float a, float b, float c)
+{
+    return __builtin_fmaxf(a, __builtin_fmaxf(b, c));
+}
+
+__global__ void __launch_bounds__(64 * mla::NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mla_decode_kernel(MlaArgs p)
 {
     using namespace mla;
-    constexpr int NQ = T::NQ, NW = T::NW, STAGES = T::STAGES, LD = T::LD, DS = T::DS,
-                  DB = T::DB;
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * TILE];
-    __shared__ __attribute__((aligned(16))) float xch[T::XCH];
+    // the tile ring, then each wave's last four Q^T fragments (160 KiB)
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * TILE + NW * QL];
     const lds_u16 *lds = (const lds_u16 *)smem;
     const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hg = wave / NQ, e = wave % NQ;   // head group, part of the head dimension
     const int hi = lane >> 5;
+    const int qbase = STAGES * TILE + wave * QL + lane * 8;   // Q^T fragment DN + j at + 512 j
     // grid x: 8 consecutive (sequence, key range) units, then the same 8
     // for the next head block, ...
     const int64_t nhb = (p.H + kMlaHeadsPerBlock - 1) / kMlaHeadsPerBlock;
@@ -578,7 +584,7 @@ mla_decode_kernel(MlaArgs p)
     if (unit >= p.B * p.splits)
         return;
     const int64_t b = unit / p.splits, sp = unit % p.splits;
-    const int64_t h = hb * kMlaHeadsPerBlock + hg * 32 + (lane & 31);
+    const int64_t h = hb * kMlaHeadsPerBlock + wave * 32 + (lane & 31);
     const bool live = h < p.H;
 
     int64_t n = p.Sk;
@@ -591,56 +597,56 @@ mla_decode_kernel(MlaArgs p)
     kend = kend < n ? kend : n;
     const int tiles = kend > kbeg ? (int)((kend - kbeg + BK - 1) / BK) : 0;
 
-    // Q^T fragments (second operand): lane holds Q[b][h][(D / NQ) e + 16 ds + 8 hi .. + 7]
+    // Q^T fragments (second operand): lane holds Q[b][h][16 ds + 8 hi .. + 7];
+    // the first DN stay in registers, the rest (the 64 values past 512) in
+    // LDS, read again for every tile: registers are what this kernel runs
+    // short of
     f16x8 qf[DS];
     {
-        const uint16_t *qrow = p.Q + (b * p.H + (live ? h : 0)) * D + e * (D / NQ);
+        // dead heads (past H) read head 0's row and keep zeros
+        const uint16_t *qrow = p.Q + (b * p.H + (live ? h : 0)) * D;
+        const bool neg = p.scale < 0.0f;   // a negative scale is carried by Q
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
-            qf[ds] = f16x8{};
-            if (live)
-                qf[ds] = *reinterpret_cast<const f16x8 *>(qrow + ds * 16 + 8 * hi);
-            if (p.scale < 0.0f)    // a negative scale is carried by Q
-                qf[ds] = -qf[ds];
+            const f16x8 v = *reinterpret_cast<const f16x8 *>(qrow + ds * 16 + 8 * hi);
+            const f16x8 q = live ? (neg ? -v : v) : f16x8{};
+            if (ds < DN)
+                qf[ds] = q;
+            else
+                *reinterpret_cast<f16x8 *>(smem + qbase + (ds - DN) * 512) = q;
         }
     }
 
     // DMA plan: slot s (16 bytes) of a tile is row s / 72, physical chunk
     // s % 72, which receives the row's logical chunk mla_swz(row, chunk);
-    // wave w moves 1 KiB blocks w, w + NW, ... (past the last block it
-    // moves the last block again: the same bytes to the same place)
-    uint32_t voff[LD];
+    // wave w moves 1 KiB blocks w, w + 4, ..., w + 32.  The byte offsets
+    // (< 36 KiB) are kept two to a register.
+    uint32_t voff2[(LD + 1) / 2];
+#pragma unroll
+    for (int i = 0; i < (LD + 1) / 2; ++i)
+        voff2[i] = 0;
 #pragma unroll
     for (int i = 0; i < LD; ++i) {
-        const int blk = wave + NW * i < BLOCKS ? wave + NW * i : BLOCKS - 1;
-        const int slot = blk * 64 + lane;
+        const int slot = (wave + NW * i) * 64 + lane;
         const int row = slot / (D / 8);
         const int pc = slot % (D / 8);
-        voff[i] = (uint32_t)((row * D + mla_swz(row, pc) * 8) * 2);
+        voff2[i / 2] |= (uint32_t)((row * D + mla_swz(row, pc) * 8) * 2) << (16 * (i % 2));
     }
     const uint16_t *kvb = p.KV + b * p.Sk * D;
-    auto issue = [&](int t) {
+    // the buffer of tile t: its visible rows (none for a tile past the
+    // range, whose loads then only write zeros into a stage nobody reads)
+    auto tile_rsrc = [&](int t) {
         const int64_t k0 = kbeg + (int64_t)t * BK;
-        const int64_t rows = kend - k0 < BK ? kend - k0 : BK;
-        i32x4 rsrc = make_rsrc(kvb + k0 * D);
-        rsrc.z = __builtin_amdgcn_readfirstlane((int)(rows * D * 2));
-        const uint32_t base = lds_base + (uint32_t)((t % STAGES) * TILE * 2);
-#pragma unroll
-        for (int i = 0; i < LD; ++i) {
-            const int blk = wave + NW * i < BLOCKS ? wave + NW * i : BLOCKS - 1;
-            dma16(rsrc, voff[i], base + (uint32_t)(blk * 1024));
-        }
+        int64_t rows = kend - k0 < BK ? kend - k0 : BK;
+        rows = rows > 0 ? rows : 0;
+        i32x4 r = make_rsrc(kvb + (rows > 0 ? k0 : 0) * D);
+        r.z = __builtin_amdgcn_readfirstlane((int)(rows * D * 2));
+        return r;
     };
-
-    f32x16 acc_o[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-        acc_o[db] = f32x16{};
-    float m_run = -1.0e30f, l_run = 0.0f;
-    const float sl2 = __builtin_fmaxf(__builtin_fabsf(p.scale) * 1.44269504088896340736f, 1.0e-30f);
-    // score exchange: float4 j of a lane of wave w at (4 w + j) * 64 + lane
-    float4 *mine = reinterpret_cast<float4 *>(xch) + wave * 4 * 64 + lane;
-    const float4 *group = reinterpret_cast<const float4 *>(xch) + hg * NQ * 4 * 64 + lane;
+    auto dma = [&](const i32x4 &rsrc, int t, int i) __attribute__((always_inline)) {
+        dma16(rsrc, (voff2[i / 2] >> (16 * (i % 2))) & 0xffffu,
+              lds_base + (uint32_t)((t % STAGES) * TILE * 2 + (wave + NW * i) * 1024));
+    };
 
     // LDS addresses as per-lane bases plus compile-time offsets: a K fragment
     // of step ds sits at kbase[ds % 4] + 64 (ds / 4) elements (adding 8 to a
@@ -651,185 +657,256 @@ mla_decode_kernel(MlaArgs p)
     {
         const int row = lane & 31;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = e * 2 * DS + 2 * j + hi;
-            kbase[j] = row * D + mla_swz(row, c) * 8;
-        }
+        for (int j = 0; j < 4; ++j)
+            kbase[j] = row * D + mla_swz(row, 2 * j + hi) * 8;
         const int dl = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int key = 8 * hh + 4 * hi + ((lane & 15) >> 2);
 #pragma unroll
             for (int par = 0; par < 2; ++par) {
-                const int d = e * (kMlaDl / NQ) + par * 32 + dl;
+                const int d = par * 32 + dl;
                 vbase[hh][par] = key * D + mla_swz(key, d >> 3) * 8 + (d & 7);
             }
         }
     }
-    // this part's score partials for tile t: lane holds head h's sums for
-    // keys k0 + 8 (r / 4) + 4 hi + r % 4
-    auto scores = [&](int t) {
-        // the stage offset kept opaque, so the addresses stay base + constant
-        const lds_u16 *Ks = lds + __builtin_amdgcn_readfirstlane((t % STAGES) * TILE);
-        const lds_u16 *kb[4] = {Ks + kbase[0], Ks + kbase[1], Ks + kbase[2], Ks + kbase[3]};
-        // K fragments read KA steps ahead of the products that use them
-        constexpr int KA = DS < 6 ? DS : 6;
-        f16x8 kf[DS];
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int ds = 0; ds < KA; ++ds)
-            kf[ds] = *reinterpret_cast<const lds_f16x8 *>(kb[ds & 3] + (ds >> 2) * 64);
-        // the scheduler may move vector and scalar ALU work across these
-        // fences, not LDS reads or matrix instructions
-        __builtin_amdgcn_sched_barrier(0x6);
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
-            if (ds + KA < DS)
-                kf[ds + KA] = *reinterpret_cast<const lds_f16x8 *>(kb[(ds + KA) & 3] + ((ds + KA) >> 2) * 64);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ds], qf[ds], acc, 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0x6);
-        }
-        return acc;
+    // the stage offset kept opaque, so the addresses stay base + constant
+    auto stage = [&](int t) { return lds + __builtin_amdgcn_readfirstlane((t % STAGES) * TILE); };
+    auto qread = [&](int ds) __attribute__((always_inline)) {
+        return *reinterpret_cast<const lds_f16x8 *>(lds + qbase + (ds - DN) * 512);
     };
-    auto publish = [&](const f32x16 &acc) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            mine[j * 64] = float4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
+    auto kread = [&](const lds_u16 *S, int ds) __attribute__((always_inline)) {
+        return *reinterpret_cast<const lds_f16x8 *>(S + kbase[ds & 3] + (ds >> 2) * 64);
     };
-    // the partner's partial for tile t added (addition commutes: both waves
-    // of the pair hold the same bits)
-    static_assert(NQ == 2, "the exchange adds one partner's partial");
-    const float4 *theirs = group + (e ^ 1) * 4 * 64;
-    auto complete = [&](int t, f32x16 &acc, bool last) {
-        float4 o[4];
+    // V^T fragment of value product i (kk = i / 16 selects the 16 keys, db =
+    // i % 16 the 32 values): the transpose reads fetch keys 4 hi .. 4 hi + 3
+    // and 8 + 4 hi .. 8 + 4 hi + 3 of the 16, the keys this lane's
+    // probabilities hold in that order
+    auto vread = [&](const lds_u16 *S, int i) __attribute__((always_inline)) {
+        const int kk = i / DB, db = i % DB;
+        s16x4 vh[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            o[j] = theirs[j * 64];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            acc[4 * j + 0] += o[j].x;
-            acc[4 * j + 1] += o[j].y;
-            acc[4 * j + 2] += o[j].z;
-            acc[4 * j + 3] += o[j].w;
-        }
-        const int64_t k0 = kbeg + (int64_t)t * BK;
-        if (last && k0 + BK > kend) {    // only the range's last tile can be partial
-            f32x16 sm[1] = {acc};
-            mask_tile<1>(sm, (int)(kend - k0), hi);
-            acc = sm[0];
-        }
+        for (int hh = 0; hh < 2; ++hh)
+            vh[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4 *)(S + vbase[hh][db & 1] + (db >> 1) * 64 + 16 * kk * D));
+        return __builtin_bit_cast(f16x8,
+                                  __builtin_shufflevector(vh[0], vh[1], 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    // this part of O^T += V^T P^T (values (512 / NQ) e ..) for tile t
-    auto values = [&](int t, const f16x8 (&pf)[2]) {
-        const lds_u16 *Vs = lds + __builtin_amdgcn_readfirstlane((t % STAGES) * TILE);
-        const lds_u16 *vb[2][2] = {{Vs + vbase[0][0], Vs + vbase[0][1]},
-                                   {Vs + vbase[1][0], Vs + vbase[1][1]}};
-        // V^T fragments read VA products ahead (products in (db, kk) order)
-        constexpr int NP = DB * 2, VA = 3;
-        f16x8 vf[NP];
-        auto load_v = [&](int i) {
-            const int db = i / 2, kk = i % 2;
-            s16x4 vh[2];
+
+    f32x16 acc_o[DB];
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-                vh[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4 *)(vb[hh][db & 1] + (db >> 1) * 64 + 16 * kk * D));
-            vf[i] = __builtin_bit_cast(
-                f16x8, __builtin_shufflevector(vh[0], vh[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        };
-#pragma unroll
-        for (int i = 0; i < VA; ++i)
-            load_v(i);
-        __builtin_amdgcn_sched_barrier(0x6);
-#pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            if (i + VA < NP)
-                load_v(i + VA);
-            acc_o[i / 2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[i], pf[i % 2], acc_o[i / 2], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0x6);
+    for (int db = 0; db < DB; ++db)
+        acc_o[db] = f32x16{};
+    float m_run = -1.0e30f, l_run = 0.0f;
+    const float sl2 = __builtin_fmaxf(__builtin_fabsf(p.scale) * 1.44269504088896340736f, 1.0e-30f);
+
+    // The softmax of one tile's raw scores s (this lane's head; register r
+    // holds key 8 (r / 4) + 4 hi + r % 4) cut into steps, each small enough
+    // to sit beside one score product of the next tile: the running maximum
+    // (raised only when the tile exceeds it by more than 2^8; `grow` and
+    // `alpha` tell the caller to rescale its output), the fp16
+    // probabilities pf in the value product's operand order and the running
+    // sum of the rounded probabilities.  Step for step the arithmetic of
+    // softmax_block.
+    float sa0 = 0.f, sa1 = 0.f, sa2 = 0.f, sa3 = 0.f, sa4 = 0.f, sa5 = 0.f;
+    float mt = 0.f, m_new = 0.f, alpha = 1.0f, neg_m = 0.f, x_even = 0.f, ls0 = 0.f, ls1 = 0.f;
+    bool grow = false;
+    f16x8 pf[2] = {f16x8{}, f16x8{}};
+    auto sm_step = [&](const f32x16 &s, int k) __attribute__((always_inline)) {
+        if (k == 0) {
+            sa0 = fmax3(s[0], s[1], s[2]);
+            sa1 = fmax3(s[3], s[4], s[5]);
+        } else if (k == 1) {
+            sa2 = fmax3(s[6], s[7], s[8]);
+            sa3 = fmax3(s[9], s[10], s[11]);
+        } else if (k == 2) {
+            sa4 = fmax3(s[12], s[13], s[14]);
+            sa5 = __builtin_fmaxf(s[15], sa0);
+        } else if (k == 3) {
+            mt = fmax3(fmax3(sa1, sa2, sa3), sa4, sa5);
+        } else if (k == 4) {
+            mt = max_pair(mt);
+        } else if (k == 5) {
+            const float m_tile = __builtin_fmaxf(mt * sl2, -1.0e30f);
+            grow = m_tile > m_run + kGrowLog2;
+            m_new = grow ? m_tile : m_run;
+        } else if (k == 6) {
+            alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            neg_m = -m_run;
+        } else if (k >= 7 && k < 23) {
+            const int j = k - 7;
+            const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], sl2, neg_m));
+            if (j % 2 == 0) {
+                x_even = x;
+            } else {
+                pf[j / 8][j % 8 - 1] = (_Float16)x_even;
+                pf[j / 8][j % 8] = (_Float16)x;
+            }
+        } else if (k >= 23 && k < 27) {
+            const int kk = (k - 23) / 2, o = 4 * ((k - 23) % 2);
+            const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+            ls0 = __builtin_amdgcn_fdot2(f16x2{pf[kk][o], pf[kk][o + 1]}, one, ls0, false);
+            ls1 = __builtin_amdgcn_fdot2(f16x2{pf[kk][o + 2], pf[kk][o + 3]}, one, ls1, false);
+        } else if (k == 27) {
+            l_run = l_run * alpha + (ls0 + ls1);
+            ls0 = ls1 = 0.0f;
         }
     };
 
     // acc_o *= alpha in place in the accumulation registers (rare: the
-    // running maximum of some head grew by more than 2^8)
-    auto rescale = [&](float alpha) {
-        // the last matrix-core writes of acc_o are a tile back; wait out the
-        // longest result latency anyway before reading them
+    // running maximum of some head grew by more than 2^8).  Inside the loop
+    // the last value products were issued a whole score loop earlier; after
+    // it they were just issued, and `fresh` waits out their result latency
+    // (the wait states here are inline assembly, which the compiler's
+    // hazard tracking does not cover).
+    auto rescale = [&](float a, bool fresh) __attribute__((always_inline)) {
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        if (fresh)
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float x = acc_o[db][r];
-                scale_agpr(x, alpha);
+                scale_agpr(x, a);
                 acc_o[db][r] = x;
             }
         }
         asm volatile("s_nop 4" ::: "memory");
     };
 
-    // Software pipeline: iteration t computes tile t's score partials on the
-    // matrix cores while the vector units finish tile t-1's softmax, then
-    // tile t-1's value product.  A barrier in the middle (every wave is past
-    // its read of the exchange and of tile t-1's stage) lets tile t's
-    // partials be published and tile t + STAGES - 1 be loaded into that
-    // stage; the barrier at the end publishes the partials and makes tile
-    // t+1 visible.
-    auto wait_tiles_beyond = [&](int n) {   // all but the n newest tiles landed
-        if (n >= 2)
-            wait_vmcnt<2 * LD>();
-        else if (n == 1)
-            wait_vmcnt<LD>();
-        else
-            wait_vmcnt<0>();
-    };
-    constexpr int AHEAD = STAGES - 1;        // tiles in flight beyond the one computed
     if (tiles > 0) {
-        for (int t = 0; t < AHEAD && t < tiles; ++t)
-            issue(t);
-        wait_tiles_beyond(tiles - 1 < AHEAD - 1 ? tiles - 1 : AHEAD - 1);
-        block_barrier();                      // tile 0 visible
-        f32x16 prev = scores(0);
-        publish(prev);
-        if (tiles > 1)
-            wait_tiles_beyond(tiles - 2 < AHEAD - 2 ? tiles - 2 : AHEAD - 2);
-        block_barrier();                      // partials 0 published, tile 1 visible
-        if (tiles > AHEAD)
-            issue(AHEAD);
-        for (int t = 1; t < tiles; ++t) {
-            // the partner's partials are read first and tile t's products
-            // issued next; tile t-1's softmax fills the gaps between them
-            complete(t - 1, prev, false);
-            const f32x16 cur = scores(t);
-            f16x8 pf[2];
-            float alpha;
-            bool grow;
-            softmax_block(prev, pf, m_run, l_run, sl2, alpha, grow);
-            // the probabilities are needed here, before the rare rescale
-            // branch, so they are computed beside tile t's products
-            asm volatile("" ::"v"(pf[0]), "v"(pf[1]));
-            if (__builtin_amdgcn_ballot_w64(grow))
-                rescale(alpha);
-            values(t - 1, pf);
-            block_barrier();                  // exchange read, tile t-1's stage free
-            publish(cur);
-            if (t + AHEAD < tiles)
-                issue(t + AHEAD);
-            prev = cur;
-            if (t + 1 < tiles) {
-                const int last = t + AHEAD < tiles ? t + AHEAD : tiles - 1;
-                wait_tiles_beyond(last - (t + 1));   // tile t+1 landed
-            }
-            block_barrier();                  // partials t published, tile t+1 visible
+        // tiles 0, 1 and 2 go to stages 0-2; tile t + 2 is loaded beside the
+        // score products of tile t, into the stage tile t - 2 left
+        // (every tile slot issues its loads, so the counts below are fixed)
+        for (int t = 0; t < 3; ++t) {
+            const i32x4 rs = tile_rsrc(t);
+#pragma unroll
+            for (int i = 0; i < LD; ++i)
+                dma(rs, t, i);
         }
-        complete(tiles - 1, prev, true);
-        f16x8 pf[2];
-        float alpha;
-        bool grow;
-        softmax_block(prev, pf, m_run, l_run, sl2, alpha, grow);
+        wait_vmcnt<2 * LD>();
+        block_barrier();                      // tile 0 visible
+
+        // raw scores of the newest tile; only the range's last tile can be
+        // partial
+        f32x16 s = f32x16{};
+        auto mask_last = [&](int t) __attribute__((always_inline)) {
+            const int64_t k0 = kbeg + (int64_t)t * BK;
+            if (t == tiles - 1 && k0 + BK > kend) {
+                f32x16 sm[1] = {s};
+                mask_tile<1>(sm, (int)(kend - k0), hi);
+                s = sm[0];
+            }
+        };
+        // carried from one tile to the next: the first KA K fragments of the
+        // next tile, the V fragments of the last VA value products and the
+        // probabilities those use
+        f16x8 kn[KA], vt[VA], pv[2];
+        {
+            const lds_u16 *Ks = stage(0);
+            f16x8 kf[DS], qv[DS - DN];
+#pragma unroll
+            for (int ds = 0; ds < KA; ++ds)
+                kf[ds] = kread(Ks, ds);
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds) {
+                if (ds + KA < DS)
+                    kf[ds + KA] = kread(Ks, ds + KA);
+                if (ds + KA >= DN && ds + KA < DS)
+                    qv[ds + KA - DN] = qread(ds + KA);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ds], ds < DN ? qf[ds] : qv[ds - DN], s,
+                                                          0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            mask_last(0);
+#pragma unroll
+            for (int k = 0; k < DS; ++k)
+                sm_step(s, k);
+        }
+        if (tiles > 1) {
+            wait_vmcnt<LD>();
+            block_barrier();                  // tile 1 visible
+            const lds_u16 *Ks = stage(1);
+#pragma unroll
+            for (int ds = 0; ds < KA; ++ds)
+                kn[ds] = kread(Ks, ds);
+        }
+        for (int t = 1; t < tiles; ++t) {
+            const lds_u16 *Ks = stage(t);
+            const lds_u16 *Vs = stage(t - 1);
+            const i32x4 rs = tile_rsrc(t + 2);
+            f16x8 kf[DS], qv[DS - DN], vf[NV];
+#pragma unroll
+            for (int ds = 0; ds < KA; ++ds)
+                kf[ds] = kn[ds];
+            // tile t's scores beside tile t+2's loads; the last products
+            // also fetch tile t-1's first V fragments
+            s = f32x16{};
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds) {
+                if (ds + KA < DS)
+                    kf[ds + KA] = kread(Ks, ds + KA);
+                if (ds + KA >= DN && ds + KA < DS)
+                    qv[ds + KA - DN] = qread(ds + KA);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ds], ds < DN ? qf[ds] : qv[ds - DN], s,
+                                                          0, 0, 0);
+                if (ds < LD)
+                    dma(rs, t + 2, ds);
+                if (ds >= DS - VA)
+                    vf[ds - (DS - VA)] = vread(Vs, ds - (DS - VA));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // tile t-1's probabilities, before tile t's softmax replaces them;
+            // its running maximum raised the output's scale if `grow`
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                pv[kk] = pf[kk];
+            if (__builtin_amdgcn_ballot_w64(grow))
+                rescale(alpha, false);
+            mask_last(t);
+            // tile t-1's value products, all but the last VA, beside tile
+            // t's softmax
+#pragma unroll
+            for (int i = 0; i < NV - VA; ++i) {
+                vf[i + VA] = vread(Vs, i + VA);
+                acc_o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[i], pv[i / DB],
+                                                                       acc_o[i % DB], 0, 0, 0);
+                sm_step(s, i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int k = NV - VA; k < DS; ++k)
+                sm_step(s, k);
+#pragma unroll
+            for (int i = 0; i < VA; ++i)
+                vt[i] = vf[NV - VA + i];
+            if (t + 1 < tiles) {
+                wait_vmcnt<LD>();             // tile t+1 landed
+                block_barrier();              // tile t-1's stage free, tile t+1 visible
+                const lds_u16 *Kn = stage(t + 1);
+#pragma unroll
+                for (int ds = 0; ds < KA; ++ds)
+                    kn[ds] = kread(Kn, ds);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int i = NV - VA; i < NV; ++i)
+                acc_o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vt[i - (NV - VA)], pv[i / DB],
+                                                                       acc_o[i % DB], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // the last tile's value products
         if (__builtin_amdgcn_ballot_w64(grow))
-            rescale(alpha);
-        values(tiles - 1, pf);
+            rescale(alpha, true);
+        const lds_u16 *Vs = stage(tiles - 1);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const f16x8 v = vread(Vs, i);
+            acc_o[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v, pf[i / DB], acc_o[i % DB],
+                                                                   0, 0, 0);
+        }
     }
     wait_vmcnt<0>();
 
@@ -837,10 +914,9 @@ mla_decode_kernel(MlaArgs p)
     const float l_all = l_run + __shfl_xor(l_run, 32);
     if (!live)
         return;
-    const int d0 = e * (kMlaDl / NQ);
     if (p.splits == 1) {
         const float inv = l_all > 0.0f ? 1.0f / l_all : 0.0f;
-        uint16_t *orow = p.O + (b * p.H + h) * kMlaDl + d0;
+        uint16_t *orow = p.O + (b * p.H + h) * kMlaDl;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -855,7 +931,7 @@ mla_decode_kernel(MlaArgs p)
         return;
     }
     const int64_t slot = (b * p.H + h) * p.splits + sp;
-    float *po = p.part + slot * kMlaDl + d0;
+    float *po = p.part + slot * kMlaDl;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -866,7 +942,7 @@ mla_decode_kernel(MlaArgs p)
                        acc_o[db][4 * g + 3]};
         }
     }
-    if (hi == 0 && e == 0) {
+    if (hi == 0) {
         float2 *ml = reinterpret_cast<float2 *>(p.part + p.B * p.H * p.splits * kMlaDl);
         ml[slot] = float2{m_run, l_all};
     }
@@ -922,8 +998,7 @@ hipError_t launch_mla_decode(const MlaArgs &p, hipStream_t stream)
     // the host has checked that the grid fits 2^31 workgroups
     const int64_t nhb = (p.H + kMlaHeadsPerBlock - 1) / kMlaHeadsPerBlock;
     const int64_t units = (p.B * p.splits + 7) / 8 * 8;
-    using C = mla::Cfg<2>;
-    hipLaunchKernelGGL(mla_decode_kernel<C>, dim3((unsigned)(units * nhb)), dim3(64 * C::NW), 0,
+    hipLaunchKernelGGL(mla_decode_kernel, dim3((unsigned)(units * nhb)), dim3(64 * mla::NW), 0,
                        stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1)

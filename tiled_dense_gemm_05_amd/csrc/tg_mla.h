@@ -24,7 +24,7 @@ struct MlaArgs {
     int splits;
     int64_t keys_per_split;
 };
-constexpr int kMlaDl = 512, kMlaDr = 64, kMlaHeadsPerBlock = 64;
+constexpr int kMlaDl = 512, kMlaDr = 64, kMlaHeadsPerBlock = 128;
 hipError_t launch_mla_decode(const MlaArgs &p, hipStream_t stream);
 
 }  // namespace tg
