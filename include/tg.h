@@ -271,8 +271,10 @@ int tg_gemm_relu_f16_splitk_noalloc(const void *A, const void *B, void *C, int64
  *     owned by the caller, used as scratch by this call only (it must not be
  *     shared by calls that may overlap).  With fewer sequences than the chip
  *     has compute units the keys of each sequence are split into ranges whose
- *     fp32 partial results live there; tg_mla_decode_workspace_bytes gives
- *     the size the call would use.  A smaller (or no) workspace is accepted
+ *     partial results live there (each range's output divided by its own
+ *     sum, as fp16, with its fp32 maximum and sum: 1032 bytes per sequence,
+ *     head and range); tg_mla_decode_workspace_bytes gives the size the call
+ *     would use.  A smaller (or no) workspace is accepted
  *     and only lowers the number of ranges (results stay within the same
  *     accuracy; the same workspace size gives the same bits).
  * Scores and sums are fp32, probabilities enter the value product as fp16.

@@ -242,7 +242,7 @@ def test_mla_decode_validation(tg):
 
 def test_mla_workspace_sizes(tg):
     ws = tg.tg_mla_decode_workspace_bytes
-    per = lambda B, H: B * H * (512 + 2) * 4   # one key range: fp32 outputs, maximum and sum
+    per = lambda B, H: B * H * (512 * 2 + 8)   # one key range: fp16 outputs, fp32 maximum and sum
     # 64 sequences of 128 heads: 64 workgroups of 128 heads, four ranges fill 256 CUs
     assert ws(64, 128, 8192) == 4 * per(64, 128)
     # one sequence: as many ranges as give each CU a workgroup, at least 8 tiles of 32 each

@@ -5,9 +5,11 @@ Tolerance, from the kernel's arithmetic (as for the attention forward):
 scores and sums are fp32, each probability is rounded to fp16 before the
 value product (relative error <= 2^-11, so the output moves by at most
 2^-11 * max|V| from the probabilities and as much again from the normalizer);
-the key ranges' fp32 partials are combined with fp32 weights; the output is
-rounded to fp16 once: |O_gpu - O_ref| <= 2^-9 * max|V| + ulp16(O_ref), V the
-latent parts of the visible rows.
+with several key ranges each range's normalised output (a convex combination
+of cached values, so at most max|V| in size) is rounded to fp16, at most
+2^-11 * max|V| more, and the ranges are combined with fp32 weights; the
+output is rounded to fp16 once: |O_gpu - O_ref| <= 2^-9 * max|V| +
+ulp16(O_ref), V the latent parts of the visible rows.
 """
 
 import math

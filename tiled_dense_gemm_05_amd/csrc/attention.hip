@@ -529,9 +529,10 @@ hipError_t launch_attn(const AttnArgs &p, hipStream_t stream)
 //    products, whose operands are already in registers, so the next tile's
 //    first K reads run under them.
 //  * When the sequences are too few to fill the chip the keys are split
-//    into ranges (flash-decoding); each range writes its unnormalised fp32
-//    output with its running maximum and sum, and a combine kernel rescales
-//    and adds the ranges in a fixed order, so results are deterministic.
+//    into ranges (flash-decoding); each range writes its output normalised
+//    by its own sum as fp16 (half the bytes of an fp32 partial) with its
+//    running maximum and sum, and a combine kernel reweights and adds the
+//    ranges in a fixed order, so results are deterministic.
 namespace mla {
 constexpr int D = kMlaDl + kMlaDr;          // 576 values per cached row
 constexpr int BK = 32;                      // cached rows per tile
@@ -716,41 +717,52 @@ mla_decode_kernel(MlaArgs p)
         if (k == 0) {
             sa0 = fmax3(s[0], s[1], s[2]);
             sa1 = fmax3(s[3], s[4], s[5]);
+            asm volatile("" ::"v"(sa0), "v"(sa1));
         } else if (k == 1) {
             sa2 = fmax3(s[6], s[7], s[8]);
             sa3 = fmax3(s[9], s[10], s[11]);
+            asm volatile("" ::"v"(sa2), "v"(sa3));
         } else if (k == 2) {
             sa4 = fmax3(s[12], s[13], s[14]);
             sa5 = __builtin_fmaxf(s[15], sa0);
+            asm volatile("" ::"v"(sa4), "v"(sa5));
         } else if (k == 3) {
             mt = fmax3(fmax3(sa1, sa2, sa3), sa4, sa5);
+            asm volatile("" ::"v"(mt));
         } else if (k == 4) {
             mt = max_pair(mt);
+            asm volatile("" ::"v"(mt));
         } else if (k == 5) {
             const float m_tile = __builtin_fmaxf(mt * sl2, -1.0e30f);
             grow = m_tile > m_run + kGrowLog2;
             m_new = grow ? m_tile : m_run;
+            asm volatile("" ::"v"(m_new));
         } else if (k == 6) {
             alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             m_run = m_new;
             neg_m = -m_run;
+            asm volatile("" ::"v"(alpha), "v"(neg_m));
         } else if (k >= 7 && k < 23) {
             const int j = k - 7;
             const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], sl2, neg_m));
             if (j % 2 == 0) {
                 x_even = x;
+                asm volatile("" ::"v"(x_even));
             } else {
                 pf[j / 8][j % 8 - 1] = (_Float16)x_even;
                 pf[j / 8][j % 8] = (_Float16)x;
+                asm volatile("" ::"v"(pf[j / 8]));
             }
         } else if (k >= 23 && k < 27) {
             const int kk = (k - 23) / 2, o = 4 * ((k - 23) % 2);
             const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
             ls0 = __builtin_amdgcn_fdot2(f16x2{pf[kk][o], pf[kk][o + 1]}, one, ls0, false);
             ls1 = __builtin_amdgcn_fdot2(f16x2{pf[kk][o + 2], pf[kk][o + 3]}, one, ls1, false);
+            asm volatile("" ::"v"(ls0), "v"(ls1));
         } else if (k == 27) {
             l_run = l_run * alpha + (ls0 + ls1);
             ls0 = ls1 = 0.0f;
+            asm volatile("" ::"v"(l_run));
         }
     };
 
@@ -930,33 +942,40 @@ mla_decode_kernel(MlaArgs p)
         }
         return;
     }
+    // a key range's partial: its output normalised by its own sum, rounded
+    // to fp16 (a convex combination of cached values, so within their
+    // range), with its running maximum and sum
     const int64_t slot = (b * p.H + h) * p.splits + sp;
-    float *po = p.part + slot * kMlaDl;
+    uint16_t *po = static_cast<uint16_t *>(p.part) + slot * kMlaDl;
+    const float inv = l_all > 0.0f ? 1.0f / l_all : 0.0f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int d = db * 32 + 8 * g + 4 * hi;
-            *reinterpret_cast<float4 *>(po + d) =
-                float4{acc_o[db][4 * g + 0], acc_o[db][4 * g + 1], acc_o[db][4 * g + 2],
-                       acc_o[db][4 * g + 3]};
+            u32x2 w;
+            w.x = epi_pack2<false>(acc_o[db][4 * g + 0] * inv, acc_o[db][4 * g + 1] * inv, false);
+            w.y = epi_pack2<false>(acc_o[db][4 * g + 2] * inv, acc_o[db][4 * g + 3] * inv, false);
+            *reinterpret_cast<u32x2 *>(po + d) = w;
         }
     }
     if (hi == 0) {
-        float2 *ml = reinterpret_cast<float2 *>(p.part + p.B * p.H * p.splits * kMlaDl);
+        float2 *ml = reinterpret_cast<float2 *>(static_cast<uint16_t *>(p.part) +
+                                                p.B * p.H * p.splits * kMlaDl);
         ml[slot] = float2{m_run, l_all};
     }
 }
 
-// Combines the key ranges of one (sequence, head): O = sum_s 2^(m_s - M) O_s
-// / sum_s 2^(m_s - M) l_s with M the largest range maximum, ranges added in
-// order; thread t owns output values 4t .. 4t + 3.
+// Combines the key ranges of one (sequence, head): with M the largest range
+// maximum and w_s = 2^(m_s - M) l_s, O = sum_s w_s o_s / sum_s w_s, ranges
+// added in order; thread t owns output values 4t .. 4t + 3.
 __global__ void __launch_bounds__(kMlaDl / 4) mla_combine_kernel(MlaArgs p)
 {
     const int64_t bh = blockIdx.x;
     const int d = threadIdx.x * 4;
     const int S = p.splits;
-    const float2 *ml = reinterpret_cast<const float2 *>(p.part + p.B * p.H * S * kMlaDl) + bh * S;
+    const uint16_t *part = static_cast<const uint16_t *>(p.part);
+    const float2 *ml = reinterpret_cast<const float2 *>(part + p.B * p.H * S * kMlaDl) + bh * S;
     float M = -1.0e30f;
     for (int s = 0; s < S; ++s)
         M = __builtin_fmaxf(M, ml[s].x);
@@ -964,13 +983,13 @@ __global__ void __launch_bounds__(kMlaDl / 4) mla_combine_kernel(MlaArgs p)
     float4 acc = float4{0.0f, 0.0f, 0.0f, 0.0f};
     for (int s = 0; s < S; ++s) {
         const float2 v = ml[s];
-        const float w = __builtin_amdgcn_exp2f(v.x - M);
-        L += w * v.y;
-        const float4 o = *reinterpret_cast<const float4 *>(p.part + (bh * S + s) * kMlaDl + d);
-        acc.x += w * o.x;
-        acc.y += w * o.y;
-        acc.z += w * o.z;
-        acc.w += w * o.w;
+        const float w = __builtin_amdgcn_exp2f(v.x - M) * v.y;
+        L += w;
+        const u32x2 o = *reinterpret_cast<const u32x2 *>(part + (bh * S + s) * kMlaDl + d);
+        acc.x += w * bits_to_float<false>((uint16_t)(o.x & 0xffff));
+        acc.y += w * bits_to_float<false>((uint16_t)(o.x >> 16));
+        acc.z += w * bits_to_float<false>((uint16_t)(o.y & 0xffff));
+        acc.w += w * bits_to_float<false>((uint16_t)(o.y >> 16));
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     u32x2 out;

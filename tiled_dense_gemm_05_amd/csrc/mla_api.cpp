@@ -29,7 +29,8 @@ constexpr int64_t kMlaCUs = 256;
 
 static int64_t mla_bytes_per_split(int64_t batch, int64_t heads)
 {
-    return batch * heads * (tg::kMlaDl + 2) * (int64_t)sizeof(float);
+    // per (sequence, head): 512 fp16 values and an fp32 (maximum, sum) pair
+    return batch * heads * (tg::kMlaDl * 2 + 2 * (int64_t)sizeof(float));
 }
 
 static int64_t mla_splits(int64_t batch, int64_t heads, int64_t seq_k, int64_t workspace_bytes)
@@ -108,7 +109,7 @@ int tg_mla_decode_f16(const void *Q, const void *KV, void *O, const int32_t *seq
     p.KV = static_cast<const uint16_t *>(KV);
     p.O = static_cast<uint16_t *>(O);
     p.seqlens = seqlens;
-    p.part = static_cast<float *>(workspace);
+    p.part = workspace;
     p.B = batch; p.H = heads; p.Sk = seq_k;
     p.scale = scale;
     const int64_t s = mla_splits(batch, heads, seq_k, workspace_bytes);

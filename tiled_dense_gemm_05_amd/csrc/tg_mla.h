@@ -11,14 +11,15 @@ namespace tg {
 // over the first n_b cached rows (n_b = seqlens[b] clamped to [0, Sk], or Sk
 // without seqlens).  Q (B, H, 576), KV (B, Sk, 576), O (B, H, 512) fp16,
 // contiguous.  With splits > 1 the keys of a sequence are cut into `splits`
-// ranges of keys_per_split (a multiple of 64) and each range writes an
-// unnormalised fp32 partial to `part` (B * H * splits * 512 floats, then
-// B * H * splits (maximum, sum) pairs), which a second kernel combines.
+// ranges of keys_per_split (a multiple of 32) and each range writes a
+// partial to `part`: B * H * splits rows of 512 fp16 values (the range's
+// output divided by its own sum of exponentials), then B * H * splits
+// fp32 (maximum, sum) pairs, which a second kernel combines.
 struct MlaArgs {
     const uint16_t *Q, *KV;
     uint16_t *O;
     const int32_t *seqlens;
-    float *part;
+    void *part;
     int64_t B, H, Sk;
     float scale;
     int splits;
