@@ -14,6 +14,9 @@ tile, K tile, stage count, swizzle, wave grid or whether loads go through
 registers or straight to LDS; trailing zero steps add exact zeros.  So their
 outputs must be bitwise identical, and the same holds inside each group of
 two-K-group configurations that deal the same K tiles to each group.  The
+configurations built on 16x16x32 products (32-wide k steps) are in the same
+set: on this part a 32-wide product step gives the bits of its two 16-wide
+halves taken in order, which this test checks along with the races.  The
 comparison runs without the activation, so negative outputs are compared too.
 One output of each set is gated against the oracle.
 """
@@ -33,13 +36,13 @@ torch = pytest.importorskip("torch")
 DTYPES = {"f16": 0, "bf16": 1}
 LAYOUTS = {"kn": 0, "nk": 1}
 
-# one K group (any tile / stages / swizzle / waves), the register-staged kernels
-# (and, below, the any-layout and ragged-layout kernels)
-KG1 = [c for c in range(32) if c not in (14, 15, 16, 20)] + [100, 101]
+# one K group (any tile / stages / swizzle / waves / product shape), the
+# register-staged kernels (and, below, the any-layout and ragged-layout kernels)
+KG1 = [c for c in range(35) if c not in (14, 15, 16, 20)] + [100, 101]
 # two K groups: K tiles of 64 (configs 14, 20) or of 32 (15, 16) dealt alternately
 KG2_GROUPS = [[14, 20], [15, 16]]
 # configurations that exist for bf16 elements and an (N,K) B
-MODE_KG1 = [8, 29, 12]
+MODE_KG1 = [8, 29, 12, 32, 34]
 
 
 def say(*a):

@@ -16,8 +16,10 @@ std::atomic<int> g_last_path{TG_PATH_AUTO};
 std::atomic<int> g_tile_variant{-1};
 
 // Default direct-to-LDS configurations of the tile paths.
-constexpr int kTile128Default = 29;  // 128x128x64, 4 stages, 8 waves (4x2, 32x64 wave tiles)
-constexpr int kTile256Default = 8;   // 256x256x64, 2 stages, 8 waves (2 per SIMD)
+// 128x128x64, 4 stages, 8 waves (4x2, 32x64 wave tiles), 16x16x32 products
+constexpr int kTile128Default = 34;
+// 256x256x64, 2 stages, 8 waves (2 per SIMD), 16x16x32 products
+constexpr int kTile256Default = 32;
 constexpr int kTile128ShortK = 12;   // 128x128x32, 2 stages, 4 waves/SIMD: several workgroups per CU
 constexpr int kTile64 = 20;          // 64x64x64, 4 stages, two K groups: grids with few tiles
 constexpr int kRegStaged128 = 100;   // register-staged kernels, kept for comparison

@@ -36,6 +36,8 @@
 //    consecutive columns of a C row), transpose reads of the row-major B
 //    (ds_read_b64_tr_b16), the swizzles, the XCD-aware tile order and the
 //    epilogue are shared with the register-staged kernel.
+#include <type_traits>
+
 #include "tg_internal.h"
 #include "tg_lds_dma.h"
 
@@ -47,6 +49,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -61,16 +64,22 @@ using dma::make_rsrc;
 using dma::wait_vmcnt;
 
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int OCC_ = 1, int KG_ = 1,
-          bool SWZ_ = true>
+          bool SWZ_ = true, int MI_ = 32>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, STAGES = STAGES_;
+    // matrix-core product: 32 (v_mfma_f32_32x32x16, 16-wide k steps) or 16
+    // (v_mfma_f32_16x16x32, 32-wide k steps)
+    static constexpr int MI = MI_;
+    static constexpr int KSTEP = MI == 16 ? 32 : 16;
+    using Acc = typename std::conditional<MI == 16, f32x4, f32x16>::type;
+    static_assert(MI == 16 || MI == 32, "product shape");
     static constexpr int OCC = OCC_;                  // waves per SIMD the registers must allow
     static constexpr int KG = KG_;                    // K groups: wave groups on alternate K tiles
     static constexpr bool SWZ = SWZ_;                 // XOR-swizzled operand tiles (off: ablation)
     static constexpr int NW = WM * WN;                // waves per K group
     static constexpr int NT = 64 * NW * KG;           // threads
     static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
-    static constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 fragments per wave
+    static constexpr int FM = TM / MI, FN = TN / MI;  // MIxMI fragments per wave
     static constexpr int CA = BK / 8, CB = BN / 8;    // 16-byte chunks per tile row
     static constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BN;
     static constexpr int STAGE = A_ELEMS + B_ELEMS;   // fp16 elements per stage
@@ -79,7 +88,7 @@ struct Cfg {
     static constexpr int LOADS = A_LD + B_LD;
     static constexpr int A_RPB = 64 / CA;             // tile rows per 1 KiB block
     static constexpr int B_RPB = 64 / CB;
-    static constexpr int KSTEPS = BK / 16;
+    static constexpr int KSTEPS = BK / KSTEP;
     static constexpr int READS = FM + 2 * FN;         // LDS reads per k step
     // With 3+ stages the loads of tile kt+STAGES-1 are spread evenly over the
     // k steps of tile kt (DPS per step); with 2 stages the only free stage is
@@ -93,7 +102,7 @@ struct Cfg {
     static_assert(!SPREAD || LOADS % KSTEPS == 0, "loads per k step");
     static_assert((A_ELEMS / 512) % NW == 0 && (B_ELEMS / 512) % NW == 0, "blocks per wave");
     static_assert(CA <= 16 && CB <= 64 && 64 % CA == 0 && 64 % CB == 0, "rows per block");
-    static_assert(TM % 32 == 0 && TN % 32 == 0 && BK % 16 == 0, "fragment shape");
+    static_assert(TM % MI == 0 && TN % MI == 0 && BK % KSTEP == 0, "fragment shape");
     static_assert(LOADS * (STAGES - 1) <= 63, "vmcnt range");
     static_assert(KSTEPS <= 4, "k steps per tile");
     static constexpr int RING = KG * STAGES * STAGE * 2;        // bytes of LDS rings
@@ -104,6 +113,9 @@ struct Cfg {
     static_assert(LDS <= 160 * 1024, "LDS size");
     // a thread's loads of one tile share one swizzled column (see load plan)
     static_assert((NW * A_RPB) % 16 == 0 && (NW * B_RPB) % 4 == 0, "swizzle period");
+    // the (K,N) B swizzle that also separates rows 8 apart needs a thread's
+    // rows to be 16 apart
+    static constexpr int BSWZ = MI == 16 && (NW * B_RPB) % 16 == 0 ? 16 : 32;
 };
 
 // Element type and B layout of a configuration.  MODE bit 0: bf16 elements
@@ -128,11 +140,17 @@ __device__ __forceinline__ int swz_a(int row, int c)
     return c ^ ((row / rows_per_line) % CA);
 }
 
-template <int CB, bool ON = true>
+// (K,N) B rows: a transpose read fetches 4 consecutive rows x 2 chunks per
+// 16-lane group, so rows k .. k+3 move to different quarters of the bank line.
+// With 16x16x32 products the two groups a read serves at once take rows 8
+// apart at the same columns: bit 3 of the row also moves the chunk by 2.
+template <int CB, bool ON = true, int MI = 32>
 __device__ __forceinline__ int swz_b(int k, int c)
 {
     if constexpr (!ON)
         return c;
+    else if constexpr (CB >= 16 && MI == 16)
+        return c ^ ((k & 3) << 2) ^ (((k >> 3) & 1) << 1);
     else if constexpr (CB >= 16)
         return c ^ ((k & 3) << 2);
     else if constexpr (CB == 8)
@@ -167,26 +185,31 @@ __device__ __forceinline__ void read_piece(const lds_u16 *As, const lds_u16 *Bs,
                                            int wn, int lane, f16x8 (&af)[T::FM],
                                            s16x4 (&bh)[T::FN][2])
 {
+    // a fragment row is lane % MI; its 8 k are chunk lane / MI of the k step
+    constexpr int LR = T::MI - 1, LS = T::MI == 16 ? 4 : 5;
     if constexpr (r < T::FM) {
-        const int row = wm * T::TM + r * 32 + (lane & 31);
-        const int c = kk * 2 + (lane >> 5);
+        const int row = wm * T::TM + r * T::MI + (lane & LR);
+        const int c = kk * (T::KSTEP / 8) + (lane >> LS);
         const int ca = swz_a<T::CA, T::SWZ>(row, c);
         af[r] = *reinterpret_cast<const lds_f16x8 *>(As + row * T::BK + ca * 8);
     } else if constexpr (T::BT) {
         // (N,K) B: the fragment is one 16-byte read of a B^T row, like A's
         constexpr int fn = r - T::FM;
-        const int row = wn * T::TN + fn * 32 + (lane & 31);
-        const int c = kk * 2 + (lane >> 5);
+        const int row = wn * T::TN + fn * T::MI + (lane & LR);
+        const int c = kk * (T::KSTEP / 8) + (lane >> LS);
         const int cb = swz_a<T::CA, T::SWZ>(row, c);
         const s16x8 v = *reinterpret_cast<const __attribute__((address_space(3))) s16x8 *>(
             Bs + row * T::BK + cb * 8);
         bh[fn][0] = __builtin_shufflevector(v, v, 0, 1, 2, 3);
         bh[fn][1] = __builtin_shufflevector(v, v, 4, 5, 6, 7);
     } else {
+        // a 32-wide fragment takes two 16-column blocks (lane bit 4), a
+        // 16-wide one the lane's 16-lane group's 8 k (lane / 16)
         constexpr int fn = (r - T::FM) / 2, hh = (r - T::FM) % 2;
-        const int k = kk * 16 + 8 * (lane >> 5) + 4 * hh + ((lane & 15) >> 2);
-        const int n = wn * T::TN + fn * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        const lds_u16 *src = Bs + k * T::BN + swz_b<T::CB, T::SWZ>(k, n >> 3) * 8 + (n & 7);
+        const int k = kk * T::KSTEP + 8 * (lane >> LS) + 4 * hh + ((lane & 15) >> 2);
+        const int n = wn * T::TN + fn * T::MI + (T::MI == 32 ? 16 * ((lane >> 4) & 1) : 0) +
+                      4 * (lane & 3);
+        const lds_u16 *src = Bs + k * T::BN + swz_b<T::CB, T::SWZ, T::BSWZ>(k, n >> 3) * 8 + (n & 7);
         bh[fn][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src);
     }
 }
@@ -211,16 +234,24 @@ __device__ __forceinline__ void join_b(const s16x4 (&bh)[T::FN][2], f16x8 (&bf)[
                                     __builtin_shufflevector(bh[fn][0], bh[fn][1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// One 32x32x16 matrix-core product in the configuration's element type (the
-// fragments hold raw 16-bit patterns either way).
+// One matrix-core product (32x32x16 or 16x16x32) in the configuration's
+// element type (the fragments hold raw 16-bit patterns either way).
 template <class T>
-__device__ __forceinline__ f32x16 mfma32(const f16x8 &b, const f16x8 &a, const f32x16 &c)
+__device__ __forceinline__ typename T::Acc mfma32(const f16x8 &b, const f16x8 &a,
+                                                  const typename T::Acc &c)
 {
-    if constexpr (T::BF16)
+    if constexpr (T::MI == 16) {
+        if constexpr (T::BF16)
+            return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b),
+                                                           __builtin_bit_cast(bf16x8, a), c, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a, c, 0, 0, 0);
+    } else if constexpr (T::BF16) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b),
                                                        __builtin_bit_cast(bf16x8, a), c, 0, 0, 0);
-    else
+    } else {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c, 0, 0, 0);
+    }
 }
 
 // Everything a thread needs to issue its loads of one tile.
@@ -256,7 +287,7 @@ __device__ __forceinline__ void issue_one(const LoadPlan<T> &lp, const i32x4 &ra
 // tile and the LDS reads of the next fragments (k step kkn of As/Bs) placed
 // between them in program order: MFMA i is followed by load D0 + i and read i.
 template <class T, int D0, int D1, int I = 0>
-__device__ __forceinline__ void step(f32x16 (&acc)[T::FM][T::FN], const f16x8 (&af)[T::FM],
+__device__ __forceinline__ void step(typename T::Acc (&acc)[T::FM][T::FN], const f16x8 (&af)[T::FM],
                                      const f16x8 (&bf)[T::FN], const LoadPlan<T> &lp,
                                      const i32x4 &ra, const i32x4 &rb, bool a_kok, int b_rows_left,
                                      uint32_t stage_addr, int wave, const lds_u16 *As,
@@ -283,7 +314,7 @@ __device__ __forceinline__ void step(f32x16 (&acc)[T::FM][T::FN], const f16x8 (&
 // The k steps 0 .. KSTEPS-2 of a tile: step kk works on fragment set kk & 1,
 // reads set (kk+1) & 1 and issues loads kk*DPS .. (kk+1)*DPS-1.
 template <class T, int KK = 0>
-__device__ __forceinline__ void inner_steps(f32x16 (&acc)[T::FM][T::FN], f16x8 (&af)[2][T::FM],
+__device__ __forceinline__ void inner_steps(typename T::Acc (&acc)[T::FM][T::FN], f16x8 (&af)[2][T::FM],
                                             f16x8 (&bf)[2][T::FN], const LoadPlan<T> &lp,
                                             const i32x4 &ra, const i32x4 &rb, bool a_kok,
                                             int b_rows_left, uint32_t stage_addr, int wave,
@@ -366,7 +397,7 @@ gemm_relu_dma_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
         }
     } else {
         const int r0 = wave * T::B_RPB + lane / T::CB;
-        const int c = swz_b<T::CB, T::SWZ>(r0, lane % T::CB);
+        const int c = swz_b<T::CB, T::SWZ, T::BSWZ>(r0, lane % T::CB);
         lp.b_row0 = r0;
         lp.b_kcol = 0;
         const bool col_ok = n0 + c * 8 < N;
@@ -391,12 +422,12 @@ gemm_relu_dma_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
         return (int)(r < 0 ? 0 : (r > T::BK ? T::BK : r));
     };
 
-    f32x16 acc[T::FM][T::FN];
+    typename T::Acc acc[T::FM][T::FN];
 #pragma unroll
     for (int fm = 0; fm < T::FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < T::FN; ++fn)
-            acc[fm][fn] = f32x16{};
+            acc[fm][fn] = typename T::Acc{};
 
     // every group runs the same number of tiles (a group past the end of K
     // loads zeros) so that the workgroup barriers line up
@@ -452,8 +483,8 @@ gemm_relu_dma_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
         // Groups 1 .. KG-1 hand their partial sums to group 0 through LDS;
         // group 0 adds them in group order (deterministic).
         block_barrier();
-        typedef __attribute__((address_space(3))) f32x16 lds_f32x16;
-        lds_f32x16 *part = (lds_f32x16 *)smem;
+        typedef __attribute__((address_space(3))) typename T::Acc lds_acc;
+        lds_acc *part = (lds_acc *)smem;
         if (kg > 0) {
 #pragma unroll
             for (int fm = 0; fm < T::FM; ++fm)
@@ -482,18 +513,23 @@ gemm_relu_dma_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
     lds_u16 *cst = (lds_u16 *)smem;
     if (kg == 0) {
         const bool relu = p.relu != 0;
+        // a lane holds four consecutive columns of one C row per group g:
+        // 32x32 fragments, row lane % 32, columns 8 g + 4 (lane / 32) (g < 4);
+        // 16x16 fragments, row lane % 16, columns 4 (lane / 16) (one group)
+        constexpr int NG = T::MI == 32 ? 4 : 1;
 #pragma unroll
         for (int fn = 0; fn < T::FN; ++fn) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
+            for (int g = 0; g < NG; ++g) {
                 // the lane's four columns of this group, the same in every row
-                const int col = wn * T::TN + fn * 32 + 8 * g + 4 * (lane >> 5);
+                const int col = wn * T::TN + fn * T::MI +
+                                (T::MI == 32 ? 8 * g + 4 * (lane >> 5) : 4 * (lane >> 4));
                 float bv[4];
                 load_bias4<T::BF16>(p.bias, n0 + col, N, bv);
 #pragma unroll
                 for (int fm = 0; fm < T::FM; ++fm) {
-                    const int row = wm * T::TM + fm * 32 + (lane & 31);
-                    const f32x16 &v = acc[fm][fn];
+                    const int row = wm * T::TM + fm * T::MI + (lane & (T::MI - 1));
+                    const typename T::Acc &v = acc[fm][fn];
                     u32x2 w;
                     w.x = epi_pack2<T::BF16>(v[4 * g + 0] + bv[0], v[4 * g + 1] + bv[1], relu);
                     w.y = epi_pack2<T::BF16>(v[4 * g + 2] + bv[2], v[4 * g + 3] + bv[3], relu);
@@ -675,7 +711,7 @@ template <class T>
 __global__ void __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(T::OCC)))
 gemm_relu_ragged_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
 {
-    static_assert(T::STAGES == 2 && T::KG == 1 && !T::BT && T::KSTEPS == 4,
+    static_assert(T::STAGES == 2 && T::KG == 1 && !T::BT && T::KSTEPS == 4 && T::MI == 32,
                   "ragged kernel: 2 stages, 64-wide K tiles, (K,N) B");
     using RP = RaggedPlan<T>;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[RP::LDS / 2];
@@ -922,17 +958,24 @@ hipError_t launch_all_configs(int cfg, const GemmArgs &p, hipStream_t stream, in
     // belong to different workgroups and meet different barriers
     case 30: return launch_dma<Mode<Cfg<256, 128, 32, 2, 2, 2, 2>, 0>>(p, stream, groupM);
     case 31: return launch_dma<Mode<Cfg<128, 256, 32, 2, 2, 2, 2>, 0>>(p, stream, groupM);
+    // 16x16x32 products (32-wide k steps): configurations 8, 2 and 29 again
+    case 32: return launch_dma<Mode<Cfg<256, 256, 64, 2, 4, 2, 1, 1, true, 16>, 0>>(p, stream, groupM);
+    case 33: return launch_dma<Mode<Cfg<256, 256, 64, 2, 2, 2, 1, 1, true, 16>, 0>>(p, stream, groupM);
+    case 34: return launch_dma<Mode<Cfg<128, 128, 64, 4, 2, 4, 1, 1, true, 16>, 0>>(p, stream, groupM);
     default: return hipErrorInvalidValue;
     }
 }
 
 
 // bf16 and (N,K)-B instances exist for the configurations the dispatcher
-// picks by default: 256x256 (8), 128x128 (29), short K (12) and few tiles (20).
+// picks by default: 256x256 (32), 128x128 (34), short K (12) and few tiles
+// (20), and for the 32x32x16 forms of the first two (8, 29).
 template <int MODE>
 hipError_t launch_default_configs(int cfg, const GemmArgs &p, hipStream_t stream, int groupM)
 {
     switch (cfg) {
+    case 32: return launch_dma<Mode<Cfg<256, 256, 64, 2, 4, 2, 1, 1, true, 16>, MODE>>(p, stream, groupM);
+    case 34: return launch_dma<Mode<Cfg<128, 128, 64, 4, 2, 4, 1, 1, true, 16>, MODE>>(p, stream, groupM);
     case 8: return launch_dma<Mode<Cfg<256, 256, 64, 2, 4, 2>, MODE>>(p, stream, groupM);
     case 29: return launch_dma<Mode<Cfg<128, 128, 64, 4, 2, 4>, MODE>>(p, stream, groupM);
     case 12: return launch_dma<Mode<Cfg<128, 128, 32, 2, 2, 2, 4>, MODE>>(p, stream, groupM);
@@ -953,7 +996,7 @@ bool dma_layout_ok(const GemmArgs &p)
 bool dma_config_has_mode(int cfg, int mode)
 {
     return mode == 0 ? (cfg >= 0 && cfg < kDmaConfigs)
-                     : (cfg == 8 || cfg == 29 || cfg == 12 || cfg == 20);
+                     : (cfg == 32 || cfg == 34 || cfg == 8 || cfg == 29 || cfg == 12 || cfg == 20);
 }
 
 hipError_t launch_ragged_config(int cfg, const GemmArgs &p, hipStream_t stream, int groupM)
