@@ -338,7 +338,9 @@ int tg_last_path(void);
  * unknown variant (the setting is unchanged).  Results are identical within
  * the accuracy contract for every variant; only speed changes.  22 and 23 are
  * ablations of configuration 0 (operand tiles without the XOR swizzle; a
- * 2-stage ring).
+ * 2-stage ring).  On the ragged path (TG_PATH_RAGGED) 0 and 1 select its
+ * 256x256 and 128x128 configurations with 32x32x16 products, 2 and 3 the same
+ * with 16x16x32 products (the defaults); other values pick by shape.
  */
 int tg_set_tile_variant(int variant);
 

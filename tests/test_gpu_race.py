@@ -118,7 +118,7 @@ def test_one_k_group_configs_bitwise_identical(tg, oracle_lib, M, N, K):
         assert used == "tile256"
     outs["generic"], used = run(tg, a_d, b_d, M, N, K, "f16", "kn", tg.TG_PATH_GENERIC, -1)
     assert used == "generic"
-    for v in (0, 1):
+    for v in (0, 1, 2, 3):
         outs[f"ragged{v}"], used = run(tg, a_d, b_d, M, N, K, "f16", "kn", tg.TG_PATH_RAGGED, v)
         assert used == "ragged"
     check_against_oracle(oracle_lib, outs[8], a, b, M, N, K, "f16", "kn")

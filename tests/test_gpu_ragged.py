@@ -96,7 +96,7 @@ def ragged_case(tg, oracle_lib, M, N, K, ldb, ldc, offb=0, offc=0, batch=1, gap=
     return outs["RAGGED"], outs["GENERIC"]
 
 
-@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
 @pytest.mark.parametrize("M,N,K,ldb,ldc,offb,offc", [
     (300, 500, 200, 500, 500, 0, 0),        # N % 8 != 0
     (301, 503, 136, 503, 503, 0, 0),        # odd N, odd ldb / ldc
@@ -120,7 +120,7 @@ def test_ragged_modes_and_bias(tg, oracle_lib, dtype, act, bias_off):
     assert np.array_equal(r, g)
 
 
-@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
 def test_ragged_batched_with_gaps(tg, oracle_lib, variant):
     r, g = ragged_case(tg, oracle_lib, 136, 203, 96, 205, 207, 1, 1, batch=3, gap=5,
                        seed=11, variant=variant)

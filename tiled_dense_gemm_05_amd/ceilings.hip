@@ -12,6 +12,8 @@
 //                      clock, depends on the data), 8 waves per CU, no memory
 //                      traffic in the loop.  Reports TFLOP/s and the shader
 //                      clock it ran at (clock64 / wall clock inside the kernel).
+//   mfma_f16_16x16x32  The same flops as v_mfma_f32_16x16x32_f16 products
+//                      (twice as many instructions on 16 accumulators).
 //   lds_read_b128      ds_read_b128 (A fragments and (N,K) B fragments):
 //                      bytes per shader clock per CU, 8 waves per CU,
 //                      conflict-free addresses.
@@ -55,6 +57,9 @@ constexpr int kChains = 8;         // independent accumulators per wave (128 reg
 
 // clock64 and the 100 MHz wall clock at the first and last instruction of
 // wave 0 of each workgroup, for the clock the loop ran at.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int MI>
 __global__ void __launch_bounds__(512) mfma_loop(const f16x8 *in, float *out, long long *clk,
                                                  int iters)
 {
@@ -66,15 +71,22 @@ __global__ void __launch_bounds__(512) mfma_loop(const f16x8 *in, float *out, lo
 #pragma unroll
     for (int i = 0; i < 2; ++i)
         b[i] = in[(t * 6 + 4 + i) % kOperands];
-    f32x16 acc[kChains];
+    // the same registers and flops either way: 8 accumulators of 16 or 16 of 4
+    constexpr int NA = MI == 32 ? kChains : 2 * kChains, NE = MI == 32 ? 16 : 4;
+    typedef float accv __attribute__((ext_vector_type(NE)));
+    accv acc[NA];
 #pragma unroll
-    for (int i = 0; i < kChains; ++i)
-        acc[i] = f32x16{};
+    for (int i = 0; i < NA; ++i)
+        acc[i] = accv{};
     const long long c0 = clock64(), w0 = wall_clock64();
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
-        for (int i = 0; i < kChains; ++i)
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i & 3], b[i >> 2], acc[i], 0, 0, 0);
+        for (int i = 0; i < NA; ++i) {
+            if constexpr (MI == 32)
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i & 3], b[i >> 2], acc[i], 0, 0, 0);
+            else
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i & 3], b[(i >> 2) & 1], acc[i], 0, 0, 0);
+        }
         // rotate the operands so consecutive products see different values
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -83,9 +95,9 @@ __global__ void __launch_bounds__(512) mfma_loop(const f16x8 *in, float *out, lo
     const long long c1 = clock64(), w1 = wall_clock64();
     float s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kChains; ++i)
+    for (int i = 0; i < NA; ++i)
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
+        for (int j = 0; j < NE; ++j)
             s += acc[i][j];
     out[t] = s;
     if (threadIdx.x == 0) {
@@ -172,11 +184,14 @@ int main(int argc, char **argv)
     std::vector<long long> clk((size_t)blocks * 2);
 
     // matrix cores: size the loop for about target_s seconds from a short run
-    {
+    for (int mi : {32, 16}) {
         int iters = 2000;
         for (int pass = 0; pass < 2; ++pass) {
             CHECK(hipEventRecord(e0, 0));
-            hipLaunchKernelGGL(mfma_loop, dim3(blocks), dim3(512), 0, 0, d_in, d_out, d_clk, iters);
+            if (mi == 32)
+                hipLaunchKernelGGL(mfma_loop<32>, dim3(blocks), dim3(512), 0, 0, d_in, d_out, d_clk, iters);
+            else
+                hipLaunchKernelGGL(mfma_loop<16>, dim3(blocks), dim3(512), 0, 0, d_in, d_out, d_clk, iters);
             CHECK(hipGetLastError());
             CHECK(hipEventRecord(e1, 0));
             CHECK(hipEventSynchronize(e1));
@@ -194,8 +209,9 @@ int main(int argc, char **argv)
             }
             const double mhz = c / (w / (wall_khz * 1e3)) / 1e6;
             const double flop = (double)blocks * 8 /* waves */ * iters * kChains * 2.0 * 32 * 32 * 16;
-            std::printf("{\"figure\": \"mfma_f16_32x32x16\", \"tflops\": %.1f, \"sclk_mhz\": %.0f, "
+            std::printf("{\"figure\": \"%s\", \"tflops\": %.1f, \"sclk_mhz\": %.0f, "
                         "\"ms\": %.3f, \"waves_per_cu\": 8, \"operands\": \"normal(0, 1/sqrt(8192))\"}\n",
+                        mi == 32 ? "mfma_f16_32x32x16" : "mfma_f16_16x16x32",
                         flop / (ms * 1e-3) / 1e12, mhz, ms);
         }
     }

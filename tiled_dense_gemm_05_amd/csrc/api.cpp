@@ -20,6 +20,8 @@ std::atomic<int> g_tile_variant{-1};
 constexpr int kTile128Default = 34;
 // 256x256x64, 2 stages, 8 waves (2 per SIMD), 16x16x32 products
 constexpr int kTile256Default = 32;
+constexpr int kRagged256 = 2;       // the ragged kernel's 256x256 and 128x128 configurations
+constexpr int kRagged128 = 3;       // (16x16x32 products)
 constexpr int kTile128ShortK = 12;   // 128x128x32, 2 stages, 4 waves/SIMD: several workgroups per CU
 constexpr int kTile64 = 20;          // 64x64x64, 4 stages, two K groups: grids with few tiles
 constexpr int kRegStaged128 = 100;   // register-staged kernels, kept for comparison
@@ -235,9 +237,10 @@ int run(const void *A, const void *B, void *C, const void *bias, bool relu, bool
     }
     case TG_PATH_RAGGED: {
         // tg_set_tile_variant 0 / 1 forces the 256x256 / 128x128 configuration
+        // with 32x32x16 products, 2 / 3 the same with 16x16x32 products
         int v = g_tile_variant.load(std::memory_order_relaxed);
-        if (v != 0 && v != 1)
-            v = prefer_256(p) ? 0 : 1;
+        if (v < 0 || v > 3)
+            v = prefer_256(p) ? kRagged256 : kRagged128;
         e = tg::launch_ragged_config(v, p, stream, g_group_m.load(std::memory_order_relaxed));
         break;
     }

@@ -693,7 +693,7 @@ __device__ __forceinline__ void ragged_b_store(const BRegs<T> &br, lds_u16 *stag
         v.z = __builtin_amdgcn_alignbit(w.w, w.z, s) & m[2];
         v.w = __builtin_amdgcn_alignbit(br.x[j], w.w, s) & m[3];
         *reinterpret_cast<__attribute__((address_space(3))) u32x4 *>(
-            stage_b + r * T::BN + swz_b<T::CB, T::SWZ>(r, c) * 8) = v;
+            stage_b + r * T::BN + swz_b<T::CB, T::SWZ, T::BSWZ>(r, c) * 8) = v;
     }
 }
 
@@ -711,7 +711,7 @@ template <class T>
 __global__ void __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(T::OCC)))
 gemm_relu_ragged_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
 {
-    static_assert(T::STAGES == 2 && T::KG == 1 && !T::BT && T::KSTEPS == 4 && T::MI == 32,
+    static_assert(T::STAGES == 2 && T::KG == 1 && !T::BT && T::BK == 64,
                   "ragged kernel: 2 stages, 64-wide K tiles, (K,N) B");
     using RP = RaggedPlan<T>;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[RP::LDS / 2];
@@ -757,12 +757,12 @@ gemm_relu_ragged_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
         ragged_b_store<T>(br, (lds_u16 *)smem + (t & 1) * T::STAGE + T::A_ELEMS, brow0, bc, bnv);
     };
 
-    f32x16 acc[T::FM][T::FN];
+    typename T::Acc acc[T::FM][T::FN];
 #pragma unroll
     for (int fm = 0; fm < T::FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < T::FN; ++fn)
-            acc[fm][fn] = f32x16{};
+            acc[fm][fn] = typename T::Acc{};
 
     const int KT = (int)((K + T::BK - 1) / T::BK);
     f16x8 af[2][T::FM], bf[2][T::FN];
@@ -784,14 +784,14 @@ gemm_relu_ragged_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
         const int stage = kt & 1;
         const lds_u16 *As = lds + stage * T::STAGE;
         const lds_u16 *Bs = As + T::A_ELEMS;
-        // k steps 0 and 1
+        // the first half of the tile's k steps (one of two, or two of four)
         {
             s16x4 bh[T::FN][2];
             step<T, 0, 0>(acc, af[0], bf[0], lp, i32x4{}, i32x4{}, false, 0, 0u, wave, As, Bs, 1,
                           wm, wn, lane, af[1], bh);
             join_b<T>(bh, bf[1]);
         }
-        {
+        if constexpr (T::KSTEPS == 4) {
             s16x4 bh[T::FN][2];
             step<T, 0, 0>(acc, af[1], bf[1], lp, i32x4{}, i32x4{}, false, 0, 0u, wave, As, Bs, 2,
                           wm, wn, lane, af[0], bh);
@@ -808,8 +808,9 @@ gemm_relu_ragged_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
         b_store(kt + 1);
         b_load(kt + 2);
         __builtin_amdgcn_sched_barrier(0);
-        inner_steps<T, 2>(acc, af, bf, lp, i32x4{}, i32x4{}, false, 0, 0u, wave, As, Bs, wm, wn,
-                          lane);
+        if constexpr (T::KSTEPS == 4)
+            inner_steps<T, 2>(acc, af, bf, lp, i32x4{}, i32x4{}, false, 0, 0u, wave, As, Bs, wm, wn,
+                              lane);
         constexpr int cur = (T::KSTEPS - 1) & 1, nxt = T::KSTEPS & 1;
         block_barrier();
         {
@@ -832,11 +833,13 @@ gemm_relu_ragged_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
     lds_u16 *cst = (lds_u16 *)smem;
     const int cpar = (int)((reinterpret_cast<uintptr_t>(C) >> 1) & 1);
     const bool relu = p.relu != 0;
+    constexpr int NG = T::MI == 32 ? 4 : 1;   // column groups per fragment, as in the aligned kernel
 #pragma unroll
     for (int fn = 0; fn < T::FN; ++fn) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int col = wn * T::TN + fn * 32 + 8 * g + 4 * (lane >> 5);
+        for (int g = 0; g < NG; ++g) {
+            const int col = wn * T::TN + fn * T::MI +
+                            (T::MI == 32 ? 8 * g + 4 * (lane >> 5) : 4 * (lane >> 4));
             float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
             if (p.bias != nullptr) {
 #pragma unroll
@@ -846,9 +849,9 @@ gemm_relu_ragged_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
             }
 #pragma unroll
             for (int fm = 0; fm < T::FM; ++fm) {
-                const int row = wm * T::TM + fm * 32 + (lane & 31);
+                const int row = wm * T::TM + fm * T::MI + (lane & (T::MI - 1));
                 const int odd = (cpar + (int)(((m0 + row) * p.ldc + n0) & 1)) & 1;
-                const f32x16 &v = acc[fm][fn];
+                const typename T::Acc &v = acc[fm][fn];
                 const uint32_t lo = epi_pack2<T::BF16>(v[4 * g + 0] + bv[0], v[4 * g + 1] + bv[1], relu);
                 const uint32_t hi = epi_pack2<T::BF16>(v[4 * g + 2] + bv[2], v[4 * g + 3] + bv[3], relu);
                 lds_u16 *dst = cst + row * RP::CLD + col;
@@ -1011,6 +1014,12 @@ hipError_t launch_ragged_config(int cfg, const GemmArgs &p, hipStream_t stream, 
     case 1:   // 128 x 128 x 64, 8 waves of 32 x 64
         return bf ? launch_ragged<Mode<Cfg<128, 128, 64, 4, 2, 2>, 1>>(p, stream, groupM)
                   : launch_ragged<Mode<Cfg<128, 128, 64, 4, 2, 2>, 0>>(p, stream, groupM);
+    case 2:   // 0 with 16x16x32 products
+        return bf ? launch_ragged<Mode<Cfg<256, 256, 64, 2, 4, 2, 1, 1, true, 16>, 1>>(p, stream, groupM)
+                  : launch_ragged<Mode<Cfg<256, 256, 64, 2, 4, 2, 1, 1, true, 16>, 0>>(p, stream, groupM);
+    case 3:   // 1 with 16x16x32 products
+        return bf ? launch_ragged<Mode<Cfg<128, 128, 64, 4, 2, 2, 1, 1, true, 16>, 1>>(p, stream, groupM)
+                  : launch_ragged<Mode<Cfg<128, 128, 64, 4, 2, 2, 1, 1, true, 16>, 0>>(p, stream, groupM);
     default: return hipErrorInvalidValue;
     }
 }
