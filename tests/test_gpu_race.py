@@ -38,11 +38,15 @@ LAYOUTS = {"kn": 0, "nk": 1}
 
 # one K group (any tile / stages / swizzle / waves / product shape), the
 # register-staged kernels (and, below, the any-layout and ragged-layout kernels)
-KG1 = [c for c in range(35) if c not in (14, 15, 16, 20)] + [100, 101]
+KG1 = [c for c in range(38) if c not in (14, 15, 16, 20)] + [100, 101]
 # two K groups: K tiles of 64 (configs 14, 20) or of 32 (15, 16) dealt alternately
 KG2_GROUPS = [[14, 20], [15, 16]]
 # configurations that exist for bf16 elements and an (N,K) B
-MODE_KG1 = [8, 29, 12, 32, 34]
+MODE_KG1 = [8, 29, 12, 32, 34, 36]
+# persistent configurations (a workgroup walks a list of tiles, its ring of K
+# tiles running across tile boundaries) and one-tile-per-workgroup ones
+STREAM = [35, 36, 37]
+ONE_SHOT = [12, 34]
 
 
 def say(*a):
@@ -151,3 +155,73 @@ def test_modes_bitwise_identical_across_configs(tg, oracle_lib, dtype, layout, M
     assert used == "generic"
     check_against_oracle(oracle_lib, outs[8], a, b, M, N, K, dtype, layout)
     assert_same(outs, 8)
+
+
+def run_batched(tg, a_d, b_d, M, N, K, batch, sA, sB, dtype, layout, variant, bias_d=None,
+                act=0):
+    """One strided-batched call of tg_gemm_ex on the 128x128 tile path."""
+    assert tg.tg_set_path(tg.TG_PATH_TILE128) >= 0
+    assert tg.tg_set_tile_variant(variant) >= -1
+    ldb = N if layout == "kn" else K
+    c_d = torch.full((batch * M * N,), 0x7E00, dtype=torch.int16, device="cuda")
+    say(f"stream race {dtype}/{layout} batch={batch} M={M} N={N} K={K} sB={sB} "
+        f"variant={variant} bias={bias_d is not None} act={act}")
+    st = tg.tg_gemm_ex(DTYPES[dtype], LAYOUTS[layout], act, a_d.data_ptr(), b_d.data_ptr(),
+                       c_d.data_ptr(), bias_d.data_ptr() if bias_d is not None else 0, M, N, K,
+                       K, ldb, N, sA, sB, M * N, batch, torch.cuda.current_stream().cuda_stream)
+    assert st == tg.TG_OK, tg.tg_status_string(st)
+    torch.cuda.synchronize()
+    return c_d.cpu().numpy().view(np.uint16), tg.tg_path_name(tg.tg_last_path())
+
+
+# batch, M, N, K, B shared by every entry: more tiles than workgroups (several
+# per workgroup, items not a multiple of the grid), K tiles per item from 1 to
+# 4 with a partial last one, ragged M and N edges
+STREAM_SHAPES = [(1024, 128, 128, 64, False), (600, 130, 136, 200, False),
+                 (9, 1000, 1000, 64, False), (300, 64, 256, 8, True), (1, 2056, 1032, 264, False)]
+
+
+@pytest.mark.parametrize("batch,M,N,K,shared_b", STREAM_SHAPES)
+def test_stream_configs_bitwise_identical(tg, oracle_lib, batch, M, N, K, shared_b):
+    """The persistent configurations give the bits of the one-tile-per-workgroup
+    ones for every tile of every batch entry (a stage reused too early, or a
+    tile's epilogue given another tile's coordinates, would show here)."""
+    a, b = wl.generate_dense(M, N, K, "uniform", 401 + K, batch=batch)
+    if shared_b:
+        b = b[:K * N]
+    a_d, b_d = dev(a), dev(b)
+    sB = 0 if shared_b else K * N
+    outs = {}
+    for v in ONE_SHOT + STREAM:
+        outs[v], used = run_batched(tg, a_d, b_d, M, N, K, batch, M * K, sB, "f16", "kn", v)
+        assert used == "tile128"
+    assert not np.any(outs[36] == 0x7E00), "a cell of C was not written"
+    for e in sorted({0, batch // 2, batch - 1}):
+        out = outs[36].reshape(batch, M * N)[e]
+        ref, S, Sa = oracle_lib.gemm_ex(a[e * M * K:(e + 1) * M * K],
+                                        b[(e * K * N if not shared_b else 0):][:K * N], M, N, K,
+                                        act="none", want_sums=True)
+        rep = gate(out, ref, K, Sa.reshape(-1), relu=False)
+        assert rep.ok, f"batch entry {e}: {rep}"
+    assert_same(outs, 34)
+
+
+@pytest.mark.parametrize("dtype,layout", [("f16", "kn"), ("bf16", "kn"), ("f16", "nk"),
+                                          ("bf16", "nk")])
+@pytest.mark.parametrize("act,with_bias", [(1, False), (1, True), (0, True)])
+def test_stream_modes_and_epilogues_match_one_shot(tg, dtype, layout, act, with_bias):
+    """Element types, B layouts, bias and activation on the persistent
+    configuration: the same bits as the one-tile-per-workgroup one."""
+    batch, M, N, K = 700, 72, 136, 96
+    a, b = wl.generate_dense(M, N, K, "uniform", 7 + act, batch=batch, dtype=dtype)
+    if layout == "nk":
+        b = wl.transpose_bits(b, K, N, batch)
+    a_d, b_d = dev(a), dev(b)
+    bias_d = dev(wl.generate_bias(N, 9, dtype=dtype, scale=0.5)) if with_bias else None
+    o34, u34 = run_batched(tg, a_d, b_d, M, N, K, batch, M * K, K * N, dtype, layout, 34,
+                           bias_d, act)
+    o36, u36 = run_batched(tg, a_d, b_d, M, N, K, batch, M * K, K * N, dtype, layout, 36,
+                           bias_d, act)
+    assert u34 == u36 == "tile128"
+    assert not np.any(o36 == 0x7E00), "a cell of C was not written"
+    assert np.array_equal(o34, o36), int(np.sum(o34 != o36))

@@ -23,6 +23,7 @@ constexpr int kTile256Default = 32;
 constexpr int kRagged256 = 2;       // the ragged kernel's 256x256 and 128x128 configurations
 constexpr int kRagged128 = 3;       // (16x16x32 products)
 constexpr int kTile128ShortK = 12;   // 128x128x32, 2 stages, 4 waves/SIMD: several workgroups per CU
+constexpr int kStream128 = 36;       // persistent workgroups over a list of 128x128 tiles
 constexpr int kTile64 = 20;          // 64x64x64, 4 stages, two K groups: grids with few tiles
 constexpr int kRegStaged128 = 100;   // register-staged kernels, kept for comparison
 constexpr int kRegStaged256 = 101;
@@ -40,6 +41,7 @@ std::atomic<int> g_attn_variant{kAttnDefault};
 // 2 something else.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_state[kMaxDevices];
+std::atomic<int> g_cus[kMaxDevices];   // compute units per device (0: not yet asked)
 
 constexpr int64_t kMaxDim = 0x7fffffff;
 constexpr __int128 kMaxExtent = (__int128)1 << 62;
@@ -61,6 +63,7 @@ int check_device()
             return TG_ERR_NO_DEVICE;
         }
         st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
         g_arch_state[dev].store(st, std::memory_order_relaxed);
     }
     return st == 1 ? TG_OK : TG_ERR_UNSUPPORTED_DEVICE;
@@ -221,10 +224,14 @@ int run(const void *A, const void *B, void *C, const void *bias, bool relu, bool
             v = -1;
         if (v < 0) {
             const int64_t tiles128 = ((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch;
-            v = path == TG_PATH_TILE256 ? kTile256Default
-                : p.K <= 64         ? kTile128ShortK
-                : tiles128 < 128    ? kTile64
-                                    : kTile128Default;
+            // many short problems: persistent workgroups, so that loads,
+            // products and stores of different tiles overlap
+            const int cus = tg::host_device_cus();
+            v = path == TG_PATH_TILE256            ? kTile256Default
+                : p.K <= 64 && tiles128 >= 4 * cus ? kStream128
+                : p.K <= 64                        ? kTile128ShortK
+                : tiles128 < 128                   ? kTile64
+                                                   : kTile128Default;
         }
         const int gm = g_group_m.load(std::memory_order_relaxed);
         if (v == kRegStaged128)
@@ -266,6 +273,23 @@ int run(const void *A, const void *B, void *C, const void *bias, bool relu, bool
 
 namespace tg {
 int host_check_device() { return check_device(); }
+int host_device_cus()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    int n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return 0;
+        }
+        g_cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 void host_set_last_path(int path) { g_last_path.store(path, std::memory_order_relaxed); }
 }  // namespace tg
 

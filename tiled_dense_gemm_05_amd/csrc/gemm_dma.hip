@@ -36,6 +36,11 @@
 //    consecutive columns of a C row), transpose reads of the row-major B
 //    (ds_read_b64_tr_b16), the swizzles, the XCD-aware tile order and the
 //    epilogue are shared with the register-staged kernel.
+//  * The epilogue's common case (no bias, ReLU) takes three VALU
+//    instructions per pair of outputs (two maxima, one packed conversion);
+//    the C tile leaves through non-temporal stores, since no kernel here
+//    reads an output again: a stream of many small products (1024 x
+//    128x128x64) runs about 8 % faster than with ordinary stores.
 #include <type_traits>
 
 #include "tg_internal.h"
@@ -252,6 +257,25 @@ __device__ __forceinline__ typename T::Acc mfma32(const f16x8 &b, const f16x8 &a
     } else {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c, 0, 0, 0);
     }
+}
+
+// The four outputs a lane holds in group g of a fragment (four consecutive
+// columns of one row), finished and packed: bias, activation and rounding.
+// FAST is the common case, no bias and the ReLU, in three VALU instructions
+// per pair of outputs (two maxima and one packed conversion).
+template <class T, bool FAST>
+__device__ __forceinline__ u32x2 finish4(const typename T::Acc &v, int g, const float (&bv)[4],
+                                         bool relu)
+{
+    u32x2 w;
+    if constexpr (FAST) {
+        w.x = pack2<T::BF16, true>(v[4 * g + 0], v[4 * g + 1]);
+        w.y = pack2<T::BF16, true>(v[4 * g + 2], v[4 * g + 3]);
+    } else {
+        w.x = epi_pack2<T::BF16>(v[4 * g + 0] + bv[0], v[4 * g + 1] + bv[1], relu);
+        w.y = epi_pack2<T::BF16>(v[4 * g + 2] + bv[2], v[4 * g + 3] + bv[3], relu);
+    }
+    return w;
 }
 
 // Everything a thread needs to issue its loads of one tile.
@@ -517,28 +541,33 @@ gemm_relu_dma_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
         // 32x32 fragments, row lane % 32, columns 8 g + 4 (lane / 32) (g < 4);
         // 16x16 fragments, row lane % 16, columns 4 (lane / 16) (one group)
         constexpr int NG = T::MI == 32 ? 4 : 1;
+        auto stage_c = [&](auto fast_c) __attribute__((always_inline)) {
+            constexpr bool FAST = decltype(fast_c)::value;
 #pragma unroll
-        for (int fn = 0; fn < T::FN; ++fn) {
+            for (int fn = 0; fn < T::FN; ++fn) {
 #pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                // the lane's four columns of this group, the same in every row
-                const int col = wn * T::TN + fn * T::MI +
-                                (T::MI == 32 ? 8 * g + 4 * (lane >> 5) : 4 * (lane >> 4));
-                float bv[4];
-                load_bias4<T::BF16>(p.bias, n0 + col, N, bv);
+                for (int g = 0; g < NG; ++g) {
+                    // the lane's four columns of this group, the same in every row
+                    const int col = wn * T::TN + fn * T::MI +
+                                    (T::MI == 32 ? 8 * g + 4 * (lane >> 5) : 4 * (lane >> 4));
+                    float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                    if constexpr (!FAST)
+                        load_bias4<T::BF16>(p.bias, n0 + col, N, bv);
 #pragma unroll
-                for (int fm = 0; fm < T::FM; ++fm) {
-                    const int row = wm * T::TM + fm * T::MI + (lane & (T::MI - 1));
-                    const typename T::Acc &v = acc[fm][fn];
-                    u32x2 w;
-                    w.x = epi_pack2<T::BF16>(v[4 * g + 0] + bv[0], v[4 * g + 1] + bv[1], relu);
-                    w.y = epi_pack2<T::BF16>(v[4 * g + 2] + bv[2], v[4 * g + 3] + bv[3], relu);
-                    const int phys = (col >> 3) ^ (row % T::CB);
-                    *reinterpret_cast<__attribute__((address_space(3))) u32x2 *>(
-                        cst + row * T::BN + phys * 8 + (col & 4)) = w;
+                    for (int fm = 0; fm < T::FM; ++fm) {
+                        const int row = wm * T::TM + fm * T::MI + (lane & (T::MI - 1));
+                        const u32x2 w = finish4<T, FAST>(acc[fm][fn], g, bv, relu);
+                        const int phys = (col >> 3) ^ (row % T::CB);
+                        *reinterpret_cast<__attribute__((address_space(3))) u32x2 *>(
+                            cst + row * T::BN + phys * 8 + (col & 4)) = w;
+                    }
                 }
             }
-        }
+        };
+        if (p.bias == nullptr && relu)
+            stage_c(std::true_type{});
+        else
+            stage_c(std::false_type{});
     }
     block_barrier();
     // N % 8 == 0 and 16-byte aligned rows: every chunk is wholly in or out
@@ -549,7 +578,7 @@ gemm_relu_dma_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
             const int phys = c ^ (row % T::CB);
             const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(
                 cst + row * T::BN + phys * 8);
-            *reinterpret_cast<u32x4 *>(C + gm * p.ldc + gn) = v;
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(C + gm * p.ldc + gn));
         }
     }
 }
@@ -576,6 +605,276 @@ hipError_t launch_dma(const GemmArgs &p, hipStream_t stream, int groupM)
             return e;
     }
     return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// Persistent form for many short problems (a strided batch of small GEMMs, or
+// any call whose K is a few tiles): the work is a list of items, one output
+// tile of one batch entry each, and a grid of one workgroup per CU walks the
+// list.  The ring of K tiles runs straight across item boundaries, so the
+// loads of the next items are in flight while an item's products, epilogue
+// and stores run; in the one-tile-per-workgroup launch every workgroup loads,
+// then computes, then stores, and the memory system sees all the reads and
+// then all the writes.
+//
+//  * Workgroup g of G takes items g', g' + G, g' + 2G, ... where g' numbers
+//    the workgroups XCD by XCD (workgroup g runs on XCD g % 8), so the items
+//    an XCD holds at one time are neighbours.
+//  * An item's K tiles are positions of the workgroup's stream; position q's
+//    tile sits in stage q % STAGES and the loads of position q + STAGES - 1
+//    are spread over the k steps of position q, exactly as in
+//    gemm_relu_dma_kernel.  Positions past the end load zeros without
+//    touching memory.
+//  * After an item's last product each wave writes its TM x TN tile through
+//    its own LDS area (16-byte chunks XOR-swizzled by the row), reads it back
+//    as whole 16-byte chunks of rows and stores them: no workgroup barrier,
+//    and the ring is not touched.
+//  * The counter waits count only the loads issued after the awaited tile;
+//    stores issued in between are awaited too, since loads and stores share
+//    the counter and need not complete in order with respect to each other.
+template <class T>
+__global__ void __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(T::OCC)))
+gemm_relu_dma_stream_kernel(GemmArgs p, int tilesM, int tilesN, int items, int KT)
+{
+    static_assert(T::KG == 1 && T::SPREAD, "one K group, loads spread over the k steps");
+    constexpr int CBW = T::TN / 8;                       // 16-byte chunks per wave-tile row
+    constexpr int CW = T::TM * T::TN;                    // fp16 elements of a wave's C area
+    static_assert(CBW <= 64 && 64 % CBW == 0 && (CW / 8) % 64 == 0, "wave tile");
+    static_assert(T::RING + T::NW * CW * 2 <= 160 * 1024, "LDS size");
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[T::RING / 2 + T::NW * CW];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / T::WN, wn = wave % T::WN;
+    const lds_u16 *lds = (const lds_u16 *)smem;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+    lds_u16 *cw = (lds_u16 *)smem + T::RING / 2 + wave * CW;
+
+    const int G = gridDim.x;
+    const int g = blockIdx.x;
+    const int first = (G % 8 == 0) ? (g % 8) * (G / 8) + g / 8 : g;
+    const int mine = first < items ? (items - first + G - 1) / G : 0;
+    const int Q = mine * KT;
+    const int tiles = tilesM * tilesN;
+    const int64_t M = p.M, N = p.N, K = p.K;
+
+    // the load-plan parts that do not depend on the item
+    int a_r0, a_c, b_r0, b_c;
+    if constexpr (T::BT) {
+        a_r0 = wave * T::A_RPB + lane / T::CA;
+        a_c = swz_a<T::CA, T::SWZ>(a_r0, lane % T::CA);
+        b_r0 = wave * T::B_RPB + lane / T::CA;
+        b_c = swz_a<T::CA, T::SWZ>(b_r0, lane % T::CA);
+    } else {
+        a_r0 = wave * T::A_RPB + lane / T::CA;
+        a_c = swz_a<T::CA, T::SWZ>(a_r0, lane % T::CA);
+        b_r0 = wave * T::B_RPB + lane / T::CB;
+        b_c = swz_b<T::CB, T::SWZ, T::BSWZ>(b_r0, lane % T::CB);
+    }
+
+    // A cursor holds a position's item (batch entry and tile) and K tile.
+    // Advancing moves to the next K tile, or after an item's last one to this
+    // workgroup's next item, G items further on; the divisions are done once.
+    struct Cursor {
+        int b, tm, tn, kt;
+    };
+    const int dB = G / tiles, dT = G - dB * tiles;
+    const int dTM = dT / tilesN, dTN = dT - dTM * tilesN;
+    Cursor c0;
+    {
+        const int f = first < items ? first : 0;
+        c0.b = f / tiles;
+        const int t = f - c0.b * tiles;
+        c0.tm = t / tilesN;
+        c0.tn = t - c0.tm * tilesN;
+        c0.kt = 0;
+    }
+    auto advance = [&](Cursor &c) __attribute__((always_inline)) {
+        if (++c.kt < KT)
+            return;
+        c.kt = 0;
+        c.b += dB;
+        c.tm += dTM;
+        c.tn += dTN;
+        if (c.tn >= tilesN) {
+            c.tn -= tilesN;
+            ++c.tm;
+        }
+        if (c.tm >= tilesM) {
+            c.tm -= tilesM;
+            ++c.b;
+        }
+    };
+
+    // Everything the loads of position q need (zeros past the end).
+    struct Load {
+        LoadPlan<T> lp;
+        i32x4 ra, rb;
+        bool akok;
+        int bleft;
+    };
+    // (A position past the end reads nothing: every offset is out of range,
+    // whatever the cursor holds.)
+    auto plan = [&](const Cursor &c, bool live) __attribute__((always_inline)) {
+        Load L;
+        const int64_t k0 = (int64_t)c.kt * T::BK;
+        const int64_t m0 = (int64_t)c.tm * T::BM, n0 = (int64_t)c.tn * T::BN;
+        const uint16_t *Ab = p.A + c.b * p.sA + m0 * p.lda + k0;
+        const uint16_t *Bb = p.B + c.b * p.sB + (T::BT ? n0 * p.ldb + k0 : k0 * p.ldb + n0);
+        L.ra = make_rsrc(Ab);
+        L.rb = make_rsrc(Bb);
+        L.lp.a_kcol = a_c * 8;
+#pragma unroll
+        for (int i = 0; i < T::A_LD; ++i) {
+            const int row = a_r0 + i * T::NW * T::A_RPB;
+            L.lp.a_voff[i] = (live && m0 + row < M) ? (uint32_t)((row * p.lda + a_c * 8) * 2) : kOutOfRange;
+        }
+        if constexpr (T::BT) {
+            L.lp.b_kcol = b_c * 8;
+            L.lp.b_row0 = 0;
+#pragma unroll
+            for (int j = 0; j < T::B_LD; ++j) {
+                const int row = b_r0 + j * T::NW * T::B_RPB;
+                L.lp.b_voff[j] = (live && n0 + row < N) ? (uint32_t)((row * p.ldb + b_c * 8) * 2) : kOutOfRange;
+            }
+            L.bleft = live && k0 + L.lp.b_kcol < K;
+        } else {
+            L.lp.b_kcol = 0;
+            L.lp.b_row0 = b_r0;
+            const bool col_ok = live && n0 + b_c * 8 < N;
+#pragma unroll
+            for (int j = 0; j < T::B_LD; ++j) {
+                const int row = b_r0 + j * T::NW * T::B_RPB;
+                L.lp.b_voff[j] = col_ok ? (uint32_t)((row * p.ldb + b_c * 8) * 2) : kOutOfRange;
+            }
+            const int64_t r = K - k0;
+            L.bleft = live ? (int)(r < 0 ? 0 : (r > T::BK ? T::BK : r)) : 0;
+        }
+        L.akok = live && k0 + L.lp.a_kcol < K;
+        return L;
+    };
+
+    typename T::Acc acc[T::FM][T::FN];
+#pragma unroll
+    for (int fm = 0; fm < T::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < T::FN; ++fn)
+            acc[fm][fn] = typename T::Acc{};
+
+    f16x8 af[2][T::FM], bf[2][T::FN];
+    Cursor cl = c0, cc = c0;   // positions being loaded / computed
+    if (Q > 0) {
+#pragma unroll
+        for (int s = 0; s < T::PROLOGUE; ++s) {
+            const Load L = plan(cl, s < Q);
+            advance(cl);
+            issue_tile<T>(L.lp, L.ra, L.rb, L.akok, L.bleft, lds_base + (uint32_t)(s * T::STAGE * 2), wave);
+        }
+        wait_vmcnt<(T::PROLOGUE - 1) * T::LOADS>();
+        block_barrier();
+        s16x4 bh[T::FN][2];
+        read_all<T>(lds, lds + T::A_ELEMS, 0, wm, wn, lane, af[0], bh);
+        join_b<T>(bh, bf[0]);
+    }
+
+    for (int q = 0; q < Q; ++q) {
+        const int stage = q % T::STAGES;
+        const lds_u16 *As = lds + stage * T::STAGE;
+        const lds_u16 *Bs = As + T::A_ELEMS;
+        const int ql = q + T::AHEAD;
+        const uint32_t laddr = lds_base + (uint32_t)((ql % T::STAGES) * T::STAGE * 2);
+        const Load L = plan(cl, ql < Q);
+        advance(cl);
+        inner_steps<T>(acc, af, bf, L.lp, L.ra, L.rb, L.akok, L.bleft, laddr, wave, As, Bs, wm, wn, lane);
+        constexpr int cur = (T::KSTEPS - 1) & 1, nxt = T::KSTEPS & 1;
+        wait_vmcnt<T::WAIT_LAST>();
+        block_barrier();
+        {
+            const lds_u16 *An = lds + ((q + 1) % T::STAGES) * T::STAGE;
+            s16x4 bh[T::FN][2];
+            constexpr int D0 = (T::KSTEPS - 1) * T::DPS;
+            step<T, D0, T::LOADS>(acc, af[cur], bf[cur], L.lp, L.ra, L.rb, L.akok, L.bleft, laddr, wave,
+                                  An, An + T::A_ELEMS, 0, wm, wn, lane, af[nxt], bh);
+            join_b<T>(bh, bf[nxt]);
+        }
+        if (cc.kt != KT - 1) {
+            advance(cc);
+            continue;
+        }
+
+        // Epilogue of the item: bias, activation, rounding; the wave's tile
+        // through its LDS area; whole 16-byte chunks of rows to C.
+        const int64_t rbase = (int64_t)cc.tm * T::BM + wm * T::TM;
+        const int64_t cbase = (int64_t)cc.tn * T::BN + wn * T::TN;
+        const bool relu = p.relu != 0;
+        constexpr int NG = T::MI == 32 ? 4 : 1;
+        auto stage_c = [&](auto fast_c) __attribute__((always_inline)) {
+            constexpr bool FAST = decltype(fast_c)::value;
+#pragma unroll
+            for (int fn = 0; fn < T::FN; ++fn) {
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) {
+                    const int col = fn * T::MI + (T::MI == 32 ? 8 * gi + 4 * (lane >> 5) : 4 * (lane >> 4));
+                    float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                    if constexpr (!FAST)
+                        load_bias4<T::BF16>(p.bias, cbase + col, N, bv);
+#pragma unroll
+                    for (int fm = 0; fm < T::FM; ++fm) {
+                        const int row = fm * T::MI + (lane & (T::MI - 1));
+                        const u32x2 o = finish4<T, FAST>(acc[fm][fn], gi, bv, relu);
+                        const int phys = (col >> 3) ^ (row % CBW);
+                        *reinterpret_cast<__attribute__((address_space(3))) u32x2 *>(
+                            cw + row * T::TN + phys * 8 + (col & 4)) = o;
+                    }
+                }
+            }
+        };
+        if (p.bias == nullptr && relu)
+            stage_c(std::true_type{});
+        else
+            stage_c(std::false_type{});
+        asm volatile("" ::: "memory");   // the wave's LDS writes precede its reads
+        uint16_t *Cb = p.C + cc.b * p.sC;
+#pragma unroll
+        for (int i = 0; i < CW / 8 / 64; ++i) {
+            const int qq = i * 64 + lane;
+            const int row = qq / CBW, c = qq % CBW;
+            const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(
+                cw + row * T::TN + (c ^ (row % CBW)) * 8);
+            const int64_t gm = rbase + row, gn = cbase + c * 8;
+            if (gm < M && gn < N)
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(Cb + gm * p.ldc + gn));
+        }
+#pragma unroll
+        for (int fm = 0; fm < T::FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < T::FN; ++fn)
+                acc[fm][fn] = typename T::Acc{};
+        advance(cc);
+    }
+    // loads issued past the end must land before the workgroup ends
+    wait_vmcnt<0>();
+}
+
+template <class T>
+hipError_t launch_stream(const GemmArgs &p, hipStream_t stream)
+{
+    const int64_t tilesM = (p.M + T::BM - 1) / T::BM;
+    const int64_t tilesN = (p.N + T::BN - 1) / T::BN;
+    const int64_t items = tilesM * tilesN * p.batch;
+    const int64_t KT = (p.K + T::BK - 1) / T::BK;
+    if (items <= 0 || KT <= 0)
+        return hipSuccess;
+    if (items > 0x3fffffff || KT > 0x3fffffff || items * KT > 0x3fffffff)
+        return hipErrorInvalidValue;
+    const int cus = host_device_cus();
+    if (cus <= 0)
+        return hipErrorInvalidDevice;
+    const int64_t grid = items < cus ? items : cus;
+    hipLaunchKernelGGL((gemm_relu_dma_stream_kernel<T>), dim3((unsigned)grid), dim3(T::NT), 0, stream,
+                       p, (int)tilesM, (int)tilesN, (int)items, (int)KT);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -834,38 +1133,43 @@ gemm_relu_ragged_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
     const int cpar = (int)((reinterpret_cast<uintptr_t>(C) >> 1) & 1);
     const bool relu = p.relu != 0;
     constexpr int NG = T::MI == 32 ? 4 : 1;   // column groups per fragment, as in the aligned kernel
+    auto stage_c = [&](auto fast_c) __attribute__((always_inline)) {
+        constexpr bool FAST = decltype(fast_c)::value;
 #pragma unroll
-    for (int fn = 0; fn < T::FN; ++fn) {
+        for (int fn = 0; fn < T::FN; ++fn) {
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            const int col = wn * T::TN + fn * T::MI +
-                            (T::MI == 32 ? 8 * g + 4 * (lane >> 5) : 4 * (lane >> 4));
-            float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (p.bias != nullptr) {
+            for (int g = 0; g < NG; ++g) {
+                const int col = wn * T::TN + fn * T::MI +
+                                (T::MI == 32 ? 8 * g + 4 * (lane >> 5) : 4 * (lane >> 4));
+                float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (!FAST && p.bias != nullptr) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    if (n0 + col + t < N)
-                        bv[t] = bits_to_float<T::BF16>(p.bias[n0 + col + t]);
-            }
+                    for (int t = 0; t < 4; ++t)
+                        if (n0 + col + t < N)
+                            bv[t] = bits_to_float<T::BF16>(p.bias[n0 + col + t]);
+                }
 #pragma unroll
-            for (int fm = 0; fm < T::FM; ++fm) {
-                const int row = wm * T::TM + fm * T::MI + (lane & (T::MI - 1));
-                const int odd = (cpar + (int)(((m0 + row) * p.ldc + n0) & 1)) & 1;
-                const typename T::Acc &v = acc[fm][fn];
-                const uint32_t lo = epi_pack2<T::BF16>(v[4 * g + 0] + bv[0], v[4 * g + 1] + bv[1], relu);
-                const uint32_t hi = epi_pack2<T::BF16>(v[4 * g + 2] + bv[2], v[4 * g + 3] + bv[3], relu);
-                lds_u16 *dst = cst + row * RP::CLD + col;
-                if (!odd) {
-                    *reinterpret_cast<__attribute__((address_space(3))) u32x2 *>(dst) = u32x2{lo, hi};
-                } else {
-                    dst[1] = (uint16_t)(lo & 0xffff);
-                    *reinterpret_cast<__attribute__((address_space(3))) uint32_t *>(dst + 2) =
-                        (lo >> 16) | (hi << 16);
-                    dst[4] = (uint16_t)(hi >> 16);
+                for (int fm = 0; fm < T::FM; ++fm) {
+                    const int row = wm * T::TM + fm * T::MI + (lane & (T::MI - 1));
+                    const int odd = (cpar + (int)(((m0 + row) * p.ldc + n0) & 1)) & 1;
+                    const u32x2 w = finish4<T, FAST>(acc[fm][fn], g, bv, relu);
+                    lds_u16 *dst = cst + row * RP::CLD + col;
+                    if (!odd) {
+                        *reinterpret_cast<__attribute__((address_space(3))) u32x2 *>(dst) = w;
+                    } else {
+                        dst[1] = (uint16_t)(w.x & 0xffff);
+                        *reinterpret_cast<__attribute__((address_space(3))) uint32_t *>(dst + 2) =
+                            (w.x >> 16) | (w.y << 16);
+                        dst[4] = (uint16_t)(w.y >> 16);
+                    }
                 }
             }
         }
-    }
+    };
+    if (p.bias == nullptr && relu)
+        stage_c(std::true_type{});
+    else
+        stage_c(std::false_type{});
     block_barrier();
     const int64_t nrow = (N - n0) < T::BN ? (N - n0) : T::BN;
     for (int q = tid; q < T::BM * RP::CCH; q += T::NT) {
@@ -878,8 +1182,9 @@ gemm_relu_ragged_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
         const int j0 = 8 * ch - odd;   // row element held by the chunk's first slot
         const lds_u16 *src = cst + row * RP::CLD + 8 * ch;
         if (j0 >= 0 && j0 + 8 <= nrow) {
-            *reinterpret_cast<u32x4_a4 *>(g + j0) =
-                *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(src);
+            __builtin_nontemporal_store(
+                *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(src),
+                reinterpret_cast<u32x4_a4 *>(g + j0));
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -965,14 +1270,19 @@ hipError_t launch_all_configs(int cfg, const GemmArgs &p, hipStream_t stream, in
     case 32: return launch_dma<Mode<Cfg<256, 256, 64, 2, 4, 2, 1, 1, true, 16>, 0>>(p, stream, groupM);
     case 33: return launch_dma<Mode<Cfg<256, 256, 64, 2, 2, 2, 1, 1, true, 16>, 0>>(p, stream, groupM);
     case 34: return launch_dma<Mode<Cfg<128, 128, 64, 4, 2, 4, 1, 1, true, 16>, 0>>(p, stream, groupM);
+    // persistent workgroups walking a list of tiles (many short problems)
+    case 35: return launch_stream<Mode<Cfg<128, 128, 64, 4, 2, 3, 1, 1, true, 16>, 0>>(p, stream);
+    case 36: return launch_stream<Mode<Cfg<128, 128, 64, 4, 2, 4, 1, 1, true, 16>, 0>>(p, stream);
+    case 37: return launch_stream<Mode<Cfg<128, 128, 64, 2, 2, 3, 1, 1, true, 16>, 0>>(p, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
 
 // bf16 and (N,K)-B instances exist for the configurations the dispatcher
-// picks by default: 256x256 (32), 128x128 (34), short K (12) and few tiles
-// (20), and for the 32x32x16 forms of the first two (8, 29).
+// picks by default: 256x256 (32), 128x128 (34), short K (12), many short
+// problems (36) and few tiles (20), and for the 32x32x16 forms of the first
+// two (8, 29).
 template <int MODE>
 hipError_t launch_default_configs(int cfg, const GemmArgs &p, hipStream_t stream, int groupM)
 {
@@ -983,6 +1293,7 @@ hipError_t launch_default_configs(int cfg, const GemmArgs &p, hipStream_t stream
     case 29: return launch_dma<Mode<Cfg<128, 128, 64, 4, 2, 4>, MODE>>(p, stream, groupM);
     case 12: return launch_dma<Mode<Cfg<128, 128, 32, 2, 2, 2, 4>, MODE>>(p, stream, groupM);
     case 20: return launch_dma<Mode<Cfg<64, 64, 64, 2, 2, 4, 1, 2>, MODE>>(p, stream, groupM);
+    case 36: return launch_stream<Mode<Cfg<128, 128, 64, 4, 2, 4, 1, 1, true, 16>, MODE>>(p, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -999,7 +1310,8 @@ bool dma_layout_ok(const GemmArgs &p)
 bool dma_config_has_mode(int cfg, int mode)
 {
     return mode == 0 ? (cfg >= 0 && cfg < kDmaConfigs)
-                     : (cfg == 32 || cfg == 34 || cfg == 8 || cfg == 29 || cfg == 12 || cfg == 20);
+                     : (cfg == 32 || cfg == 34 || cfg == 8 || cfg == 29 || cfg == 12 || cfg == 20 ||
+                        cfg == 36);
 }
 
 hipError_t launch_ragged_config(int cfg, const GemmArgs &p, hipStream_t stream, int groupM)

@@ -27,24 +27,43 @@ struct GemmArgs {
     int b_nk;
 };
 
+// x if x > 0 else +0, NaN included: v_max_f32 against 0 returns the operand
+// that is not a NaN.  Written out because the compiler puts a canonicalising
+// max in front of fmaxf on values it cannot prove canonical (matrix-core
+// results), one more VALU instruction per element.  The accumulations that
+// feed it never produce -0 (their sums start from +0).
+__device__ __forceinline__ float relu_f32(float x)
+{
+    float r;
+    asm("v_max_f32 %0, 0, %1" : "=v"(r) : "v"(x));
+    return r;
+}
+
+// Two outputs rounded to nearest even into fp16 (bf16 when BF16), low | high
+// << 16, in one v_cvt_pk instruction; RELU applies relu_f32 first.
+template <bool BF16, bool RELU>
+__device__ __forceinline__ uint32_t pack2(float a, float b)
+{
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    if constexpr (RELU) {
+        a = relu_f32(a);
+        b = relu_f32(b);
+    }
+    const f32x2_t v = {a, b};
+    if constexpr (BF16)
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+
 // Epilogue of two outputs: ReLU (x if x > 0 else +0) when `relu`, then round
 // to nearest even into fp16 (or bf16 when BF16); packed low | high << 16.
 template <bool BF16 = false>
 __device__ __forceinline__ uint32_t epi_pack2(float a, float b, bool relu)
 {
-    if (relu) {
-        a = a > 0.0f ? a : 0.0f;
-        b = b > 0.0f ? b : 0.0f;
-    }
-    uint16_t ha, hb;
-    if constexpr (BF16) {
-        ha = __builtin_bit_cast(uint16_t, (__bf16)a);
-        hb = __builtin_bit_cast(uint16_t, (__bf16)b);
-    } else {
-        ha = __builtin_bit_cast(uint16_t, (_Float16)a);
-        hb = __builtin_bit_cast(uint16_t, (_Float16)b);
-    }
-    return (uint32_t)ha | ((uint32_t)hb << 16);
+    return relu ? pack2<BF16, true>(a, b) : pack2<BF16, false>(a, b);
 }
 
 // One element's bit pattern (fp16, or bf16 when BF16) as a float.
@@ -138,9 +157,11 @@ struct AttnArgs {
 hipError_t launch_attention(const AttnArgs &p, hipStream_t stream);
 
 // Host helpers of the entry points (defined in api.cpp): the per-device
-// architecture check (TG_OK or an error status) and the record of the last
+// architecture check (TG_OK or an error status), the current device's
+// compute-unit count (0 when it cannot be had) and the record of the last
 // path used.
 int host_check_device();
+int host_device_cus();
 void host_set_last_path(int path);
 
 // Every launcher enqueues on `stream` and returns hipGetLastError().  The
@@ -154,7 +175,7 @@ hipError_t launch_tile256(const GemmArgs &p, hipStream_t stream, int groupM);
 // block tile / K tile / stage count; see gemm_dma.hip.
 // Every configuration exists for fp16 with a (K,N) B (mode 0); bf16 and (N,K)
 // B (mode bits 1 and 2) exist for the default configurations only.
-constexpr int kDmaConfigs = 35;
+constexpr int kDmaConfigs = 38;
 hipError_t launch_dma_config(int cfg, const GemmArgs &p, hipStream_t stream, int groupM);
 // Ragged layouts (see gemm_dma.hip): A as for the direct-to-LDS kernels
 // (16-byte aligned rows, K a multiple of 8), B stored (K,N) with any 2-byte
