@@ -16,8 +16,8 @@ std::atomic<int> g_last_path{TG_PATH_AUTO};
 std::atomic<int> g_tile_variant{-1};
 
 // Default direct-to-LDS configurations of the tile paths.
-// 128x128x64, 4 stages, 8 waves (4x2, 32x64 wave tiles), 16x16x32 products
-constexpr int kTile128Default = 34;
+// 128x128x64, 4 stages, 8 waves (2x4, 64x32 wave tiles), 16x16x32 products
+constexpr int kTile128Default = 38;
 // 256x256x64, 2 stages, 8 waves (2 per SIMD), 16x16x32 products
 constexpr int kTile256Default = 32;
 constexpr int kRagged256 = 2;       // the ragged kernel's 256x256 and 128x128 configurations

@@ -240,43 +240,6 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[KB], f16x8 (&pf)[2 * KB
     l_run += ls[0] + ls[1];
 }
 
-// The softmax step of softmax_tile for one 32-key block without the
-// accumulator rescale: raises the running maximum when the block exceeds it
-// by more than 2^8 (`grow`, with `alpha` the factor the caller must apply to
-// its output accumulator), rescales the sum and writes the fp16
-// probabilities.  Free of branches, so it can share a basic block (and the
-// scheduler's interleaving) with independent matrix work.
-__device__ __forceinline__ void softmax_block(const f32x16 &s, f16x8 (&pf)[2], float &m_run,
-                                              float &l_run, float sl2, float &alpha, bool &grow)
-{
-    float mt = -__builtin_inff();
-#pragma unroll
-    for (int r = 0; r < 16; r += 2)
-        mt = __builtin_fmaxf(mt, __builtin_fmaxf(s[r], s[r + 1]));
-    mt = max_pair(mt);
-    const float m_tile = __builtin_fmaxf(mt * sl2, -1.0e30f);
-    grow = m_tile > m_run + kGrowLog2;
-    const float m_new = grow ? m_tile : m_run;
-    alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    const float neg_m = -m_run;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            pf[kk][j] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * kk + j], sl2, neg_m));
-    }
-    float ls[2] = {0.0f, 0.0f};
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            ls[j & 1] = __builtin_amdgcn_fdot2(f16x2{pf[kk][2 * j], pf[kk][2 * j + 1]},
-                                               f16x2{(_Float16)1.0f, (_Float16)1.0f}, ls[j & 1], false);
-    }
-    l_run = l_run * alpha + (ls[0] + ls[1]);
-}
-
 // Two waves per SIMD: lets the scheduler keep LDS reads in flight ahead of
 // the matrix instructions that consume them instead of minimizing registers.
 template <class T>
@@ -707,8 +670,11 @@ mla_decode_kernel(MlaArgs p)
     // (raised only when the tile exceeds it by more than 2^8; `grow` and
     // `alpha` tell the caller to rescale its output), the fp16
     // probabilities pf in the value product's operand order and the running
-    // sum of the rounded probabilities.  Step for step the arithmetic of
-    // softmax_block.
+    // sum of the rounded probabilities.  The arithmetic: the tile maximum
+    // of the scores (this lane's 16 and its partner lane's), scaled by sl2
+    // and floored at -1e30; grow when it exceeds m_run by more than 2^8, then
+    // alpha = exp2(m_run - m_new); p = fp16(exp2(s * sl2 - m_run)); l_run =
+    // l_run * alpha + the sum of the fp16 p (dot products with ones).
     float sa0 = 0.f, sa1 = 0.f, sa2 = 0.f, sa3 = 0.f, sa4 = 0.f, sa5 = 0.f;
     float mt = 0.f, m_new = 0.f, alpha = 1.0f, neg_m = 0.f, x_even = 0.f, ls0 = 0.f, ls1 = 0.f;
     bool grow = false;

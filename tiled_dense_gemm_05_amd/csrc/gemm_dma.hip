@@ -1274,21 +1274,25 @@ hipError_t launch_all_configs(int cfg, const GemmArgs &p, hipStream_t stream, in
     case 35: return launch_stream<Mode<Cfg<128, 128, 64, 4, 2, 3, 1, 1, true, 16>, 0>>(p, stream);
     case 36: return launch_stream<Mode<Cfg<128, 128, 64, 4, 2, 4, 1, 1, true, 16>, 0>>(p, stream);
     case 37: return launch_stream<Mode<Cfg<128, 128, 64, 2, 2, 3, 1, 1, true, 16>, 0>>(p, stream);
+    // 64x32 wave tiles (a 2x4 wave grid): each wave's B fragments, read by
+    // transpose, serve four A fragments, so a k step needs fewer LDS bytes
+    case 38: return launch_dma<Mode<Cfg<128, 128, 64, 2, 4, 4, 1, 1, true, 16>, 0>>(p, stream, groupM);
     default: return hipErrorInvalidValue;
     }
 }
 
 
 // bf16 and (N,K)-B instances exist for the configurations the dispatcher
-// picks by default: 256x256 (32), 128x128 (34), short K (12), many short
-// problems (36) and few tiles (20), and for the 32x32x16 forms of the first
-// two (8, 29).
+// picks by default: 256x256 (32), 128x128 (38), short K (12), many short
+// problems (36) and few tiles (20), for the 4x2 wave grid of 128x128 (34) and
+// for the 32x32x16 forms of 32 and 34 (8, 29).
 template <int MODE>
 hipError_t launch_default_configs(int cfg, const GemmArgs &p, hipStream_t stream, int groupM)
 {
     switch (cfg) {
     case 32: return launch_dma<Mode<Cfg<256, 256, 64, 2, 4, 2, 1, 1, true, 16>, MODE>>(p, stream, groupM);
     case 34: return launch_dma<Mode<Cfg<128, 128, 64, 4, 2, 4, 1, 1, true, 16>, MODE>>(p, stream, groupM);
+    case 38: return launch_dma<Mode<Cfg<128, 128, 64, 2, 4, 4, 1, 1, true, 16>, MODE>>(p, stream, groupM);
     case 8: return launch_dma<Mode<Cfg<256, 256, 64, 2, 4, 2>, MODE>>(p, stream, groupM);
     case 29: return launch_dma<Mode<Cfg<128, 128, 64, 4, 2, 4>, MODE>>(p, stream, groupM);
     case 12: return launch_dma<Mode<Cfg<128, 128, 32, 2, 2, 2, 4>, MODE>>(p, stream, groupM);
@@ -1311,7 +1315,7 @@ bool dma_config_has_mode(int cfg, int mode)
 {
     return mode == 0 ? (cfg >= 0 && cfg < kDmaConfigs)
                      : (cfg == 32 || cfg == 34 || cfg == 8 || cfg == 29 || cfg == 12 || cfg == 20 ||
-                        cfg == 36);
+                        cfg == 36 || cfg == 38);
 }
 
 hipError_t launch_ragged_config(int cfg, const GemmArgs &p, hipStream_t stream, int groupM)
