@@ -541,7 +541,8 @@ def summarize(workload: str, stats_dir: str, fetch_dir: str, write_dir: str, com
     g_fetch = sum(fetch[gemm_name]) / len(fetch[gemm_name]) * kib * f_fetch
     g_write = sum(write[gemm_name]) / len(write[gemm_name]) * kib * f_write
     w = wl.WORKLOADS[workload]
-    family = ("gemm_relu_dma_kernel" if "dma_kernel" in top["Name"] else
+    family = ("gemm_relu_dma_stream_kernel" if "dma_stream_kernel" in top["Name"] else
+              "gemm_relu_dma_kernel" if "dma_kernel" in top["Name"] else
               "gemm_relu_skinny_kernel" if "skinny_kernel" in top["Name"] else
               "gemm_relu_tile_kernel" if "tile_kernel" in top["Name"] else "kernel")
     md = os.path.join(PROFILES, f"{family}-{workload}.md")
@@ -694,7 +695,8 @@ def summarize_run(workload: str, root: str, commands: list[str]):
     peak = PEAK_F16_TFLOPS if compute else PEAK_HBM_GBS
     unit = "TFLOP/s" if compute else "GB/s"
     rate_trace = work / (trace_ns * 1e-9) / scale
-    family = ("gemm_relu_dma_kernel" if "dma_kernel" in name else
+    family = ("gemm_relu_dma_stream_kernel" if "dma_stream_kernel" in name else
+              "gemm_relu_dma_kernel" if "dma_kernel" in name else
               "gemm_relu_ragged_kernel" if "ragged_kernel" in name else
               "gemm_relu_skinny_kernel" if "skinny_kernel" in name else
               "gemm_relu_tile_kernel" if "tile_kernel" in name else "kernel")

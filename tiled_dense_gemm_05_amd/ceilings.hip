@@ -22,6 +22,16 @@
 //   hbm_read           A plain streaming read: 16 bytes per lane, grid-stride
 //                      over 256 MiB, three buffers taken in turn so that no
 //                      pass is served from the 256 MB last-level cache.
+//   hbm_copy_batched   The traffic of the strided batch of 1024 128x128x64
+//                      products without the arithmetic: 1024 workgroups, each
+//                      reading 16 KiB from each of two buffers and writing
+//                      32 KiB, 16 bytes per lane, non-temporal loads and
+//                      stores, ten buffer sets taken in turn (64 MiB a pass,
+//                      none of it left in the last-level cache).
+//   l2_load_per_cu     What one CU's loads fetch from data the L2 holds: one
+//                      8-wave workgroup per CU, each wave streaming 4 KiB
+//                      blocks of a 2 MiB buffer (16 bytes per lane), bytes per
+//                      shader clock per CU and GB/s per CU.
 //
 // Usage: tg_ceilings [seconds_per_figure]   (default 0.2)
 #include <hip/hip_runtime.h>
@@ -155,6 +165,57 @@ __global__ void __launch_bounds__(512) hbm_read(const u32x4 *p, int64_t n16, uin
         out[blockIdx.x] = v;
 }
 
+// Workgroup g reads a[g] and b[g] (16 KiB each) and writes c[g] (32 KiB).
+__global__ void __launch_bounds__(256) copy_batched(const u32x4 *a, const u32x4 *b, u32x4 *c)
+{
+    const int t = threadIdx.x;
+    const size_t g = blockIdx.x;
+    const u32x4 *ag = a + g * 1024, *bg = b + g * 1024;
+    u32x4 *cg = c + g * 2048;
+    u32x4 ra[4], rb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        ra[i] = __builtin_nontemporal_load(ag + i * 256 + t);
+        rb[i] = __builtin_nontemporal_load(bg + i * 256 + t);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        __builtin_nontemporal_store(ra[i], cg + i * 256 + t);
+        __builtin_nontemporal_store(rb[i], cg + (i + 4) * 256 + t);
+    }
+}
+
+// Each wave streams 4 KiB blocks (four 16-byte loads per lane) of an
+// L2-resident buffer of `blocks4k` blocks, starting at its own block and
+// stepping 37 blocks at a time; clock64 around wave 0's loop.
+__global__ void __launch_bounds__(512) l2_load(const u32x4 *p, int blocks4k, int iters, uint32_t *out,
+                                               long long *clk)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int blk = (blockIdx.x * 8 + w) % blocks4k;
+    __syncthreads();
+    const long long c0 = clock64();
+    u32x4 acc = {0, 0, 0, 0};
+    for (int it = 0; it < iters; ++it) {
+        const u32x4 *q = p + (size_t)blk * 256;
+        u32x4 v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v[j] = q[j * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc ^= v[j];
+        blk = (blk + 37) % blocks4k;
+    }
+    const uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    if (x == 0x9e3779b9u)   // practically never: keeps the loads without a store per lane
+        out[blockIdx.x] = x;
+    __syncthreads();
+    const long long c1 = clock64();
+    if (threadIdx.x == 0)
+        clk[blockIdx.x] = c1 - c0;
+}
+
 }  // namespace
 
 int main(int argc, char **argv)
@@ -261,6 +322,70 @@ int main(int argc, char **argv)
                     (double)bytes * reps / (ms * 1e-3) / 1e9, ms * 1e3 / reps);
         for (auto &b : buf)
             CHECK(hipFree(b));
+    }
+    // the batched product's traffic, no arithmetic
+    {
+        constexpr int kSets = 10, kGroups = 1024;
+        const size_t ab = (size_t)kGroups * 16384, cb = (size_t)kGroups * 32768;
+        u32x4 *a[kSets], *b[kSets], *c[kSets];
+        for (int i = 0; i < kSets; ++i) {
+            CHECK(hipMalloc(&a[i], ab));
+            CHECK(hipMalloc(&b[i], ab));
+            CHECK(hipMalloc(&c[i], cb));
+            CHECK(hipMemset(a[i], 1, ab));
+            CHECK(hipMemset(b[i], 2, ab));
+        }
+        for (int i = 0; i < 2 * kSets; ++i)
+            hipLaunchKernelGGL(copy_batched, dim3(kGroups), dim3(256), 0, 0, a[i % kSets], b[i % kSets],
+                               c[i % kSets]);
+        CHECK(hipGetLastError());
+        CHECK(hipDeviceSynchronize());
+        const int reps = 400;
+        CHECK(hipEventRecord(e0, 0));
+        for (int i = 0; i < reps; ++i)
+            hipLaunchKernelGGL(copy_batched, dim3(kGroups), dim3(256), 0, 0, a[i % kSets], b[i % kSets],
+                               c[i % kSets]);
+        CHECK(hipGetLastError());
+        CHECK(hipEventRecord(e1, 0));
+        CHECK(hipEventSynchronize(e1));
+        float ms = 0;
+        CHECK(hipEventElapsedTime(&ms, e0, e1));
+        const double us = ms * 1e3 / reps;
+        std::printf("{\"figure\": \"hbm_copy_batched\", \"us_per_pass\": %.2f, \"gbs\": %.0f, "
+                    "\"bytes_per_pass\": %zu}\n", us, (double)(2 * ab + cb) / (us * 1e-6) / 1e9, 2 * ab + cb);
+        for (int i = 0; i < kSets; ++i) {
+            CHECK(hipFree(a[i]));
+            CHECK(hipFree(b[i]));
+            CHECK(hipFree(c[i]));
+        }
+    }
+    // one CU's loads from L2-resident data
+    {
+        const int blocks4k = 512;   // 2 MiB
+        u32x4 *buf;
+        CHECK(hipMalloc(&buf, (size_t)blocks4k * 4096));
+        CHECK(hipMemset(buf, 3, (size_t)blocks4k * 4096));
+        const int iters = 4096;
+        for (int pass = 0; pass < 2; ++pass) {
+            CHECK(hipEventRecord(e0, 0));
+            hipLaunchKernelGGL(l2_load, dim3(blocks), dim3(512), 0, 0, buf, blocks4k, iters,
+                               (uint32_t *)d_out, d_clk);
+            CHECK(hipGetLastError());
+            CHECK(hipEventRecord(e1, 0));
+            CHECK(hipEventSynchronize(e1));
+        }
+        float ms = 0;
+        CHECK(hipEventElapsedTime(&ms, e0, e1));
+        CHECK(hipMemcpy(clk.data(), d_clk, (size_t)blocks * sizeof(long long), hipMemcpyDeviceToHost));
+        double cyc = 0;
+        for (int i = 0; i < blocks; ++i)
+            cyc += (double)clk[i];
+        cyc /= blocks;
+        const double per_cu = 8.0 * iters * 4096;   // bytes one workgroup loads
+        std::printf("{\"figure\": \"l2_load_per_cu\", \"bytes_per_clock_per_cu\": %.1f, "
+                    "\"gbs_per_cu\": %.1f, \"waves_per_cu\": 8}\n",
+                    per_cu / cyc, per_cu / (ms * 1e-3) / 1e9);
+        CHECK(hipFree(buf));
     }
     CHECK(hipFree(d_in));
     CHECK(hipFree(d_out));
