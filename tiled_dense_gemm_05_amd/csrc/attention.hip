@@ -932,13 +932,17 @@ mla_decode_kernel(MlaArgs p)
     }
 }
 
-// Combines the key ranges of one (sequence, head): with M the largest range
+// Combines the key ranges of (sequence, head) rows: with M the largest range
 // maximum and w_s = 2^(m_s - M) l_s, O = sum_s w_s o_s / sum_s w_s, ranges
-// added in order; thread t owns output values 4t .. 4t + 3.
-__global__ void __launch_bounds__(kMlaDl / 4) mla_combine_kernel(MlaArgs p)
+// added in order.  Wave r of a workgroup owns row 4 * blockIdx.x + r, lane t
+// its output values 8t .. 8t + 7 (16-byte loads and stores).
+constexpr int kCombineRows = 4;
+__global__ void __launch_bounds__(64 * kCombineRows) mla_combine_kernel(MlaArgs p)
 {
-    const int64_t bh = blockIdx.x;
-    const int d = threadIdx.x * 4;
+    const int64_t bh = (int64_t)blockIdx.x * kCombineRows + (threadIdx.x >> 6);
+    if (bh >= p.B * p.H)
+        return;
+    const int d = (threadIdx.x & 63) * 8;
     const int S = p.splits;
     const uint16_t *part = static_cast<const uint16_t *>(p.part);
     const float2 *ml = reinterpret_cast<const float2 *>(part + p.B * p.H * S * kMlaDl) + bh * S;
@@ -946,22 +950,24 @@ __global__ void __launch_bounds__(kMlaDl / 4) mla_combine_kernel(MlaArgs p)
     for (int s = 0; s < S; ++s)
         M = __builtin_fmaxf(M, ml[s].x);
     float L = 0.0f;
-    float4 acc = float4{0.0f, 0.0f, 0.0f, 0.0f};
+    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
     for (int s = 0; s < S; ++s) {
         const float2 v = ml[s];
         const float w = __builtin_amdgcn_exp2f(v.x - M) * v.y;
         L += w;
-        const u32x2 o = *reinterpret_cast<const u32x2 *>(part + (bh * S + s) * kMlaDl + d);
-        acc.x += w * bits_to_float<false>((uint16_t)(o.x & 0xffff));
-        acc.y += w * bits_to_float<false>((uint16_t)(o.x >> 16));
-        acc.z += w * bits_to_float<false>((uint16_t)(o.y & 0xffff));
-        acc.w += w * bits_to_float<false>((uint16_t)(o.y >> 16));
+        const u32x4 o = *reinterpret_cast<const u32x4 *>(part + (bh * S + s) * kMlaDl + d);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc[2 * j] += w * bits_to_float<false>((uint16_t)(o[j] & 0xffff));
+            acc[2 * j + 1] += w * bits_to_float<false>((uint16_t)(o[j] >> 16));
+        }
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    u32x2 out;
-    out.x = epi_pack2<false>(acc.x * inv, acc.y * inv, false);
-    out.y = epi_pack2<false>(acc.z * inv, acc.w * inv, false);
-    *reinterpret_cast<u32x2 *>(p.O + bh * kMlaDl + d) = out;
+    u32x4 out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        out[j] = epi_pack2<false>(acc[2 * j] * inv, acc[2 * j + 1] * inv, false);
+    __builtin_nontemporal_store(out, reinterpret_cast<u32x4 *>(p.O + bh * kMlaDl + d));
 }
 
 }  // namespace
@@ -988,8 +994,9 @@ hipError_t launch_mla_decode(const MlaArgs &p, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1)
         return e;
-    hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(p.B * p.H)), dim3(kMlaDl / 4), 0,
-                       stream, p);
+    hipLaunchKernelGGL(mla_combine_kernel,
+                       dim3((unsigned)((p.B * p.H + kCombineRows - 1) / kCombineRows)),
+                       dim3(64 * kCombineRows), 0, stream, p);
     return hipGetLastError();
 }
 
