@@ -111,7 +111,7 @@ struct Cfg {
     static_assert(LOADS * (STAGES - 1) <= 63, "vmcnt range");
     static_assert(KSTEPS <= 4, "k steps per tile");
     static constexpr int RING = KG * STAGES * STAGE * 2;        // bytes of LDS rings
-    static constexpr int RED = (KG - 1) * NW * FM * FN * 64 * 64; // partial sums of groups > 0
+    static constexpr int RED = (KG - 1) * NW * FM * FN * 64 * (int)sizeof(Acc); // partial sums of groups > 0
     static constexpr int CST = BM * BN * 2;                      // the fp16 C tile (epilogue)
     static constexpr int LDS0 = RING > RED ? RING : RED;
     static constexpr int LDS = LDS0 > CST ? LDS0 : CST;
