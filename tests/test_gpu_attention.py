@@ -90,7 +90,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
 @pytest.mark.parametrize("B,Sq,Sk,H,D,causal", CASES)
 def test_attention_matches_oracle(tg, oracle_lib, variant, B, Sq, Sk, H, D, causal):
     q, k, v = qkv(B, Sq, Sk, H, D, Sq + Sk + D)
@@ -190,7 +190,7 @@ def test_more_heads_than_a_grid_row(tg, oracle_lib):
         check(run(tg, q, k, v, B, Sq, Sk, H, D, 0.125, causal), ref, v)
 
 
-@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
 def test_more_query_blocks_than_a_grid_column(tg, variant):
     # 65536 * 256 + 100 queries: more query blocks than 65535 (the grid's y
     # extent), so the launcher splits them over several launches.  One key:
@@ -264,7 +264,7 @@ def run_gqa(tg, q, k, v, B, Sq, Sk, H, Hkv, D, scale, causal):
     return out[:n]
 
 
-@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
 @pytest.mark.parametrize("B,Sq,Sk,H,Hkv,D,causal", GQA_CASES)
 def test_grouped_query_matches_oracle(tg, oracle_lib, variant, B, Sq, Sk, H, Hkv, D, causal):
     q, k, v = qkv_gqa(B, Sq, Sk, H, Hkv, D, Sq + Sk + H)

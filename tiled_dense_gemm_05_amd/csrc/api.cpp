@@ -470,7 +470,7 @@ int tg_set_attention_variant(int variant)
 {
     if (variant == -1)
         variant = kAttnDefault;
-    if (variant < 0 || variant > 1)
+    if (variant < 0 || variant > 3)
         return -2;
     return g_attn_variant.exchange(variant);
 }

@@ -449,6 +449,287 @@ hipError_t launch_attn(const AttnArgs &p, hipStream_t stream)
 }
 
 // ---------------------------------------------------------------------------
+// The same attention forward on v_mfma_f32_16x16x32_f16 products.  The
+// matrix cores run the same flops on twice as many smaller products, which
+// draw less power each; on this power-capped part that buys clock.
+//
+// Layout (operand roles swapped as above: S^T = K Q^T, O^T = V^T P^T):
+//  * A wave owns 32 query rows as two blocks of 16 (qb); lane c = lane % 16
+//    of 16-lane group g = lane / 16 holds row 16 qb + c of each block.
+//  * Score fragment (qb, kb) covers 16 keys of the 64-key tile: the lane
+//    holds keys 16 kb + 4 g .. 4 g + 3 of its row.  A row's 64 scores sit in
+//    the four lanes c, c + 16, c + 32, c + 48: its maximum and sum take two
+//    exchanges (v_permlane16_swap, then v_permlane32_swap).
+//  * The probabilities of k step ks (keys 32 ks .. 32 ks + 31) are the P^T
+//    operand as they lie: the lane's 8 k values are keys 32 ks + 4 g + 0..3
+//    and 32 ks + 16 + 4 g + 0..3; the V^T operand takes the same keys by two
+//    transpose reads of 4 consecutive rows each.
+//  * Output fragment (qb, db): the lane holds values 16 db + 4 g .. + 3 of
+//    its row.
+
+// The maximum of x over the four lanes c, c + 16, c + 32, c + 48.
+__device__ __forceinline__ float max_quad(float x)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float m = __builtin_fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    return __builtin_fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// The sum of x over the same four lanes (in a fixed order: every lane gets
+// the same bits).
+__device__ __forceinline__ float sum_quad(float x)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+template <class T>
+__global__ void __launch_bounds__(64 * T::NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attention_fwd16_kernel(AttnArgs p)
+{
+    constexpr int DS = T::D / 32;    // 32-wide d steps of the scores
+    constexpr int DB = T::D / 16;    // 16-wide d blocks of the output
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[T::LDS / 2];
+    const lds_u16 *lds = (const lds_u16 *)smem;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int c16 = lane & 15, g4 = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t bh = blockIdx.x;                 // (batch, key/value head)
+    const int64_t b = bh / p.Hkv, kvh = bh % p.Hkv;
+    const int64_t Sq = p.Sq, Sk = p.Sk;
+    const int64_t g = p.H / p.Hkv;                   // query heads per key/value head
+    const int64_t rows = Sq * g;
+    const int64_t qj = p.qb0 + (int64_t)blockIdx.y;
+    const int64_t qblk = p.causal ? p.nqb - 1 - qj : qj;
+    const int64_t q0 = qblk * T::BQ;               // first row of the block
+    const int64_t rs = p.Hkv * T::D;                 // K/V elements between positions
+    const int64_t shift = Sk - Sq;
+    const int64_t wq0 = (q0 + wave * 32) / g;        // position of the wave's first row
+    const int64_t wq1 = (q0 + wave * 32 + 31) / g;   // ... and of its last
+    // this lane's two rows (one per 16-row block): position, head, horizon
+    bool live[2];
+    int64_t qpos[2], head[2], horizon[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int64_t r = q0 + wave * 32 + qb * 16 + c16;
+        live[qb] = r < rows;
+        qpos[qb] = r / g;
+        head[qb] = kvh * g + r % g;
+        horizon[qb] = qpos[qb] + shift;
+    }
+
+    int64_t kend = Sk;
+    if (p.causal) {
+        const int64_t lim = (q0 + T::BQ - 1) / g + shift + 1;
+        kend = lim < 0 ? 0 : (lim < Sk ? lim : Sk);
+    }
+    const int tiles = (int)((kend + kBK - 1) / kBK);
+
+    // Q^T fragments: lane holds Q[row][32 ds + 8 g .. + 7] of each block.
+    f16x8 qf[2][DS];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const uint16_t *qrow =
+            p.Q + ((b * Sq + (live[qb] ? qpos[qb] : 0)) * p.H + (live[qb] ? head[qb] : 0)) * T::D;
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+            qf[qb][ds] = f16x8{};
+            if (live[qb])
+                qf[qb][ds] = *reinterpret_cast<const f16x8 *>(qrow + ds * 32 + 8 * g4);
+            if (p.scale < 0.0f)
+                qf[qb][ds] = -qf[qb][ds];
+        }
+    }
+
+    // DMA plan, as in attention_fwd_kernel.
+    uint32_t k_voff[T::LD], v_voff[T::LD];
+    int k_row[T::LD];
+#pragma unroll
+    for (int i = 0; i < T::LD; ++i) {
+        const int blk = wave + T::NW * i;
+        const int row = blk * T::RPB + lane / T::CD;
+        const int pc = lane % T::CD;
+        k_row[i] = row;
+        k_voff[i] = (uint32_t)((row * rs + swz_k<T::CD>(row, pc) * 8) * 2);
+        v_voff[i] = (uint32_t)((row * rs + swz_v<T::CD>(row, pc) * 8) * 2);
+    }
+    const uint16_t *Kb = p.K + (b * Sk * p.Hkv + kvh) * T::D;
+    const uint16_t *Vb = p.V + (b * Sk * p.Hkv + kvh) * T::D;
+    auto issue = [&](int t) {
+        const int64_t k0 = (int64_t)t * kBK;
+        const i32x4 rk = make_rsrc(Kb + k0 * rs);
+        const i32x4 rv = make_rsrc(Vb + k0 * rs);
+        const uint32_t base = lds_base + (uint32_t)((t & 1) * T::STAGE * 2);
+#pragma unroll
+        for (int i = 0; i < T::LD; ++i) {
+            const bool ok = k0 + k_row[i] < kend;
+            dma16(rk, ok ? k_voff[i] : kOutOfRange, base + (uint32_t)((wave + T::NW * i) * 1024));
+            dma16(rv, ok ? v_voff[i] : kOutOfRange,
+                  base + (uint32_t)(T::TILE * 2 + (wave + T::NW * i) * 1024));
+        }
+    };
+
+    f32x4 acc_o[2][DB];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            acc_o[qb][db] = f32x4{};
+    float m_run[2] = {-1.0e30f, -1.0e30f}, l_run[2] = {0.0f, 0.0f};
+    const float sl2 = __builtin_fmaxf(__builtin_fabsf(p.scale) * 1.44269504088896340736f, 1.0e-30f);
+
+    if (tiles > 0)
+        issue(0);
+    for (int t = 0; t < tiles; ++t) {
+        wait_vmcnt<0>();
+        block_barrier();
+        if (t + 1 < tiles)
+            issue(t + 1);
+        const int64_t k0 = (int64_t)t * kBK;
+        if (p.causal && k0 > wq1 + shift)
+            continue;
+        const lds_u16 *Ks = lds + (t & 1) * T::STAGE;
+        const lds_u16 *Vs = Ks + T::TILE;
+
+        // S^T = K Q^T: one 16-byte K read per (key block, d step) serves
+        // both row blocks.
+        f32x4 s[2][4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            s[0][kb] = f32x4{};
+            s[1][kb] = f32x4{};
+            const int row = kb * 16 + c16;
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds) {
+                const int c = ds * 4 + g4;
+                const f16x8 kf = *reinterpret_cast<const lds_f16x8 *>(
+                    Ks + row * T::D + swz_k<T::CD>(row, c) * 8);
+                s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[0][ds], s[0][kb], 0, 0, 0);
+                s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[1][ds], s[1][kb], 0, 0, 0);
+            }
+        }
+        if (!(k0 + kBK <= kend && (!p.causal || k0 + kBK - 1 <= wq0 + shift))) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                int64_t lim = kend - k0;
+                if (p.causal && horizon[qb] + 1 - k0 < lim)
+                    lim = horizon[qb] + 1 - k0;
+                lim = lim < 0 ? 0 : (lim > kBK ? kBK : lim);
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        s[qb][kb][i] = kb * 16 + 4 * g4 + i < lim ? s[qb][kb][i] : -__builtin_inff();
+            }
+        }
+        // softmax per row block; probabilities in the P^T operand order
+        f16x8 pf[2][2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            float mt = -__builtin_inff();
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                mt = __builtin_fmaxf(mt, __builtin_fmaxf(__builtin_fmaxf(s[qb][kb][0], s[qb][kb][1]),
+                                                         __builtin_fmaxf(s[qb][kb][2], s[qb][kb][3])));
+            mt = max_quad(mt);
+            const float m_tile = __builtin_fmaxf(mt * sl2, -1.0e30f);
+            const bool grow = m_tile > m_run[qb] + kGrowLog2;
+            if (__builtin_amdgcn_ballot_w64(grow)) {
+                const float m_new = grow ? m_tile : m_run[qb];
+                const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+                m_run[qb] = m_new;
+                l_run[qb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    acc_o[qb][db] *= alpha;
+            }
+            const float neg_m = -m_run[qb];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    pf[qb][ks][j] = (_Float16)__builtin_amdgcn_exp2f(
+                        __builtin_fmaf(s[qb][2 * ks + j / 4][j % 4], sl2, neg_m));
+            float ls[2] = {0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    ls[j & 1] = __builtin_amdgcn_fdot2(f16x2{pf[qb][ks][2 * j], pf[qb][ks][2 * j + 1]},
+                                                       f16x2{(_Float16)1.0f, (_Float16)1.0f}, ls[j & 1],
+                                                       false);
+            l_run[qb] += ls[0] + ls[1];
+        }
+        // O^T += V^T P^T: one pair of transpose reads per (d block, k step)
+        // serves both row blocks.
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                s16x4 vh[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int key = ks * 32 + 16 * hh + 4 * g4 + (c16 >> 2);
+                    const int d = db * 16 + 4 * (lane & 3);
+                    const lds_u16 *src = Vs + key * T::D + swz_v<T::CD>(key, d >> 3) * 8 + (d & 7);
+                    vh[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src);
+                }
+                const f16x8 vf = __builtin_bit_cast(
+                    f16x8, __builtin_shufflevector(vh[0], vh[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                acc_o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[0][ks], acc_o[0][db], 0, 0, 0);
+                acc_o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[1][ks], acc_o[1][db], 0, 0, 0);
+            }
+        }
+    }
+    wait_vmcnt<0>();
+
+    // Output: a row's sum of exponentials is split over its four lanes.
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const float l_all = sum_quad(l_run[qb]);
+        const float inv = l_all > 0.0f ? 1.0f / l_all : 0.0f;
+        if (live[qb]) {
+            uint16_t *orow = p.O + ((b * Sq + qpos[qb]) * p.H + head[qb]) * T::D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                u32x2 w;
+                w.x = epi_pack2<false>(acc_o[qb][db][0] * inv, acc_o[qb][db][1] * inv, false);
+                w.y = epi_pack2<false>(acc_o[qb][db][2] * inv, acc_o[qb][db][3] * inv, false);
+                *reinterpret_cast<u32x2 *>(orow + db * 16 + 4 * g4) = w;
+            }
+        }
+    }
+}
+
+template <int D, int NW>
+hipError_t launch_attn16(const AttnArgs &p, hipStream_t stream)
+{
+    const int64_t bh = p.B * p.Hkv;
+    const int64_t nqb = (p.Sq * (p.H / p.Hkv) + 32 * NW - 1) / (32 * NW);
+    if (bh > 0x7fffffff)
+        return hipErrorInvalidValue;
+    for (int64_t y0 = 0; y0 < nqb; y0 += 65535) {
+        AttnArgs q = p;
+        q.nqb = nqb;
+        q.qb0 = y0;
+        const int64_t gy = (nqb - y0) < 65535 ? (nqb - y0) : 65535;
+        hipLaunchKernelGGL((attention_fwd16_kernel<AttnCfg<D, NW>>), dim3((unsigned)bh, (unsigned)gy),
+                           dim3(64 * NW), 0, stream, q);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
 // Latent-attention decode (the MLA decode the pages measure: "TileLang paper
 // reading" page, section 5; "80-line MLA article" page, sections 1-2, which
 // give its 512 + 64 head size).  One query per sequence; every cached token
@@ -974,7 +1255,14 @@ __global__ void __launch_bounds__(64 * kCombineRows) mla_combine_kernel(MlaArgs 
 
 hipError_t launch_attention(const AttnArgs &p, hipStream_t stream)
 {
-    const int nw = p.variant == 1 ? 8 : 4;
+    // 0 / 1: four / eight waves on 32x32x16 products; 2 / 3: the same on
+    // 16x16x32 products
+    const int nw = (p.variant & 1) ? 8 : 4;
+    if (p.variant >= 2) {
+        if (p.D == 64)
+            return nw == 8 ? launch_attn16<64, 8>(p, stream) : launch_attn16<64, 4>(p, stream);
+        return nw == 8 ? launch_attn16<128, 8>(p, stream) : launch_attn16<128, 4>(p, stream);
+    }
     if (p.D == 64)
         return nw == 8 ? launch_attn<64, 8>(p, stream) : launch_attn<64, 4>(p, stream);
     return nw == 8 ? launch_attn<128, 8>(p, stream) : launch_attn<128, 4>(p, stream);
