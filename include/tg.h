@@ -370,9 +370,10 @@ int tg_set_raster(int group_m);
 /*
  * Tuning knob for benchmarks: the attention forward's workgroup shape, 0 =
  * four waves (128 queries per workgroup), 1 = eight waves (256 queries, K/V
- * tiles shared by twice the queries); -1 restores the default (1).  Returns
- * the previous setting, or -2 for an unknown value.  Results are identical
- * within the attention tolerance for both.
+ * tiles shared by twice the queries), on 32x32x16 matrix-core products; 2
+ * and 3 = the same two shapes on 16x16x32 products; -1 restores the default
+ * (1).  Returns the previous setting, or -2 for an unknown value.  Results
+ * are identical within the attention tolerance for all four.
  */
 int tg_set_attention_variant(int variant);
 
