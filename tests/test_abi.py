@@ -194,8 +194,9 @@ def test_attention_validation(tg):
     assert call(B=0) == tg.TG_OK and call(Sq=0) == tg.TG_OK and call(H=0) == tg.TG_OK
     assert tg.tg_path_name(tg.TG_PATH_ATTENTION) == "attention"
     assert tg.tg_set_attention_variant(0) == 1
-    assert tg.tg_set_attention_variant(2) == -2
-    assert tg.tg_set_attention_variant(-1) == 0
+    assert tg.tg_set_attention_variant(3) == 0
+    assert tg.tg_set_attention_variant(4) == -2
+    assert tg.tg_set_attention_variant(-1) == 3
 
 
 def test_grouped_query_attention_validation(tg):
