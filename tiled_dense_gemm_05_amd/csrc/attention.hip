@@ -110,6 +110,16 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_ad
                  : "v"(voff), "s"(rsrc), "s"(lds_addr)
                  : "m0");
 }
+// The same with the non-temporal hint, for data read once (the latent cache).
+__device__ __forceinline__ void dma16_nt(i32x4 rsrc, uint32_t voff, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %2\n\t"
+                 "s_nop 0\n\t"
+                 "buffer_load_dwordx4 %0, %1, 0 offen nt lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(lds_addr)
+                 : "m0");
+}
 #pragma clang diagnostic pop
 
 // K tile rows (keys) are read as 16-byte chunks by 32 lanes of consecutive
@@ -752,7 +762,8 @@ hipError_t launch_attn16(const AttnArgs &p, hipStream_t stream)
 //    each SIMD: about 80 % of the LDS's time, the rest of it hidden behind
 //    the matrix cores.
 //  * Tiles of 32 cached rows (36 KiB) are staged in a 4-stage LDS ring by
-//    buffer_load_dwordx4 ... lds; the buffer's record count ends at the
+//    buffer_load_dwordx4 ... lds with the non-temporal hint (each row is
+//    read once: 2-3 % faster per call); the buffer's record count ends at the
 //    range's last visible row, so later rows read as zeros (and are masked
 //    out of the softmax).  Each wave moves 9 of a tile's 36 1-KiB blocks,
 //    one beside each of the first 9 score products two tiles earlier.
@@ -889,7 +900,7 @@ mla_decode_kernel(MlaArgs p)
         return r;
     };
     auto dma = [&](const i32x4 &rsrc, int t, int i) __attribute__((always_inline)) {
-        dma16(rsrc, (voff2[i / 2] >> (16 * (i % 2))) & 0xffffu,
+        dma16_nt(rsrc, (voff2[i / 2] >> (16 * (i % 2))) & 0xffffu,
               lds_base + (uint32_t)((t % STAGES) * TILE * 2 + (wave + NW * i) * 1024));
     };
 
