@@ -38,14 +38,14 @@ LAYOUTS = {"kn": 0, "nk": 1}
 
 # one K group (any tile / stages / swizzle / waves / product shape), the
 # register-staged kernels (and, below, the any-layout and ragged-layout kernels)
-KG1 = [c for c in range(39) if c not in (14, 15, 16, 20)] + [100, 101]
+KG1 = [c for c in range(40) if c not in (14, 15, 16, 20)] + [100, 101]
 # two K groups: K tiles of 64 (configs 14, 20) or of 32 (15, 16) dealt alternately
 KG2_GROUPS = [[14, 20], [15, 16]]
 # configurations that exist for bf16 elements and an (N,K) B
-MODE_KG1 = [8, 29, 12, 32, 34, 36, 38]
+MODE_KG1 = [8, 29, 12, 32, 34, 36, 38, 39]
 # persistent configurations (a workgroup walks a list of tiles, its ring of K
 # tiles running across tile boundaries) and one-tile-per-workgroup ones
-STREAM = [35, 36, 37]
+STREAM = [35, 36, 37, 39]
 ONE_SHOT = [12, 34, 38]
 
 
@@ -195,7 +195,8 @@ def test_stream_configs_bitwise_identical(tg, oracle_lib, batch, M, N, K, shared
     for v in ONE_SHOT + STREAM:
         outs[v], used = run_batched(tg, a_d, b_d, M, N, K, batch, M * K, sB, "f16", "kn", v)
         assert used == "tile128"
-    assert not np.any(outs[36] == 0x7E00), "a cell of C was not written"
+    for v in STREAM:
+        assert not np.any(outs[v] == 0x7E00), f"configuration {v}: a cell of C was not written"
     for e in sorted({0, batch // 2, batch - 1}):
         out = outs[36].reshape(batch, M * N)[e]
         ref, S, Sa = oracle_lib.gemm_ex(a[e * M * K:(e + 1) * M * K],
@@ -220,8 +221,9 @@ def test_stream_modes_and_epilogues_match_one_shot(tg, dtype, layout, act, with_
     bias_d = dev(wl.generate_bias(N, 9, dtype=dtype, scale=0.5)) if with_bias else None
     o34, u34 = run_batched(tg, a_d, b_d, M, N, K, batch, M * K, K * N, dtype, layout, 34,
                            bias_d, act)
-    o36, u36 = run_batched(tg, a_d, b_d, M, N, K, batch, M * K, K * N, dtype, layout, 36,
-                           bias_d, act)
-    assert u34 == u36 == "tile128"
-    assert not np.any(o36 == 0x7E00), "a cell of C was not written"
-    assert np.array_equal(o34, o36), int(np.sum(o34 != o36))
+    for v in (36, 39):
+        o, u = run_batched(tg, a_d, b_d, M, N, K, batch, M * K, K * N, dtype, layout, v, bias_d,
+                           act)
+        assert u34 == u == "tile128"
+        assert not np.any(o == 0x7E00), f"configuration {v}: a cell of C was not written"
+        assert np.array_equal(o34, o), (v, int(np.sum(o34 != o)))

@@ -22,8 +22,10 @@ constexpr int kTile128Default = 38;
 constexpr int kTile256Default = 32;
 constexpr int kRagged256 = 2;       // the ragged kernel's 256x256 and 128x128 configurations
 constexpr int kRagged128 = 3;       // (16x16x32 products)
-constexpr int kTile128ShortK = 12;   // 128x128x32, 2 stages, 4 waves/SIMD: several workgroups per CU
-constexpr int kStream128 = 36;       // persistent workgroups over a list of 128x128 tiles
+// short K: persistent workgroups walking the list of 128x128 tiles, two per
+// CU (39), or one per CU with a deeper ring when the list is very long (36)
+constexpr int kStream128 = 39;
+constexpr int kStream128Long = 36;
 constexpr int kTile64 = 20;          // 64x64x64, 4 stages, two K groups: grids with few tiles
 constexpr int kRegStaged128 = 100;   // register-staged kernels, kept for comparison
 constexpr int kRegStaged256 = 101;
@@ -163,8 +165,8 @@ int choose_path(const tg::GemmArgs &p)
         return (ragged_layout(p) && p.M > 64) ? TG_PATH_RAGGED : TG_PATH_GENERIC;
     if (p.M <= 64 && tg::skinny_layout_ok(p))
         return TG_PATH_SKINNY;
-    // Short K (the batched shapes) stays on the 128x128 kernel, which then
-    // runs several workgroups per CU.
+    // Short K (the batched shapes) stays on 128x128 tiles, walked by
+    // persistent workgroups.
     if (p.K <= 64)
         return TG_PATH_TILE128;
     return prefer_256(p) ? TG_PATH_TILE256 : TG_PATH_TILE128;
@@ -224,12 +226,12 @@ int run(const void *A, const void *B, void *C, const void *bias, bool relu, bool
             v = -1;
         if (v < 0) {
             const int64_t tiles128 = ((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch;
-            // many short problems: persistent workgroups, so that loads,
-            // products and stores of different tiles overlap
+            // short K: persistent workgroups, so that loads, products and
+            // stores of different tiles overlap
             const int cus = tg::host_device_cus();
             v = path == TG_PATH_TILE256            ? kTile256Default
-                : p.K <= 64 && tiles128 >= 4 * cus ? kStream128
-                : p.K <= 64                        ? kTile128ShortK
+                : p.K <= 64 && tiles128 >= 8 * cus ? kStream128Long
+                : p.K <= 64                        ? kStream128
                 : tiles128 < 128                   ? kTile64
                                                    : kTile128Default;
         }

@@ -871,7 +871,12 @@ hipError_t launch_stream(const GemmArgs &p, hipStream_t stream)
     const int cus = host_device_cus();
     if (cus <= 0)
         return hipErrorInvalidDevice;
-    const int64_t grid = items < cus ? items : cus;
+    // workgroups a CU holds at once: by registers (OCC waves per SIMD) and LDS
+    constexpr int kLds = T::RING + T::NW * T::TM * T::TN * 2;
+    constexpr int by_regs = 4 * T::OCC / T::NW > 0 ? 4 * T::OCC / T::NW : 1;
+    constexpr int per_cu = by_regs < (160 * 1024) / kLds ? by_regs : (160 * 1024) / kLds;
+    const int64_t slots = (int64_t)cus * per_cu;
+    const int64_t grid = items < slots ? items : slots;
     hipLaunchKernelGGL((gemm_relu_dma_stream_kernel<T>), dim3((unsigned)grid), dim3(T::NT), 0, stream,
                        p, (int)tilesM, (int)tilesN, (int)items, (int)KT);
     return hipGetLastError();
@@ -1277,15 +1282,19 @@ hipError_t launch_all_configs(int cfg, const GemmArgs &p, hipStream_t stream, in
     // 64x32 wave tiles (a 2x4 wave grid): each wave's B fragments, read by
     // transpose, serve four A fragments, so a k step needs fewer LDS bytes
     case 38: return launch_dma<Mode<Cfg<128, 128, 64, 2, 4, 4, 1, 1, true, 16>, 0>>(p, stream, groupM);
+    // persistent, two workgroups of four waves per CU (80 KiB of LDS each:
+    // a 3-stage ring of 32-wide K tiles and the waves' C areas)
+    case 39: return launch_stream<Mode<Cfg<128, 128, 32, 2, 2, 3, 2>, 0>>(p, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
 
 // bf16 and (N,K)-B instances exist for the configurations the dispatcher
-// picks by default: 256x256 (32), 128x128 (38), short K (12), many short
-// problems (36) and few tiles (20), for the 4x2 wave grid of 128x128 (34) and
-// for the 32x32x16 forms of 32 and 34 (8, 29).
+// picks by default: 256x256 (32), 128x128 (38), short K (39, and 36 for very
+// many tiles) and few tiles (20), for the one-tile-per-workgroup short-K tile
+// (12), the 4x2 wave grid of 128x128 (34) and the 32x32x16 forms of 32 and 34
+// (8, 29).
 template <int MODE>
 hipError_t launch_default_configs(int cfg, const GemmArgs &p, hipStream_t stream, int groupM)
 {
@@ -1298,6 +1307,7 @@ hipError_t launch_default_configs(int cfg, const GemmArgs &p, hipStream_t stream
     case 12: return launch_dma<Mode<Cfg<128, 128, 32, 2, 2, 2, 4>, MODE>>(p, stream, groupM);
     case 20: return launch_dma<Mode<Cfg<64, 64, 64, 2, 2, 4, 1, 2>, MODE>>(p, stream, groupM);
     case 36: return launch_stream<Mode<Cfg<128, 128, 64, 4, 2, 4, 1, 1, true, 16>, MODE>>(p, stream);
+    case 39: return launch_stream<Mode<Cfg<128, 128, 32, 2, 2, 3, 2>, MODE>>(p, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1315,7 +1325,7 @@ bool dma_config_has_mode(int cfg, int mode)
 {
     return mode == 0 ? (cfg >= 0 && cfg < kDmaConfigs)
                      : (cfg == 32 || cfg == 34 || cfg == 8 || cfg == 29 || cfg == 12 || cfg == 20 ||
-                        cfg == 36 || cfg == 38);
+                        cfg == 36 || cfg == 38 || cfg == 39);
 }
 
 hipError_t launch_ragged_config(int cfg, const GemmArgs &p, hipStream_t stream, int groupM)
