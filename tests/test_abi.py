@@ -56,7 +56,7 @@ def test_path_control(tg):
 
 def test_tuning_knobs(tg):
     assert tg.tg_set_tile_variant(29) == -1
-    assert tg.tg_set_tile_variant(40) == -2
+    assert tg.tg_set_tile_variant(43) == -2
     assert tg.tg_set_tile_variant(-1) == 29
     assert tg.tg_set_skinny_variant(10) == -2
     assert tg.tg_set_raster(0) == 8          # default: panels of 8 tile rows

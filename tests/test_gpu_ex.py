@@ -144,6 +144,17 @@ def test_batched_with_shared_bias(tg, oracle_lib, dtype, layout, act, M, N, K, b
 
 
 @pytest.mark.parametrize("dtype,layout", MODES)
+@pytest.mark.parametrize("bias_mode,act", [(None, "relu"), ("aligned", "none")])
+def test_default_dispatch_256x128_tiles(tg, oracle_lib, dtype, layout, bias_mode, act):
+    """2560 x 2520 outputs take two rounds of 128x128 tiles but one of 256x128
+    tiles, which the default dispatch then picks; N and K are ragged against
+    the tile (2520 = 19.7 x 128, 200 = 3 x 64 + 8)."""
+    used, _, _ = ex_case(tg, oracle_lib, 2560, 2520, 200, act, bias_mode, seed=31, dtype=dtype,
+                         layout=layout)
+    assert used == "tile128"
+
+
+@pytest.mark.parametrize("dtype,layout", MODES)
 @pytest.mark.parametrize("act", ["none", "relu"])
 def test_padded_leading_dimensions(tg, oracle_lib, dtype, layout, act):
     ldb_a, ldb_b = (280, 263) if layout == "kn" else (216, 205)

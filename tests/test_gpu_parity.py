@@ -343,7 +343,7 @@ def test_workloads_full_size(tg, oracle_lib, name, n):
 
 # ------------------------------------------------------ every tile configuration
 
-VARIANTS = list(range(40)) + [100, 101]
+VARIANTS = list(range(43)) + [100, 101]
 
 
 @pytest.mark.parametrize("variant", VARIANTS)

@@ -38,11 +38,11 @@ LAYOUTS = {"kn": 0, "nk": 1}
 
 # one K group (any tile / stages / swizzle / waves / product shape), the
 # register-staged kernels (and, below, the any-layout and ragged-layout kernels)
-KG1 = [c for c in range(40) if c not in (14, 15, 16, 20)] + [100, 101]
+KG1 = [c for c in range(43) if c not in (14, 15, 16, 20)] + [100, 101]
 # two K groups: K tiles of 64 (configs 14, 20) or of 32 (15, 16) dealt alternately
 KG2_GROUPS = [[14, 20], [15, 16]]
 # configurations that exist for bf16 elements and an (N,K) B
-MODE_KG1 = [8, 29, 12, 32, 34, 36, 38, 39]
+MODE_KG1 = [8, 29, 12, 32, 34, 36, 38, 39, 41]
 # persistent configurations (a workgroup walks a list of tiles, its ring of K
 # tiles running across tile boundaries) and one-tile-per-workgroup ones
 STREAM = [35, 36, 37, 39]

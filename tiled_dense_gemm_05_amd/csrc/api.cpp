@@ -20,6 +20,8 @@ std::atomic<int> g_tile_variant{-1};
 constexpr int kTile128Default = 38;
 // 256x256x64, 2 stages, 8 waves (2 per SIMD), 16x16x32 products
 constexpr int kTile256Default = 32;
+// 256x128x64, 3 stages, 8 waves (2x4, 128x32 wave tiles), 16x16x32 products
+constexpr int kTile256x128 = 41;
 constexpr int kRagged256 = 2;       // the ragged kernel's 256x256 and 128x128 configurations
 constexpr int kRagged128 = 3;       // (16x16x32 products)
 // short K: persistent workgroups walking the list of 128x128 tiles, two per
@@ -144,9 +146,9 @@ bool ragged_layout(const tg::GemmArgs &p)
 }
 
 // Rounds of one workgroup per compute unit for square tiles of side `t`.
-int64_t tile_rounds(const tg::GemmArgs &p, int64_t t)
+int64_t tile_rounds(const tg::GemmArgs &p, int64_t tm, int64_t tn)
 {
-    const int64_t tiles = ((p.M + t - 1) / t) * ((p.N + t - 1) / t) * p.batch;
+    const int64_t tiles = ((p.M + tm - 1) / tm) * ((p.N + tn - 1) / tn) * p.batch;
     return (tiles + 255) / 256;
 }
 
@@ -156,7 +158,15 @@ int64_t tile_rounds(const tg::GemmArgs &p, int64_t t)
 // long (measured from 2048^2 to 8192^2, K >= 1000); pick the cheaper one.
 bool prefer_256(const tg::GemmArgs &p)
 {
-    return (double)tile_rounds(p, 256) * 2.6 < (double)tile_rounds(p, 128);
+    return (double)tile_rounds(p, 256, 256) * 2.6 < (double)tile_rounds(p, 128, 128);
+}
+
+// A round of 256x128 tiles (twice the work of a 128x128 round) takes about
+// 1.8 times as long (seven shapes from 2048x2048 to 6144x4096, K 1024 and
+// 2048): worth it where it saves whole rounds, e.g. one round instead of two.
+bool prefer_256x128(const tg::GemmArgs &p)
+{
+    return (double)tile_rounds(p, 256, 128) * 1.8 < (double)tile_rounds(p, 128, 128);
 }
 
 int choose_path(const tg::GemmArgs &p)
@@ -233,6 +243,7 @@ int run(const void *A, const void *B, void *C, const void *bias, bool relu, bool
                 : p.K <= 64 && tiles128 >= 8 * cus ? kStream128Long
                 : p.K <= 64                        ? kStream128
                 : tiles128 < 128                   ? kTile64
+                : prefer_256x128(p)                ? kTile256x128
                                                    : kTile128Default;
         }
         const int gm = g_group_m.load(std::memory_order_relaxed);

@@ -121,6 +121,8 @@ struct Cfg {
     // the (K,N) B swizzle that also separates rows 8 apart needs a thread's
     // rows to be 16 apart
     static constexpr int BSWZ = MI == 16 && (NW * B_RPB) % 16 == 0 ? 16 : 32;
+    // the fragment sets alternate between k steps and every tile starts on set 0
+    static_assert(KSTEPS % 2 == 0, "an even number of k steps per tile");
 };
 
 // Element type and B layout of a configuration.  MODE bit 0: bf16 elements
@@ -1285,14 +1287,19 @@ hipError_t launch_all_configs(int cfg, const GemmArgs &p, hipStream_t stream, in
     // persistent, two workgroups of four waves per CU (80 KiB of LDS each:
     // a 3-stage ring of 32-wide K tiles and the waves' C areas)
     case 39: return launch_stream<Mode<Cfg<128, 128, 32, 2, 2, 3, 2>, 0>>(p, stream);
+    // 256x128 tiles of eight waves (one round where 128x128 tiles take two):
+    // 64x64 or 128x32 wave tiles with 16x16x32 products, 64x64 with 32x32x16
+    case 40: return launch_dma<Mode<Cfg<256, 128, 64, 4, 2, 3, 1, 1, true, 16>, 0>>(p, stream, groupM);
+    case 41: return launch_dma<Mode<Cfg<256, 128, 64, 2, 4, 3, 1, 1, true, 16>, 0>>(p, stream, groupM);
+    case 42: return launch_dma<Mode<Cfg<256, 128, 64, 4, 2, 2>, 0>>(p, stream, groupM);
     default: return hipErrorInvalidValue;
     }
 }
 
 
 // bf16 and (N,K)-B instances exist for the configurations the dispatcher
-// picks by default: 256x256 (32), 128x128 (38), short K (39, and 36 for very
-// many tiles) and few tiles (20), for the one-tile-per-workgroup short-K tile
+// picks by default: 256x256 (32), 128x128 (38), 256x128 (41), short K (39, and
+// 36 for very many tiles) and few tiles (20), for the one-tile-per-workgroup short-K tile
 // (12), the 4x2 wave grid of 128x128 (34) and the 32x32x16 forms of 32 and 34
 // (8, 29).
 template <int MODE>
@@ -1308,6 +1315,7 @@ hipError_t launch_default_configs(int cfg, const GemmArgs &p, hipStream_t stream
     case 20: return launch_dma<Mode<Cfg<64, 64, 64, 2, 2, 4, 1, 2>, MODE>>(p, stream, groupM);
     case 36: return launch_stream<Mode<Cfg<128, 128, 64, 4, 2, 4, 1, 1, true, 16>, MODE>>(p, stream);
     case 39: return launch_stream<Mode<Cfg<128, 128, 32, 2, 2, 3, 2>, MODE>>(p, stream);
+    case 41: return launch_dma<Mode<Cfg<256, 128, 64, 2, 4, 3, 1, 1, true, 16>, MODE>>(p, stream, groupM);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1325,7 +1333,7 @@ bool dma_config_has_mode(int cfg, int mode)
 {
     return mode == 0 ? (cfg >= 0 && cfg < kDmaConfigs)
                      : (cfg == 32 || cfg == 34 || cfg == 8 || cfg == 29 || cfg == 12 || cfg == 20 ||
-                        cfg == 36 || cfg == 38 || cfg == 39);
+                        cfg == 36 || cfg == 38 || cfg == 39 || cfg == 41);
 }
 
 hipError_t launch_ragged_config(int cfg, const GemmArgs &p, hipStream_t stream, int groupM)

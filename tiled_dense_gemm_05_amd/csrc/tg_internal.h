@@ -175,7 +175,7 @@ hipError_t launch_tile256(const GemmArgs &p, hipStream_t stream, int groupM);
 // block tile / K tile / stage count; see gemm_dma.hip.
 // Every configuration exists for fp16 with a (K,N) B (mode 0); bf16 and (N,K)
 // B (mode bits 1 and 2) exist for the default configurations only.
-constexpr int kDmaConfigs = 40;
+constexpr int kDmaConfigs = 43;
 hipError_t launch_dma_config(int cfg, const GemmArgs &p, hipStream_t stream, int groupM);
 // Ragged layouts (see gemm_dma.hip): A as for the direct-to-LDS kernels
 // (16-byte aligned rows, K a multiple of 8), B stored (K,N) with any 2-byte
