@@ -109,7 +109,7 @@ def assert_same(outs, ref_key):
     assert not bad, f"outputs differing from {ref_key} (count of differing elements): {bad}"
 
 
-SHAPES = [(520, 392, 1000), (2048, 2048, 2048), (257, 264, 136), (384, 256, 40)]
+SHAPES = [(520, 392, 1000), (2048, 2048, 2048), (257, 264, 136), (384, 256, 40), (264, 392, 440)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)

@@ -302,8 +302,10 @@ __device__ __forceinline__ void issue_one(const LoadPlan<T> &lp, const i32x4 &ra
         dma16(ra, v, stage_addr + (uint32_t)((wave + I * T::NW) * 1024));
     } else {
         constexpr int J = I - T::A_LD;
+        // (K,N) B: a whole K tile (BK rows left or more) needs no row test
         const bool ok = T::BT ? b_rows_left != 0
-                              : (lp.b_row0 + J * T::NW * T::B_RPB) < b_rows_left;
+                              : b_rows_left >= T::BK ||
+                                    (lp.b_row0 + J * T::NW * T::B_RPB) < b_rows_left;
         const uint32_t v = ok ? lp.b_voff[J] : kOutOfRange;
         dma16(rb, v, stage_addr + (uint32_t)(T::A_ELEMS * 2 + (wave + J * T::NW) * 1024));
     }
@@ -355,6 +357,16 @@ __device__ __forceinline__ void inner_steps(typename T::Acc (&acc)[T::FM][T::FN]
         join_b<T>(bh, bf[(KK + 1) & 1]);
         inner_steps<T, KK + 1>(acc, af, bf, lp, ra, rb, a_kok, b_rows_left, stage_addr, wave, As,
                                Bs, wm, wn, lane);
+    }
+}
+
+// f(kt + S, S, whole) for S = S0 .. N-1, S a compile-time constant.
+template <int S, int N, class F, class W>
+__device__ __forceinline__ void for_stages(F &f, int kt, W whole)
+{
+    if constexpr (S < N) {
+        f(kt + S, std::integral_constant<int, S>{}, whole);
+        for_stages<S + 1, N>(f, kt, whole);
     }
 }
 
@@ -473,17 +485,42 @@ gemm_relu_dma_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
         join_b<T>(bh, bf[0]);
     }
 
-    for (int kt = 0; kt < KT; ++kt) {
-        const int stage = kt % T::STAGES;
+    // Iteration kt loads the group's K tile kt + AHEAD.  Its operand
+    // addresses and the K left from its first k advance by a fixed step per
+    // iteration: a few scalar adds instead of a 64-bit product per tile.
+    const int64_t kstep = (int64_t)T::KG * T::BK;
+    const int64_t k_first = ((int64_t)T::AHEAD * T::KG + kg) * T::BK;
+    const int64_t b_adv = T::BT ? kstep : kstep * p.ldb;
+    // descriptors carried from iteration to iteration: only the base moves
+    i32x4 ra_c = make_rsrc(Ab + k_first);
+    i32x4 rb_c = make_rsrc(Bb + (T::BT ? k_first : k_first * p.ldb));
+    const uint64_t a_adv_bytes = (uint64_t)kstep * 2, b_adv_bytes = (uint64_t)b_adv * 2;
+    auto advance = [](i32x4 &r, uint64_t by) __attribute__((always_inline)) {
+        // the 48-bit base sits in words 0-1 with a zero stride above it
+        const uint64_t v = (((uint64_t)(uint32_t)r.y << 32) | (uint32_t)r.x) + by;
+        r.x = (int)(uint32_t)v;
+        r.y = (int)(uint32_t)(v >> 32);
+    };
+    int k_rem = (int)(K - k_first);   // negative past the end; K < 2^31
+    // One iteration.  S is kt % STAGES when it is known at compile time (-1
+    // otherwise): in the unrolled rounds of the ring every stage offset is a
+    // constant.  WHOLE: the K tile it loads lies wholly inside K, so no load
+    // needs a K test.
+    auto iteration = [&](int kt, auto s_ic, auto whole_ic) __attribute__((always_inline)) {
+        constexpr int S = decltype(s_ic)::value;
+        constexpr bool WHOLE = decltype(whole_ic)::value;
+        const int stage = S >= 0 ? S : kt % T::STAGES;
+        // loads of tile kt + AHEAD go to the stage that tile held
+        const int lstage = S >= 0 ? (S + T::AHEAD) % T::STAGES : (kt + T::AHEAD) % T::STAGES;
+        const int nstage = S >= 0 ? (S + 1) % T::STAGES : (kt + 1) % T::STAGES;
         const lds_u16 *As = lds + stage * T::STAGE;
         const lds_u16 *Bs = As + T::A_ELEMS;
-        // loads of tile kt + AHEAD go to the stage that tile held
-        const int kl = kt + T::AHEAD;
-        const int lstage = kl % T::STAGES;
         const uint32_t laddr = lds_base + (uint32_t)(lstage * T::STAGE * 2);
-        const i32x4 ra = rsrc_a(kl), rb = rsrc_b(kl);
-        const bool akok = a_kok(kl);
-        const int bleft = b_left(kl);
+        const i32x4 ra = ra_c, rb = rb_c;
+        const bool akok = WHOLE || lp.a_kcol < k_rem;
+        const int bleft = T::BT ? (int)(WHOLE || lp.b_kcol < k_rem)
+                        : WHOLE ? T::BK
+                                : (k_rem < 0 ? 0 : (k_rem > T::BK ? T::BK : k_rem));
         inner_steps<T>(acc, af, bf, lp, ra, rb, akok, bleft, laddr, wave, As, Bs, wm, wn, lane);
         constexpr int cur = (T::KSTEPS - 1) & 1, nxt = T::KSTEPS & 1;
         // Tile kt+1 has landed once at most WAIT_LAST later loads of this wave
@@ -493,7 +530,6 @@ gemm_relu_dma_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
         wait_vmcnt<T::WAIT_LAST>();
         block_barrier();
         {
-            const int nstage = (kt + 1) % T::STAGES;
             const lds_u16 *An = lds + nstage * T::STAGE;
             s16x4 bh[T::FN][2];
             constexpr int D0 = T::SPREAD ? (T::KSTEPS - 1) * T::DPS : 0;
@@ -501,7 +537,19 @@ gemm_relu_dma_kernel(GemmArgs p, int tilesM, int tilesN, int groupM)
                                   An + T::A_ELEMS, 0, wm, wn, lane, af[nxt], bh);
             join_b<T>(bh, bf[nxt]);
         }
-    }
+        advance(ra_c, a_adv_bytes);
+        advance(rb_c, b_adv_bytes);
+        k_rem -= (int)kstep;
+    };
+    // Rounds of STAGES iterations whose loads all fall on K tiles wholly
+    // inside K (the group's t-th tile is whole for t < K / kstep), then the
+    // rest one at a time with the K tests.
+    const int KTW = (int)(K / kstep);
+    int kt = 0;
+    for (; kt + T::STAGES + T::AHEAD <= KTW; kt += T::STAGES)
+        for_stages<0, T::STAGES>(iteration, kt, std::true_type{});
+    for (; kt < KT; ++kt)
+        iteration(kt, std::integral_constant<int, -1>{}, std::false_type{});
     // loads issued past the end of K must land before the LDS is released
     wait_vmcnt<0>();
 
