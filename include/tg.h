@@ -332,9 +332,11 @@ int tg_last_path(void);
 /*
  * Tuning knob for benchmarks: selects the kernel configuration (block tile,
  * K tile, pipeline depth, matrix-core product shape) that the tile paths use.
- * -1 restores the defaults; 0..34 are the direct-to-LDS configurations (32..34
- * use 16x16x32 products, the rest 32x32x16), 100 and 101 the register-staged
- * 128x128 and 256x256 kernels.  Returns the previous setting, or -2 for an
+ * -1 restores the defaults; 0..42 are the direct-to-LDS configurations (32..38,
+ * 40 and 41 use 16x16x32 products, the rest 32x32x16; 35..37 and 39 are the
+ * persistent form that walks a list of tiles; 40..42 use 256x128 tiles), 100
+ * and 101 the register-staged 128x128 and 256x256 kernels.  Returns the
+ * previous setting, or -2 for an
  * unknown variant (the setting is unchanged).  Results are identical within
  * the accuracy contract for every variant; only speed changes.  22 and 23 are
  * ablations of configuration 0 (operand tiles without the XOR swizzle; a
