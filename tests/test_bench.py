@@ -75,6 +75,16 @@ def test_json_line_contract():
     assert t["rate_at_min"] >= t["rate_at_median"] > 0
     sc = d["sclk_mhz"]
     assert sc is None or (100 < sc["min"] <= sc["median"] <= sc["max"] < 5000)
+    # the other workloads of the hot-path table ride along, each on its own protocol run
+    others = {o["workload"]: o for o in d["other_workloads"]}
+    assert set(others) == {"mid_2048", "batched_1024x128x128x64", "ragged_3001x5003x1000",
+                           "small_512"}
+    for o in list(others.values()) + [d["secondary"]]:
+        assert o["value"] > 0 and o["ms_per_step"] > 0 and o["steps"] == 20
+        orf = o["roofline"]
+        assert orf["bound"] in ("mfma", "hbm") and orf["frac"] == pytest.approx(orf["achieved"] / orf["peak"])
+        assert o["timing"]["trials"] >= 10
+    assert others["mid_2048"]["unit"] == "TFLOP/s" and others["batched_1024x128x128x64"]["unit"] == "GB/s"
 
 
 @pytest.mark.gpu
