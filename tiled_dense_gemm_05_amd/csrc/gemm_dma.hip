@@ -166,22 +166,6 @@ __device__ __forceinline__ int swz_b(int k, int c)
         return c;
 }
 
-// Scheduling hint: alternate one MFMA with one LDS read, then the rest.
-template <int MFMAS, int READS>
-__device__ __forceinline__ void interleave_mfma_lds()
-{
-    constexpr int pairs = MFMAS < READS ? MFMAS : READS;
-#pragma unroll
-    for (int i = 0; i < pairs; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-    }
-    if constexpr (MFMAS > pairs)
-        __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - pairs, 0);
-    if constexpr (READS > pairs)
-        __builtin_amdgcn_sched_group_barrier(0x100, READS - pairs, 0);
-}
-
 // Piece r of the fragments of k step kk: r < FM is the A^T fragment r (lane
 // holds A[row][8 consecutive k], one 16-byte read); FM + 2 fn + hh is half hh
 // of the B^T fragment fn (a transpose read: source lane s of each 16-lane
