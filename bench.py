@@ -6,7 +6,9 @@ operands (compute-bound, measured in TFLOP/s against the dense fp16 MFMA
 peak); the M=16 decode-shaped workload (HBM-bound, GB/s against the HBM peak)
 is reported alongside as a secondary figure, and with the headline workload the
 other workloads (2048^3, the strided batch, the ragged shape, 512^3) follow in
-`other_workloads`, each timed the same way.  Prints one JSON line.
+`other_workloads`, each timed the same way, and the measured NEXT rows (attention
+forward, the latent-attention decode, int4 weights) in `next_rows`, each the object
+its own --attention / --mla / --w4 mode prints.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--no-secondary]
@@ -784,6 +786,76 @@ def summarize_stats(out_md: str, title: str, stats_dir: str, commands: list[str]
     print(f"wrote {out_md}")
 
 
+def attention_line(tg, torch, causal: bool, kv_heads: int, steps: int, warmup: int,
+                   trials: int) -> dict:
+    """One line for the fused attention forward, 4 x 4096 x 32 heads x 128."""
+    B, S, H, D = 4, 4096, 32, 128
+    timing = run_attention(tg, torch, B, S, H, kv_heads, D, causal, steps, warmup, trials)
+    ms = timing["ms_per_step"]
+    # two products of 2*S*S*D flop per (batch, head); half the pairs when causal
+    flops = 4.0 * B * H * S * S * D * (0.5 if causal else 1.0)
+    tflops = flops / (ms * 1e-3) / 1e12
+    name = f"attention_{B}x{S}x{H}x{D}" + (f"_kv{kv_heads}" if kv_heads != H else "")
+    mode = "causal" if causal else "full"
+    log(f"{name} {mode}: {ms * 1e3:.1f} us/call, {tflops:.1f} TFLOP/s")
+    return {
+        "metric": "TFLOP/s fused attention forward", "value": tflops, "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{name}_{mode}", "batch": B, "seq": S, "heads": H,
+                   "kv_heads": kv_heads, "head_dim": D, "causal": causal,
+                   "path": tg.tg_path_name(tg.tg_last_path())},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_F16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / PEAK_F16_TFLOPS, "traffic": None},
+        "timing": timing_fields(timing, None, flops, 1e12)[0]}
+
+
+def mla_line(tg, torch, steps: int, warmup: int, trials: int) -> dict:
+    """One line for the latent-attention decode, 64 x 8192 x 128 heads."""
+    w = wl.MLA_WORKLOAD
+    B, H, Sk = w["B"], w["H"], w["Sk"]
+    timing, path, need = run_mla(tg, torch, steps, warmup, trials)
+    ms = timing["ms_per_step"]
+    # score product over 576 values and value product over 512, per (sequence, head, token)
+    flops = 2.0 * B * H * Sk * (576 + 512)
+    nbytes = 2.0 * (B * Sk * 576 + B * H * 576 + B * H * 512)
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"{w['name']}: {ms * 1e3:.1f} us/call, {tflops:.1f} TFLOP/s, {gbs:.0f} GB/s, "
+        f"workspace {need} bytes")
+    return {
+        "metric": "GB/s latent-attention decode", "value": gbs, "unit": "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w["name"], "batch": B, "heads": H, "seq_k": Sk,
+                   "row": "512+64", "tflops": tflops, "path": path, "splits": -1,
+                   "workspace_bytes": need},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": None},
+        "timing": timing_fields(timing, None, nbytes, 1e9)[0]}
+
+
+def w4_line(tg, torch, dtype: str, steps: int, warmup: int, trials: int) -> dict:
+    """One line for the weight-only int4 GEMM+ReLU at the decode shape."""
+    M, N, K, G = 16, 16384, 8192, 128
+    timing, path, nbuf, nbytes = run_w4(tg, torch, M, N, K, G, steps, warmup, dtype, trials)
+    ms = timing["ms_per_step"]
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"w4 {M}x{N}x{K} g{G}: {ms * 1e3:.1f} us/call, {gbs:.0f} GB/s, path={path}")
+    return {
+        "metric": "GB/s weight-only int4 GEMM+ReLU (decode shape)", "value": gbs,
+        "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dtype, "data": "synthetic",
+        "config": {"workload": f"w4_{M}x{N}x{K}_g{G}", "M": M, "N": N, "K": K,
+                   "group_size": G, "path": path, "weight_copies": nbuf},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": None},
+        "timing": timing_fields(timing, None, nbytes, 1e9)[0]}
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-run":
         # bench.py --summarize-run WORKLOAD ROOT_DIR "cmd1" ...
@@ -903,33 +975,12 @@ def main():
             "timing": timing_fields(timing, None, w.flops, 1e12)[0]}), flush=True)
         return
     if args.attention:
-        B, S, H, D = 4, 4096, 32, 128
         if args.attention_variant != -1:
             tg.tg_set_attention_variant(args.attention_variant)
-        Hkv = args.kv_heads
-        if Hkv <= 0 or H % Hkv:
-            sys.exit(f"--kv-heads must divide {H}")
-        causal = args.attention == "causal"
-        timing = run_attention(tg, torch, B, S, H, Hkv, D, causal, args.steps, args.warmup,
-                               args.trials)
-        ms = timing["ms_per_step"]
-        # two products of 2*S*S*D flop per (batch, head); half the pairs when causal
-        flops = 4.0 * B * H * S * S * D * (0.5 if causal else 1.0)
-        tflops = flops / (ms * 1e-3) / 1e12
-        name = f"attention_{B}x{S}x{H}x{D}" + (f"_kv{Hkv}" if Hkv != H else "")
-        log(f"{name} {args.attention}: {ms * 1e3:.1f} us/call, {tflops:.1f} TFLOP/s")
-        print(json.dumps({
-            "metric": "TFLOP/s fused attention forward", "value": tflops, "unit": "TFLOP/s",
-            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
-            "data": "synthetic",
-            "config": {"workload": f"{name}_{args.attention}", "batch": B,
-                       "seq": S, "heads": H, "kv_heads": Hkv, "head_dim": D, "causal": causal,
-                       "path": tg.tg_path_name(tg.tg_last_path())},
-            "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_F16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": tflops / PEAK_F16_TFLOPS,
-                         "traffic": None},
-            "timing": timing_fields(timing, None, flops, 1e12)[0]}), flush=True)
+        if args.kv_heads <= 0 or 32 % args.kv_heads:
+            sys.exit("--kv-heads must divide 32")
+        print(json.dumps(attention_line(tg, torch, args.attention == "causal", args.kv_heads,
+                                        args.steps, args.warmup, args.trials)), flush=True)
         return
     if args.skinny_splitk:
         w = wl.WORKLOADS["skinny_16x16384x8192"]
@@ -952,46 +1003,13 @@ def main():
     if args.mla:
         if args.mla_splits != -1:
             tg.tg_set_mla_splits(args.mla_splits)
-        w = wl.MLA_WORKLOAD
-        B, H, Sk = w["B"], w["H"], w["Sk"]
-        timing, path, need = run_mla(tg, torch, args.steps, args.warmup, args.trials)
-        ms = timing["ms_per_step"]
-        # score product over 576 values and value product over 512, per (sequence, head, token)
-        flops = 2.0 * B * H * Sk * (576 + 512)
-        nbytes = 2.0 * (B * Sk * 576 + B * H * 576 + B * H * 512)
-        tflops = flops / (ms * 1e-3) / 1e12
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        log(f"{w['name']}: {ms * 1e3:.1f} us/call, {tflops:.1f} TFLOP/s, {gbs:.0f} GB/s, "
-            f"workspace {need} bytes")
-        print(json.dumps({
-            "metric": "GB/s latent-attention decode", "value": gbs, "unit": "GB/s",
-            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
-            "data": "synthetic",
-            "config": {"workload": w["name"], "batch": B, "heads": H, "seq_k": Sk,
-                       "row": "512+64", "tflops": tflops, "path": path,
-                       "splits": args.mla_splits, "workspace_bytes": need},
-            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": gbs / PEAK_HBM_GBS, "traffic": None},
-            "timing": timing_fields(timing, None, nbytes, 1e9)[0]}), flush=True)
+        line = mla_line(tg, torch, args.steps, args.warmup, args.trials)
+        line["config"]["splits"] = args.mla_splits
+        print(json.dumps(line), flush=True)
         return
     if args.w4:
-        M, N, K, G = 16, 16384, 8192, 128
-        timing, path, nbuf, nbytes = run_w4(tg, torch, M, N, K, G, args.steps, args.warmup,
-                                            args.dtype, args.trials)
-        ms = timing["ms_per_step"]
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        log(f"w4 {M}x{N}x{K} g{G}: {ms * 1e3:.1f} us/call, {gbs:.0f} GB/s, path={path}")
-        print(json.dumps({
-            "metric": "GB/s weight-only int4 GEMM+ReLU (decode shape)", "value": gbs,
-            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": args.dtype, "data": "synthetic",
-            "config": {"workload": f"w4_{M}x{N}x{K}_g{G}", "M": M, "N": N, "K": K,
-                       "group_size": G, "path": path, "weight_copies": nbuf},
-            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": gbs / PEAK_HBM_GBS, "traffic": None},
-            "timing": timing_fields(timing, None, nbytes, 1e9)[0]}), flush=True)
+        print(json.dumps(w4_line(tg, torch, args.dtype, args.steps, args.warmup, args.trials)),
+              flush=True)
         return
     w = wl.WORKLOADS[args.workload]
     log(f"workload {w.name}: M={w.M} N={w.N} K={w.K} batch={w.batch}")
@@ -1080,6 +1098,13 @@ def main():
             side_line(wl.WORKLOADS[name], max(args.steps, 20))
             for name in ("mid_2048", "batched_1024x128x128x64", "ragged_3001x5003x1000",
                          "small_512")]
+        # the measured NEXT rows (attention forward full and causal, the
+        # latent-attention decode, int4 weights), their own lines as objects
+        st = max(args.steps, 20)
+        out["next_rows"] = [attention_line(tg, torch, False, 32, st, args.warmup, args.trials),
+                            attention_line(tg, torch, True, 32, st, args.warmup, args.trials),
+                            mla_line(tg, torch, st, args.warmup, args.trials),
+                            w4_line(tg, torch, "f16", st, args.warmup, args.trials)]
 
     if not args.no_cpu_baseline:
         log("timing the oracle on the host cores ...")

@@ -85,6 +85,12 @@ def test_json_line_contract():
         assert orf["bound"] in ("mfma", "hbm") and orf["frac"] == pytest.approx(orf["achieved"] / orf["peak"])
         assert o["timing"]["trials"] >= 10
     assert others["mid_2048"]["unit"] == "TFLOP/s" and others["batched_1024x128x128x64"]["unit"] == "GB/s"
+    # and the measured NEXT rows, each the object its own mode prints
+    nxt = [o["config"]["workload"] for o in d["next_rows"]]
+    assert nxt == ["attention_4x4096x32x128_full", "attention_4x4096x32x128_causal",
+                   "mla_decode_64x128x8192", "w4_16x16384x8192_g128"]
+    for o in d["next_rows"]:
+        assert o["value"] > 0 and o["steps"] == 20 and o["timing"]["trials"] >= 10
 
 
 @pytest.mark.gpu
