@@ -154,6 +154,16 @@ def test_default_dispatch_256x128_tiles(tg, oracle_lib, dtype, layout, bias_mode
     assert used == "tile128"
 
 
+@pytest.mark.parametrize("dtype,layout", [("f16", "kn"), ("bf16", "nk")])
+def test_default_dispatch_256x128_tiles_batched(tg, oracle_lib, dtype, layout):
+    """Two batch entries of 2048 x 2040 outputs: two rounds of 128x128 tiles,
+    one of 256x128 tiles (the grid's second dimension walks the batch); K ragged
+    against the 64-wide K tile, bias and ReLU."""
+    used, _, _ = ex_case(tg, oracle_lib, 2048, 2040, 136, "relu", "aligned", batch=2, seed=37,
+                         dtype=dtype, layout=layout)
+    assert used == "tile128"
+
+
 @pytest.mark.parametrize("dtype,layout", MODES)
 @pytest.mark.parametrize("act", ["none", "relu"])
 def test_padded_leading_dimensions(tg, oracle_lib, dtype, layout, act):
