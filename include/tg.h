@@ -314,8 +314,10 @@ enum {
     TG_PATH_AUTO = 0,
     TG_PATH_NAIVE = 1,      /* one thread per output; a slow, plain kernel */
     TG_PATH_GENERIC = 2,    /* 128x128 tiles, any alignment, masked loads */
-    TG_PATH_TILE128 = 3,    /* 128x128x32 tiles, 256 threads, aligned operands */
-    TG_PATH_TILE256 = 4,    /* 256x256 tiles for large shapes, aligned operands */
+    TG_PATH_TILE128 = 3,    /* aligned operands, mid shapes: 128x128x64 tiles of 8 waves;
+                               256x128 where that saves whole rounds; persistent
+                               workgroups when K <= 64; 64x64 when tiles are few */
+    TG_PATH_TILE256 = 4,    /* 256x256x64 tiles of 8 waves for large shapes, aligned operands */
     TG_PATH_SKINNY = 5,     /* M <= 64: column slices streaming B, K steps dealt to waves */
     TG_PATH_W4 = 6,         /* tg_gemm_w4's int4-weight kernel (reported, not forced) */
     TG_PATH_ATTENTION = 7,  /* the attention entry points' kernel (reported, not forced) */
